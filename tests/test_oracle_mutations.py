@@ -1,0 +1,165 @@
+"""Plant plausible mistakes in a private copy of the oracle (CPU only) and check
+that at least one pin of tests/test_oracle.py fails for each."""
+import importlib.util
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import test_oracle as T
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "rld_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("rld_oracle_mutant", ORACLE_SRC)
+    m = importlib.util.module_from_spec(spec)
+    sys.modules[spec.name] = m
+    spec.loader.exec_module(m)
+    return m
+
+
+def _mut_truncating_round(m):
+    orig = m.round_bf16
+
+    def rb(v):
+        v = np.asarray(v, np.float64)
+        bits = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        return np.where(np.isnan(v), orig(v), bits).astype(np.uint16)
+    m.round_bf16 = rb
+
+
+def _mut_fused_fold(m):
+    def fold_row(x, w, out):
+        xa = m.round_bf16(w.a64() @ m.bf16_to_f64(x))
+        d = m.round_bf16(w.b64() @ m.bf16_to_f64(xa))
+        s = m.bf16_to_f64(out) + np.float64(w.scale) * m.bf16_to_f64(d)
+        return xa, m.round_bf16(s)
+    m.fold_row = fold_row
+
+
+def _mut_transposed_A(m):
+    def fold_row(x, w, out):
+        xa = m.round_bf16(m.bf16_to_f64(x) @ w.a64())
+        d = m.round_bf16(w.b64() @ m.bf16_to_f64(xa))
+        t = np.float32(w.scale) * m.bf16_to_f32(d)
+        return xa, m.round_bf16(m.bf16_to_f32(out) + t)
+    m.fold_row = fold_row
+
+
+def _mut_dropped_term(m):
+    def fold_row(x, w, out):
+        xa = m.round_bf16(w.a64()[:, :-1] @ m.bf16_to_f64(x)[:-1])
+        d = m.round_bf16(w.b64() @ m.bf16_to_f64(xa))
+        t = np.float32(w.scale) * m.bf16_to_f32(d)
+        return xa, m.round_bf16(m.bf16_to_f32(out) + t)
+    m.fold_row = fold_row
+
+
+def _mut_scale_before_round(m):
+    def fold_row(x, w, out):
+        xa = m.round_bf16(w.a64() @ m.bf16_to_f64(x))
+        d = m.round_bf16(np.float64(w.scale) * (w.b64() @ m.bf16_to_f64(xa)))
+        return xa, m.round_bf16(m.bf16_to_f32(out) + m.bf16_to_f32(d))
+    m.fold_row = fold_row
+
+
+def _mut_unrounded_xa(m):
+    def fold_row(x, w, out):
+        xa_exact = w.a64() @ m.bf16_to_f64(x)
+        d = m.round_bf16(w.b64() @ xa_exact)
+        t = np.float32(w.scale) * m.bf16_to_f32(d)
+        return m.round_bf16(xa_exact), m.round_bf16(m.bf16_to_f32(out) + t)
+    m.fold_row = fold_row
+
+
+def _mut_sign(m):
+    def fold_row(x, w, out):
+        xa = m.round_bf16(w.a64() @ m.bf16_to_f64(x))
+        d = m.round_bf16(w.b64() @ m.bf16_to_f64(xa))
+        t = np.float32(w.scale) * m.bf16_to_f32(d)
+        return xa, m.round_bf16(m.bf16_to_f32(out) - t)
+    m.fold_row = fold_row
+
+
+def _mut_rslora_always(m):
+    import math
+    m.scale_for = lambda alpha, rank, rs: np.float32(alpha / math.sqrt(rank))
+
+
+def _mut_gather_token_mod(m):
+    m.gather_row_token = lambda row, top_k: row % top_k
+
+
+def _mut_owner_off_by_one(m):
+    def expert_owner(off, lo, hi):
+        off = np.asarray(off, np.int64)
+        owner = np.full(hi - lo, -1, np.int64)
+        for e in range(len(off) - 1):
+            a, b = max(int(off[e]) + 1, lo), min(int(off[e + 1]) + 1, hi)
+            if a < b:
+                owner[a - lo:b - lo] = e
+        return owner
+    m.expert_owner = expert_owner
+
+
+def _mut_grouped_adapter_by_row(m):
+    orig = m.moe_grouped
+
+    def moe_grouped(pairs, E, k_in, n_out, R, x, xs, xg, nt, off, stid, ra, lo, hi, base, os_):
+        # looks the adapter up with the sorted row index instead of the token
+        fake = None if ra is None else np.resize(ra, max(len(stid), 1))
+        return orig(pairs, E, k_in, n_out, R, x, xs, xg, len(stid) if stid is not None else nt,
+                    off, None if stid is None else np.arange(len(stid), dtype=np.int32) if not xg
+                    else stid, fake, lo, hi, base, os_)
+    m.moe_grouped = moe_grouped
+
+
+def _mut_ignore_out_offset(m):
+    orig = m.bgmv
+    m.bgmv = lambda s, k, n_out, R, x, xs, seq, n, base, off, os_: orig(
+        s, k, n_out, R, x, xs, seq, n, base, 0, os_)
+
+
+def _mut_xa_not_zeroed(m):
+    orig = m.bgmv
+
+    def bgmv(*a):
+        xa, out = orig(*a)
+        seq = a[6]
+        xa[np.asarray(seq[:len(xa)]) < 0] = 0x3F80
+        return xa, out
+    m.bgmv = bgmv
+
+
+def _mut_wc_floor(m):
+    m.grouped_down_wc = lambda lo, hi: max(1, (hi - lo) // 64)
+
+
+def _mut_pack_first_wins(m):
+    orig = m.pack_expert_tables
+
+    def pet(entries):
+        return orig(list(reversed(entries)))
+    m.pack_expert_tables = pet
+
+
+MUTANTS = [_mut_truncating_round, _mut_fused_fold, _mut_transposed_A, _mut_dropped_term,
+           _mut_scale_before_round, _mut_unrounded_xa, _mut_sign, _mut_rslora_always,
+           _mut_gather_token_mod, _mut_owner_off_by_one, _mut_grouped_adapter_by_row,
+           _mut_ignore_out_offset, _mut_xa_not_zeroed, _mut_wc_floor, _mut_pack_first_wins]
+
+
+@pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
+def test_a_pin_catches(mutate):
+    m = fresh_oracle()
+    mutate(m)
+    failed = []
+    for pin in T.PINS:
+        try:
+            pin(m)
+        except Exception:  # an assertion or a shape error both count as caught
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught {mutate.__name__}"
