@@ -1,0 +1,66 @@
+// Host-side helpers shared by the launchers: argument checks and launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rld.h"
+
+namespace rld {
+
+void record_hip_error(hipError_t e);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool mult8(uint64_t v) { return (v & 7u) == 0; }
+inline uint32_t div_ceil(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+
+// Checks common to every route: dims non-zero, multiples of 8, rank bound.
+inline int check_dims(uint32_t k_in, uint32_t n_out, uint32_t max_rank) {
+  if (k_in == 0 || n_out == 0 || max_rank == 0) return RLD_EINVAL;
+  if (max_rank > RLD_MAX_RANK) return RLD_EUNSUPPORTED;
+  if (!mult8(k_in) || !mult8(n_out) || !mult8(max_rank)) return RLD_EALIGN;
+  return RLD_OK;
+}
+
+inline int check_route(const rld_route* r) {
+  if (!r || !r->a_table || !r->b_table || !r->scale_table || r->max_loras == 0) return RLD_EINVAL;
+  return check_dims(r->k_in, r->n_out, r->max_rank);
+}
+
+inline int check_moe_route(const rld_moe_route* r) {
+  if (!r || !r->a_table || !r->b_table || !r->scale_table || r->max_loras == 0 ||
+      r->num_experts == 0)
+    return RLD_EINVAL;
+  return check_dims(r->k_in, r->n_out, r->max_rank);
+}
+
+inline int check_rows(const void* p, uint32_t stride, uint32_t width) {
+  if (!p) return RLD_EINVAL;
+  if (stride < width) return RLD_EINVAL;
+  if (!mult8(stride) || !aligned16(p)) return RLD_EALIGN;
+  return RLD_OK;
+}
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return RLD_ELAUNCH;
+  }
+  return RLD_OK;
+}
+
+// k_in split of the BGMV shrink: a function of (k_in, max_rank) only, so a row's
+// summation order never depends on the batch.
+inline uint32_t bgmv_chunk(uint32_t k_in, uint32_t max_rank) {
+  const uint32_t kc = max_rank <= 16 ? 512u : 1024u;
+  return k_in <= kc ? k_in : kc;
+}
+
+// Output columns per block of the gather expand (two per thread).
+constexpr uint32_t kGatherCols = 512;
+
+// Grid padded to a multiple of 8 for the XCD remap.
+inline uint32_t xcd_grid(uint32_t total) { return 8u * div_ceil(total, 8u); }
+
+}  // namespace rld

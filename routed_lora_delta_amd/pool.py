@@ -1,0 +1,113 @@
+"""Adapter pools and route tables on the device (install time).
+
+The padded A and B of every adapter of one module live in a single device
+buffer (each tensor 256-byte aligned).  Padding goes through
+rld_pad_adapter_host and the tables through rld_route_pack /
+rld_moe_tables_pack (the C ABI); torch only provides the device memory the
+results are copied into.  Objects keep their tensors alive, so the addresses
+in the tables stay valid for the object's lifetime.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence
+
+import numpy as np
+import torch
+
+from . import (check, rld_adapter_entry, rld_moe_route, rld_moe_tables_pack,
+               rld_pad_adapter_host, rld_route, rld_route_pack)
+
+_ALIGN_ELEMS = 128  # 256 bytes of BF16
+
+
+def _round_up(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+def to_device_u16(arr: np.ndarray, device) -> torch.Tensor:
+    """uint16 BF16 bits -> device int16 tensor holding the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device)
+
+
+def from_device_u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+class _Pool:
+    def __init__(self, adapters: Sequence, k_in: int, n_out: int, max_rank: int, device):
+        self.k_in, self.n_out, self.max_rank = k_in, n_out, max_rank
+        a_elems = _round_up(max_rank * k_in, _ALIGN_ELEMS)
+        b_elems = _round_up(n_out * max_rank, _ALIGN_ELEMS)
+        total = max(1, len(adapters)) * (a_elems + b_elems)
+        host = np.zeros(total, np.uint16)
+        offs = []
+        for i, ad in enumerate(adapters):
+            oa = i * (a_elems + b_elems)
+            ob = oa + a_elems
+            A = np.ascontiguousarray(ad.A, np.uint16)
+            B = np.ascontiguousarray(ad.B, np.uint16)
+            check(rld_pad_adapter_host(A, B, ad.rank, k_in, n_out, max_rank,
+                                       host.ctypes.data + 2 * oa, host.ctypes.data + 2 * ob),
+                  "rld_pad_adapter_host")
+            offs.append((oa, ob))
+        self.buf = to_device_u16(host, device)
+        base = self.buf.data_ptr()
+        self.entries = (rld_adapter_entry * max(1, len(adapters)))()
+        for i, (ad, (oa, ob)) in enumerate(zip(adapters, offs)):
+            e = self.entries[i]
+            e.slot = ad.slot
+            e.expert = -1 if ad.expert is None else ad.expert
+            e.a_addr = base + 2 * oa
+            e.b_addr = base + 2 * ob
+            e.rank = ad.rank
+            e.alpha = ad.alpha
+            e.use_rslora = int(ad.use_rslora)
+        self.n_entries = len(adapters)
+        self.nbytes = 2 * total
+
+
+class DenseRoute:
+    """Slot-keyed route of one module (LoraRoute): tables [max_loras]."""
+
+    def __init__(self, adapters: Sequence, max_loras: int, max_rank: int, k_in: int, n_out: int,
+                 device="cuda"):
+        self.pool = _Pool(adapters, k_in, n_out, max_rank, device)
+        a = np.zeros(max_loras, np.uint64)
+        b = np.zeros(max_loras, np.uint64)
+        s = np.zeros(max_loras, np.float32)
+        check(rld_route_pack(self.pool.entries, self.pool.n_entries, max_loras, max_rank, a, b, s),
+              "rld_route_pack")
+        self.a_host, self.b_host, self.scale_host = a, b, s
+        self.a_table = torch.from_numpy(a.view(np.int64).copy()).to(device)
+        self.b_table = torch.from_numpy(b.view(np.int64).copy()).to(device)
+        self.scale_table = torch.from_numpy(s.copy()).to(device)
+        self.route = rld_route(self.a_table.data_ptr(), self.b_table.data_ptr(),
+                               self.scale_table.data_ptr(), max_loras, k_in, n_out, max_rank)
+
+    def set_table_entry(self, slot: int, a_addr=None, b_addr=None):
+        """Overwrite one table entry on the device (tests of the 0 = base-only rule)."""
+        if a_addr is not None:
+            self.a_table[slot] = int(np.int64(np.uint64(a_addr)))
+        if b_addr is not None:
+            self.b_table[slot] = int(np.int64(np.uint64(b_addr)))
+
+
+class MoeRoute:
+    """Expert routing tables of one MoE projection: [max_loras][num_experts]."""
+
+    def __init__(self, adapters: Sequence, max_loras: int, num_experts: int, max_rank: int,
+                 k_in: int, n_out: int, device="cuda"):
+        self.pool = _Pool(adapters, k_in, n_out, max_rank, device)
+        n = max_loras * num_experts
+        a = np.zeros(n, np.uint64)
+        b = np.zeros(n, np.uint64)
+        s = np.zeros(n, np.float32)
+        check(rld_moe_tables_pack(self.pool.entries, self.pool.n_entries, max_loras, num_experts,
+                                  max_rank, a, b, s), "rld_moe_tables_pack")
+        self.a_table = torch.from_numpy(a.view(np.int64).copy()).to(device)
+        self.b_table = torch.from_numpy(b.view(np.int64).copy()).to(device)
+        self.scale_table = torch.from_numpy(s.copy()).to(device)
+        self.route = rld_moe_route(self.a_table.data_ptr(), self.b_table.data_ptr(),
+                                   self.scale_table.data_ptr(), max_loras, num_experts, k_in,
+                                   n_out, max_rank)

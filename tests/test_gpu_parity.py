@@ -1,0 +1,305 @@
+"""GPU parity of every hot-path entry point against the CPU oracle.
+
+Every case calls librld.so through the C ABI on cuda:0 and compares, element by
+element, with the oracle on the same seeded inputs: xa within 1 BF16 ulp,
+folded outputs within 2 BF16 ulp or 1e-3 absolute, and bit-exact everything
+that is routing: base rows, xa rows of base rows, regions outside [0, n_out)
+of each row, guard bands around every output buffer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import routed_lora_delta_amd as R
+import workloads as W
+from gpu_util import (BgmvRun, GroupedRun, abs_sums_bgmv, abs_sums_gather, abs_sums_grouped,
+                      abs_sums_rows, assert_out_close, assert_xa_close, compare_bgmv, dev_i32,
+                      expand_depth, oracle_gather, oracle_grouped_window, require_gpu,
+                      run_gather, say, shrink_depth)
+from routed_lora_delta_amd.pool import DenseRoute, from_device_u16, to_device_u16
+
+pytestmark = pytest.mark.gpu
+
+
+def _base_rows_xa_zero(wl, run):
+    for i, c in enumerate(wl.calls):
+        xa = run.xa_by_call[i]
+        for r in range(wl.n):
+            s = int(wl.seq_slot[r])
+            if not (0 <= s < c.max_loras and any(a.slot == s for a in c.adapters)):
+                assert np.all(xa[r] == 0), f"xa row {r} of a base row is not zero"
+
+
+# ------------------------------------------------------------------- BGMV ----
+
+def test_bgmv_tiny_config():
+    dev = require_gpu()
+    wl = W.bgmv_tiny()
+    say(f"case: {wl.name} seq={wl.seq_slot.tolist()}")
+    run = BgmvRun(wl, dev)
+    run.run_all()
+    compare_bgmv(run, wl.name)
+    _base_rows_xa_zero(wl, run)
+
+
+BGMV_SHAPES = [
+    # n, k_in, n_out, max_rank, max_loras, ranks, absent slots
+    (1, 256, 256, 8, 2, (4, 8), ()),
+    (5, 1000, 264, 16, 3, (8, 16), ()),
+    (37, 4096, 1032, 16, 16, (8, 16), (3, 7)),
+    (70, 2056, 520, 24, 5, (8, 24), (1,)),
+    (130, 12288, 4096, 64, 8, (8, 16, 32, 64), ()),
+    (300, 512, 768, 128, 4, (64, 128), ()),
+    (600, 1536, 264, 32, 40, (16, 32), (0, 39)),
+    (1200, 256, 264, 16, 2, (8, 16), ()),
+]
+
+
+@pytest.mark.parametrize("shape", BGMV_SHAPES, ids=lambda s: f"n{s[0]}k{s[1]}o{s[2]}r{s[3]}")
+def test_bgmv_shapes(shape):
+    dev = require_gpu()
+    n, k_in, n_out, R_, L, ranks, absent = shape
+    wl = W.bgmv_custom(n, n, k_in, n_out, R_, L, ranks, base_frac=0.1, absent=absent,
+                       zipf=1.1 if n > 100 else None)
+    say(f"case: bgmv {shape}")
+    run = BgmvRun(wl, dev)
+    run.run_all()
+    compare_bgmv(run, str(shape))
+    _base_rows_xa_zero(wl, run)
+
+
+def test_bgmv_out_of_range_slots_and_missing_tables():
+    """Slots >= max_loras, negative slots and slots whose A or B entry is 0
+    leave their rows untouched and write zero xa."""
+    dev = require_gpu()
+    wl = W.bgmv_custom(9, 12, 520, 264, 16, 4, (16,), base_frac=0.0)
+    wl.seq_slot[:] = np.array([0, 1, 2, 3, 4, 77, -1, -9, 1, 2, 3, 0], np.int32)
+    say("case: bgmv out-of-range slots / zeroed table entries")
+    run = BgmvRun(wl, dev)
+    run.routes[0].set_table_entry(2, b_addr=0)  # slot 2: B entry 0 -> base only
+    run.routes[0].set_table_entry(3, a_addr=0)  # slot 3: A entry 0 -> base only
+    run.run_all()
+    c = wl.calls[0]
+    slots = O.pack_slots(c.adapters, c.max_loras, c.max_rank)
+    slots[2] = O.SlotWeights(slots[2].A, None, slots[2].scale)
+    slots[3] = O.SlotWeights(None, slots[3].B, slots[3].scale)
+    xa_o, out_o = O.bgmv(slots, c.k_in, c.n_out, c.max_rank, wl.buffers["x"], c.x_row_stride,
+                         wl.seq_slot, wl.n, wl.buffers["out"], 0, c.n_out)
+    out_g = run.outputs()["out"]
+    assert_xa_close(run.xa_by_call[0], xa_o, "xa", abs_sums_bgmv(wl, c),
+                    shrink_depth("bgmv", c.k_in, c.max_rank))
+    assert_out_close(out_g, out_o, "out")
+    for r, s in enumerate(wl.seq_slot):
+        row = slice(r * c.n_out, (r + 1) * c.n_out)
+        if s not in (0, 1):
+            assert np.array_equal(out_g[row], wl.buffers["out"][row])
+            assert np.all(run.xa_by_call[0][r] == 0)
+
+
+def test_bgmv_batched_equals_single_rows():
+    """BGMV over n rows is bit-identical to n calls with n = 1 on offset
+    pointers (xa and folded output)."""
+    dev = require_gpu()
+    for n, k_in, n_out, R_, ranks in ((64, 4096, 1024, 16, (8, 16)), (200, 12288, 520, 64, (8, 64))):
+        wl = W.bgmv_custom(11, n, k_in, n_out, R_, 8, ranks, base_frac=0.1, zipf=1.1)
+        say(f"case: batched vs single rows n={n} k_in={k_in}")
+        run = BgmvRun(wl, dev)
+        run.run_all()
+        batched_out = run.outputs()["out"]
+        batched_xa = run.xa_by_call[0]
+        c = wl.calls[0]
+        single = BgmvRun(wl, dev)
+        xa1 = torch.zeros(R_ + 8, dtype=torch.int16, device=dev)
+        ws_b = R.rld_bgmv_workspace_bytes(1, k_in, R_)
+        ws1 = torch.zeros(max(ws_b, 16) // 4 + 4, dtype=torch.float32, device=dev)
+        xas = []
+        for i in range(n):
+            R.check(R.rld_bgmv(single.routes[0].route, single.bufs["x"].ptr(i * c.x_row_stride),
+                               c.x_row_stride, single.seq.data_ptr() + 4 * i, 1,
+                               single.bufs["out"].ptr(i * c.out_row_stride), c.out_row_stride,
+                               xa1, ws1, ws_b), "single-row bgmv")
+            torch.cuda.synchronize()
+            xas.append(from_device_u16(xa1)[:R_].copy())
+        assert np.array_equal(np.stack(xas), batched_xa)
+        assert np.array_equal(single.outputs()["out"], batched_out)
+
+
+def test_bgmv_delta_stage():
+    """The expand's delta (observed with scale 1 and base 0) is within 1 ulp of
+    the oracle's delta computed from the GPU's own xa."""
+    dev = require_gpu()
+    n, k_in, n_out, R_ = 50, 4096, 4096, 16
+    rng = W.rng_for(5, salt=3)
+    ads = [W.make_adapter(rng, s, r, k_in, n_out, float(r), False) for s, r in enumerate((16, 8, 12))]
+    seq = rng.integers(-1, 3, size=n).astype(np.int32)
+    x = W._normal(rng, (n, k_in)).ravel()
+    zero = np.zeros(n * n_out, np.uint16)
+    wl = W.BgmvWorkload("delta", n, seq, {"x": x, "out": zero},
+                        [W.BgmvCall("p", k_in, n_out, R_, 3, ads, "x", k_in, "out", 0, n_out)])
+    say("case: delta stage")
+    run = BgmvRun(wl, dev)
+    run.run_all()
+    xa_g = run.xa_by_call[0]
+    delta_g = run.outputs()["out"].reshape(n, n_out)
+    slots = O.pack_slots(ads, 3, R_)
+    for i in range(n):
+        s = int(seq[i])
+        if s < 0:
+            assert np.all(delta_g[i] == 0)
+            continue
+        d_o = O.round_bf16(slots[s].b64() @ O.bf16_to_f64(xa_g[i]))
+        assert_xa_close(delta_g[i], d_o, f"delta row {i}",
+                        abs_sums_rows(xa_g[i][None], slots[s].B)[0], expand_depth("bgmv", R_))
+
+
+def test_bgmv_attn_decode_config():
+    """Qwen3-8B attention side: q contiguous, k/v folded inside [Q|K|V] rows."""
+    dev = require_gpu()
+    wl = W.bgmv_attn_decode()
+    say(f"case: {wl.name}")
+    run = BgmvRun(wl, dev)
+    run.run_all()
+    compare_bgmv(run, wl.name)
+    _base_rows_xa_zero(wl, run)
+
+
+def test_bgmv_ffn_decode_config():
+    dev = require_gpu()
+    wl = W.bgmv_ffn_decode()
+    say(f"case: {wl.name}")
+    run = BgmvRun(wl, dev)
+    run.run_all()
+    compare_bgmv(run, wl.name)
+    _base_rows_xa_zero(wl, run)
+
+
+# ------------------------------------------------------------------ gather ---
+
+@pytest.mark.parametrize("variant", ["config", "null_adapter", "ragged"])
+def test_moe_gather(variant):
+    dev = require_gpu()
+    if variant == "config":
+        wl = W.moe_gather()
+        ra = "wl"
+    elif variant == "null_adapter":
+        wl = W.moe_gather(num_tokens=20, top_k=4, num_experts=16, k_in=264, n_out=1032,
+                          max_loras=1, n_adapted=10, max_rank=16)
+        ra = None
+    else:
+        wl = W.moe_gather(num_tokens=13, top_k=6, num_experts=40, k_in=1000, n_out=520,
+                          max_loras=5, n_adapted=25, ranks=(8, 24), max_rank=24)
+        wl.indices[3] = -1
+        wl.indices[10] = 999
+        ra = "wl"
+    say(f"case: gather {variant} {wl.name}")
+    xa_g, out_g = run_gather(wl, dev, ra)
+    xa_o, out_o = oracle_gather(wl, ra)
+    assert_xa_close(xa_g, xa_o, "gather xa", abs_sums_gather(wl, ra),
+                    shrink_depth("gather", wl.k_in, wl.max_rank))
+    assert_out_close(out_g, out_o, "gather out")
+    inactive = np.all(xa_o == 0, axis=1)
+    base2 = wl.base.reshape(wl.n_rows, wl.n_out)
+    assert np.array_equal(out_g.reshape(wl.n_rows, wl.n_out)[inactive], base2[inactive])
+    assert np.all(xa_g[inactive] == 0)
+
+
+# ----------------------------------------------------------------- grouped ---
+
+def _small_grouped(seed=4, num_tokens=300, **kw):
+    args = dict(num_tokens=num_tokens, top_k=4, num_experts=16, hidden=520, inter=264,
+                max_loras=3, n_adapted=12, ranks=(8, 16, 32), max_rank=32, cap=256)
+    args.update(kw)
+    return W.moe_grouped(seed, **args)
+
+
+@pytest.mark.parametrize("proj", ["down", "gate"])
+@pytest.mark.parametrize("adapter_mode", ["row_adapter", "null"])
+def test_moe_grouped_small(proj, adapter_mode):
+    dev = require_gpu()
+    wl = _small_grouped(projections=(proj,), max_loras=1 if adapter_mode == "null" else 3)
+    p = wl.projections[0]
+    ra = "wl" if adapter_mode == "row_adapter" else None
+    say(f"case: grouped small {proj} {adapter_mode}")
+    run = GroupedRun(wl, p, dev, cap=wl.cap, row_adapter=ra)
+    xas = run.run()
+    out_g = run.base.body()
+    base = p.base.ravel().copy()
+    for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
+        xa_o, base = oracle_grouped_window(wl, p, lo, hi, base, ra)
+        assert_xa_close(xa_g, xa_o, f"grouped xa [{lo},{hi})",
+                        abs_sums_grouped(wl, p, lo, hi, ra),
+                        shrink_depth("grouped", p.k_in, wl.max_rank))
+        assert np.all(xa_g[np.all(xa_o == 0, axis=1)] == 0)
+    assert_out_close(out_g, base, "grouped out")
+    unchanged_o = base == p.base.ravel()
+    # rows the oracle leaves untouched must be bit-identical on the GPU too
+    rows_o = unchanged_o.reshape(wl.te, p.n_out).all(axis=1)
+    assert np.array_equal(out_g.reshape(wl.te, p.n_out)[rows_o],
+                          p.base.reshape(wl.te, p.n_out)[rows_o])
+
+
+def test_moe_grouped_window_union_bit_exact():
+    """A full-window call equals the union of its chunk windows, bit for bit,
+    for caps that are and are not multiples of 64."""
+    dev = require_gpu()
+    wl = _small_grouped(projections=("down", "gate"), cap=2048)
+    for p in wl.projections:
+        say(f"case: window union {p.name}")
+        full = GroupedRun(wl, p, dev, cap=wl.te)
+        xa_full = full.run([(0, wl.te)])[0]
+        out_full = full.base.body()
+        for cap in (64, 100, 333):
+            part = GroupedRun(wl, p, dev, cap=cap)
+            xas = part.run(O.grouped_down_windows(wl.te, cap))
+            assert np.array_equal(np.concatenate(xas), xa_full), cap
+            assert np.array_equal(part.base.body(), out_full), cap
+
+
+def test_moe_grouped_edge_windows():
+    """Empty window (launches one m-tile, writes nothing), a single-row window,
+    and a window over rows outside every expert span."""
+    dev = require_gpu()
+    wl = _small_grouped(projections=("down",))
+    p = wl.projections[0]
+    say("case: grouped edge windows")
+    run = GroupedRun(wl, p, dev, cap=256)
+    run.run([(50, 50)])
+    assert np.array_equal(run.base.body(), p.base.ravel())
+    xas = run.run([(77, 78)])
+    xa_o, out_o = oracle_grouped_window(wl, p, 77, 78, p.base.ravel().copy())
+    assert_xa_close(xas[0], xa_o, "single row xa", abs_sums_grouped(wl, p, 77, 78),
+                    shrink_depth("grouped", p.k_in, wl.max_rank))
+    assert_out_close(run.base.body(), out_o, "single row out")
+    # offsets that put the last 40 rows outside every span
+    off = wl.expert_offsets.copy()
+    off[-1] = off[-1] - 40
+    off = np.minimum(off, off[-1])
+    run2 = GroupedRun(wl, p, dev, cap=wl.te)
+    run2.off = dev_i32(off, dev)
+    run2.run([(0, wl.te)])
+    wl2 = W.MoeGroupedWorkload(**{**wl.__dict__, "expert_offsets": off})
+    xa_o2, out_o2 = oracle_grouped_window(wl2, p, 0, wl.te, p.base.ravel().copy())
+    assert_out_close(run2.base.body(), out_o2, "rows outside spans")
+    tail = slice((wl.te - 40) * p.n_out, wl.te * p.n_out)
+    assert np.array_equal(run2.base.body()[tail], p.base.ravel()[tail])
+
+
+def test_determinism_repeat_runs():
+    dev = require_gpu()
+    wl = _small_grouped(projections=("gate",))
+    p = wl.projections[0]
+    say("case: determinism")
+    outs = []
+    for _ in range(2):
+        run = GroupedRun(wl, p, dev, cap=512)
+        run.run()
+        outs.append(run.base.body())
+    assert np.array_equal(outs[0], outs[1])
+    wlb = W.bgmv_custom(3, 100, 4096, 1024, 16, 8, (8, 16), zipf=1.1)
+    o2 = []
+    for _ in range(2):
+        r = BgmvRun(wlb, dev)
+        r.run_all()
+        o2.append(r.outputs()["out"])
+    assert np.array_equal(o2[0], o2[1])
