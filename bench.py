@@ -1,0 +1,461 @@
+"""Throughput of the routed LoRA fold on one MI355X.
+
+One step is one pass of every hot-path call over one batch of seeded synthetic
+inputs shaped like the routed-LoRA workloads:
+  attention decode BGMV   n=64, hidden 4096, q/k/v/o (k/v inside [Q|K|V] rows)
+  FFN decode BGMV         n=256, gate/up 4096->12288, down 12288->4096, 32 slots
+  MoE decode gather fold  32 tokens x top-8 of 128 experts, down 768->2048
+  MoE grouped prefill     4096 tokens x top-8, te=32768 sorted rows, windows of
+                          8192; down 768->2048 and gate/up 2048->768 (x gather)
+Every call goes through librld.so's C ABI on torch's current stream.
+
+Timing.  The step is captured once as a HIP graph; timed region A replays it K
+times back to back and its wall clock gives ms_per_step and the value.  Timed
+regions B and C time every call with HIP events on the launch stream: the
+grouped-window calls are issued eagerly, each between two events, right after
+a replay of the captured BGMV+gather part (region B), and the BGMV and gather
+calls the same way after a replay of the captured grouped part (region C), so
+the host is always ahead of the GPU and an event pair brackets exactly one
+call.  The kernel with the largest total time is reported against its
+roofline: achieved = its algorithmic bytes per launch / its mean launch
+duration (a BGMV shrink call includes its k-split reduce launch).
+Algorithmic bytes are counted from the actual inputs: x rows that fold, A and
+B of each distinct (slot[, expert]) pair a call touches, the base rows read
+and written, xa written and read, and the index arrays.
+
+The CPU oracle (test infrastructure) is timed on a bounded sample of the same
+step for the cpu_baseline field only.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed LoRA fold rows/s + achieved HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+# ------------------------------------------------------------- byte counts --
+
+def _bgmv_active(wl, c):
+    have = {a.slot for a in c.adapters}
+    act = np.array([int(s) in have for s in wl.seq_slot])
+    slots = {int(s) for s, a in zip(wl.seq_slot, act) if a}
+    return act, slots
+
+
+def bgmv_bytes(wl, c):
+    act, slots = _bgmv_active(wl, c)
+    n_act, S, R = int(act.sum()), len(slots), c.max_rank
+    idx = 4 * wl.n
+    shrink = 2 * (n_act * c.k_in + S * R * c.k_in + wl.n * R) + idx
+    expand = 2 * (S * c.n_out * R + n_act * R + 2 * n_act * c.n_out) + idx
+    flops = 2 * n_act * R * (c.k_in + c.n_out)
+    return shrink, expand, flops, n_act
+
+
+def gather_bytes(wl):
+    pairs = {(a.slot, a.expert) for a in wl.adapters}
+    act, S = 0, set()
+    for rho in range(wl.n_rows):
+        s = int(wl.row_adapter[rho // wl.top_k]) if wl.row_adapter is not None else 0
+        key = (s, int(wl.indices[rho]))
+        if key in pairs:
+            act += 1
+            S.add(key)
+    R = wl.max_rank
+    idx = 4 * (wl.n_rows + wl.num_tokens)
+    shrink = 2 * (act * wl.k_in + len(S) * R * wl.k_in + wl.n_rows * R) + idx
+    expand = 2 * (len(S) * wl.n_out * R + act * R + 2 * act * wl.n_out) + idx
+    return shrink, expand, 2 * act * R * (wl.k_in + wl.n_out), act
+
+
+def grouped_window_bytes(wl, p, lo, hi):
+    pairs = {(a.slot, a.expert) for a in p.adapters}
+    toks = wl.sorted_token_ids[lo:hi]
+    exps = wl.sorted_expert[lo:hi]
+    slots = (wl.row_adapter[toks] if wl.row_adapter is not None
+             else np.zeros(hi - lo, np.int32))
+    act = np.array([(int(s), int(e)) in pairs for s, e in zip(slots, exps)], bool)
+    S = len({(int(s), int(e)) for s, e, a in zip(slots, exps, act) if a})
+    n_act, R, nw = int(act.sum()), wl.max_rank, hi - lo
+    x_rows = len(set(toks[act].tolist())) if p.x_gather else n_act
+    idx = 4 * (2 * nw + wl.num_experts + 1)
+    shrink = 2 * (x_rows * p.k_in + S * R * p.k_in + nw * R) + idx
+    expand = 2 * (S * p.n_out * R + n_act * R + 2 * n_act * p.n_out) + idx
+    return shrink, expand, 2 * n_act * R * (p.k_in + p.n_out), n_act
+
+
+# ------------------------------------------------------------------ GPU side --
+
+class Step:
+    """Device state of the whole step and the ordered list of its calls."""
+
+    def __init__(self, dev, workloads):
+        import torch
+
+        import routed_lora_delta_amd as R
+        from routed_lora_delta_amd.pool import DenseRoute, MoeRoute, to_device_u16
+
+        self.R, self.torch = R, torch
+        self.calls = []  # (label, kernel name, fn, algorithmic bytes, flops, rows)
+        self.rows = 0
+        keep = []
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+        for tag, wl in workloads:
+            if tag in ("attn", "ffn"):
+                seq = i32(wl.seq_slot)
+                bufs = {k: to_device_u16(v, dev) for k, v in wl.buffers.items()}
+                rmax = max(c.max_rank for c in wl.calls)
+                xa = torch.zeros(wl.n * rmax + 8, dtype=torch.int16, device=dev)
+                wsb = max(R.rld_bgmv_workspace_bytes(wl.n, c.k_in, c.max_rank) for c in wl.calls)
+                ws = torch.zeros(max(wsb, 16) // 4 + 4, dtype=torch.float32, device=dev)
+                keep += [seq, bufs, xa, ws]
+                for c in wl.calls:
+                    rt = DenseRoute(c.adapters, c.max_loras, c.max_rank, c.k_in, c.n_out, dev)
+                    keep.append(rt)
+                    sb, eb, fl, _ = bgmv_bytes(wl, c)
+                    x = bufs[c.x_buf].data_ptr()
+                    out = bufs[c.out_buf].data_ptr() + 2 * c.out_offset
+
+                    def shrink(rt=rt, c=c, x=x, seq=seq, xa=xa, ws=ws, wsb=wsb, n=wl.n):
+                        return R.rld_bgmv_shrink(rt.route, x, c.x_row_stride, seq, n, xa, ws, wsb)
+
+                    def expand(rt=rt, c=c, out=out, seq=seq, xa=xa, n=wl.n):
+                        return R.rld_bgmv_expand_fold(rt.route, xa, seq, n, out, c.out_row_stride)
+
+                    self.calls.append((f"{tag}.{c.module}.shrink", "bgmv_shrink_kernel", shrink,
+                                       sb, fl / 2, wl.n))
+                    self.calls.append((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", expand,
+                                       eb, fl / 2, 0))
+                    self.rows += wl.n
+            elif tag == "gather":
+                rt = MoeRoute(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank, wl.k_in,
+                              wl.n_out, dev)
+                x = to_device_u16(wl.x.ravel(), dev)
+                base = to_device_u16(wl.base.ravel(), dev)
+                idx = i32(wl.indices)
+                rad = i32(wl.row_adapter)
+                xa = torch.zeros(wl.n_rows * wl.max_rank + 8, dtype=torch.int16, device=dev)
+                keep += [rt, x, base, idx, rad, xa]
+                sb, eb, fl, _ = gather_bytes(wl)
+                def gshrink(rt=rt, x=x, idx=idx, rad=rad, xa=xa, wl=wl):
+                    return R.rld_moe_gather_shrink(rt.route, x, wl.k_in, idx, rad, wl.top_k,
+                                                   wl.n_rows, xa)
+
+                def gexpand(rt=rt, base=base, idx=idx, rad=rad, xa=xa, wl=wl):
+                    return R.rld_moe_gather_expand_fold(rt.route, xa, idx, rad, wl.top_k,
+                                                        wl.n_rows, base, wl.n_out)
+                self.calls.append(("gather.down.shrink", "gather_shrink_kernel", gshrink, sb,
+                                   fl / 2, wl.n_rows))
+                self.calls.append(("gather.down.expand", "gather_expand_kernel", gexpand, eb,
+                                   fl / 2, 0))
+                self.rows += wl.n_rows
+            elif tag == "grouped":
+                off = i32(wl.expert_offsets)
+                stid = i32(wl.sorted_token_ids)
+                rad = i32(wl.row_adapter)
+                xa = torch.zeros(wl.cap * wl.max_rank + 8, dtype=torch.int16, device=dev)
+                keep += [off, stid, rad, xa]
+                wins = [(k * wl.cap, min((k + 1) * wl.cap, wl.te))
+                        for k in range(-(-wl.te // wl.cap))]
+                for p in wl.projections:
+                    rt = MoeRoute(p.adapters, wl.max_loras, wl.num_experts, wl.max_rank, p.k_in,
+                                  p.n_out, dev)
+                    x = to_device_u16(p.x.ravel(), dev)
+                    base = to_device_u16(p.base.ravel(), dev)
+                    keep += [rt, x, base]
+                    for lo, hi in wins:
+                        sb, eb, fl, _ = grouped_window_bytes(wl, p, lo, hi)
+
+                        def shrink(rt=rt, x=x, p=p, lo=lo, hi=hi, off=off, stid=stid, rad=rad,
+                                   xa=xa, wl=wl):
+                            return R.rld_moe_grouped_shrink(rt.route, x, p.k_in, p.x_gather,
+                                                            wl.num_tokens, off, wl.num_experts,
+                                                            stid, rad, lo, hi, xa, wl.cap)
+
+                        def expand(rt=rt, base=base, p=p, lo=lo, hi=hi, off=off, stid=stid,
+                                   rad=rad, xa=xa, wl=wl):
+                            return R.rld_moe_grouped_expand_fold(rt.route, xa, wl.num_tokens, off,
+                                                                 wl.num_experts, stid, rad, lo,
+                                                                 hi, base, p.n_out)
+
+                        self.calls.append((f"grouped.{p.name}.[{lo},{hi}).shrink",
+                                           "grouped_shrink_kernel", shrink, sb, fl / 2, hi - lo))
+                        self.calls.append((f"grouped.{p.name}.[{lo},{hi}).expand",
+                                           "grouped_expand_kernel", expand, eb, fl / 2, 0))
+                    self.rows += wl.te
+        self._keep = keep
+        self.bytes = sum(c[3] for c in self.calls)
+        self.flops = sum(c[4] for c in self.calls)
+
+    def enqueue(self, events=None):
+        """Issue every call on the current stream; events[i] is recorded before
+        call i and events[-1] after the last call."""
+        for i, (label, _, fn, _, _, _) in enumerate(self.calls):
+            if events is not None:
+                events[i].record()
+            st = fn()
+            if st != 0:
+                raise RuntimeError(f"{label}: {self.R.rld_status_string(st)}")
+        if events is not None:
+            events[-1].record()
+
+
+def select_workloads(name):
+    import workloads as W
+    out = []
+    if name in ("step", "attn"):
+        out.append(("attn", W.bgmv_attn_decode()))
+    if name in ("step", "ffn"):
+        out.append(("ffn", W.bgmv_ffn_decode()))
+    if name in ("step", "gather"):
+        out.append(("gather", W.moe_gather()))
+    if name in ("step", "grouped"):
+        out.append(("grouped", W.moe_grouped()))
+    return out
+
+
+WORKLOAD_NAMES = {
+    "step": "routed-fold step: attn-decode BGMV q/k/v/o n=64 h4096 r16 L16 + ffn-decode BGMV "
+            "gate/up/down n=256 4096x12288 r64 L32 + MoE gather down 32tok top8 E128 768->2048 "
+            "r16 L8 + MoE grouped down/gate/up 4096tok top8 E128 te32768 cap8192 r32 L4",
+    "attn": "attn-decode BGMV q/k/v/o n=64 hidden=4096 r16 L16 ([Q|K|V] stride 6144)",
+    "ffn": "ffn-decode BGMV gate/up/down n=256 4096x12288 r64 L32",
+    "gather": "MoE gather down 32 tokens top8 E128 768->2048 r16 L8",
+    "grouped": "MoE grouped down/gate/up 4096 tokens top8 E128 te=32768 cap=8192 r32 L4",
+}
+
+
+def _timed_eager(step, idx, lead_graph, steps, torch):
+    """K steps of: replay lead_graph (long GPU work, so the host runs ahead),
+    then the calls idx eagerly with a HIP event recorded before each call and
+    after the last.  Returns the mean duration of each call in ms."""
+    evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(len(idx) + 1)]
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    for evs in evsets:
+        lead_graph.replay()
+        for e, i in zip(evs, idx):
+            e.record()
+            if step.calls[i][2]() != 0:
+                raise RuntimeError(step.calls[i][0])
+        evs[-1].record()
+    torch.cuda.synchronize()
+    return np.array([[evs[j].elapsed_time(evs[j + 1]) for j in range(len(idx))]
+                     for evs in evsets]).mean(axis=0)
+
+
+def run_gpu(args):
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wls = select_workloads(args.workload)
+    step = Step(dev, wls)
+    ncalls = len(step.calls)
+    grouped = [i for i, c in enumerate(step.calls) if c[0].startswith("grouped.")]
+    other = [i for i in range(ncalls) if i not in grouped]
+
+    for _ in range(args.warmup):
+        step.enqueue()
+    torch.cuda.synchronize()
+
+    cap_stream = torch.cuda.Stream()
+
+    def capture(idx):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for i in idx:
+                if step.calls[i][2]() != 0:
+                    raise RuntimeError("call failed during capture")
+        return g
+
+    full = capture(range(ncalls))
+    g_other = capture(other) if other else None
+    g_grouped = capture(grouped) if grouped else None
+    for _ in range(3):
+        full.replay()
+    torch.cuda.synchronize()
+
+    # timed region A: K replays of the whole step, back to back
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        full.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # timed regions B and C: every call timed by HIP events on the launch stream
+    per_call_ms = np.zeros(ncalls)
+    if grouped:
+        lead = g_other if g_other is not None else g_grouped
+        per_call_ms[grouped] = _timed_eager(step, grouped, lead, args.steps, torch)
+    if other:
+        lead = g_grouped if g_grouped is not None else g_other
+        per_call_ms[other] = _timed_eager(step, other, lead, args.steps, torch)
+    segs = [(i, i + 1) for i in range(ncalls)]
+    seg_ms = per_call_ms
+
+    ms_per_step = wall * 1e3 / args.steps
+    # launches timed one by one (single-call segments), grouped by kernel
+    kernels = {}
+    for (a, b), ms in zip(segs, seg_ms):
+        if b - a != 1:
+            continue
+        _, kname, _, by, fl, _ = step.calls[a]
+        k = kernels.setdefault(kname, {"launches": 0, "ms": 0.0, "bytes": 0, "flops": 0.0})
+        k["launches"] += 1
+        k["ms"] += float(ms)
+        k["bytes"] += int(by)
+        k["flops"] += float(fl)
+    dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["ms"])
+    avg_launch_s = dom["ms"] / dom["launches"] * 1e-3
+    bytes_per_launch = dom["bytes"] / dom["launches"]
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+
+    per_workload = {}
+    for tag, _ in wls:
+        sel = [j for j, (a, b) in enumerate(segs) if step.calls[a][0].startswith(tag + ".")]
+        ms = float(seg_ms[sel].sum())
+        calls = [c for (a, b) in (segs[j] for j in sel) for c in step.calls[a:b]]
+        by = sum(c[3] for c in calls)
+        fl = sum(c[4] for c in calls)
+        rows = sum(c[5] for c in calls)
+        ent = {"ms": round(ms, 5), "rows": rows, "rows_per_s": round(rows / (ms * 1e-3), 1),
+               "algo_bytes": int(by), "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if tag == "grouped":
+            ent["mfma_util"] = round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)
+        per_workload[tag] = ent
+
+    kern_out = {k: {"launches_per_step": v["launches"],
+                    "avg_us": round(v["ms"] / v["launches"] * 1e3, 3),
+                    "algo_bytes_per_launch": int(v["bytes"] / v["launches"]),
+                    "gbs": round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)}
+                for k, v in kernels.items()}
+    return {
+        "ms_per_step": ms_per_step,
+        "ms_per_step_calls": float(seg_ms.sum()),
+        "rows": step.rows,
+        "bytes": step.bytes,
+        "flops": step.flops,
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algo_bytes_per_launch": int(bytes_per_launch),
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "launches_per_step": dom["launches"]},
+        "kernels": kern_out,
+        "per_workload": per_workload,
+    }
+
+
+# ------------------------------------------------------------- CPU oracle ---
+
+def cpu_baseline(args):
+    """The oracle, as it stands, on a bounded sample of the step: every BGMV
+    and gather call in full, and the first window (cap rows) of each grouped
+    projection.  BLAS is held to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    import workloads as W
+    wls = dict(select_workloads(args.workload))
+    rows = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for tag in ("attn", "ffn"):
+            if tag not in wls:
+                continue
+            wl = wls[tag]
+            bufs = {k: v.copy() for k, v in wl.buffers.items()}
+            for c in wl.calls:
+                slots = O.pack_slots(c.adapters, c.max_loras, c.max_rank)
+                _, bufs[c.out_buf] = O.bgmv(slots, c.k_in, c.n_out, c.max_rank, bufs[c.x_buf],
+                                            c.x_row_stride, wl.seq_slot, wl.n, bufs[c.out_buf],
+                                            c.out_offset, c.out_row_stride)
+                rows += wl.n
+        if "gather" in wls:
+            wl = wls["gather"]
+            pairs = O.pack_expert_pairs(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank)
+            O.moe_gather(pairs, wl.num_experts, wl.k_in, wl.n_out, wl.max_rank, wl.x.ravel(),
+                         wl.k_in, wl.indices, wl.row_adapter, wl.top_k, wl.n_rows,
+                         wl.base.ravel(), wl.n_out)
+            rows += wl.n_rows
+        if "grouped" in wls:
+            wl = wls["grouped"]
+            for p in wl.projections:
+                pairs = O.pack_expert_pairs(p.adapters, wl.max_loras, wl.num_experts,
+                                            wl.max_rank)
+                hi = min(args.cpu_rows, wl.te)
+                O.moe_grouped(pairs, wl.num_experts, p.k_in, p.n_out, wl.max_rank, p.x.ravel(),
+                              p.k_in, p.x_gather, wl.num_tokens, wl.expert_offsets,
+                              wl.sorted_token_ids, wl.row_adapter, 0, hi, p.base.ravel(),
+                              p.n_out)
+                rows += hi
+    dt = time.perf_counter() - t0
+    return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} rows of the step (every BGMV and gather row, the first "
+                      f"{args.cpu_rows} sorted rows of each grouped projection), "
+                      f"{dt:.1f} s on one host core"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="step", choices=list(WORKLOAD_NAMES))
+    ap.add_argument("--cpu-rows", type=int, default=32768,
+                    help="sorted rows per grouped projection in the cpu_baseline sample "
+                         "(the default covers the whole step)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the routed fold has no multi-GPU path in this "
+              "library (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    g = run_gpu(args)
+    rows_per_s = g["rows"] / (g["ms_per_step"] * 1e-3)
+    gbs = g["bytes"] / (g["ms_per_step"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded PCG64; shapes and routing of the routed-LoRA workloads)",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "rows_per_step": g["rows"],
+                   "algo_bytes_per_step": int(g["bytes"]), "flops_per_step": int(g["flops"])},
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "ms_per_step_calls": round(g["ms_per_step_calls"], 5),
+        "roofline": g["roofline"],
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(args),
+        "kernels": g["kernels"],
+        "per_workload": g["per_workload"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
