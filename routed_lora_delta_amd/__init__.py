@@ -27,7 +27,7 @@ RLD_M_TILE = 64
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                      "or python -m routed_lora_delta_amd.build")
+                      "or python routed_lora_delta_amd/build.py")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

@@ -1,6 +1,8 @@
 """Build librld.so (HIP C++ for gfx950) in-tree with hipcc.
 
-    python -m routed_lora_delta_amd.build [-v]
+    python routed_lora_delta_amd/build.py [-v]
+
+(run by path: importing the package itself needs the library this builds).
 
 Every call recompiles every source.  Objects go to routed_lora_delta_amd/_build/,
 the library to routed_lora_delta_amd/librld.so.

@@ -214,8 +214,8 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(
             for (int ks = 0; ks < 4; ++ks)
               if (ks < nks) acc = mfma_bf16_16x16x32(aop[m][ks], bop[ks], acc);
             // lane holds delta[row p*16+cl][cols m*16 + 4*lg .. +3] of this wave's slice
-            const uint32_t d01 = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-            const uint32_t d23 = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+            const uint32_t d01 = pack_bf16x2(acc[0], acc[1]);
+            const uint32_t d23 = pack_bf16x2(acc[2], acc[3]);
             *reinterpret_cast<uint2*>(&dl[(p * 16 + cl) * kDlStride + wave * 64 + m * 16 +
                                           4 * lg]) = make_uint2(d01, d23);
           }

@@ -25,16 +25,20 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round a binary32 value to bfloat16, ties to even (IEEE 754 roundTiesToEven
-// applied to the 16 dropped significand bits).  NaN -> quiet NaN with the sign
-// kept; overflow -> infinity; subnormals are rounded like normals (the bit
-// pattern spacing is uniform across the subnormal/normal boundary).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x0040u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round binary32 values to bfloat16, ties to even, with gfx950's
+// v_cvt_pk_bf16_f32 (two values per instruction): round to nearest even on the
+// 16 dropped significand bits, NaN -> quiet NaN with the sign kept, overflow ->
+// infinity, subnormals rounded like normals.  (The instruction's results were
+// checked against that definition on every exponent with tie, above-tie and
+// below-tie patterns, on subnormals and around the largest finite value.)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 __device__ __forceinline__ floatx4 mfma_bf16_16x16x32(const uint4& a, const uint4& b,
                                                       const floatx4& c) {
@@ -50,17 +54,15 @@ __device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // out = bf16(f32(base) + f32(scale * f32(delta))): the product is rounded to
 // fp32 before the add (base += scale * bf16(delta) in fp32), never fused.
-__device__ __forceinline__ uint32_t fold1(uint32_t base16, uint32_t delta16, float scale) {
+__device__ __forceinline__ float fold_f32(uint32_t base16, uint32_t delta16, float scale) {
 #pragma clang fp contract(off)
   const float t = scale * bf16_to_f32(delta16);
-  const float s = bf16_to_f32(base16) + t;
-  return f32_to_bf16(s);
+  return bf16_to_f32(base16) + t;
 }
 
 __device__ __forceinline__ uint32_t fold2(uint32_t base2, uint32_t delta2, float scale) {
-  const uint32_t lo = fold1(base2 & 0xffffu, delta2 & 0xffffu, scale);
-  const uint32_t hi = fold1(base2 >> 16, delta2 >> 16, scale);
-  return lo | (hi << 16);
+  return pack_bf16x2(fold_f32(base2 & 0xffffu, delta2 & 0xffffu, scale),
+                     fold_f32(base2 >> 16, delta2 >> 16, scale));
 }
 
 __device__ __forceinline__ uint4 fold8(const uint4& base, const uint4& delta, float scale) {
@@ -95,48 +97,6 @@ __device__ __forceinline__ int append_matching_rows(const int32_t* __restrict__ 
   if (hit) list[off + __popcll(m & lanemask_lt(lane))] = (int)row;
   __syncthreads();
   return tot;
-}
-
-// Row classification of one grouped m-tile.  For tile rows r0 + l (l < nr),
-// `key` is the (slot, expert) pair index s*E + e of a row that folds, or -1.
-// Rows are grouped by key in first-occurrence order; within a group rows stay
-// ascending.  Run by one full wave (lane = tile row); results in LDS.
-struct TileGroups {
-  int ngroups;
-  int gkey[64];
-  int gstart[64];
-  int gcount[64];
-  int grow[64];    // tile-local rows, grouped
-  int rowgrp[64];  // group of each tile row, or -1
-  int tok[64];     // token of each tile row (gather source)
-};
-
-__device__ __forceinline__ void group_tile_rows(int key, int tok, TileGroups& tg) {
-  const int lane = threadIdx.x & 63;
-  tg.rowgrp[lane] = -1;
-  tg.tok[lane] = tok;
-  uint64_t pending = __ballot(key >= 0);
-  int ng = 0;
-  int start = 0;
-  while (pending) {
-    const int leader = __ffsll((long long)pending) - 1;
-    const int lk = __shfl(key, leader);
-    const uint64_t m = __ballot(key == lk);
-    const int cnt = __popcll(m);
-    if (lane == 0) {
-      tg.gkey[ng] = lk;
-      tg.gstart[ng] = start;
-      tg.gcount[ng] = cnt;
-    }
-    if (key == lk) {
-      tg.grow[start + __popcll(m & lanemask_lt(lane))] = lane;
-      tg.rowgrp[lane] = ng;
-    }
-    start += cnt;
-    ++ng;
-    pending &= ~m;
-  }
-  if (lane == 0) tg.ngroups = ng;
 }
 
 // Owner expert of sorted row r: the largest e < E with off[e] <= r, accepted

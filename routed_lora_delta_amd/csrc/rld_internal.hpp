@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/rld.h"
+#include "rld.h"
 
 namespace rld {
 
