@@ -226,8 +226,11 @@ int rld_moe_gather(const rld_moe_route* route, const void* x, uint32_t x_row_str
  *                    t = sorted_token_ids[r]
  *   xa               device BF16 [xa_rows_cap, max_rank]; row r is written at
  *                    the window-local row r - row_offset
- * The launch always has max(1, ceil((row_end-row_offset)/64)) m-tiles.
- * RLD_ENOSPACE if row_end - row_offset > xa_rows_cap. */
+ * The launch shape depends only on the host arguments (route sizes and the
+ * window), so a captured call replays with new routing contents; an empty
+ * window (row_end == row_offset) launches nothing and returns RLD_OK.
+ * RLD_EUNSUPPORTED if max_loras * num_experts > 2048 (the per-launch pair
+ * list); RLD_ENOSPACE if row_end - row_offset > xa_rows_cap. */
 int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x, uint32_t x_row_stride,
                            int x_gather, uint32_t num_tokens, const int32_t* expert_offsets,
                            uint32_t num_experts_off, const int32_t* sorted_token_ids,

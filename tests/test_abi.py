@@ -1,0 +1,278 @@
+"""C ABI of librld.so, on the CPU: the library loads, exports every function
+include/rld.h declares, its pure host helpers agree with the oracle's
+statements of the same helpers, and the device entry points reject bad
+arguments with the documented status before any launch.
+
+No device work is done here: every device entry point is called only with
+arguments that fail validation, or with an empty batch / empty window (a no-op
+that launches nothing), and with stream 0 so no GPU runtime is needed.
+"""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import routed_lora_delta_amd as R
+
+# a fake, 16-byte-aligned "device" address: validation never dereferences it
+FAKE = 0x7F0000001000
+
+
+def test_library_exports_every_header_symbol():
+    names = R.header_symbols()
+    assert len(names) >= 20, names
+    lib = ctypes.CDLL(R.library_path())
+    for n in names:
+        assert hasattr(lib, n), f"librld.so does not export {n}"
+        assert hasattr(R, n), f"the binding has no {n}"
+    assert R.rld_version().startswith("rld")
+    for st in (R.RLD_OK, R.RLD_EINVAL, R.RLD_EALIGN, R.RLD_EUNSUPPORTED, R.RLD_ELAUNCH,
+               R.RLD_ENOSPACE):
+        assert R.rld_status_string(st) != "unknown status"
+
+
+@pytest.mark.parametrize("alpha,rank,rs", [(16.0, 4, 0), (16.0, 8, 0), (32.0, 8, 1),
+                                           (32.0, 32, 1), (32.0, 64, 1), (16.0, 3, 0),
+                                           (7.0, 48, 1)])
+def test_scale_matches_oracle(alpha, rank, rs):
+    out = ctypes.c_float()
+    assert R.rld_scale(alpha, rank, rs, ctypes.byref(out)) == R.RLD_OK
+    assert np.float32(out.value) == O.scale_for(alpha, rank, bool(rs))
+
+
+def test_scale_rejects_rank_zero():
+    out = ctypes.c_float()
+    assert R.rld_scale(16.0, 0, 0, ctypes.byref(out)) == R.RLD_EINVAL
+
+
+@pytest.mark.parametrize("rank,max_rank", [(4, 8), (8, 8), (13, 16), (1, 64)])
+def test_pad_adapter_matches_oracle(rank, max_rank):
+    rng = np.random.default_rng(rank * 100 + max_rank)
+    k_in, n_out = 40, 24
+    A = rng.integers(0, 65536, size=(rank, k_in), dtype=np.uint16)
+    B = rng.integers(0, 65536, size=(n_out, rank), dtype=np.uint16)
+    ap = np.full((max_rank, k_in), 0xFFFF, np.uint16)
+    bp = np.full((n_out, max_rank), 0xFFFF, np.uint16)
+    assert R.rld_pad_adapter_host(A, B, rank, k_in, n_out, max_rank, ap, bp) == R.RLD_OK
+    Ao, Bo = O.pad_adapter(A, B, max_rank)
+    assert np.array_equal(ap, Ao) and np.array_equal(bp, Bo)
+    assert R.rld_pad_adapter_host(A, B, max_rank + 1, k_in, n_out, max_rank, ap, bp) == \
+        R.RLD_EINVAL
+
+
+def _entries(rows):
+    arr = (R.rld_adapter_entry * max(1, len(rows)))()
+    for i, (slot, expert, a, b, rank, alpha, rs) in enumerate(rows):
+        arr[i] = R.rld_adapter_entry(slot, expert, a, b, rank, alpha, rs)
+    return arr
+
+
+def test_route_pack_last_wins_and_empty_slots():
+    rows = [(0, -1, FAKE, FAKE + 256, 8, 16.0, 0),
+            (2, -1, FAKE + 512, FAKE + 768, 16, 32.0, 1),
+            (0, -1, FAKE + 1024, FAKE + 1280, 4, 16.0, 0)]  # slot 0 again: last wins
+    a = np.full(4, 7, np.uint64)
+    b = np.full(4, 7, np.uint64)
+    s = np.full(4, 7, np.float32)
+    assert R.rld_route_pack(_entries(rows), len(rows), 4, 16, a, b, s) == R.RLD_OK
+    assert a.tolist() == [FAKE + 1024, 0, FAKE + 512, 0]
+    assert b.tolist() == [FAKE + 1280, 0, FAKE + 768, 0]
+    assert s[0] == O.scale_for(16.0, 4, False) and s[2] == O.scale_for(32.0, 16, True)
+    assert s[1] == 0.0 and s[3] == 0.0
+
+
+@pytest.mark.parametrize("row,status", [
+    ((4, -1, FAKE, FAKE, 8, 16.0, 0), R.RLD_EINVAL),        # slot >= max_loras
+    ((1, -1, FAKE, FAKE, 0, 16.0, 0), R.RLD_EINVAL),        # rank 0
+    ((1, -1, FAKE, FAKE, 17, 16.0, 0), R.RLD_EINVAL),       # rank > max_rank
+    ((1, -1, 0, FAKE, 8, 16.0, 0), R.RLD_EINVAL),           # null address
+    ((1, -1, FAKE + 8, FAKE, 8, 16.0, 0), R.RLD_EALIGN),    # misaligned address
+])
+def test_route_pack_rejects(row, status):
+    a = np.zeros(4, np.uint64)
+    b = np.zeros(4, np.uint64)
+    s = np.zeros(4, np.float32)
+    assert R.rld_route_pack(_entries([row]), 1, 4, 16, a, b, s) == status
+
+
+def test_moe_tables_pack_slot_major():
+    E = 5
+    rows = [(1, 3, FAKE, FAKE + 256, 8, 16.0, 0), (0, 0, FAKE + 512, FAKE + 768, 16, 16.0, 0),
+            (1, 3, FAKE + 1024, FAKE + 1280, 16, 16.0, 0)]
+    a = np.zeros(2 * E, np.uint64)
+    b = np.zeros(2 * E, np.uint64)
+    s = np.zeros(2 * E, np.float32)
+    assert R.rld_moe_tables_pack(_entries(rows), 3, 2, E, 16, a, b, s) == R.RLD_OK
+    want_a = np.zeros(2 * E, np.uint64)
+    want_a[0 * E + 0] = FAKE + 512
+    want_a[1 * E + 3] = FAKE + 1024
+    assert np.array_equal(a, want_a)
+    assert s[1 * E + 3] == O.scale_for(16.0, 16, False)
+    bad = [(0, E, FAKE, FAKE, 8, 16.0, 0)]
+    assert R.rld_moe_tables_pack(_entries(bad), 1, 2, E, 16, a, b, s) == R.RLD_EINVAL
+    bad = [(0, -1, FAKE, FAKE, 8, 16.0, 0)]
+    assert R.rld_moe_tables_pack(_entries(bad), 1, 2, E, 16, a, b, s) == R.RLD_EINVAL
+
+
+@pytest.mark.parametrize("ids", [[3, 0, 7], [5, 5, 1], [0], []])
+def test_pack_expert_tables_matches_oracle(ids):
+    n = len(ids)
+    eids = np.array(ids, np.uint32) if n else np.zeros(1, np.uint32)
+    aa = np.array([FAKE + 256 * i for i in range(n)] or [0], np.uint64)
+    bb = np.array([FAKE + 4096 + 256 * i for i in range(n)] or [0], np.uint64)
+    sc = np.array([0.5 + i for i in range(n)] or [0], np.float32)
+    cap = 16
+    a = np.zeros(cap, np.uint64)
+    b = np.zeros(cap, np.uint64)
+    s = np.zeros(cap, np.float32)
+    cnt = ctypes.c_uint32(99)
+    assert R.rld_pack_expert_tables(eids, aa, bb, sc, n, cap, a, b, s, ctypes.byref(cnt)) == \
+        R.RLD_OK
+    want = O.pack_expert_tables([(ids[i], aa[i], bb[i], sc[i]) for i in range(n)])
+    if want is None:
+        assert cnt.value == 0
+        return
+    ne, wa, wb, ws = want
+    assert cnt.value == ne
+    assert a[:ne].tolist() == wa and b[:ne].tolist() == wb
+    assert np.array_equal(s[:ne], np.array(ws, np.float32))
+    cnt2 = ctypes.c_uint32()
+    assert R.rld_pack_expert_tables(eids, aa, bb, sc, n, ne - 1, a, b, s,
+                                    ctypes.byref(cnt2)) == R.RLD_ENOSPACE
+
+
+@pytest.mark.parametrize("total,cap", [(0, 8192), (1, 8192), (32768, 8192), (32769, 8192),
+                                       (300, 100), (300, 64), (8191, 8192), (5, 1)])
+def test_grouped_windows_and_wc_match_oracle(total, cap):
+    mx = 1024
+    st = np.zeros(mx, np.uint32)
+    en = np.zeros(mx, np.uint32)
+    cnt = ctypes.c_uint32(99)
+    assert R.rld_grouped_windows(total, cap, st, en, mx, ctypes.byref(cnt)) == R.RLD_OK
+    want = O.grouped_down_windows(total, cap)
+    assert cnt.value == len(want)
+    assert list(zip(st[:cnt.value].tolist(), en[:cnt.value].tolist())) == want
+    for lo, hi in want + [(0, 0), (10, 10)]:
+        assert R.rld_grouped_wc(lo, hi) == O.grouped_down_wc(lo, hi)
+    if len(want) > 1:
+        assert R.rld_grouped_windows(total, cap, st, en, len(want) - 1,
+                                     ctypes.byref(cnt)) == R.RLD_ENOSPACE
+    assert R.rld_grouped_windows(total, 0, st, en, mx, ctypes.byref(cnt)) == R.RLD_EINVAL
+
+
+def test_gather_row_token_and_grids():
+    for top_k in (1, 4, 8):
+        for row in (0, 1, 7, 8, 255, 1000):
+            assert R.rld_gather_row_token(row, top_k) == O.gather_row_token(row, top_k)
+    g = np.zeros(12, np.uint32)
+    assert R.rld_gather_grids(16, 2048, 256, g) == R.RLD_OK
+    # one shrink block per flat row; expand covers n_out with whole blocks per row
+    assert g[0] == 256 and g[3] * g[4] * g[5] >= 64
+    assert g[6] == 256 and g[7] * g[9] * 2 >= 2048
+
+
+# ------------------------------------------------ device entry points: validation
+
+
+def _route(k_in=256, n_out=256, max_rank=16, max_loras=4, tables=True):
+    t = FAKE if tables else 0
+    return R.rld_route(t, t, t, max_loras, k_in, n_out, max_rank)
+
+
+def _moe_route(k_in=256, n_out=256, max_rank=16, max_loras=2, E=8):
+    return R.rld_moe_route(FAKE, FAKE, FAKE, max_loras, E, k_in, n_out, max_rank)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(tables=False), R.RLD_EINVAL),
+    (dict(max_loras=0), R.RLD_EINVAL),
+    (dict(k_in=0), R.RLD_EINVAL),
+    (dict(max_rank=136), R.RLD_EUNSUPPORTED),
+    (dict(k_in=250), R.RLD_EALIGN),
+    (dict(n_out=100), R.RLD_EALIGN),
+    (dict(max_rank=12), R.RLD_EALIGN),
+])
+def test_bgmv_rejects_bad_routes(kw, status):
+    rt = _route(**kw)
+    assert R.rld_bgmv_shrink(rt, FAKE, 256, FAKE, 4, FAKE, FAKE, 1 << 20, 0) == status
+    assert R.rld_bgmv_expand_fold(rt, FAKE, FAKE, 4, FAKE, 256, 0) == status
+    assert R.rld_bgmv(rt, FAKE, 256, FAKE, 4, FAKE, 256, FAKE, FAKE, 1 << 20, 0) == status
+
+
+def test_bgmv_rejects_bad_buffers():
+    rt = _route()
+    n = 4
+    ws = R.rld_bgmv_workspace_bytes(n, 256, 16)
+    sh = lambda **k: R.rld_bgmv_shrink(  # noqa: E731
+        rt, k.get("x", FAKE), k.get("xs", 256), k.get("seq", FAKE), n, k.get("xa", FAKE),
+        k.get("ws", FAKE), k.get("wsb", ws), 0)
+    assert sh(x=0) == R.RLD_EINVAL
+    assert sh(xs=128) == R.RLD_EINVAL            # stride < k_in
+    assert sh(xs=260) == R.RLD_EALIGN            # stride not a multiple of 8
+    assert sh(x=FAKE + 2) == R.RLD_EALIGN        # x not 16-byte aligned
+    assert sh(seq=0) == R.RLD_EINVAL
+    assert sh(xa=0) == R.RLD_EINVAL
+    assert sh(xa=FAKE + 8) == R.RLD_EALIGN
+    ex = lambda **k: R.rld_bgmv_expand_fold(  # noqa: E731
+        rt, k.get("xa", FAKE), k.get("seq", FAKE), n, k.get("out", FAKE), k.get("os", 256), 0)
+    assert ex(out=0) == R.RLD_EINVAL
+    assert ex(os=200) == R.RLD_EINVAL            # stride < n_out
+    assert ex(out=FAKE + 4) == R.RLD_EALIGN
+    assert ex(xa=0) == R.RLD_EINVAL
+
+
+def test_bgmv_workspace_contract():
+    # k-split shapes need a workspace; a short one is refused before any launch
+    rt = _route(k_in=12288, n_out=4096, max_rank=64, max_loras=32)
+    need = R.rld_bgmv_workspace_bytes(256, 12288, 64)
+    assert need > 0
+    assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, FAKE, need - 4, 0) == \
+        R.RLD_ENOSPACE
+    assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, 0, need, 0) == R.RLD_ENOSPACE
+    assert R.rld_bgmv_workspace_bytes(256, 0, 64) == 0
+
+
+def test_empty_batches_are_noops():
+    rt = _route()
+    assert R.rld_bgmv(rt, FAKE, 256, FAKE, 0, FAKE, 256, FAKE, FAKE, 0, 0) == R.RLD_OK
+    assert R.rld_bgmv_shrink(rt, FAKE, 256, FAKE, 0, FAKE, 0, 0, 0) == R.RLD_OK
+    assert R.rld_bgmv_expand_fold(rt, FAKE, FAKE, 0, FAKE, 256, 0) == R.RLD_OK
+    mr = _moe_route()
+    assert R.rld_moe_gather(mr, FAKE, 256, FAKE, FAKE, 8, 0, FAKE, 256, FAKE, 0) == R.RLD_OK
+    # empty grouped window: validated, then nothing to launch
+    assert R.rld_moe_grouped(mr, FAKE, 256, 1, 64, FAKE, 8, FAKE, FAKE, 100, 100, FAKE, 256,
+                             FAKE, 0, 0) == R.RLD_OK
+
+
+def test_moe_rejects_bad_arguments():
+    mr = _moe_route()
+    g = lambda **k: R.rld_moe_grouped_shrink(  # noqa: E731
+        k.get("rt", mr), FAKE, 256, k.get("xg", 1), 64, k.get("off", FAKE), k.get("Eo", 8),
+        k.get("stid", FAKE), FAKE, k.get("lo", 0), k.get("hi", 64), k.get("xa", FAKE),
+        k.get("cap", 64), 0)
+    assert g(off=0) == R.RLD_EINVAL
+    assert g(Eo=0) == R.RLD_EINVAL
+    assert g(lo=10, hi=5) == R.RLD_EINVAL         # row_end < row_offset
+    assert g(stid=0) == R.RLD_EINVAL              # x gather needs sorted_token_ids
+    assert g(cap=63) == R.RLD_ENOSPACE            # window larger than the xa arena
+    assert g(xa=FAKE + 8) == R.RLD_EALIGN
+    big = R.rld_moe_route(FAKE, FAKE, FAKE, 64, 128, 256, 256, 16)   # 8192 pairs
+    assert g(rt=big) == R.RLD_EUNSUPPORTED
+    bad = R.rld_moe_route(FAKE, FAKE, FAKE, 2, 0, 256, 256, 16)
+    assert g(rt=bad) == R.RLD_EINVAL
+    ga = lambda **k: R.rld_moe_gather_shrink(  # noqa: E731
+        mr, k.get("x", FAKE), k.get("xs", 256), FAKE, FAKE, 8, 16, k.get("xa", FAKE), 0)
+    assert ga(x=0) == R.RLD_EINVAL
+    assert ga(xs=8) == R.RLD_EINVAL
+    assert ga(xa=0) == R.RLD_EINVAL
+    assert ga(xa=FAKE + 2) == R.RLD_EALIGN
+
+
+def test_scale_table_values_are_exact_closed_forms():
+    # the fp32 scales of the decode workloads: alpha/r and alpha/sqrt(r), rounded once
+    for alpha, r in ((32.0, 8), (32.0, 32), (16.0, 16)):
+        out = ctypes.c_float()
+        R.rld_scale(alpha, r, 1, ctypes.byref(out))
+        assert out.value == float(np.float32(alpha / math.sqrt(r)))
