@@ -29,6 +29,16 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                       "or python routed_lora_delta_amd/build.py")
 
+# The library must run on the same HIP runtime instance as the framework whose
+# device memory and streams it is handed.  torch ships its own libamdhip64;
+# loading it first makes librld.so's libamdhip64.so.7 dependency resolve to
+# that copy.  Loaded the other way round, the process would hold two HIP
+# runtimes, and the second to open the GPU finds no device.
+try:
+    import torch  # noqa: F401
+except ImportError:  # standalone use: librld.so's own ROCm runtime
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 

@@ -121,4 +121,14 @@ __device__ __forceinline__ uint32_t xcd_work_item(uint32_t total) {
   return (blockIdx.x & 7u) * per + (blockIdx.x >> 3);
 }
 
+// Block index remap that keeps each group of `group` consecutive work items on
+// one XCD (they share inputs through that XCD's L2) and deals the groups out
+// to the 8 XCDs in turn (so a run of heavy groups spreads over the chip).
+// The grid must be 8 * group * ceil(ceil(total / group) / 8) blocks (see
+// xcd_group_grid); returns >= total for padding blocks.
+__device__ __forceinline__ uint32_t xcd_group_item(uint32_t group) {
+  const uint32_t p = blockIdx.x >> 3;
+  return ((p / group) * 8u + (blockIdx.x & 7u)) * group + p % group;
+}
+
 }  // namespace rld

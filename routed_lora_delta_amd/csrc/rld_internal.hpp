@@ -51,10 +51,16 @@ inline int launch_status() {
 }
 
 // k_in split of the BGMV shrink: a function of (k_in, max_rank) only, so a row's
-// summation order never depends on the batch.
+// summation order never depends on the batch.  Narrow ranks get shorter chunks
+// so that a call still spreads over many blocks.
 inline uint32_t bgmv_chunk(uint32_t k_in, uint32_t max_rank) {
-  const uint32_t kc = max_rank <= 16 ? 512u : 1024u;
+  const uint32_t kc = max_rank <= 16 ? 256u : max_rank <= 32 ? 512u : 1024u;
   return k_in <= kc ? k_in : kc;
+}
+
+// Grid of xcd_group_item: 8 XCDs x whole groups, covering `total` items.
+inline uint32_t xcd_group_grid(uint32_t total, uint32_t group) {
+  return 8u * group * div_ceil(div_ceil(total, group), 8u);
 }
 
 // Output columns per block of the gather expand (two per thread).

@@ -53,6 +53,7 @@ BGMV_SHAPES = [
     (300, 512, 768, 128, 4, (64, 128), ()),
     (600, 1536, 264, 32, 40, (16, 32), (0, 39)),
     (1200, 256, 264, 16, 2, (8, 16), ()),
+    (1400, 1024, 264, 16, 2, (8, 16), ()),  # k split with > 512 rows per slot
 ]
 
 
