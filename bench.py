@@ -18,7 +18,7 @@ calls the same way after a replay of the captured grouped part (region C), so
 the host is always ahead of the GPU and an event pair brackets exactly one
 call.  The kernel with the largest total time is reported against its
 roofline: achieved = its algorithmic bytes per launch / its mean launch
-duration (a BGMV shrink call includes its k-split reduce launch).
+duration.
 Algorithmic bytes are counted from the actual inputs: x rows that fold, A and
 B of each distinct (slot[, expert]) pair a call touches, the base rows read
 and written, xa written and read, and the index arrays.
@@ -130,16 +130,12 @@ class Step:
                     x = bufs[c.x_buf].data_ptr()
                     out = bufs[c.out_buf].data_ptr() + 2 * c.out_offset
 
-                    def shrink(rt=rt, c=c, x=x, seq=seq, xa=xa, ws=ws, wsb=wsb, n=wl.n):
-                        return R.rld_bgmv_shrink(rt.route, x, c.x_row_stride, seq, n, xa, ws, wsb)
+                    def bgmv(rt=rt, c=c, x=x, out=out, seq=seq, xa=xa, ws=ws, wsb=wsb, n=wl.n):
+                        return R.rld_bgmv(rt.route, x, c.x_row_stride, seq, n, out,
+                                          c.out_row_stride, xa, ws, wsb)
 
-                    def expand(rt=rt, c=c, out=out, seq=seq, xa=xa, n=wl.n):
-                        return R.rld_bgmv_expand_fold(rt.route, xa, seq, n, out, c.out_row_stride)
-
-                    self.calls.append((f"{tag}.{c.module}.shrink", "bgmv_shrink_kernel", shrink,
-                                       sb, fl / 2, wl.n))
-                    self.calls.append((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", expand,
-                                       eb, fl / 2, 0))
+                    self.calls.append((f"{tag}.{c.module}", "bgmv_fused_kernel", bgmv, sb + eb,
+                                       fl, wl.n))
                     self.rows += wl.n
             elif tag == "gather":
                 rt = MoeRoute(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank, wl.k_in,

@@ -3,27 +3,41 @@
 // xa[i] = bf16(x_i @ A_s^T) and the expand folds bf16(xa[i] @ B_s^T), scaled in
 // fp32 after the rounding, into the row's output.
 //
-// Kernels are slot-grouped: a block serves one slot and all rows that name it,
-// so each slot's A_s / B_s tile is streamed from HBM once per call instead of
-// once per row.  The row list of a slot is rebuilt in every block from
-// seq_slot (no host read), in ascending row order.
+// Work is slot-grouped: an item serves one slot and all rows that name it, so
+// each slot's A_s / B_s tile is streamed from HBM once per call instead of once
+// per row.  The row list of a slot is rebuilt by every item from seq_slot (no
+// host read), in ascending row order.
 //
-//   shrink  block = (slot, k_in chunk, 16 columns of xa).  Each of the four
-//           waves owns every fourth 32-wide K step of the chunk and issues all
-//           of its A fragments at once; x fragments of the next 16 rows are in
-//           flight while the current ones multiply.  The waves' partial sums
-//           are added in wave order.  With several chunks, each block writes
-//           fp32 partials, and the block that finishes the last chunk of a
-//           (slot, 16 columns) pair adds the chunks in chunk order and writes
-//           xa (a counter per pair in the workspace; no second launch).  The
-//           chunk length depends only on (k_in, max_rank), so a row's
-//           summation order is the same whatever the batch holds: a batched
-//           call is bit-identical to one-row calls.
-//   expand  block = (slot, 256 output columns).  B_s rows of the tile stay in
-//           registers as MFMA A operands; rows of the slot stream through as
-//           the B operand (16 rows per MFMA).  The base values of a 64-row pass
-//           are loaded before its MFMAs, deltas are rounded to BF16 into LDS,
-//           and the fold writes 16-byte coalesced vectors.
+//   shrink item  (slot, k_in chunk, 16 columns of xa).  Each of the four waves
+//                owns every fourth 32-wide K step of the chunk and issues all
+//                of its A fragments at once; x fragments of the next 16 rows
+//                are in flight while the current ones multiply.  The waves'
+//                partial sums are added in wave order.  With several chunks,
+//                each item writes fp32 partials, and the item that finishes
+//                the last chunk of a (slot, 16 columns) pair adds the chunks in
+//                chunk order and writes xa (a counter per pair in the
+//                workspace).  The chunk length depends only on (k_in,
+//                max_rank), so a row's summation order is the same whatever
+//                the batch holds: a batched call is bit-identical to one-row
+//                calls.
+//   expand item  (slot, 256 output columns).  B_s rows of the tile stay in
+//                registers as MFMA A operands; rows of the slot stream through
+//                as the B operand (16 rows per MFMA).  The base values of a
+//                64-row pass are loaded before its MFMAs, deltas are rounded to
+//                BF16 into LDS, and the fold writes 16-byte coalesced vectors.
+//
+// rld_bgmv_shrink and rld_bgmv_expand_fold launch one kernel each.  rld_bgmv
+// runs both stages in one persistent kernel: blocks claim items from a counter
+// in the workspace, every shrink item before every expand item.  An expand item
+// loads its B tile and the base values of its first pass, then waits until its
+// slot's xa is complete (a per-slot counter, raised by the shrink items that
+// finish it).  An item waits only on items claimed before it, whose blocks are
+// running and never wait, so the wait always ends; one slot's expand streams
+// while later slots still shrink.  Cross-block data (fp32 partials, xa inside
+// the fused kernel, counters) moves with agent-scope stores and loads, which
+// are coherent across the XCDs' L2 caches, and each producer's stores have
+// completed before it raises a counter.  The per-row arithmetic is the same in
+// both forms, so they give identical bits.
 #include "rld_device.hpp"
 #include "rld_internal.hpp"
 
@@ -32,17 +46,61 @@ namespace rld {
 constexpr int kShrinkMT = 4;     // 16-row M-subtiles per shrink pass
 constexpr int kShrinkSteps = 8;  // K steps per wave per chunk (chunk <= 1024 = 4 waves x 8 x 32)
 constexpr int kListCap = 512;    // rows collected per pass over seq_slot
-constexpr int kJT = 256;         // output columns per expand block
+constexpr int kJT = 256;         // output columns per expand item
 constexpr int kExpRows = 64;     // rows per fold pass of the expand
 constexpr int kDlStride = kJT + 8;
 constexpr int kFoldVecs = kExpRows * (kJT / 8) / 256;  // base vectors per thread per pass
+constexpr uint32_t kSpinLimit = 1u << 22;             // polls before a wait gives up
+constexpr int kFusedBlocksPerCU = 2;
 
 static_assert(kShrinkSteps * 4 * 32 >= 1024, "a chunk is at most 1024 elements");
 
-__device__ __forceinline__ bool slot_active(const uint64_t* __restrict__ a_table,
-                                            const uint64_t* __restrict__ b_table,
-                                            uint32_t max_loras, int s) {
-  return s >= 0 && (uint32_t)s < max_loras && a_table[s] != 0ull && b_table[s] != 0ull;
+struct BgmvArgs {
+  const uint16_t* x;
+  const int32_t* seq_slot;
+  const uint64_t* a_table;
+  const uint64_t* b_table;
+  const float* scale_table;
+  float* partial;      // [nch][n][R] fp32 (k split only)
+  uint32_t* counters;  // [n][ntr]: chunks done per (slot, 16 columns), keyed by first row
+  uint32_t* ready;     // [n]: finished 16-column groups of a slot's xa, keyed by first row
+  uint32_t* ctl;       // [0] next item, [1] blocks done, [2] a wait gave up
+  uint16_t* xa;
+  uint16_t* out;
+  uint32_t xs, n, max_loras, k_in, n_out, R, kc, nch, ntr, os;
+};
+
+struct ShrinkSmem {
+  int rows[kListCap];
+  int wcount[4];
+  floatx4 red[4][kShrinkMT][kWave];
+  int flag;
+};
+
+struct ExpandSmem {
+  int rows[kListCap];
+  int wcount[4];
+  __attribute__((aligned(16))) uint16_t dl[kExpRows * kDlStride];
+};
+
+union BgmvSmem {
+  ShrinkSmem sh;
+  ExpandSmem ex;
+};
+
+__device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
+  return s >= 0 && (uint32_t)s < a.max_loras && a.a_table[s] != 0ull && a.b_table[s] != 0ull;
+}
+
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16 bytes of xa written by another block of the running kernel: four
+// agent-scope dword loads (coherent across XCDs).
+__device__ __forceinline__ uint4 load16_agent(const uint16_t* p) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+  return make_uint4(load_agent(q), load_agent(q + 1), load_agent(q + 2), load_agent(q + 3));
 }
 
 // Appends to `rows` (LDS) the rows of slot s from seq_slot[*pos ...], until
@@ -58,45 +116,50 @@ __device__ __forceinline__ int collect_slot_rows(const int32_t* __restrict__ seq
   return cnt;
 }
 
-__global__ __launch_bounds__(256) void bgmv_shrink_kernel(
-    const uint16_t* __restrict__ x, uint32_t xs, const int32_t* __restrict__ seq_slot, uint32_t n,
-    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
-    uint32_t max_loras, uint32_t k_in, uint32_t R, uint32_t kc, uint32_t nchunks, uint32_t ntr,
-    uint32_t total, float* __restrict__ partial, uint32_t* __restrict__ counters,
-    uint16_t* __restrict__ xa) {
-  __shared__ int rows[kListCap];
-  __shared__ int wcount[4];
-  __shared__ floatx4 red[4][kShrinkMT][kWave];
-  __shared__ int last_flag;
+// Block-wide: this thread's stores have completed, then the block meets, then
+// thread 0 adds 1 to *ctr (agent scope) and every thread gets the old value.
+__device__ __forceinline__ uint32_t block_signal(uint32_t* ctr, int* slot) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *slot = (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t old = (uint32_t)*slot;
+  __syncthreads();
+  return old;
+}
 
-  // the ntr items of one (slot, chunk) share an XCD, and so the x rows in its L2
-  const uint32_t w = xcd_group_item(ntr);
-  if (w >= total) return;
+// Shrink item w (slot-major over (slot, chunk, 16 columns)).  FUSED: xa goes
+// out with agent-scope stores and the slot's ready counter is raised when this
+// item completes a 16-column group of xa.
+template <bool FUSED>
+__device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
+  const uint32_t n = a.n, R = a.R, nchunks = a.nch, ntr = a.ntr;
   const uint32_t rt = w % ntr;
   const uint32_t c = (w / ntr) % nchunks;
   const int s = (int)(w / (ntr * nchunks));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  // The first work item also writes the zero xa rows of base rows.
+  // The first item also writes the zero xa rows of base rows.
   if (w == 0) {
     const uint32_t r8 = R / 8;
     for (uint32_t e = threadIdx.x; e < n * r8; e += 256) {
       const uint32_t row = e / r8;
-      if (!slot_active(a_table, b_table, max_loras, seq_slot[row]))
-        *reinterpret_cast<uint4*>(xa + (size_t)row * R + (e % r8) * 8) = zero16();
+      if (!slot_active(a, a.seq_slot[row]))
+        *reinterpret_cast<uint4*>(a.xa + (size_t)row * R + (e % r8) * 8) = zero16();
     }
   }
-  if (!slot_active(a_table, b_table, max_loras, s)) return;
+  if (!slot_active(a, s)) return;
 
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(a_table[s]);
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(a.a_table[s]);
   const int lg = lane >> 4;
   const int cl = lane & 15;
   const uint32_t col = rt * 16 + cl;  // xa column = A_s row served by this lane
   const bool col_ok = col < R;
-  const uint16_t* Arow = A + (size_t)(col_ok ? col : 0) * k_in;
-  const uint32_t kb = c * kc;
-  const uint32_t ke = min(kb + kc, k_in);
+  const uint16_t* Arow = A + (size_t)(col_ok ? col : 0) * a.k_in;
+  const uint32_t kb = c * a.kc;
+  const uint32_t ke = min(kb + a.kc, a.k_in);
   const uint32_t nsteps = (ke - kb + 31) / 32;
 
   // This wave's K steps are wave, wave + 4, ...: all of its A fragments are
@@ -116,10 +179,10 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(
   int first_row = -1;
   int scans = 0, last_cnt = 0;
   while (pos < n) {
-    const int cnt = collect_slot_rows(seq_slot, n, &pos, s, rows, wcount);
+    const int cnt = collect_slot_rows(a.seq_slot, n, &pos, s, sm.rows, sm.wcount);
     ++scans;
     last_cnt = cnt;
-    if (first_row < 0 && cnt > 0) first_row = rows[0];
+    if (first_row < 0 && cnt > 0) first_row = sm.rows[0];
     for (int b0 = 0; b0 < cnt; b0 += kShrinkMT * 16) {
       const int nb = min(cnt - b0, kShrinkMT * 16);
       const int nmt = (nb + 15) >> 4;
@@ -132,7 +195,7 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(
       for (int i = 0; i < kShrinkSteps; ++i) nxt[i] = zero16();
       {
         const bool ok = cl < nb;
-        const uint16_t* xr = x + (size_t)(ok ? rows[b0 + cl] : 0) * xs;
+        const uint16_t* xr = a.x + (size_t)(ok ? sm.rows[b0 + cl] : 0) * a.xs;
 #pragma unroll
         for (int i = 0; i < kShrinkSteps; ++i)
           cur[i] = (ok && kok[i]) ? load16(xr + kof[i]) : zero16();
@@ -143,7 +206,7 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(
           if (q + 1 < nmt) {
             const int li = (q + 1) * 16 + cl;
             const bool ok = li < nb;
-            const uint16_t* xr = x + (size_t)(ok ? rows[b0 + li] : 0) * xs;
+            const uint16_t* xr = a.x + (size_t)(ok ? sm.rows[b0 + li] : 0) * a.xs;
 #pragma unroll
             for (int i = 0; i < kShrinkSteps; ++i)
               nxt[i] = (ok && kok[i]) ? load16(xr + kof[i]) : zero16();
@@ -157,24 +220,30 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(
       }
 #pragma unroll
       for (int q = 0; q < kShrinkMT; ++q)
-        if (q < nmt) red[wave][q][lane] = acc[q];
+        if (q < nmt) sm.red[wave][q][lane] = acc[q];
       __syncthreads();
       for (int q = wave; q < nmt; q += 4) {
-        floatx4 sum = red[0][q][lane];
-        sum += red[1][q][lane];
-        sum += red[2][q][lane];
-        sum += red[3][q][lane];
+        floatx4 sum = sm.red[0][q][lane];
+        sum += sm.red[1][q][lane];
+        sum += sm.red[2][q][lane];
+        sum += sm.red[3][q][lane];
         if (col_ok) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int li = q * 16 + 4 * lg + i;
             if (li < nb) {
-              const uint32_t row = (uint32_t)rows[b0 + li];
-              if (nchunks == 1)
-                xa[(size_t)row * R + col] = (uint16_t)f32_to_bf16(sum[i]);
-              else  // agent-scope store: written through to where every XCD reads it
-                __hip_atomic_store(partial + ((size_t)c * n + row) * R + col, sum[i],
+              const uint32_t row = (uint32_t)sm.rows[b0 + li];
+              if (nchunks == 1) {
+                const uint16_t v = (uint16_t)f32_to_bf16(sum[i]);
+                if (FUSED)
+                  __hip_atomic_store(a.xa + (size_t)row * R + col, v, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+                else
+                  a.xa[(size_t)row * R + col] = v;
+              } else {  // agent-scope store: written through to where every XCD reads it
+                __hip_atomic_store(a.partial + ((size_t)c * n + row) * R + col, sum[i],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
             }
           }
         }
@@ -182,22 +251,17 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(
       __syncthreads();
     }
   }
-  if (nchunks == 1 || first_row < 0) return;
+  if (first_row < 0) return;
+  if (nchunks == 1) {
+    if (FUSED) block_signal(a.ready + first_row, &sm.flag);
+    return;
+  }
 
-  // k split: the block that completes the last chunk of its (slot, 16 xa
+  // k split: the item that completes the last chunk of its (slot, 16 xa
   // columns) adds the chunks in chunk order and writes xa.  The pair's counter
   // is keyed by the slot's first row (unique per slot) and is left at zero.
-  // Partials travel with agent-scope (L2-coherent) stores and loads, and each
-  // thread's stores have completed before the block's counter increment, so no
-  // whole-cache writeback or invalidate is needed.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  uint32_t* ctr = counters + (size_t)first_row * ntr + rt;
-  if (threadIdx.x == 0)
-    last_flag = (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 nchunks - 1) ? 1 : 0;
-  __syncthreads();
-  if (!last_flag) return;
+  uint32_t* ctr = a.counters + (size_t)first_row * ntr + rt;
+  if (block_signal(ctr, &sm.flag) != nchunks - 1) return;
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   const int rl = threadIdx.x >> 4;  // 16 rows x 16 columns per step
@@ -210,12 +274,12 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(
       cnt = last_cnt;
     } else {
       if (rpos >= n) break;
-      cnt = collect_slot_rows(seq_slot, n, &rpos, s, rows, wcount);
+      cnt = collect_slot_rows(a.seq_slot, n, &rpos, s, sm.rows, sm.wcount);
     }
     if (rcol < R) {
       for (int li = rl; li < cnt; li += 16) {
-        const uint32_t row = (uint32_t)rows[li];
-        float* pp = partial + (size_t)row * R + rcol;
+        const uint32_t row = (uint32_t)sm.rows[li];
+        float* pp = a.partial + (size_t)row * R + rcol;
         const size_t cstride = (size_t)n * R;
         float sum = 0.f;
         for (uint32_t c0 = 0; c0 < nchunks; c0 += 8) {
@@ -229,32 +293,46 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(
           for (int j = 0; j < 8; ++j)
             if (c0 + j < nchunks) sum = (c0 + j == 0) ? v[j] : sum + v[j];
         }
-        xa[(size_t)row * R + rcol] = (uint16_t)f32_to_bf16(sum);
+        const uint16_t bits = (uint16_t)f32_to_bf16(sum);
+        if (FUSED)
+          __hip_atomic_store(a.xa + (size_t)row * R + rcol, bits, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        else
+          a.xa[(size_t)row * R + rcol] = bits;
       }
     }
     __syncthreads();
   }
+  if (FUSED) block_signal(a.ready + first_row, &sm.flag);
 }
 
-template <int NKS>
-__global__ __launch_bounds__(256) void bgmv_expand_kernel(
-    const uint16_t* __restrict__ xa, const int32_t* __restrict__ seq_slot, uint32_t n,
-    const uint64_t* __restrict__ a_table, const uint64_t* __restrict__ b_table,
-    const float* __restrict__ scale_table, uint32_t max_loras, uint32_t n_out, uint32_t R,
-    uint16_t* __restrict__ out, uint32_t os) {
-  __shared__ int rows[kListCap];
-  __shared__ int wcount[4];
-  __shared__ __attribute__((aligned(16))) uint16_t dl[kExpRows * kDlStride];
+// Thread 0 polls the slot's ready counter (bounded; a wait that gives up sets
+// ctl[2] and lets the item go on), then the block meets.
+__device__ __forceinline__ void wait_ready(const BgmvArgs& a, int first_row) {
+  if (threadIdx.x == 0) {
+    uint32_t polls = 0;
+    while (load_agent(a.ready + first_row) < a.ntr) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++polls == kSpinLimit) {
+        __hip_atomic_store(a.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
 
-  const int s = (int)blockIdx.y;
-  if (!slot_active(a_table, b_table, max_loras, s)) return;
-  const uint16_t* B = reinterpret_cast<const uint16_t*>(b_table[s]);
-  const float scale = scale_table[s];
+// Expand item (slot s, 256 output columns from j0).  NKS = ceil(max_rank/32).
+template <int NKS, bool FUSED>
+__device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& sm) {
+  if (!slot_active(a, s)) return;
+  const uint16_t* B = reinterpret_cast<const uint16_t*>(a.b_table[s]);
+  const float scale = a.scale_table[s];
+  const uint32_t n = a.n, R = a.R, n_out = a.n_out, os = a.os;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lg = lane >> 4;
   const int cl = lane & 15;
-  const uint32_t j0 = blockIdx.x * kJT;
 
   // B_s rows of this wave's 64 columns, as MFMA A operands for every K step.
   uint4 aop[4][NKS];
@@ -275,29 +353,35 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(
   const bool fcol_ok = j0 + c8 < n_out;
 
   uint32_t pos = 0;
+  bool waited = !FUSED;
   while (pos < n) {
-    const int cnt = collect_slot_rows(seq_slot, n, &pos, s, rows, wcount);
+    const int cnt = collect_slot_rows(a.seq_slot, n, &pos, s, sm.rows, sm.wcount);
     for (int b0 = 0; b0 < cnt; b0 += kExpRows) {
       const int nb = min(cnt - b0, kExpRows);
-      // base values of the pass, issued before the MFMAs
+      // base values of the pass, issued before the MFMAs (and before the wait)
       uint4 bv[kFoldVecs];
 #pragma unroll
       for (int i = 0; i < kFoldVecs; ++i) {
         const int rl = frow + 8 * i;
         bv[i] = (rl < nb && fcol_ok)
-                    ? *reinterpret_cast<const uint4*>(out + (size_t)rows[b0 + rl] * os + j0 + c8)
+                    ? *reinterpret_cast<const uint4*>(a.out + (size_t)sm.rows[b0 + rl] * os + j0 + c8)
                     : zero16();
+      }
+      if (!waited) {  // the first pass holds the slot's first row
+        wait_ready(a, sm.rows[0]);
+        waited = true;
       }
       uint4 bop[4][NKS];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int li = p * 16 + cl;
         const bool ok = li < nb;
-        const uint16_t* xr = xa + (size_t)(ok ? rows[b0 + li] : 0) * R;
+        const uint16_t* xr = a.xa + (size_t)(ok ? sm.rows[b0 + li] : 0) * R;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const uint32_t k = ks * 32 + lg * 8;
-          bop[p][ks] = (p * 16 < nb && ok && k < R) ? load16(xr + k) : zero16();
+          const bool ld = p * 16 < nb && ok && k < R;
+          bop[p][ks] = ld ? (FUSED ? load16_agent(xr + k) : load16(xr + k)) : zero16();
         }
       }
 #pragma unroll
@@ -311,8 +395,8 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(
             // lane holds delta[row p*16+cl][cols m*16 + 4*lg .. +3] of this wave's slice
             const uint32_t d01 = pack_bf16x2(acc[0], acc[1]);
             const uint32_t d23 = pack_bf16x2(acc[2], acc[3]);
-            *reinterpret_cast<uint2*>(&dl[(p * 16 + cl) * kDlStride + wave * 64 + m * 16 +
-                                          4 * lg]) = make_uint2(d01, d23);
+            *reinterpret_cast<uint2*>(&sm.dl[(p * 16 + cl) * kDlStride + wave * 64 + m * 16 +
+                                             4 * lg]) = make_uint2(d01, d23);
           }
         }
       }
@@ -321,8 +405,8 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(
       for (int i = 0; i < kFoldVecs; ++i) {
         const int rl = frow + 8 * i;
         if (rl < nb && fcol_ok) {
-          const uint4 dv = *reinterpret_cast<const uint4*>(&dl[rl * kDlStride + c8]);
-          *reinterpret_cast<uint4*>(out + (size_t)rows[b0 + rl] * os + j0 + c8) =
+          const uint4 dv = *reinterpret_cast<const uint4*>(&sm.dl[rl * kDlStride + c8]);
+          *reinterpret_cast<uint4*>(a.out + (size_t)sm.rows[b0 + rl] * os + j0 + c8) =
               fold8(bv[i], dv, scale);
         }
       }
@@ -331,10 +415,143 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(
   }
 }
 
-// Workspace layout of a k-split shrink: fp32 partials [chunks][n][max_rank],
-// then one uint32 counter per (row, 16 xa columns).
-static size_t partial_bytes(uint32_t n, uint32_t nch, uint32_t R) {
-  return (size_t)nch * n * R * sizeof(float);
+__global__ __launch_bounds__(256) void bgmv_shrink_kernel(BgmvArgs a, uint32_t total) {
+  __shared__ ShrinkSmem sm;
+  // the ntr items of one (slot, chunk) share an XCD, and so the x rows in its L2
+  const uint32_t w = xcd_group_item(a.ntr);
+  if (w >= total) return;
+  shrink_item<false>(a, w, sm);
+}
+
+template <int NKS>
+__global__ __launch_bounds__(256) void bgmv_expand_kernel(BgmvArgs a) {
+  __shared__ ExpandSmem sm;
+  expand_item<NKS, false>(a, (int)blockIdx.y, blockIdx.x * kJT, sm);
+}
+
+// Both stages in one launch: items [0, n_shrink) are shrink items, then
+// (slot, column tile) expand items, claimed in order from ctl[0].  The last
+// block to finish puts the claim and ready counters back to zero.
+template <int NKS>
+__global__ __launch_bounds__(256) void bgmv_fused_kernel(BgmvArgs a, uint32_t n_shrink,
+                                                         uint32_t njt) {
+  __shared__ BgmvSmem sm;
+  __shared__ int claim;
+  const uint32_t total = n_shrink + a.max_loras * njt;
+  for (;;) {
+    if (threadIdx.x == 0)
+      claim = (int)__hip_atomic_fetch_add(a.ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t it = (uint32_t)claim;
+    __syncthreads();
+    if (it >= total) break;
+    if (it < n_shrink) {
+      shrink_item<true>(a, it, sm.sh);
+    } else {
+      const uint32_t e = it - n_shrink;
+      expand_item<NKS, true>(a, (int)(e / njt), (e % njt) * kJT, sm.ex);
+    }
+    __syncthreads();
+  }
+  if (block_signal(a.ctl + 1, &claim) == gridDim.x - 1) {
+    for (uint32_t i = threadIdx.x; i < a.n; i += 256)
+      __hip_atomic_store(a.ready + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(a.ctl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ctl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Workspace layout: fp32 partials [nch][n][R] (k split only), chunk counters
+// [n][ntr], ready counters [n], 4 control words.  Every region but the
+// partials must be zero before the first call and is zero after every call.
+struct WsLayout {
+  size_t partial, counters, ready, ctl, total;
+};
+
+static size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+static WsLayout ws_layout(uint32_t n, uint32_t k_in, uint32_t R) {
+  const uint32_t nch = div_ceil(k_in, bgmv_chunk(k_in, R));
+  const uint32_t ntr = div_ceil(R, 16);
+  WsLayout l;
+  l.partial = 0;
+  l.counters = round16(nch > 1 ? (size_t)nch * n * R * sizeof(float) : 0);
+  l.ready = l.counters + round16((size_t)n * ntr * sizeof(uint32_t));
+  l.ctl = l.ready + round16((size_t)n * sizeof(uint32_t));
+  l.total = l.ctl + 16;
+  return l;
+}
+
+static int make_args(const rld_route* route, const void* x, uint32_t x_row_stride,
+                     const int32_t* seq_slot, uint32_t n, void* xa, void* workspace,
+                     size_t workspace_bytes, void* base_out, uint32_t out_row_stride,
+                     BgmvArgs* a) {
+  const uint32_t R = route->max_rank, k_in = route->k_in;
+  const WsLayout l = ws_layout(n, k_in, R);
+  if (!workspace || workspace_bytes < l.total) return RLD_ENOSPACE;
+  if (!aligned16(workspace)) return RLD_EALIGN;
+  char* ws = static_cast<char*>(workspace);
+  a->x = static_cast<const uint16_t*>(x);
+  a->seq_slot = seq_slot;
+  a->a_table = route->a_table;
+  a->b_table = route->b_table;
+  a->scale_table = route->scale_table;
+  a->partial = reinterpret_cast<float*>(ws + l.partial);
+  a->counters = reinterpret_cast<uint32_t*>(ws + l.counters);
+  a->ready = reinterpret_cast<uint32_t*>(ws + l.ready);
+  a->ctl = reinterpret_cast<uint32_t*>(ws + l.ctl);
+  a->xa = static_cast<uint16_t*>(xa);
+  a->out = static_cast<uint16_t*>(base_out);
+  a->xs = x_row_stride;
+  a->n = n;
+  a->max_loras = route->max_loras;
+  a->k_in = k_in;
+  a->n_out = route->n_out;
+  a->R = R;
+  a->kc = bgmv_chunk(k_in, R);
+  a->nch = div_ceil(k_in, a->kc);
+  a->ntr = div_ceil(R, 16);
+  a->os = out_row_stride;
+  return RLD_OK;
+}
+
+typedef void (*BgmvKernel)(BgmvArgs);
+typedef void (*FusedKernel)(BgmvArgs, uint32_t, uint32_t);
+
+static BgmvKernel pick_expand(uint32_t R) {
+  switch (div_ceil(R, 32)) {
+    case 1: return bgmv_expand_kernel<1>;
+    case 2: return bgmv_expand_kernel<2>;
+    case 3: return bgmv_expand_kernel<3>;
+    default: return bgmv_expand_kernel<4>;
+  }
+}
+
+static FusedKernel pick_fused(uint32_t R) {
+  switch (div_ceil(R, 32)) {
+    case 1: return bgmv_fused_kernel<1>;
+    case 2: return bgmv_fused_kernel<2>;
+    case 3: return bgmv_fused_kernel<3>;
+    default: return bgmv_fused_kernel<4>;
+  }
+}
+
+// Persistent grid of the fused kernel: kFusedBlocksPerCU blocks per compute unit
+// of the current device (queried once per device).
+static uint32_t fused_grid() {
+  static uint32_t cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = (uint32_t)cus * kFusedBlocksPerCU;
+  }
+  return cached[dev];
 }
 
 }  // namespace rld
@@ -343,10 +560,7 @@ using namespace rld;
 
 extern "C" size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank) {
   if (k_in == 0 || max_rank == 0) return 0;
-  const uint32_t nch = div_ceil(k_in, bgmv_chunk(k_in, max_rank));
-  if (nch <= 1) return 0;
-  const size_t ctr = (size_t)n * div_ceil(max_rank, 16) * sizeof(uint32_t);
-  return partial_bytes(n, nch, max_rank) + ((ctr + 15) & ~(size_t)15);
+  return ws_layout(n, k_in, max_rank).total;
 }
 
 extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x_row_stride,
@@ -359,23 +573,13 @@ extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x
   if (!seq_slot || !xa) return RLD_EINVAL;
   if ((st = check_rows(x, x_row_stride, route->k_in))) return st;
   if (!aligned16(xa)) return RLD_EALIGN;
-  const uint32_t R = route->max_rank, k_in = route->k_in;
-  const uint32_t kc = bgmv_chunk(k_in, R);
-  const uint32_t nch = div_ceil(k_in, kc);
-  const uint32_t ntr = div_ceil(R, 16);
-  const size_t need = rld_bgmv_workspace_bytes(n, k_in, R);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return RLD_ENOSPACE;
-  if (need > 0 && !aligned16(workspace)) return RLD_EALIGN;
-  float* partial = static_cast<float*>(workspace);
-  uint32_t* counters =
-      need > 0 ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                             partial_bytes(n, nch, R))
-               : nullptr;
-  const uint32_t total = route->max_loras * nch * ntr;
-  hipLaunchKernelGGL(bgmv_shrink_kernel, dim3(xcd_group_grid(total, ntr)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x),
-                     x_row_stride, seq_slot, n, route->a_table, route->b_table, route->max_loras,
-                     k_in, R, kc, nch, ntr, total, partial, counters, static_cast<uint16_t*>(xa));
+  BgmvArgs a;
+  if ((st = make_args(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
+                      nullptr, 0, &a)))
+    return st;
+  const uint32_t total = route->max_loras * a.nch * a.ntr;
+  hipLaunchKernelGGL(bgmv_shrink_kernel, dim3(xcd_group_grid(total, a.ntr)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), a, total);
   return launch_status();
 }
 
@@ -389,18 +593,22 @@ extern "C" int rld_bgmv_expand_fold(const rld_route* route, const void* xa,
   if (!seq_slot || !xa) return RLD_EINVAL;
   if (!aligned16(xa)) return RLD_EALIGN;
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
-  auto kern = bgmv_expand_kernel<1>;
-  switch (div_ceil(route->max_rank, 32)) {
-    case 1: kern = bgmv_expand_kernel<1>; break;
-    case 2: kern = bgmv_expand_kernel<2>; break;
-    case 3: kern = bgmv_expand_kernel<3>; break;
-    default: kern = bgmv_expand_kernel<4>; break;
-  }
-  hipLaunchKernelGGL(kern, dim3(div_ceil(route->n_out, kJT), route->max_loras), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint16_t*>(xa),
-                     seq_slot, n, route->a_table, route->b_table, route->scale_table,
-                     route->max_loras, route->n_out, route->max_rank,
-                     static_cast<uint16_t*>(base_out), out_row_stride);
+  BgmvArgs a = {};
+  a.seq_slot = seq_slot;
+  a.a_table = route->a_table;
+  a.b_table = route->b_table;
+  a.scale_table = route->scale_table;
+  a.xa = const_cast<uint16_t*>(static_cast<const uint16_t*>(xa));
+  a.out = static_cast<uint16_t*>(base_out);
+  a.n = n;
+  a.max_loras = route->max_loras;
+  a.k_in = route->k_in;
+  a.n_out = route->n_out;
+  a.R = route->max_rank;
+  a.ntr = div_ceil(a.R, 16);
+  a.os = out_row_stride;
+  hipLaunchKernelGGL(pick_expand(a.R), dim3(div_ceil(route->n_out, kJT), route->max_loras),
+                     dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
   return launch_status();
 }
 
@@ -410,10 +618,19 @@ extern "C" int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_st
                         size_t workspace_bytes, void* stream) {
   int st = check_route(route);
   if (st) return st;
+  if (route->max_loras > 65535u) return RLD_EUNSUPPORTED;
   if (n == 0) return RLD_OK;
+  if (!seq_slot || !xa) return RLD_EINVAL;
+  if ((st = check_rows(x, x_row_stride, route->k_in))) return st;
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
-  st = rld_bgmv_shrink(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
-                       stream);
-  if (st) return st;
-  return rld_bgmv_expand_fold(route, xa, seq_slot, n, base_out, out_row_stride, stream);
+  if (!aligned16(xa)) return RLD_EALIGN;
+  BgmvArgs a;
+  if ((st = make_args(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
+                      base_out, out_row_stride, &a)))
+    return st;
+  const uint32_t n_shrink = route->max_loras * a.nch * a.ntr;
+  const uint32_t njt = div_ceil(route->n_out, kJT);
+  hipLaunchKernelGGL(pick_fused(a.R), dim3(fused_grid()), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), a, n_shrink, njt);
+  return launch_status();
 }

@@ -179,10 +179,23 @@ class BgmvRun:
                         self.xa, self.ws, self.ws_bytes, stream)
         R.check(st, f"rld_bgmv {c.module}")
 
-    def run_all(self, keep_xa=True):
+    def run_call_two_stage(self, i, stream=None):
+        """The same call through rld_bgmv_shrink then rld_bgmv_expand_fold."""
+        c = self.wl.calls[i]
+        R.check(R.rld_bgmv_shrink(self.routes[i].route, self.bufs[c.x_buf].ptr(), c.x_row_stride,
+                                  self.seq, self.wl.n, self.xa, self.ws, self.ws_bytes, stream),
+                f"rld_bgmv_shrink {c.module}")
+        R.check(R.rld_bgmv_expand_fold(self.routes[i].route, self.xa, self.seq, self.wl.n,
+                                       self.bufs[c.out_buf].ptr(c.out_offset), c.out_row_stride,
+                                       stream), f"rld_bgmv_expand_fold {c.module}")
+
+    def run_all(self, keep_xa=True, two_stage=False):
         self.xa_by_call = []
         for i, c in enumerate(self.wl.calls):
-            self.run_call(i)
+            if two_stage:
+                self.run_call_two_stage(i)
+            else:
+                self.run_call(i)
             if keep_xa:
                 torch.cuda.synchronize()
                 self.xa_by_call.append(
