@@ -120,7 +120,8 @@ class Step:
                 bufs = {k: to_device_u16(v, dev) for k, v in wl.buffers.items()}
                 rmax = max(c.max_rank for c in wl.calls)
                 xa = torch.zeros(wl.n * rmax + 8, dtype=torch.int16, device=dev)
-                wsb = max(R.rld_bgmv_workspace_bytes(wl.n, c.k_in, c.max_rank) for c in wl.calls)
+                wsb = max(R.rld_bgmv_workspace_bytes(wl.n, c.k_in, c.max_rank, c.max_loras)
+                          for c in wl.calls)
                 ws = torch.zeros(max(wsb, 16) // 4 + 4, dtype=torch.float32, device=dev)
                 keep += [seq, bufs, xa, ws]
                 for c in wl.calls:
@@ -130,12 +131,16 @@ class Step:
                     x = bufs[c.x_buf].data_ptr()
                     out = bufs[c.out_buf].data_ptr() + 2 * c.out_offset
 
-                    def bgmv(rt=rt, c=c, x=x, out=out, seq=seq, xa=xa, ws=ws, wsb=wsb, n=wl.n):
-                        return R.rld_bgmv(rt.route, x, c.x_row_stride, seq, n, out,
-                                          c.out_row_stride, xa, ws, wsb)
+                    def shrink(rt=rt, c=c, x=x, seq=seq, xa=xa, ws=ws, wsb=wsb, n=wl.n):
+                        return R.rld_bgmv_shrink(rt.route, x, c.x_row_stride, seq, n, xa, ws, wsb)
 
-                    self.calls.append((f"{tag}.{c.module}", "bgmv_fused_kernel", bgmv, sb + eb,
-                                       fl, wl.n))
+                    def expand(rt=rt, c=c, out=out, seq=seq, xa=xa, n=wl.n):
+                        return R.rld_bgmv_expand_fold(rt.route, xa, seq, n, out, c.out_row_stride)
+
+                    self.calls.append((f"{tag}.{c.module}.shrink", "bgmv_shrink_kernel", shrink,
+                                       sb, fl / 2, wl.n))
+                    self.calls.append((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", expand,
+                                       eb, fl / 2, 0))
                     self.rows += wl.n
             elif tag == "gather":
                 rt = MoeRoute(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank, wl.k_in,

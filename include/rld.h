@@ -161,9 +161,22 @@ int rld_gather_grids(uint32_t max_rank, uint32_t n_out, uint32_t n_rows, uint32_
 
 /* -------------------------------------------------------------- device ---- */
 
-/* Bytes of fp32 workspace rld_bgmv_shrink needs for n rows (partial sums of
- * the k_in split; 0 when the split has a single chunk). */
-size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank);
+/* Bytes of workspace the BGMV entry points need for a call with these sizes:
+ * the fp32 partial sums of the k_in split ([chunks][n][max_rank], none when
+ * k_in fits one chunk) plus 32 * max_loras bytes of chunk counters.  Returns
+ * 0 if k_in, max_rank or max_loras is 0.
+ *
+ * Workspace contract (rld_bgmv_shrink and rld_bgmv):
+ *   - device memory, 16-byte aligned, of workspace_bytes >= the size above;
+ *     one buffer may serve calls of different shapes if it is as large as the
+ *     largest of them and the same workspace_bytes is passed every time (the
+ *     counters sit at the end of the buffer, keyed by slot);
+ *   - zero-filled once before its first use (e.g. hipMemset at allocation);
+ *     every call leaves the counters at zero again; do not write them;
+ *   - calls that share a workspace must not run at the same time (same stream,
+ *     or otherwise ordered). */
+size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank,
+                                uint32_t max_loras);
 
 /* Routed BGMV shrink (apply_lora_bgmv, kernel 1): for every row i < n with an
  * active slot s = seq_slot[i], xa[i, k] = bf16(sum_c x[i*x_row_stride + c] *
@@ -171,8 +184,7 @@ size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank);
  *   x        device BF16, row i at x + i*x_row_stride, k_in elements read
  *   seq_slot device int32 [n], contents may change between calls
  *   xa       device BF16 [n, max_rank] (row stride max_rank), written
- *   workspace device, >= rld_bgmv_workspace_bytes(n, k_in, max_rank) bytes
- *            (may be NULL when that is 0); contents are scratch.
+ *   workspace see rld_bgmv_workspace_bytes (RLD_ENOSPACE if smaller)
  * n == 0 is a no-op.  The per-row result does not depend on n or on the
  * other rows, so a batched call is bit-identical to n one-row calls. */
 int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x_row_stride,
@@ -188,7 +200,8 @@ int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x_row_stride
 int rld_bgmv_expand_fold(const rld_route* route, const void* xa, const int32_t* seq_slot,
                          uint32_t n, void* base_out, uint32_t out_row_stride, void* stream);
 
-/* apply_lora_bgmv: shrink then expand + fold on the same stream. */
+/* apply_lora_bgmv: rld_bgmv_shrink then rld_bgmv_expand_fold on the same
+ * stream. */
 int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_stride,
              const int32_t* seq_slot, uint32_t n, void* base_out, uint32_t out_row_stride,
              void* xa, void* workspace, size_t workspace_bytes, void* stream);

@@ -83,7 +83,7 @@ _SIGS = {
     "rld_grouped_wc": (c_uint32, [c_uint32, c_uint32]),
     "rld_gather_row_token": (c_uint32, [c_uint32, c_uint32]),
     "rld_gather_grids": (c_int, [c_uint32, c_uint32, c_uint32, _P]),
-    "rld_bgmv_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32]),
+    "rld_bgmv_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32, c_uint32]),
     "rld_bgmv_shrink": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
     "rld_bgmv_expand_fold": (c_int, [_R, _P, _P, c_uint32, _P, c_uint32, _P]),
     "rld_bgmv": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
@@ -188,8 +188,8 @@ def rld_gather_grids(max_rank, n_out, n_rows, out):
     return _lib.rld_gather_grids(max_rank, n_out, n_rows, ptr(out))
 
 
-def rld_bgmv_workspace_bytes(n, k_in, max_rank):
-    return _lib.rld_bgmv_workspace_bytes(n, k_in, max_rank)
+def rld_bgmv_workspace_bytes(n, k_in, max_rank, max_loras):
+    return _lib.rld_bgmv_workspace_bytes(n, k_in, max_rank, max_loras)
 
 
 def rld_status_string(status):

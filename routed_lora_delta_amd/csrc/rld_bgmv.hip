@@ -26,18 +26,11 @@
 //                64-row pass are loaded before its MFMAs, deltas are rounded to
 //                BF16 into LDS, and the fold writes 16-byte coalesced vectors.
 //
-// rld_bgmv_shrink and rld_bgmv_expand_fold launch one kernel each.  rld_bgmv
-// runs both stages in one persistent kernel: blocks claim items from a counter
-// in the workspace, every shrink item before every expand item.  An expand item
-// loads its B tile and the base values of its first pass, then waits until its
-// slot's xa is complete (a per-slot counter, raised by the shrink items that
-// finish it).  An item waits only on items claimed before it, whose blocks are
-// running and never wait, so the wait always ends; one slot's expand streams
-// while later slots still shrink.  Cross-block data (fp32 partials, xa inside
-// the fused kernel, counters) moves with agent-scope stores and loads, which
-// are coherent across the XCDs' L2 caches, and each producer's stores have
-// completed before it raises a counter.  The per-row arithmetic is the same in
-// both forms, so they give identical bits.
+// k-split partials move between blocks with agent-scope (L2-coherent across
+// XCDs) stores and loads, and each block's stores have completed before it
+// raises its group's counter, so no whole-cache writeback or invalidate is
+// needed.  rld_bgmv launches the shrink, then the expand, on the caller's
+// stream.
 #include "rld_device.hpp"
 #include "rld_internal.hpp"
 
@@ -50,8 +43,6 @@ constexpr int kJT = 256;         // output columns per expand item
 constexpr int kExpRows = 64;     // rows per fold pass of the expand
 constexpr int kDlStride = kJT + 8;
 constexpr int kFoldVecs = kExpRows * (kJT / 8) / 256;  // base vectors per thread per pass
-constexpr uint32_t kSpinLimit = 1u << 22;             // polls before a wait gives up
-constexpr int kFusedBlocksPerCU = 2;
 
 static_assert(kShrinkSteps * 4 * 32 >= 1024, "a chunk is at most 1024 elements");
 
@@ -61,10 +52,9 @@ struct BgmvArgs {
   const uint64_t* a_table;
   const uint64_t* b_table;
   const float* scale_table;
-  float* partial;      // [nch][n][R] fp32 (k split only)
-  uint32_t* counters;  // [n][ntr]: chunks done per (slot, 16 columns), keyed by first row
-  uint32_t* ready;     // [n]: finished 16-column groups of a slot's xa, keyed by first row
-  uint32_t* ctl;       // [0] next item, [1] blocks done, [2] a wait gave up
+  float* partial;  // [nch][n][R] fp32 (k split only), at the start of the workspace
+  uint32_t* book;  // end of the workspace: slot s's 8 chunk counters (one per
+                   // 16-column group of xa) are the 8 words at book - 8 (s + 1)
   uint16_t* xa;
   uint16_t* out;
   uint32_t xs, n, max_loras, k_in, n_out, R, kc, nch, ntr, os;
@@ -83,24 +73,12 @@ struct ExpandSmem {
   __attribute__((aligned(16))) uint16_t dl[kExpRows * kDlStride];
 };
 
-union BgmvSmem {
-  ShrinkSmem sh;
-  ExpandSmem ex;
-};
+__device__ __forceinline__ uint32_t* slot_counters(const BgmvArgs& a, int s) {
+  return a.book - 8 * ((size_t)s + 1);
+}
 
 __device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
   return s >= 0 && (uint32_t)s < a.max_loras && a.a_table[s] != 0ull && a.b_table[s] != 0ull;
-}
-
-__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// 16 bytes of xa written by another block of the running kernel: four
-// agent-scope dword loads (coherent across XCDs).
-__device__ __forceinline__ uint4 load16_agent(const uint16_t* p) {
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-  return make_uint4(load_agent(q), load_agent(q + 1), load_agent(q + 2), load_agent(q + 3));
 }
 
 // Appends to `rows` (LDS) the rows of slot s from seq_slot[*pos ...], until
@@ -129,10 +107,7 @@ __device__ __forceinline__ uint32_t block_signal(uint32_t* ctr, int* slot) {
   return old;
 }
 
-// Shrink item w (slot-major over (slot, chunk, 16 columns)).  FUSED: xa goes
-// out with agent-scope stores and the slot's ready counter is raised when this
-// item completes a 16-column group of xa.
-template <bool FUSED>
+// Shrink item w (slot-major over (slot, chunk, 16 columns)).
 __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
   const uint32_t n = a.n, R = a.R, nchunks = a.nch, ntr = a.ntr;
   const uint32_t rt = w % ntr;
@@ -234,12 +209,7 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
             if (li < nb) {
               const uint32_t row = (uint32_t)sm.rows[b0 + li];
               if (nchunks == 1) {
-                const uint16_t v = (uint16_t)f32_to_bf16(sum[i]);
-                if (FUSED)
-                  __hip_atomic_store(a.xa + (size_t)row * R + col, v, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-                else
-                  a.xa[(size_t)row * R + col] = v;
+                a.xa[(size_t)row * R + col] = (uint16_t)f32_to_bf16(sum[i]);
               } else {  // agent-scope store: written through to where every XCD reads it
                 __hip_atomic_store(a.partial + ((size_t)c * n + row) * R + col, sum[i],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -251,16 +221,12 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
       __syncthreads();
     }
   }
-  if (first_row < 0) return;
-  if (nchunks == 1) {
-    if (FUSED) block_signal(a.ready + first_row, &sm.flag);
-    return;
-  }
+  if (first_row < 0 || nchunks == 1) return;
 
   // k split: the item that completes the last chunk of its (slot, 16 xa
-  // columns) adds the chunks in chunk order and writes xa.  The pair's counter
-  // is keyed by the slot's first row (unique per slot) and is left at zero.
-  uint32_t* ctr = a.counters + (size_t)first_row * ntr + rt;
+  // columns) adds the chunks in chunk order and writes xa.  The group's
+  // counter is left at zero.
+  uint32_t* ctr = slot_counters(a, s) + rt;
   if (block_signal(ctr, &sm.flag) != nchunks - 1) return;
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
@@ -293,37 +259,15 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
           for (int j = 0; j < 8; ++j)
             if (c0 + j < nchunks) sum = (c0 + j == 0) ? v[j] : sum + v[j];
         }
-        const uint16_t bits = (uint16_t)f32_to_bf16(sum);
-        if (FUSED)
-          __hip_atomic_store(a.xa + (size_t)row * R + rcol, bits, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        else
-          a.xa[(size_t)row * R + rcol] = bits;
+        a.xa[(size_t)row * R + rcol] = (uint16_t)f32_to_bf16(sum);
       }
     }
     __syncthreads();
   }
-  if (FUSED) block_signal(a.ready + first_row, &sm.flag);
-}
-
-// Thread 0 polls the slot's ready counter (bounded; a wait that gives up sets
-// ctl[2] and lets the item go on), then the block meets.
-__device__ __forceinline__ void wait_ready(const BgmvArgs& a, int first_row) {
-  if (threadIdx.x == 0) {
-    uint32_t polls = 0;
-    while (load_agent(a.ready + first_row) < a.ntr) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++polls == kSpinLimit) {
-        __hip_atomic_store(a.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __syncthreads();
 }
 
 // Expand item (slot s, 256 output columns from j0).  NKS = ceil(max_rank/32).
-template <int NKS, bool FUSED>
+template <int NKS>
 __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& sm) {
   if (!slot_active(a, s)) return;
   const uint16_t* B = reinterpret_cast<const uint16_t*>(a.b_table[s]);
@@ -353,12 +297,11 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
   const bool fcol_ok = j0 + c8 < n_out;
 
   uint32_t pos = 0;
-  bool waited = !FUSED;
   while (pos < n) {
     const int cnt = collect_slot_rows(a.seq_slot, n, &pos, s, sm.rows, sm.wcount);
     for (int b0 = 0; b0 < cnt; b0 += kExpRows) {
       const int nb = min(cnt - b0, kExpRows);
-      // base values of the pass, issued before the MFMAs (and before the wait)
+      // base values of the pass, issued before the MFMAs
       uint4 bv[kFoldVecs];
 #pragma unroll
       for (int i = 0; i < kFoldVecs; ++i) {
@@ -366,10 +309,6 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
         bv[i] = (rl < nb && fcol_ok)
                     ? *reinterpret_cast<const uint4*>(a.out + (size_t)sm.rows[b0 + rl] * os + j0 + c8)
                     : zero16();
-      }
-      if (!waited) {  // the first pass holds the slot's first row
-        wait_ready(a, sm.rows[0]);
-        waited = true;
       }
       uint4 bop[4][NKS];
 #pragma unroll
@@ -380,8 +319,7 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const uint32_t k = ks * 32 + lg * 8;
-          const bool ld = p * 16 < nb && ok && k < R;
-          bop[p][ks] = ld ? (FUSED ? load16_agent(xr + k) : load16(xr + k)) : zero16();
+          bop[p][ks] = (p * 16 < nb && ok && k < R) ? load16(xr + k) : zero16();
         }
       }
 #pragma unroll
@@ -420,77 +358,38 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(BgmvArgs a, uint32_t t
   // the ntr items of one (slot, chunk) share an XCD, and so the x rows in its L2
   const uint32_t w = xcd_group_item(a.ntr);
   if (w >= total) return;
-  shrink_item<false>(a, w, sm);
+  shrink_item(a, w, sm);
 }
 
 template <int NKS>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(BgmvArgs a) {
   __shared__ ExpandSmem sm;
-  expand_item<NKS, false>(a, (int)blockIdx.y, blockIdx.x * kJT, sm);
+  expand_item<NKS>(a, (int)blockIdx.y, blockIdx.x * kJT, sm);
 }
 
-// Both stages in one launch: items [0, n_shrink) are shrink items, then
-// (slot, column tile) expand items, claimed in order from ctl[0].  The last
-// block to finish puts the claim and ready counters back to zero.
-template <int NKS>
-__global__ __launch_bounds__(256) void bgmv_fused_kernel(BgmvArgs a, uint32_t n_shrink,
-                                                         uint32_t njt) {
-  __shared__ BgmvSmem sm;
-  __shared__ int claim;
-  const uint32_t total = n_shrink + a.max_loras * njt;
-  for (;;) {
-    if (threadIdx.x == 0)
-      claim = (int)__hip_atomic_fetch_add(a.ctl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const uint32_t it = (uint32_t)claim;
-    __syncthreads();
-    if (it >= total) break;
-    if (it < n_shrink) {
-      shrink_item<true>(a, it, sm.sh);
-    } else {
-      const uint32_t e = it - n_shrink;
-      expand_item<NKS, true>(a, (int)(e / njt), (e % njt) * kJT, sm.ex);
-    }
-    __syncthreads();
-  }
-  if (block_signal(a.ctl + 1, &claim) == gridDim.x - 1) {
-    for (uint32_t i = threadIdx.x; i < a.n; i += 256)
-      __hip_atomic_store(a.ready + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) {
-      __hip_atomic_store(a.ctl, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.ctl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-}
-
-// Workspace layout: fp32 partials [nch][n][R] (k split only), chunk counters
-// [n][ntr], ready counters [n], 4 control words.  Every region but the
-// partials must be zero before the first call and is zero after every call.
-struct WsLayout {
-  size_t partial, counters, ready, ctl, total;
-};
-
+// Workspace: fp32 partials [nch][n][R] from the start (k split only), and at
+// the end of the caller's buffer (its size rounded down to 16 bytes) 8 chunk
+// counters per slot.  Keying the counters to the end of the buffer and to
+// slots keeps them in one place for every call that shares the buffer,
+// whatever their shapes.  They must be zero before the first call and are zero
+// after every call.
 static size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
 
-static WsLayout ws_layout(uint32_t n, uint32_t k_in, uint32_t R) {
+static size_t partial_bytes(uint32_t n, uint32_t k_in, uint32_t R) {
   const uint32_t nch = div_ceil(k_in, bgmv_chunk(k_in, R));
-  const uint32_t ntr = div_ceil(R, 16);
-  WsLayout l;
-  l.partial = 0;
-  l.counters = round16(nch > 1 ? (size_t)nch * n * R * sizeof(float) : 0);
-  l.ready = l.counters + round16((size_t)n * ntr * sizeof(uint32_t));
-  l.ctl = l.ready + round16((size_t)n * sizeof(uint32_t));
-  l.total = l.ctl + 16;
-  return l;
+  return nch > 1 ? round16((size_t)nch * n * R * sizeof(float)) : 0;
 }
+
+static size_t book_bytes(uint32_t max_loras) { return (size_t)max_loras * 32; }
 
 static int make_args(const rld_route* route, const void* x, uint32_t x_row_stride,
                      const int32_t* seq_slot, uint32_t n, void* xa, void* workspace,
                      size_t workspace_bytes, void* base_out, uint32_t out_row_stride,
                      BgmvArgs* a) {
   const uint32_t R = route->max_rank, k_in = route->k_in;
-  const WsLayout l = ws_layout(n, k_in, R);
-  if (!workspace || workspace_bytes < l.total) return RLD_ENOSPACE;
+  const size_t end = workspace_bytes & ~(size_t)15;
+  if (!workspace || end < partial_bytes(n, k_in, R) + book_bytes(route->max_loras))
+    return RLD_ENOSPACE;
   if (!aligned16(workspace)) return RLD_EALIGN;
   char* ws = static_cast<char*>(workspace);
   a->x = static_cast<const uint16_t*>(x);
@@ -498,10 +397,8 @@ static int make_args(const rld_route* route, const void* x, uint32_t x_row_strid
   a->a_table = route->a_table;
   a->b_table = route->b_table;
   a->scale_table = route->scale_table;
-  a->partial = reinterpret_cast<float*>(ws + l.partial);
-  a->counters = reinterpret_cast<uint32_t*>(ws + l.counters);
-  a->ready = reinterpret_cast<uint32_t*>(ws + l.ready);
-  a->ctl = reinterpret_cast<uint32_t*>(ws + l.ctl);
+  a->partial = reinterpret_cast<float*>(ws);
+  a->book = reinterpret_cast<uint32_t*>(ws + end);
   a->xa = static_cast<uint16_t*>(xa);
   a->out = static_cast<uint16_t*>(base_out);
   a->xs = x_row_stride;
@@ -518,7 +415,6 @@ static int make_args(const rld_route* route, const void* x, uint32_t x_row_strid
 }
 
 typedef void (*BgmvKernel)(BgmvArgs);
-typedef void (*FusedKernel)(BgmvArgs, uint32_t, uint32_t);
 
 static BgmvKernel pick_expand(uint32_t R) {
   switch (div_ceil(R, 32)) {
@@ -529,38 +425,14 @@ static BgmvKernel pick_expand(uint32_t R) {
   }
 }
 
-static FusedKernel pick_fused(uint32_t R) {
-  switch (div_ceil(R, 32)) {
-    case 1: return bgmv_fused_kernel<1>;
-    case 2: return bgmv_fused_kernel<2>;
-    case 3: return bgmv_fused_kernel<3>;
-    default: return bgmv_fused_kernel<4>;
-  }
-}
-
-// Persistent grid of the fused kernel: kFusedBlocksPerCU blocks per compute unit
-// of the current device (queried once per device).
-static uint32_t fused_grid() {
-  static uint32_t cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    cached[dev] = (uint32_t)cus * kFusedBlocksPerCU;
-  }
-  return cached[dev];
-}
-
 }  // namespace rld
 
 using namespace rld;
 
-extern "C" size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank) {
-  if (k_in == 0 || max_rank == 0) return 0;
-  return ws_layout(n, k_in, max_rank).total;
+extern "C" size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank,
+                                           uint32_t max_loras) {
+  if (k_in == 0 || max_rank == 0 || max_loras == 0) return 0;
+  return partial_bytes(n, k_in, max_rank) + book_bytes(max_loras);
 }
 
 extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x_row_stride,
@@ -618,19 +490,10 @@ extern "C" int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_st
                         size_t workspace_bytes, void* stream) {
   int st = check_route(route);
   if (st) return st;
-  if (route->max_loras > 65535u) return RLD_EUNSUPPORTED;
   if (n == 0) return RLD_OK;
-  if (!seq_slot || !xa) return RLD_EINVAL;
-  if ((st = check_rows(x, x_row_stride, route->k_in))) return st;
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
-  if (!aligned16(xa)) return RLD_EALIGN;
-  BgmvArgs a;
-  if ((st = make_args(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
-                      base_out, out_row_stride, &a)))
-    return st;
-  const uint32_t n_shrink = route->max_loras * a.nch * a.ntr;
-  const uint32_t njt = div_ceil(route->n_out, kJT);
-  hipLaunchKernelGGL(pick_fused(a.R), dim3(fused_grid()), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), a, n_shrink, njt);
-  return launch_status();
+  st = rld_bgmv_shrink(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
+                       stream);
+  if (st) return st;
+  return rld_bgmv_expand_fold(route, xa, seq_slot, n, base_out, out_row_stride, stream);
 }

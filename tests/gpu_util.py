@@ -167,7 +167,8 @@ class BgmvRun:
                        for c in wl.calls]
         rmax = max(c.max_rank for c in wl.calls)
         self.xa = torch.zeros(max(1, wl.n) * rmax + 8, dtype=torch.int16, device=device)
-        ws = max(R.rld_bgmv_workspace_bytes(wl.n, c.k_in, c.max_rank) for c in wl.calls)
+        ws = max(R.rld_bgmv_workspace_bytes(wl.n, c.k_in, c.max_rank, c.max_loras)
+                 for c in wl.calls)
         self.ws_bytes = ws
         self.ws = torch.zeros(max(ws, 16) // 4 + 4, dtype=torch.float32, device=device)
         self.xa_by_call = []

@@ -204,7 +204,7 @@ def test_bgmv_rejects_bad_routes(kw, status):
 def test_bgmv_rejects_bad_buffers():
     rt = _route()
     n = 4
-    ws = R.rld_bgmv_workspace_bytes(n, 256, 16)
+    ws = R.rld_bgmv_workspace_bytes(n, 256, 16, 4)
     sh = lambda **k: R.rld_bgmv_shrink(  # noqa: E731
         rt, k.get("x", FAKE), k.get("xs", 256), k.get("seq", FAKE), n, k.get("xa", FAKE),
         k.get("ws", FAKE), k.get("wsb", ws), 0)
@@ -224,14 +224,24 @@ def test_bgmv_rejects_bad_buffers():
 
 
 def test_bgmv_workspace_contract():
-    # k-split shapes need a workspace; a short one is refused before any launch
+    # the workspace holds the k-split partials and per-slot bookkeeping; a short
+    # one is refused before any launch, by every entry point that takes one
     rt = _route(k_in=12288, n_out=4096, max_rank=64, max_loras=32)
-    need = R.rld_bgmv_workspace_bytes(256, 12288, 64)
-    assert need > 0
-    assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, FAKE, need - 4, 0) == \
-        R.RLD_ENOSPACE
+    need = R.rld_bgmv_workspace_bytes(256, 12288, 64, 32)
+    # 12 chunks of fp32 partials, then 8 chunk counters per slot
+    assert need == 12 * 256 * 64 * 4 + 32 * 32
+    for short in (need - 32, need // 2, 16, 0):
+        assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, FAKE, short, 0) == \
+            R.RLD_ENOSPACE
+        assert R.rld_bgmv(rt, FAKE, 12288, FAKE, 256, FAKE, 4096, FAKE, FAKE, short, 0) == \
+            R.RLD_ENOSPACE
     assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, 0, need, 0) == R.RLD_ENOSPACE
-    assert R.rld_bgmv_workspace_bytes(256, 0, 64) == 0
+    assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, FAKE + 8, need, 0) == \
+        R.RLD_EALIGN
+    # a single chunk needs no partials, only the counters
+    assert R.rld_bgmv_workspace_bytes(4, 256, 64, 2) == 2 * 32
+    assert R.rld_bgmv_workspace_bytes(256, 0, 64, 32) == 0
+    assert R.rld_bgmv_workspace_bytes(256, 4096, 64, 0) == 0
 
 
 def test_empty_batches_are_noops():

@@ -112,7 +112,7 @@ def test_bgmv_batched_equals_single_rows():
         c = wl.calls[0]
         single = BgmvRun(wl, dev)
         xa1 = torch.zeros(R_ + 8, dtype=torch.int16, device=dev)
-        ws_b = R.rld_bgmv_workspace_bytes(1, k_in, R_)
+        ws_b = R.rld_bgmv_workspace_bytes(1, k_in, R_, 8)
         ws1 = torch.zeros(max(ws_b, 16) // 4 + 4, dtype=torch.float32, device=dev)
         xas = []
         for i in range(n):
@@ -126,41 +126,14 @@ def test_bgmv_batched_equals_single_rows():
         assert np.array_equal(single.outputs()["out"], batched_out)
 
 
-FUSED_CASES = [
-    # n, k_in, n_out, max_rank, max_loras, ranks, zipf
-    (4, 256, 256, 8, 2, (4, 8), None),
-    (64, 4096, 1024, 16, 16, (8, 16), None),
-    (256, 12288, 4096, 64, 32, (8, 16, 32, 64), 1.1),
-    (700, 2048, 776, 32, 5, (16, 32), 1.1),
-    (1400, 1024, 264, 16, 2, (8, 16), None),
-]
-
-
-@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: f"n{c[0]}k{c[1]}o{c[2]}r{c[3]}")
-def test_bgmv_fused_equals_two_stage(case):
-    """rld_bgmv (one persistent kernel) and rld_bgmv_shrink + rld_bgmv_expand_fold
-    give bit-identical xa and outputs; the two-stage result also meets the
-    oracle."""
-    dev = require_gpu()
-    n, k_in, n_out, R_, L, ranks, zipf = case
-    wl = W.bgmv_custom(21, n, k_in, n_out, R_, L, ranks, base_frac=0.1, zipf=zipf)
-    say(f"case: fused vs two-stage {case}")
-    fused = BgmvRun(wl, dev)
-    fused.run_all()
-    two = BgmvRun(wl, dev)
-    two.run_all(two_stage=True)
-    assert np.array_equal(fused.xa_by_call[0], two.xa_by_call[0])
-    assert np.array_equal(fused.outputs()["out"], two.outputs()["out"])
-    compare_bgmv(two, f"two-stage {case}")
-
-
-def test_bgmv_fused_graph_replays():
-    """The fused call captured in a HIP graph: every replay (with eager work and
-    synchronisations between replays) gives the eager call's bits, and the
-    workspace counters are back at zero after each."""
+def test_bgmv_graph_replays():
+    """rld_bgmv captured in a HIP graph (k split over 4 chunks): every replay,
+    with eager work and synchronisations between replays, gives the eager
+    call's bits, and the chunk counters at the end of the workspace are back at
+    zero after each."""
     dev = require_gpu()
     wl = W.bgmv_custom(22, 256, 4096, 2048, 64, 16, (16, 64), base_frac=0.05, zipf=1.1)
-    say("case: fused graph replays")
+    say("case: graph replays")
     eager = BgmvRun(wl, dev)
     eager.run_all(keep_xa=False)
     want = eager.outputs()["out"]
@@ -171,19 +144,15 @@ def test_bgmv_fused_graph_replays():
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(g, stream=s):
         run.run_call(0, stream=s)
+    end = run.ws_bytes // 16 * 16
     for rep in range(4):
         run.bufs["out"].t.copy_(pristine)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(run.outputs()["out"], want), f"replay {rep}"
-        # workspace = [fp32 partials][chunk counters n*ntr][ready n][4 control words]:
-        # everything after the partials is zero again, including the gave-up flag
-        r16 = lambda v: (v + 15) // 16 * 16  # noqa: E731
-        tail = r16(wl.n * (64 // 16) * 4) + r16(wl.n * 4) + 16
-        total = R.rld_bgmv_workspace_bytes(wl.n, 4096, 64)
-        words = run.ws.view(torch.int32).cpu().numpy()[(total - tail) // 4: total // 4]
-        assert np.all(words == 0), f"replay {rep}: counters not reset {np.flatnonzero(words)[:8]}"
+        counters = run.ws.view(torch.int32).cpu().numpy()[(end - 32 * 16) // 4: end // 4]
+        assert np.all(counters == 0), f"replay {rep}: counters {np.flatnonzero(counters)[:8]}"
         _ = torch.ones(1 << 20, device=dev).sum().item()  # eager work between replays
 
 
@@ -234,6 +203,24 @@ def test_bgmv_ffn_decode_config():
     run.run_all()
     compare_bgmv(run, wl.name)
     _base_rows_xa_zero(wl, run)
+
+
+def test_bgmv_shared_workspace_second_pass():
+    """One workspace shared by calls of different shapes (gate/up split k_in in
+    4 chunks, down in 12), used for a second pass after the first: the second
+    pass (outputs restored to the base values first, now through the separate
+    shrink and expand entry points) still meets the oracle, so no call's scratch
+    disturbs another's counters."""
+    dev = require_gpu()
+    wl = W.bgmv_ffn_decode()
+    say(f"case: shared workspace, second pass, {wl.name}")
+    run = BgmvRun(wl, dev)
+    pristine = {k: b.t.clone() for k, b in run.bufs.items()}
+    run.run_all(keep_xa=False)
+    for k, b in run.bufs.items():
+        b.t.copy_(pristine[k])
+    run.run_all(two_stage=True)
+    compare_bgmv(run, "second pass " + wl.name)
 
 
 # ------------------------------------------------------------------ gather ---
