@@ -10,8 +10,8 @@
 //
 //   shrink item  (slot, k_in chunk, 16 columns of xa).  Each of the four waves
 //                owns every fourth 32-wide K step of the chunk and issues all
-//                of its A fragments at once; x fragments of the next 16 rows
-//                are in flight while the current ones multiply.  The waves'
+//                of its A fragments at once, then the x fragments of up to 64
+//                rows at once.  The waves'
 //                partial sums are added in wave order.  With several chunks,
 //                each item writes fp32 partials, and the item that finishes
 //                the last chunk of a (slot, 16 columns) pair adds the chunks in
@@ -37,27 +37,33 @@
 namespace rld {
 
 constexpr int kShrinkMT = 4;     // 16-row M-subtiles per shrink pass
-constexpr int kShrinkSteps = 8;  // K steps per wave per chunk (chunk <= 1024 = 4 waves x 8 x 32)
+constexpr int kShrinkSteps = 4;  // K steps per wave per chunk (chunk <= 512 = 4 waves x 4 x 32)
 constexpr int kListCap = 512;    // rows collected per pass over seq_slot
 constexpr int kJT = 256;         // output columns per expand item
 constexpr int kExpRows = 64;     // rows per fold pass of the expand
 constexpr int kDlStride = kJT + 8;
 constexpr int kFoldVecs = kExpRows * (kJT / 8) / 256;  // base vectors per thread per pass
 
-static_assert(kShrinkSteps * 4 * 32 >= 1024, "a chunk is at most 1024 elements");
+static_assert(kShrinkSteps * 4 * 32 >= 512, "a chunk is at most 512 elements");
 
+// Kernel arguments; device addresses are kept as integers and read through
+// the global-pointer accessors.
 struct BgmvArgs {
-  const uint16_t* x;
-  const int32_t* seq_slot;
-  const uint64_t* a_table;
-  const uint64_t* b_table;
-  const float* scale_table;
-  float* partial;  // [nch][n][R] fp32 (k split only), at the start of the workspace
-  uint32_t* book;  // end of the workspace: slot s's 8 chunk counters (one per
-                   // 16-column group of xa) are the 8 words at book - 8 (s + 1)
-  uint16_t* xa;
-  uint16_t* out;
+  uint64_t x_, seq_, atab_, btab_, stab_;
+  uint64_t partial_;  // [nch][n][R] fp32 (k split only), at the start of the workspace
+  uint64_t book_;     // end of the workspace: slot s's 8 chunk counters (one per
+                      // 16-column group of xa) are the 8 words at book - 8 (s + 1)
+  uint64_t xa_, out_;
   uint32_t xs, n, max_loras, k_in, n_out, R, kc, nch, ntr, os;
+  __device__ const RLD_GLOBAL uint16_t* x() const { return gp<const uint16_t>(x_); }
+  __device__ const RLD_GLOBAL int32_t* seq_slot() const { return gp<const int32_t>(seq_); }
+  __device__ const RLD_GLOBAL uint64_t* a_table() const { return gp<const uint64_t>(atab_); }
+  __device__ const RLD_GLOBAL uint64_t* b_table() const { return gp<const uint64_t>(btab_); }
+  __device__ const RLD_GLOBAL float* scale_table() const { return gp<const float>(stab_); }
+  __device__ RLD_GLOBAL float* partial() const { return gp<float>(partial_); }
+  __device__ RLD_GLOBAL uint32_t* book() const { return gp<uint32_t>(book_); }
+  __device__ RLD_GLOBAL uint16_t* xa() const { return gp<uint16_t>(xa_); }
+  __device__ RLD_GLOBAL uint16_t* out() const { return gp<uint16_t>(out_); }
 };
 
 struct ShrinkSmem {
@@ -73,30 +79,65 @@ struct ExpandSmem {
   __attribute__((aligned(16))) uint16_t dl[kExpRows * kDlStride];
 };
 
-__device__ __forceinline__ uint32_t* slot_counters(const BgmvArgs& a, int s) {
-  return a.book - 8 * ((size_t)s + 1);
+__device__ __forceinline__ RLD_GLOBAL uint32_t* slot_counters(const BgmvArgs& a, int s) {
+  return a.book() - 8 * ((size_t)s + 1);
 }
 
 __device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
-  return s >= 0 && (uint32_t)s < a.max_loras && a.a_table[s] != 0ull && a.b_table[s] != 0ull;
+  if (s < 0 || (uint32_t)s >= a.max_loras) return false;
+  const uint64_t ta = a.a_table()[s], tb = a.b_table()[s];  // both in flight together
+  return ta != 0ull && tb != 0ull;
 }
 
 // Appends to `rows` (LDS) the rows of slot s from seq_slot[*pos ...], until
 // n is reached or the list cannot take another 256; advances *pos.  Returns
-// the count (the same in every thread).
-__device__ __forceinline__ int collect_slot_rows(const int32_t* __restrict__ seq_slot, uint32_t n,
-                                                 uint32_t* pos, int s, int* rows, int* wcount) {
+// the count (the same in every thread).  key0 is this thread's seq_slot entry
+// of the first 256 rows (row threadIdx.x), loaded by the caller ahead of its
+// tile loads so the first scan does not wait behind them.
+__device__ __forceinline__ int collect_slot_rows(const RLD_GLOBAL int32_t* seq_slot, uint32_t n,
+                                                 uint32_t* pos, int s, int* rows, int* wcount,
+                                                 int key0) {
   int cnt = 0;
   while (*pos < n && cnt <= kListCap - 256) {
-    cnt += append_matching_rows(seq_slot, n, *pos, s, rows, cnt, wcount);
+    const uint32_t row = *pos + threadIdx.x;
+    const int key = *pos == 0 ? key0 : (row < n ? seq_slot[row] : -1);
+    cnt += append_hits(row < n && key == s, row, rows, cnt, wcount);
     *pos += 256;
   }
   return cnt;
 }
 
+// Compiler-level memory barrier: the loads written before it are issued
+// before it (they cannot be moved past it), without waiting for their data.
+__device__ __forceinline__ void issue_point() { asm volatile("" ::: "memory"); }
+
+// This thread's seq_slot entry among the first 256 rows (-1 past n).  The
+// load is unconditional (a row < n is always readable) so that it stays in the
+// prologue, ahead of the tile loads.
+__device__ __forceinline__ int first_key(const RLD_GLOBAL int32_t* seq_slot, uint32_t n) {
+  const int k = seq_slot[min(threadIdx.x, n - 1)];
+  issue_point();  // issued before any load that follows
+  return threadIdx.x < n ? k : -1;
+}
+
+// Table entries of a slot s < max_loras, read together (one round trip).
+struct SlotEntry {
+  uint64_t a, b;
+  float scale;
+  __device__ bool active() const { return a != 0ull && b != 0ull; }
+};
+
+__device__ __forceinline__ SlotEntry slot_entry(const BgmvArgs& a, int s) {
+  SlotEntry e;
+  e.a = a.a_table()[s];
+  e.b = a.b_table()[s];
+  e.scale = a.scale_table()[s];
+  return e;
+}
+
 // Block-wide: this thread's stores have completed, then the block meets, then
 // thread 0 adds 1 to *ctr (agent scope) and every thread gets the old value.
-__device__ __forceinline__ uint32_t block_signal(uint32_t* ctr, int* slot) {
+__device__ __forceinline__ uint32_t block_signal(RLD_GLOBAL uint32_t* ctr, int* slot) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
@@ -108,7 +149,7 @@ __device__ __forceinline__ uint32_t block_signal(uint32_t* ctr, int* slot) {
 }
 
 // Shrink item w (slot-major over (slot, chunk, 16 columns)).
-__device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
+__device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, ShrinkSmem& sm) {
   const uint32_t n = a.n, R = a.R, nchunks = a.nch, ntr = a.ntr;
   const uint32_t rt = w % ntr;
   const uint32_t c = (w / ntr) % nchunks;
@@ -116,29 +157,37 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  // The first item also writes the zero xa rows of base rows.
-  if (w == 0) {
+  // The block's seq_slot entries and the slot's table entries go out first.
+  const int key0 = first_key(a.seq_slot(), n);
+  const SlotEntry ent = slot_entry(a, s);
+
+  // The last item (a slot of the last index, usually cold) also writes the
+  // zero xa rows of base rows.
+  if (w == total - 1) {
     const uint32_t r8 = R / 8;
     for (uint32_t e = threadIdx.x; e < n * r8; e += 256) {
       const uint32_t row = e / r8;
-      if (!slot_active(a, a.seq_slot[row]))
-        *reinterpret_cast<uint4*>(a.xa + (size_t)row * R + (e % r8) * 8) = zero16();
+      if (!slot_active(a, a.seq_slot()[row]))
+        store16(a.xa() + (size_t)row * R + (e % r8) * 8, zero16());
     }
   }
-  if (!slot_active(a, s)) return;
+  if (!ent.active()) return;
 
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(a.a_table[s]);
+  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ent.a);
   const int lg = lane >> 4;
   const int cl = lane & 15;
   const uint32_t col = rt * 16 + cl;  // xa column = A_s row served by this lane
   const bool col_ok = col < R;
-  const uint16_t* Arow = A + (size_t)(col_ok ? col : 0) * a.k_in;
+  const RLD_GLOBAL uint16_t* Arow = A + (size_t)(col_ok ? col : 0) * a.k_in;
   const uint32_t kb = c * a.kc;
   const uint32_t ke = min(kb + a.kc, a.k_in);
   const uint32_t nsteps = (ke - kb + 31) / 32;
 
-  // This wave's K steps are wave, wave + 4, ...: all of its A fragments are
-  // issued here, before the row scan waits on seq_slot.
+  // Every A fragment of this wave's K steps (wave, wave + 4, ...) is issued
+  // before the row scan, which needs only the seq_slot entries already in
+  // flight; the x loads the scan enables then overlap the A tile's arrival.
+  // The loads are unconditional (out-of-range lanes read the chunk's first
+  // element of row 0 and drop it) so they stay here in the prologue.
   uint4 bop[kShrinkSteps];
   uint32_t kof[kShrinkSteps];
   bool kok[kShrinkSteps];
@@ -146,15 +195,19 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
   for (int i = 0; i < kShrinkSteps; ++i) {
     const uint32_t st = wave + 4 * i;
     kof[i] = kb + st * 32 + lg * 8;
-    kok[i] = st < nsteps && kof[i] < ke;
-    bop[i] = (col_ok && kok[i]) ? load16(Arow + kof[i]) : zero16();
+    kok[i] = col_ok && st < nsteps && kof[i] < ke;
+    bop[i] = load16(kok[i] ? Arow + kof[i] : A + kb);
   }
+  issue_point();
+#pragma unroll
+  for (int i = 0; i < kShrinkSteps; ++i)
+    if (!kok[i]) bop[i] = zero16();
 
   uint32_t pos = 0;
   int first_row = -1;
   int scans = 0, last_cnt = 0;
   while (pos < n) {
-    const int cnt = collect_slot_rows(a.seq_slot, n, &pos, s, sm.rows, sm.wcount);
+    const int cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
     ++scans;
     last_cnt = cnt;
     if (first_row < 0 && cnt > 0) first_row = sm.rows[0];
@@ -164,33 +217,23 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
       floatx4 acc[kShrinkMT];
 #pragma unroll
       for (int q = 0; q < kShrinkMT; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-      // x fragments of subtile q + 1 are issued before the MFMAs of subtile q
-      uint4 cur[kShrinkSteps], nxt[kShrinkSteps];
+      // x fragments of every subtile of the pass, all in flight together
+      uint4 xf[kShrinkMT][kShrinkSteps];
 #pragma unroll
-      for (int i = 0; i < kShrinkSteps; ++i) nxt[i] = zero16();
-      {
-        const bool ok = cl < nb;
-        const uint16_t* xr = a.x + (size_t)(ok ? sm.rows[b0 + cl] : 0) * a.xs;
+      for (int q = 0; q < kShrinkMT; ++q) {
+        const int li = q * 16 + cl;
+        const bool ok = li < nb;
+        const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)(ok ? sm.rows[b0 + li] : 0) * a.xs;
 #pragma unroll
         for (int i = 0; i < kShrinkSteps; ++i)
-          cur[i] = (ok && kok[i]) ? load16(xr + kof[i]) : zero16();
+          xf[q][i] = (q < nmt && ok && kof[i] < ke) ? load16(xr + kof[i]) : zero16();
       }
 #pragma unroll
       for (int q = 0; q < kShrinkMT; ++q) {
         if (q < nmt) {
-          if (q + 1 < nmt) {
-            const int li = (q + 1) * 16 + cl;
-            const bool ok = li < nb;
-            const uint16_t* xr = a.x + (size_t)(ok ? sm.rows[b0 + li] : 0) * a.xs;
-#pragma unroll
-            for (int i = 0; i < kShrinkSteps; ++i)
-              nxt[i] = (ok && kok[i]) ? load16(xr + kof[i]) : zero16();
-          }
 #pragma unroll
           for (int i = 0; i < kShrinkSteps; ++i)
-            acc[q] = mfma_bf16_16x16x32(cur[i], bop[i], acc[q]);
-#pragma unroll
-          for (int i = 0; i < kShrinkSteps; ++i) cur[i] = nxt[i];
+            acc[q] = mfma_bf16_16x16x32(xf[q][i], bop[i], acc[q]);
         }
       }
 #pragma unroll
@@ -209,9 +252,9 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
             if (li < nb) {
               const uint32_t row = (uint32_t)sm.rows[b0 + li];
               if (nchunks == 1) {
-                a.xa[(size_t)row * R + col] = (uint16_t)f32_to_bf16(sum[i]);
+                a.xa()[(size_t)row * R + col] = (uint16_t)f32_to_bf16(sum[i]);
               } else {  // agent-scope store: written through to where every XCD reads it
-                __hip_atomic_store(a.partial + ((size_t)c * n + row) * R + col, sum[i],
+                __hip_atomic_store(a.partial() + ((size_t)c * n + row) * R + col, sum[i],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               }
             }
@@ -226,7 +269,7 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
   // k split: the item that completes the last chunk of its (slot, 16 xa
   // columns) adds the chunks in chunk order and writes xa.  The group's
   // counter is left at zero.
-  uint32_t* ctr = slot_counters(a, s) + rt;
+  RLD_GLOBAL uint32_t* ctr = slot_counters(a, s) + rt;
   if (block_signal(ctr, &sm.flag) != nchunks - 1) return;
   if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
@@ -240,26 +283,40 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
       cnt = last_cnt;
     } else {
       if (rpos >= n) break;
-      cnt = collect_slot_rows(a.seq_slot, n, &rpos, s, sm.rows, sm.wcount);
+      cnt = collect_slot_rows(a.seq_slot(), n, &rpos, s, sm.rows, sm.wcount, key0);
     }
     if (rcol < R) {
-      for (int li = rl; li < cnt; li += 16) {
-        const uint32_t row = (uint32_t)sm.rows[li];
-        float* pp = a.partial + (size_t)row * R + rcol;
-        const size_t cstride = (size_t)n * R;
-        float sum = 0.f;
-        for (uint32_t c0 = 0; c0 < nchunks; c0 += 8) {
-          float v[8];
+      const size_t cstride = (size_t)n * R;
+      // two rows per thread per step, 16 chunks of each in flight
+      for (int li = rl; li < cnt; li += 32) {
+        const bool two = li + 16 < cnt;
+        const uint32_t r0 = (uint32_t)sm.rows[li];
+        const uint32_t r1 = two ? (uint32_t)sm.rows[li + 16] : r0;
+        RLD_GLOBAL float* p0 = a.partial() + (size_t)r0 * R + rcol;
+        RLD_GLOBAL float* p1 = a.partial() + (size_t)r1 * R + rcol;
+        float s0 = 0.f, s1 = 0.f;
+        for (uint32_t c0 = 0; c0 < nchunks; c0 += 16) {
+          float v0[16], v1[16];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            v[j] = (c0 + j < nchunks) ? __hip_atomic_load(pp + (c0 + j) * cstride, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT)
-                                      : 0.f;
+          for (int j = 0; j < 16; ++j) {
+            const bool ok = c0 + j < nchunks;
+            v0[j] = ok ? __hip_atomic_load(p0 + (c0 + j) * cstride, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : 0.f;
+            v1[j] = (ok && two) ? __hip_atomic_load(p1 + (c0 + j) * cstride, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.f;
+          }
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (c0 + j < nchunks) sum = (c0 + j == 0) ? v[j] : sum + v[j];
+          for (int j = 0; j < 16; ++j) {
+            if (c0 + j < nchunks) {  // chunk order
+              s0 = (c0 + j == 0) ? v0[j] : s0 + v0[j];
+              s1 = (c0 + j == 0) ? v1[j] : s1 + v1[j];
+            }
+          }
         }
-        a.xa[(size_t)row * R + rcol] = (uint16_t)f32_to_bf16(sum);
+        a.xa()[(size_t)r0 * R + rcol] = (uint16_t)f32_to_bf16(s0);
+        if (two) a.xa()[(size_t)r1 * R + rcol] = (uint16_t)f32_to_bf16(s1);
       }
     }
     __syncthreads();
@@ -269,27 +326,34 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem& sm) {
 // Expand item (slot s, 256 output columns from j0).  NKS = ceil(max_rank/32).
 template <int NKS>
 __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& sm) {
-  if (!slot_active(a, s)) return;
-  const uint16_t* B = reinterpret_cast<const uint16_t*>(a.b_table[s]);
-  const float scale = a.scale_table[s];
   const uint32_t n = a.n, R = a.R, n_out = a.n_out, os = a.os;
+  // seq_slot entries and the slot's table entries first (one round trip)
+  const int key0 = first_key(a.seq_slot(), n);
+  const SlotEntry ent = slot_entry(a, s);
+  if (!ent.active()) return;
+  const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(ent.b);
+  const float scale = ent.scale;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lg = lane >> 4;
   const int cl = lane & 15;
 
-  // B_s rows of this wave's 64 columns, as MFMA A operands for every K step.
+  // B_s rows of this wave's 64 columns, as MFMA A operands for every K step,
+  // issued before the row scan (unconditional loads: out-of-range lanes read
+  // B's first element and drop it).
   uint4 aop[4][NKS];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const uint32_t col = j0 + wave * 64 + m * 16 + cl;
-    const bool ok = col < n_out;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const uint32_t k = ks * 32 + lg * 8;
-      aop[m][ks] = (ok && k < R) ? load16(B + (size_t)col * R + k) : zero16();
+      const bool ok = col < n_out && k < R;
+      aop[m][ks] = load16(ok ? B + (size_t)col * R + k : B);
+      if (!ok) aop[m][ks] = zero16();
     }
   }
+  issue_point();
 
   // fold mapping: vector i of a thread is row (tid / 32) + 8 i, columns c8 .. c8+7
   const int frow = threadIdx.x >> 5;
@@ -298,7 +362,7 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
 
   uint32_t pos = 0;
   while (pos < n) {
-    const int cnt = collect_slot_rows(a.seq_slot, n, &pos, s, sm.rows, sm.wcount);
+    const int cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
     for (int b0 = 0; b0 < cnt; b0 += kExpRows) {
       const int nb = min(cnt - b0, kExpRows);
       // base values of the pass, issued before the MFMAs
@@ -307,7 +371,7 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
       for (int i = 0; i < kFoldVecs; ++i) {
         const int rl = frow + 8 * i;
         bv[i] = (rl < nb && fcol_ok)
-                    ? *reinterpret_cast<const uint4*>(a.out + (size_t)sm.rows[b0 + rl] * os + j0 + c8)
+                    ? load16(a.out() + (size_t)sm.rows[b0 + rl] * os + j0 + c8)
                     : zero16();
       }
       uint4 bop[4][NKS];
@@ -315,7 +379,7 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
       for (int p = 0; p < 4; ++p) {
         const int li = p * 16 + cl;
         const bool ok = li < nb;
-        const uint16_t* xr = a.xa + (size_t)(ok ? sm.rows[b0 + li] : 0) * R;
+        const RLD_GLOBAL uint16_t* xr = a.xa() + (size_t)(ok ? sm.rows[b0 + li] : 0) * R;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const uint32_t k = ks * 32 + lg * 8;
@@ -344,8 +408,7 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
         const int rl = frow + 8 * i;
         if (rl < nb && fcol_ok) {
           const uint4 dv = *reinterpret_cast<const uint4*>(&sm.dl[rl * kDlStride + c8]);
-          *reinterpret_cast<uint4*>(a.out + (size_t)sm.rows[b0 + rl] * os + j0 + c8) =
-              fold8(bv[i], dv, scale);
+          store16(a.out() + (size_t)sm.rows[b0 + rl] * os + j0 + c8, fold8(bv[i], dv, scale));
         }
       }
       __syncthreads();
@@ -358,7 +421,7 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(BgmvArgs a, uint32_t t
   // the ntr items of one (slot, chunk) share an XCD, and so the x rows in its L2
   const uint32_t w = xcd_group_item(a.ntr);
   if (w >= total) return;
-  shrink_item(a, w, sm);
+  shrink_item(a, w, total, sm);
 }
 
 template <int NKS>
@@ -392,15 +455,15 @@ static int make_args(const rld_route* route, const void* x, uint32_t x_row_strid
     return RLD_ENOSPACE;
   if (!aligned16(workspace)) return RLD_EALIGN;
   char* ws = static_cast<char*>(workspace);
-  a->x = static_cast<const uint16_t*>(x);
-  a->seq_slot = seq_slot;
-  a->a_table = route->a_table;
-  a->b_table = route->b_table;
-  a->scale_table = route->scale_table;
-  a->partial = reinterpret_cast<float*>(ws);
-  a->book = reinterpret_cast<uint32_t*>(ws + end);
-  a->xa = static_cast<uint16_t*>(xa);
-  a->out = static_cast<uint16_t*>(base_out);
+  a->x_ = reinterpret_cast<uint64_t>(x);
+  a->seq_ = reinterpret_cast<uint64_t>(seq_slot);
+  a->atab_ = reinterpret_cast<uint64_t>(route->a_table);
+  a->btab_ = reinterpret_cast<uint64_t>(route->b_table);
+  a->stab_ = reinterpret_cast<uint64_t>(route->scale_table);
+  a->partial_ = reinterpret_cast<uint64_t>(ws);
+  a->book_ = reinterpret_cast<uint64_t>(ws + end);
+  a->xa_ = reinterpret_cast<uint64_t>(xa);
+  a->out_ = reinterpret_cast<uint64_t>(base_out);
   a->xs = x_row_stride;
   a->n = n;
   a->max_loras = route->max_loras;
@@ -466,12 +529,12 @@ extern "C" int rld_bgmv_expand_fold(const rld_route* route, const void* xa,
   if (!aligned16(xa)) return RLD_EALIGN;
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
   BgmvArgs a = {};
-  a.seq_slot = seq_slot;
-  a.a_table = route->a_table;
-  a.b_table = route->b_table;
-  a.scale_table = route->scale_table;
-  a.xa = const_cast<uint16_t*>(static_cast<const uint16_t*>(xa));
-  a.out = static_cast<uint16_t*>(base_out);
+  a.seq_ = reinterpret_cast<uint64_t>(seq_slot);
+  a.atab_ = reinterpret_cast<uint64_t>(route->a_table);
+  a.btab_ = reinterpret_cast<uint64_t>(route->b_table);
+  a.stab_ = reinterpret_cast<uint64_t>(route->scale_table);
+  a.xa_ = reinterpret_cast<uint64_t>(xa);
+  a.out_ = reinterpret_cast<uint64_t>(base_out);
   a.n = n;
   a.max_loras = route->max_loras;
   a.k_in = route->k_in;

@@ -46,8 +46,30 @@ __device__ __forceinline__ floatx4 mfma_bf16_16x16x32(const uint4& a, const uint
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint4 load16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
+// Device memory is reached only through address-space-1 (global) pointers,
+// so every access compiles to global_load / global_store, which count on
+// vmcnt alone.  A flat access (what a generic pointer gives) also counts on
+// lgkmcnt, so every LDS wait and every barrier would wait for it as well and
+// loads issued early could no longer overlap the work after them.  Addresses
+// travel in kernel argument structs as uint64_t and become global pointers
+// through gp().
+#define RLD_GLOBAL __attribute__((address_space(1)))
+
+template <class T>
+__device__ __forceinline__ RLD_GLOBAL T* gp(uint64_t addr) {
+  return (RLD_GLOBAL T*)addr;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load16(const RLD_GLOBAL uint16_t* p) {
+  const u32x4 v = *reinterpret_cast<const RLD_GLOBAL u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store16(RLD_GLOBAL uint16_t* p, const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  *reinterpret_cast<RLD_GLOBAL u32x4*>(p) = w;
 }
 
 __device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
@@ -74,16 +96,13 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// A block of 256 threads appends to `list` (LDS) the indices of rows in
-// [pos, min(pos+256, n)) whose key equals `want`, in ascending order.
-// Returns the number appended.  `wcount` is LDS scratch of 4 ints.
-__device__ __forceinline__ int append_matching_rows(const int32_t* __restrict__ keys, uint32_t n,
-                                                    uint32_t pos, int32_t want, int* list,
-                                                    int base, int* wcount) {
+// A block of 256 threads appends to `list` (LDS), in thread order, the `row`
+// of every thread whose `hit` is set.  Returns the number appended (in every
+// thread).  `wcount` is LDS scratch of 4 ints.
+__device__ __forceinline__ int append_hits(bool hit, uint32_t row, int* list, int base,
+                                           int* wcount) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const uint32_t row = pos + threadIdx.x;
-  const bool hit = row < n && keys[row] == want;
   const uint64_t m = __ballot(hit);
   if (lane == 0) wcount[wave] = __popcll(m);
   __syncthreads();
@@ -99,10 +118,21 @@ __device__ __forceinline__ int append_matching_rows(const int32_t* __restrict__ 
   return tot;
 }
 
+// A block of 256 threads appends to `list` (LDS) the indices of rows in
+// [pos, min(pos+256, n)) whose key equals `want`, in ascending order.
+// Returns the number appended.  `wcount` is LDS scratch of 4 ints.
+__device__ __forceinline__ int append_matching_rows(const RLD_GLOBAL int32_t* keys, uint32_t n,
+                                                    uint32_t pos, int32_t want, int* list,
+                                                    int base, int* wcount) {
+  const uint32_t row = pos + threadIdx.x;
+  return append_hits(row < n && keys[row] == want, row, list, base, wcount);
+}
+
 // Owner expert of sorted row r: the largest e < E with off[e] <= r, accepted
 // only if r < off[e+1].  Reads stay inside off[0..E]; non-monotone offsets give
-// some defined answer without faulting.
-__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ off, int E, int r) {
+// some defined answer without faulting.  P is an LDS or a global pointer.
+template <class P>
+__device__ __forceinline__ int expert_of_row(P off, int E, int r) {
   if (E <= 0 || r < off[0]) return -1;
   int lo = 0, hi = E - 1;  // invariant: off[lo] <= r
   while (lo < hi) {

@@ -33,7 +33,7 @@
 
 namespace rld {
 
-constexpr int kOffCap = 512;     // expert_offsets entries staged in LDS (else searched in place)
+constexpr int kOffCap = 1024;    // expert_offsets entries staged in LDS (num_experts_off < kOffCap)
 constexpr int kPairCap = 2048;   // max_loras * num_experts held in the LDS worklist
 constexpr int kListCap = 512;    // rows of a pair collected per scan
 constexpr int kBatch = 64;       // rows of a pair per MFMA pass (4 subtiles of 16)
@@ -45,30 +45,31 @@ constexpr int kPeCols = 512;     // output columns per expand item
 constexpr int kPeGrid = 512;     // expand blocks per launch
 constexpr int kDlStride = kPeCols + 8;
 
+// Routing inputs of a window; device addresses are integers read through the
+// global-pointer accessors (see gp()).
 struct GroupedRows {
-  const int32_t* off;
-  const int32_t* stid;
-  const int32_t* radapt;
-  const uint64_t* a_table;
-  const uint64_t* b_table;
+  uint64_t off_, stid_, radapt_, atab_, btab_;
   uint32_t E_off;
   uint32_t num_tokens;
   uint32_t max_loras;
   uint32_t E;
   int need_tok;
+  __device__ const RLD_GLOBAL int32_t* off() const { return gp<const int32_t>(off_); }
+  __device__ const RLD_GLOBAL int32_t* stid() const { return gp<const int32_t>(stid_); }
+  __device__ const RLD_GLOBAL int32_t* radapt() const { return gp<const int32_t>(radapt_); }
+  __device__ const RLD_GLOBAL uint64_t* a_table() const { return gp<const uint64_t>(atab_); }
+  __device__ const RLD_GLOBAL uint64_t* b_table() const { return gp<const uint64_t>(btab_); }
 };
 
-// All threads: expert_offsets into LDS when it fits; returns the copy to search.
-__device__ __forceinline__ const int32_t* stage_offsets(const GroupedRows& g, int* off_s) {
-  const bool lds = g.E_off + 1 <= (uint32_t)kOffCap;
-  if (lds)
-    for (uint32_t i = threadIdx.x; i <= g.E_off; i += blockDim.x) off_s[i] = g.off[i];
+// All threads: expert_offsets into LDS (the launchers require E_off < kOffCap).
+__device__ __forceinline__ const int* stage_offsets(const GroupedRows& g, int* off_s) {
+  for (uint32_t i = threadIdx.x; i <= g.E_off; i += blockDim.x) off_s[i] = g.off()[i];
   __syncthreads();
-  return lds ? off_s : g.off;
+  return off_s;
 }
 
 // Window part [lo, hi) of expert e's span (empty when e has no offsets entry).
-__device__ __forceinline__ void span_in_window(const int32_t* off, const GroupedRows& g, int e,
+__device__ __forceinline__ void span_in_window(const int* off, const GroupedRows& g, int e,
                                                uint32_t row_offset, uint32_t row_end,
                                                uint32_t& lo, uint32_t& hi) {
   lo = hi = row_end;
@@ -84,17 +85,17 @@ __device__ __forceinline__ void span_in_window(const int32_t* off, const Grouped
 __device__ __forceinline__ int row_slot(const GroupedRows& g, uint32_t r, int* tok) {
   int t = 0;
   if (g.need_tok) {
-    t = g.stid[r];
+    t = g.stid()[r];
     if (t < 0 || (uint32_t)t >= g.num_tokens) return -1;
   }
   *tok = t;
-  return g.radapt ? g.radapt[t] : 0;
+  return g.radapt_ ? g.radapt()[t] : 0;
 }
 
 // Appends to list/toks (LDS) the rows of [c0, c1) (c1 - c0 <= blockDim) that
 // expert e owns and whose slot is s, in ascending order; returns how many.
 // Called by every thread.
-__device__ __forceinline__ int append_pair_rows(const GroupedRows& g, const int32_t* off, int e,
+__device__ __forceinline__ int append_pair_rows(const GroupedRows& g, const int* off, int e,
                                                 int s, uint32_t c0, uint32_t c1, int* list,
                                                 int* toks, int base, int* wcount) {
   const int lane = threadIdx.x & 63;
@@ -122,9 +123,9 @@ __device__ __forceinline__ int append_pair_rows(const GroupedRows& g, const int3
   return tot;
 }
 
-__device__ __forceinline__ void zero_xa_row(uint16_t* xa, uint32_t local_row, uint32_t R) {
-  uint4* p = reinterpret_cast<uint4*>(xa + (size_t)local_row * R);
-  for (uint32_t i = 0; i < R / 8; ++i) p[i] = zero16();
+__device__ __forceinline__ void zero_xa_row(RLD_GLOBAL uint16_t* xa, uint32_t local_row,
+                                            uint32_t R) {
+  for (uint32_t i = 0; i < R / 8; ++i) store16(xa + (size_t)local_row * R + 8 * i, zero16());
 }
 
 // Every thread: stage expert_offsets, read the A/B table entries of every pair
@@ -132,21 +133,19 @@ __device__ __forceinline__ void zero_xa_row(uint16_t* xa, uint32_t local_row, ui
 // valid and own rows of [row_offset, row_end).  The offsets and table reads go
 // out together, so this costs one round of loads.  Returns the pair count.
 __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row_offset,
-                                              uint32_t row_end, int* off_s,
-                                              const int32_t** offp, uint8_t* valid,
+                                              uint32_t row_end, int* off_s, uint8_t* valid,
                                               int16_t* apairs, int* wcount) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const uint32_t np = g.max_loras * g.E;
-  const bool lds = g.E_off + 1 <= (uint32_t)kOffCap;
-  if (lds)
-    for (uint32_t i = threadIdx.x; i <= g.E_off; i += blockDim.x) off_s[i] = g.off[i];
-  for (uint32_t p = threadIdx.x; p < np; p += blockDim.x)
-    valid[p] = (g.a_table[p] != 0ull && g.b_table[p] != 0ull) ? 1 : 0;
+  for (uint32_t i = threadIdx.x; i <= g.E_off; i += blockDim.x) off_s[i] = g.off()[i];
+  for (uint32_t p = threadIdx.x; p < np; p += blockDim.x) {
+    const uint64_t ta = g.a_table()[p], tb = g.b_table()[p];
+    valid[p] = (ta != 0ull && tb != 0ull) ? 1 : 0;
+  }
   __syncthreads();
-  const int32_t* off = lds ? off_s : g.off;
-  *offp = off;
+  const int* off = off_s;
   int na = 0;
   for (uint32_t c0 = 0; c0 < np; c0 += blockDim.x) {
     const uint32_t p = c0 + threadIdx.x;
@@ -179,9 +178,10 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
 // that range of A once per pass and of each x row once; the 8 partial sums
 // meet in LDS in wave order.
 __global__ __launch_bounds__(kPsThreads) void grouped_shrink_kernel(
-    const uint16_t* __restrict__ x, uint32_t xs, int x_gather, GroupedRows gr, uint32_t k_in,
-    uint32_t R, uint32_t row_offset, uint32_t row_end, uint32_t kw, uint32_t total,
-    uint16_t* __restrict__ xa) {
+    uint64_t x_addr, uint32_t xs, int x_gather, GroupedRows gr, uint32_t k_in, uint32_t R,
+    uint32_t row_offset, uint32_t row_end, uint32_t kw, uint32_t total, uint64_t xa_addr) {
+  const RLD_GLOBAL uint16_t* x = gp<const uint16_t>(x_addr);
+  RLD_GLOBAL uint16_t* xa = gp<uint16_t>(xa_addr);
   __shared__ int off_s[kOffCap];
   __shared__ int list[kListCap];
   __shared__ int toks[kListCap];
@@ -194,8 +194,9 @@ __global__ __launch_bounds__(kPsThreads) void grouped_shrink_kernel(
   const int h = (int)(w % kPsSplit);
   const int s = pair / (int)gr.E;
   const int e = pair % (int)gr.E;
-  const bool pair_ok = gr.a_table[pair] != 0ull && gr.b_table[pair] != 0ull;  // with the offsets
-  const int32_t* off = stage_offsets(gr, off_s);
+  const uint64_t ta = gr.a_table()[pair], tb = gr.b_table()[pair];  // with the offsets
+  const int* off = stage_offsets(gr, off_s);
+  const bool pair_ok = ta != 0ull && tb != 0ull;
   uint32_t lo, hi;
   span_in_window(off, gr, e, row_offset, row_end, lo, hi);
 
@@ -208,7 +209,8 @@ __global__ __launch_bounds__(kPsThreads) void grouped_shrink_kernel(
       bool act = sr >= 0 && (uint32_t)sr < gr.max_loras;
       if (act) {
         const int pr = sr * (int)gr.E + e;
-        act = gr.a_table[pr] != 0ull && gr.b_table[pr] != 0ull;
+        const uint64_t pa = gr.a_table()[pr], pb = gr.b_table()[pr];
+        act = pa != 0ull && pb != 0ull;
       }
       if (!act) zero_xa_row(xa, r - row_offset, R);
     }
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(kPsThreads) void grouped_shrink_kernel(
   }
   if (!pair_ok || hi <= lo) return;
 
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(gr.a_table[pair]);
+  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ta);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lg = lane >> 4;
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kPsThreads) void grouped_shrink_kernel(
     // this block's subtiles: q = h, h + kPsSplit, ... of the (cnt+15)/16
     const int nsub = (cnt + 15) >> 4;
     for (int q0 = h; q0 < nsub; q0 += 4 * kPsSplit) {
-      const uint16_t* xr[4];
+      const RLD_GLOBAL uint16_t* xr[4];
       bool rok[4];
       int nq = 0;
 #pragma unroll
@@ -339,9 +341,12 @@ __global__ __launch_bounds__(kPsThreads) void grouped_shrink_kernel(
 // NKS = ceil(max_rank / 32) K steps.
 template <int NKS>
 __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
-    const uint16_t* __restrict__ xa, GroupedRows gr, const float* __restrict__ scale_table,
+    uint64_t xa_addr, GroupedRows gr, uint64_t scale_addr,
     uint32_t n_out, uint32_t R, uint32_t row_offset, uint32_t row_end, uint32_t nct,
-    uint16_t* __restrict__ out, uint32_t os) {
+    uint64_t out_addr, uint32_t os) {
+  const RLD_GLOBAL uint16_t* xa = gp<const uint16_t>(xa_addr);
+  const RLD_GLOBAL float* scale_table = gp<const float>(scale_addr);
+  RLD_GLOBAL uint16_t* out = gp<uint16_t>(out_addr);
   __shared__ int off_s[kOffCap];
   __shared__ uint8_t valid[kPairCap];
   __shared__ int16_t apairs[kPairCap];
@@ -350,8 +355,8 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
   __shared__ int wcount[kPeThreads / kWave];
   __shared__ __attribute__((aligned(16))) uint16_t dl[kBatch * kDlStride];
 
-  const int32_t* off;
-  const int na = build_worklist(gr, row_offset, row_end, off_s, &off, valid, apairs, wcount);
+  const int na = build_worklist(gr, row_offset, row_end, off_s, valid, apairs, wcount);
+  const int* off = off_s;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lg = lane >> 4;
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
     const uint32_t j0 = (uint32_t)(it % (int)nct) * kPeCols;
     const int s = pair / (int)gr.E;
     const int e = pair % (int)gr.E;
-    const uint16_t* B = reinterpret_cast<const uint16_t*>(gr.b_table[pair]);
+    const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(gr.b_table()[pair]);
     const float scale = scale_table[pair];
     uint4 aop[4][NKS];
 #pragma unroll
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
           if (p * 16 >= nb) continue;
           const int li = p * 16 + cl;
           const bool ok = li < nb;
-          const uint16_t* xr =
+          const RLD_GLOBAL uint16_t* xr =
               xa + (size_t)((ok ? (uint32_t)list[b0 + li] : row_offset) - row_offset) * R;
           uint4 bop[NKS];
 #pragma unroll
@@ -429,8 +434,7 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
           const uint32_t c = j0 + c8;
           if (rl < nb && c < n_out) {
             const uint4 dv = *reinterpret_cast<const uint4*>(&dl[rl * kDlStride + c8]);
-            *reinterpret_cast<uint4*>(out + (size_t)list[b0 + rl] * os + c) =
-                fold8(bv[j], dv, scale);
+            store16(out + (size_t)list[b0 + rl] * os + c, fold8(bv[j], dv, scale));
           }
         }
         __syncthreads();
@@ -446,6 +450,7 @@ static int check_grouped(const rld_moe_route* route, int x_gather, const int32_t
   if (st) return st;
   if ((uint64_t)route->max_loras * route->num_experts > (uint64_t)kPairCap) return RLD_EUNSUPPORTED;
   if (!expert_offsets || num_experts_off == 0) return RLD_EINVAL;
+  if (num_experts_off >= (uint32_t)kOffCap) return RLD_EUNSUPPORTED;
   if (row_end < row_offset || row_end > 0x7fffffffu) return RLD_EINVAL;
   if ((x_gather || row_adapter) && !sorted_token_ids) return RLD_EINVAL;
   return RLD_OK;
@@ -455,11 +460,11 @@ static GroupedRows make_rows(const rld_moe_route* route, int x_gather, uint32_t 
                              const int32_t* expert_offsets, uint32_t num_experts_off,
                              const int32_t* sorted_token_ids, const int32_t* row_adapter) {
   GroupedRows g;
-  g.off = expert_offsets;
-  g.stid = sorted_token_ids;
-  g.radapt = row_adapter;
-  g.a_table = route->a_table;
-  g.b_table = route->b_table;
+  g.off_ = reinterpret_cast<uint64_t>(expert_offsets);
+  g.stid_ = reinterpret_cast<uint64_t>(sorted_token_ids);
+  g.radapt_ = reinterpret_cast<uint64_t>(row_adapter);
+  g.atab_ = reinterpret_cast<uint64_t>(route->a_table);
+  g.btab_ = reinterpret_cast<uint64_t>(route->b_table);
   g.E_off = num_experts_off;
   g.num_tokens = num_tokens;
   g.max_loras = route->max_loras;
@@ -495,10 +500,10 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
                              sorted_token_ids, row_adapter);
   const uint32_t total = route->max_loras * route->num_experts * kPsSplit;
   hipLaunchKernelGGL(grouped_shrink_kernel, dim3(xcd_grid(total)), dim3(kPsThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x),
+                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<uint64_t>(x),
                      x_row_stride, x_gather ? 1 : 0, gr, route->k_in, route->max_rank,
                      row_offset, row_end, shrink_range(route->k_in), total,
-                     static_cast<uint16_t*>(xa));
+                     reinterpret_cast<uint64_t>(xa));
   return launch_status();
 }
 
@@ -527,9 +532,10 @@ extern "C" int rld_moe_grouped_expand_fold(const rld_moe_route* route, const voi
     default: kern = grouped_expand_kernel<4>; break;
   }
   hipLaunchKernelGGL(kern, dim3(kPeGrid), dim3(kPeThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint16_t*>(xa), gr,
-                     route->scale_table, route->n_out, route->max_rank, row_offset, row_end, nct,
-                     static_cast<uint16_t*>(base_out), out_row_stride);
+                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<uint64_t>(xa), gr,
+                     reinterpret_cast<uint64_t>(route->scale_table), route->n_out,
+                     route->max_rank, row_offset, row_end, nct,
+                     reinterpret_cast<uint64_t>(base_out), out_row_stride);
   return launch_status();
 }
 

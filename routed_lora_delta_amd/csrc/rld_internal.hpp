@@ -54,7 +54,7 @@ inline int launch_status() {
 // summation order never depends on the batch.  Narrow ranks get shorter chunks
 // so that a call still spreads over many blocks.
 inline uint32_t bgmv_chunk(uint32_t k_in, uint32_t max_rank) {
-  const uint32_t kc = max_rank <= 16 ? 256u : max_rank <= 32 ? 512u : 1024u;
+  const uint32_t kc = max_rank <= 16 ? 256u : 512u;
   return k_in <= kc ? k_in : kc;
 }
 

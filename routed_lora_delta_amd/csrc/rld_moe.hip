@@ -14,18 +14,30 @@
 
 namespace rld {
 
+// Kernel arguments of the gather fold; device addresses are integers read
+// through global-pointer accessors (see gp()).
+struct GatherArgs {
+  uint64_t x_, idx_, radapt_, atab_, btab_, stab_, xa_, out_;
+  uint32_t xs, top_k, max_loras, E, k_in, n_out, R, os;
+  __device__ const RLD_GLOBAL uint16_t* x() const { return gp<const uint16_t>(x_); }
+  __device__ const RLD_GLOBAL int32_t* indices() const { return gp<const int32_t>(idx_); }
+  __device__ const RLD_GLOBAL int32_t* row_adapter() const { return gp<const int32_t>(radapt_); }
+  __device__ const RLD_GLOBAL uint64_t* a_table() const { return gp<const uint64_t>(atab_); }
+  __device__ const RLD_GLOBAL uint64_t* b_table() const { return gp<const uint64_t>(btab_); }
+  __device__ const RLD_GLOBAL float* scale_table() const { return gp<const float>(stab_); }
+  __device__ RLD_GLOBAL uint16_t* xa() const { return gp<uint16_t>(xa_); }
+  __device__ RLD_GLOBAL uint16_t* out() const { return gp<uint16_t>(out_); }
+};
+
 // ------------------------------------------------------------------ gather --
 
-__device__ __forceinline__ int gather_pair(uint32_t rho, const int32_t* __restrict__ indices,
-                                           const int32_t* __restrict__ row_adapter,
-                                           uint32_t top_k, const uint64_t* __restrict__ a_table,
-                                           const uint64_t* __restrict__ b_table,
-                                           uint32_t max_loras, uint32_t E) {
-  const int s = row_adapter ? row_adapter[rho / top_k] : 0;
-  const int e = indices[rho];
-  if (s < 0 || (uint32_t)s >= max_loras || e < 0 || (uint32_t)e >= E) return -1;
-  const int pair = s * (int)E + e;
-  if (a_table[pair] == 0ull || b_table[pair] == 0ull) return -1;
+__device__ __forceinline__ int gather_pair(const GatherArgs& a, uint32_t rho) {
+  const int s = a.radapt_ ? a.row_adapter()[rho / a.top_k] : 0;
+  const int e = a.indices()[rho];
+  if (s < 0 || (uint32_t)s >= a.max_loras || e < 0 || (uint32_t)e >= a.E) return -1;
+  const int pair = s * (int)a.E + e;
+  const uint64_t ta = a.a_table()[pair], tb = a.b_table()[pair];  // both in flight together
+  if (ta == 0ull || tb == 0ull) return -1;
   return pair;
 }
 
@@ -41,24 +53,21 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float acc)
   return acc;
 }
 
-__global__ __launch_bounds__(256) void gather_shrink_kernel(
-    const uint16_t* __restrict__ x, uint32_t xs, const int32_t* __restrict__ indices,
-    const int32_t* __restrict__ row_adapter, uint32_t top_k, const uint64_t* __restrict__ a_table,
-    const uint64_t* __restrict__ b_table, uint32_t max_loras, uint32_t E, uint32_t k_in,
-    uint32_t R, uint16_t* __restrict__ xa) {
+__global__ __launch_bounds__(256) void gather_shrink_kernel(GatherArgs a) {
   const uint32_t rho = blockIdx.x;
-  uint16_t* xo = xa + (size_t)rho * R;
-  const int pair = gather_pair(rho, indices, row_adapter, top_k, a_table, b_table, max_loras, E);
+  const uint32_t R = a.R, k_in = a.k_in;
+  RLD_GLOBAL uint16_t* xo = a.xa() + (size_t)rho * R;
+  const int pair = gather_pair(a, rho);
   if (pair < 0) {
     for (uint32_t k = threadIdx.x; k < R; k += 256) xo[k] = 0;
     return;
   }
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(a_table[pair]);
-  const uint16_t* xr = x + (size_t)rho * xs;
+  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(a.a_table()[pair]);
+  const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)rho * a.xs;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   for (uint32_t k = wave; k < R; k += 4) {
-    const uint16_t* Ak = A + (size_t)k * k_in;
+    const RLD_GLOBAL uint16_t* Ak = A + (size_t)k * k_in;
     float acc = 0.f;
     for (uint32_t c = lane * 8; c < k_in; c += 512) acc = dot8(load16(xr + c), load16(Ak + c), acc);
 #pragma unroll
@@ -67,29 +76,48 @@ __global__ __launch_bounds__(256) void gather_shrink_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void gather_expand_kernel(
-    const uint16_t* __restrict__ xa, const int32_t* __restrict__ indices,
-    const int32_t* __restrict__ row_adapter, uint32_t top_k, const uint64_t* __restrict__ a_table,
-    const uint64_t* __restrict__ b_table, const float* __restrict__ scale_table,
-    uint32_t max_loras, uint32_t E, uint32_t n_out, uint32_t R, uint16_t* __restrict__ out,
-    uint32_t os) {
+__global__ __launch_bounds__(256) void gather_expand_kernel(GatherArgs a) {
   const uint32_t rho = blockIdx.x;
-  const int pair = gather_pair(rho, indices, row_adapter, top_k, a_table, b_table, max_loras, E);
+  const uint32_t R = a.R;
+  const int pair = gather_pair(a, rho);
   if (pair < 0) return;
   const uint32_t j = blockIdx.y * kGatherCols + threadIdx.x * 2;
-  if (j >= n_out) return;
-  const uint16_t* B0 = reinterpret_cast<const uint16_t*>(b_table[pair]) + (size_t)j * R;
-  const uint16_t* B1 = B0 + R;
-  const uint16_t* xr = xa + (size_t)rho * R;
+  if (j >= a.n_out) return;
+  const RLD_GLOBAL uint16_t* B0 = gp<const uint16_t>(a.b_table()[pair]) + (size_t)j * R;
+  const RLD_GLOBAL uint16_t* B1 = B0 + R;
+  const RLD_GLOBAL uint16_t* xr = a.xa() + (size_t)rho * R;
   float d0 = 0.f, d1 = 0.f;
   for (uint32_t k = 0; k < R; k += 8) {
     const uint4 xv = load16(xr + k);
     d0 = dot8(load16(B0 + k), xv, d0);
     d1 = dot8(load16(B1 + k), xv, d1);
   }
-  uint32_t* p = reinterpret_cast<uint32_t*>(out + (size_t)rho * os + j);
+  RLD_GLOBAL uint32_t* p = reinterpret_cast<RLD_GLOBAL uint32_t*>(a.out() + (size_t)rho * a.os + j);
   const uint32_t dd = pack_bf16x2(d0, d1);
-  *p = fold2(*p, dd, scale_table[pair]);
+  *p = fold2(*p, dd, a.scale_table()[pair]);
+}
+
+static GatherArgs gather_args(const rld_moe_route* route, const void* x, uint32_t x_row_stride,
+                              const int32_t* indices, const int32_t* row_adapter, uint32_t top_k,
+                              const void* xa, void* base_out, uint32_t out_row_stride) {
+  GatherArgs a = {};
+  a.x_ = reinterpret_cast<uint64_t>(x);
+  a.idx_ = reinterpret_cast<uint64_t>(indices);
+  a.radapt_ = reinterpret_cast<uint64_t>(row_adapter);
+  a.atab_ = reinterpret_cast<uint64_t>(route->a_table);
+  a.btab_ = reinterpret_cast<uint64_t>(route->b_table);
+  a.stab_ = reinterpret_cast<uint64_t>(route->scale_table);
+  a.xa_ = reinterpret_cast<uint64_t>(xa);
+  a.out_ = reinterpret_cast<uint64_t>(base_out);
+  a.xs = x_row_stride;
+  a.top_k = top_k;
+  a.max_loras = route->max_loras;
+  a.E = route->num_experts;
+  a.k_in = route->k_in;
+  a.n_out = route->n_out;
+  a.R = route->max_rank;
+  a.os = out_row_stride;
+  return a;
 }
 
 }  // namespace rld
@@ -117,10 +145,9 @@ extern "C" int rld_moe_gather_shrink(const rld_moe_route* route, const void* x,
   if (!xa) return RLD_EINVAL;
   if (!aligned16(xa)) return RLD_EALIGN;
   hipLaunchKernelGGL(gather_shrink_kernel, dim3(n_rows), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x),
-                     x_row_stride, indices, row_adapter, top_k, route->a_table, route->b_table,
-                     route->max_loras, route->num_experts, route->k_in, route->max_rank,
-                     static_cast<uint16_t*>(xa));
+                     reinterpret_cast<hipStream_t>(stream),
+                     gather_args(route, x, x_row_stride, indices, row_adapter, top_k, xa,
+                                 nullptr, 0));
   return launch_status();
 }
 
@@ -135,10 +162,8 @@ extern "C" int rld_moe_gather_expand_fold(const rld_moe_route* route, const void
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
   hipLaunchKernelGGL(gather_expand_kernel, dim3(n_rows, div_ceil(route->n_out, kGatherCols)),
                      dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
-                     static_cast<const uint16_t*>(xa), indices, row_adapter, top_k,
-                     route->a_table, route->b_table, route->scale_table, route->max_loras,
-                     route->num_experts, route->n_out, route->max_rank,
-                     static_cast<uint16_t*>(base_out), out_row_stride);
+                     gather_args(route, nullptr, 0, indices, row_adapter, top_k, xa, base_out,
+                                 out_row_stride));
   return launch_status();
 }
 

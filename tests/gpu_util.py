@@ -66,7 +66,7 @@ def shrink_depth(path: str, k_in: int, max_rank: int) -> int:
     the kernels (an upper bound): 32 for one MFMA's internal 32-term sum, plus
     the sequential K steps, plus the fixed-order reductions after them."""
     if path == "bgmv":
-        kc = min(256 if max_rank <= 16 else 512 if max_rank <= 32 else 1024, k_in)
+        kc = min(256 if max_rank <= 16 else 512, k_in)
         nch = -(-k_in // kc)
         steps = -(-kc // 32)
         return 32 + -(-steps // 4) + 4 + nch
