@@ -107,10 +107,6 @@ __device__ __forceinline__ int collect_slot_rows(const RLD_GLOBAL int32_t* seq_s
   return cnt;
 }
 
-// Compiler-level memory barrier: the loads written before it are issued
-// before it (they cannot be moved past it), without waiting for their data.
-__device__ __forceinline__ void issue_point() { asm volatile("" ::: "memory"); }
-
 // This thread's seq_slot entry among the first 256 rows (-1 past n).  The
 // load is unconditional (a row < n is always readable) so that it stays in the
 // prologue, ahead of the tile loads.

@@ -74,6 +74,10 @@ __device__ __forceinline__ void store16(RLD_GLOBAL uint16_t* p, const uint4& v) 
 
 __device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Compiler-level memory barrier: the loads written before it are issued
+// before it (no load can be moved across it), without waiting for their data.
+__device__ __forceinline__ void issue_point() { asm volatile("" ::: "memory"); }
+
 // out = bf16(f32(base) + f32(scale * f32(delta))): the product is rounded to
 // fp32 before the add (base += scale * bf16(delta) in fp32), never fused.
 __device__ __forceinline__ float fold_f32(uint32_t base16, uint32_t delta16, float scale) {

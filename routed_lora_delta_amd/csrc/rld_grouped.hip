@@ -377,7 +377,8 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const uint32_t k = ks * 32 + lg * 8;
-        aop[m][ks] = (c < n_out && k < R) ? load16(B + (size_t)c * R + k) : zero16();
+        aop[m][ks] = load16(B + (c < n_out && k < R ? (size_t)c * R + k : 0));
+        if (c >= n_out || k >= R) aop[m][ks] = zero16();
       }
     }
     uint32_t lo, hi;
@@ -398,26 +399,37 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
           const int ei = threadIdx.x + kPeThreads * j;
           const int rl = ei / (kPeCols / 8);
           const uint32_t c = j0 + (ei % (kPeCols / 8)) * 8;
-          bv[j] = (rl < nb && c < n_out) ? load16(out + (size_t)list[b0 + rl] * os + c) : zero16();
+          // clamped in-bounds address; entries past the batch or n_out are not stored
+          bv[j] = load16(out + (size_t)list[b0 + (rl < nb ? rl : 0)] * os + (c < n_out ? c : j0));
         }
+        // xa rows of the batch's four subtiles, all in flight with the base
+        // values (clamped in-bounds addresses; k past max_rank zeroed)
+        uint4 bop[kBatch / 16][NKS];
 #pragma unroll
         for (int p = 0; p < kBatch / 16; ++p) {
-          if (p * 16 >= nb) continue;
           const int li = p * 16 + cl;
-          const bool ok = li < nb;
           const RLD_GLOBAL uint16_t* xr =
-              xa + (size_t)((ok ? (uint32_t)list[b0 + li] : row_offset) - row_offset) * R;
-          uint4 bop[NKS];
+              xa + (size_t)((uint32_t)list[b0 + (li < nb ? li : 0)] - row_offset) * R;
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
             const uint32_t k = ks * 32 + lg * 8;
-            bop[ks] = (ok && k < R) ? load16(xr + k) : zero16();
+            bop[p][ks] = load16(xr + (k < R ? k : 0));
           }
+        }
+        issue_point();
+#pragma unroll
+        for (int p = 0; p < kBatch / 16; ++p)
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            if (ks * 32 + lg * 8 >= (int)R) bop[p][ks] = zero16();
+#pragma unroll
+        for (int p = 0; p < kBatch / 16; ++p) {
+          if (p * 16 >= nb) continue;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) acc = mfma_bf16_16x16x32(aop[m][ks], bop[ks], acc);
+            for (int ks = 0; ks < NKS; ++ks) acc = mfma_bf16_16x16x32(aop[m][ks], bop[p][ks], acc);
             const uint32_t d01 = pack_bf16x2(acc[0], acc[1]);
             const uint32_t d23 = pack_bf16x2(acc[2], acc[3]);
             *reinterpret_cast<uint2*>(
