@@ -95,6 +95,122 @@ def grouped_window_bytes(wl, p, lo, hi):
     return shrink, expand, 2 * n_act * R * (p.k_in + p.n_out), n_act
 
 
+# ------------------------------------------------------ counters and profiles --
+
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_digest():
+    """sha256 of the library's kernel sources and header: counter readings
+    taken for other sources do not describe the kernels that run."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "routed_lora_delta_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "rld.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _kernel_key(name):
+    """'void rld::bgmv_expand_kernel<2>(rld::BgmvArgs)' -> 'bgmv_expand_kernel'."""
+    n = name.split("(")[0].split("<")[0]
+    return n.split("::")[-1].strip()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary in
+    profiles/ (calibrated FETCH_SIZE + WRITE_SIZE), or None when there is none
+    for the current kernel sources."""
+    import glob
+    digest = source_digest()
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*counters*.md"))):
+        with open(f) as fh:
+            txt = fh.read()
+        for block in txt.split("```json")[1:]:
+            try:
+                d = json.loads(block.split("```")[0])
+            except ValueError:
+                continue
+            if d.get("source_digest") == digest and kernel in d.get("kernels", {}):
+                return int(d["kernels"][kernel]["traffic_bytes_per_launch"])
+    return None
+
+
+def summarize(dirs, bench_json=None):
+    """Markdown summary of rocprofv3 output directories: kernel-trace stats
+    (*_kernel_stats.csv) and FETCH_SIZE / WRITE_SIZE counter runs
+    (*_counter_collection.csv) calibrated on the COPY_BYTES copy of
+    --copy-calibration (the copy dispatch with the largest reading)."""
+    import csv
+    import glob
+    lines = []
+    stats = [f for d in dirs for f in glob.glob(os.path.join(d, "**", "*_kernel_stats.csv"),
+                                                 recursive=True)]
+    for f in stats:
+        rows = list(csv.DictReader(open(f)))
+        lines.append(f"Kernel trace statistics ({os.path.relpath(f)}):\n")
+        lines.append("| kernel | calls | mean us | min us | max us | share |")
+        lines.append("|---|---|---|---|---|---|")
+        for r in rows:
+            lines.append(f"| {r['Name'][:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                         f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+        lines.append("")
+    counters = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                counters.setdefault(r["Counter_Name"], []).append(r)
+    if counters:
+        factor = {}
+        per = {}
+        for cname, rows in counters.items():
+            copies = [float(r["Counter_Value"]) for r in rows
+                      if "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()]
+            big = max(copies) if copies else 0.0
+            factor[cname] = COPY_BYTES / (big * 1024.0) if big > 0 else None
+            for r in rows:
+                if "rld::" not in r["Kernel_Name"]:
+                    continue
+                k = per.setdefault(_kernel_key(r["Kernel_Name"]), {})
+                k.setdefault(cname, []).append(float(r["Counter_Value"]))
+        lines.append(f"Counter calibration: a {COPY_BYTES >> 20} MiB device copy reads as "
+                     + ", ".join(f"{c} {COPY_BYTES / 1024 / factor[c]:.1f} KiB (factor "
+                                 f"{factor[c]:.4f})" for c in sorted(factor) if factor[c]) + "\n")
+        lines.append("| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
+                     "HBM MB/dispatch (calibrated) |")
+        lines.append("|---|---|---|---|---|")
+        out = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES,
+               "factors": factor, "kernels": {}}
+        for k, v in sorted(per.items()):
+            fk = float(np.mean(v.get("FETCH_SIZE", [0.0])))
+            wk = float(np.mean(v.get("WRITE_SIZE", [0.0])))
+            tb = fk * 1024 * (factor.get("FETCH_SIZE") or 1.0) + \
+                wk * 1024 * (factor.get("WRITE_SIZE") or 1.0)
+            out["kernels"][k] = {"dispatches": len(v.get("FETCH_SIZE", v.get("WRITE_SIZE", []))),
+                                 "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                                 "traffic_bytes_per_launch": int(tb)}
+            lines.append(f"| {k} | {out['kernels'][k]['dispatches']} | {fk:.1f} | {wk:.1f} | "
+                         f"{tb / 1e6:.2f} |")
+        lines.append("")
+        lines.append("```json\n" + json.dumps(out, indent=1) + "\n```")
+    if bench_json:
+        with open(bench_json) as fh:
+            b = json.loads(fh.read().strip().splitlines()[-1])
+        lines.append("\nBench line of the same build (kernels: mean us per launch):\n")
+        lines.append("| kernel | launches/step | mean us | algorithmic MB/launch | GB/s |")
+        lines.append("|---|---|---|---|---|")
+        for k, v in b.get("kernels", {}).items():
+            lines.append(f"| {k} | {v['launches_per_step']} | {v['avg_us']} | "
+                         f"{v['algo_bytes_per_launch'] / 1e6:.2f} | {v['gbs']} |")
+        lines.append(f"\nms_per_step {b['ms_per_step']}, value {b['value']} {b['unit']}, "
+                     f"roofline {json.dumps(b['roofline'])}")
+    return "\n".join(lines)
+
+
 # ------------------------------------------------------------------ GPU side --
 
 class Step:
@@ -259,11 +375,57 @@ def _timed_eager(step, idx, lead_graph, steps, torch):
                      for evs in evsets]).mean(axis=0)
 
 
+def _timed_by_kernel(step, lead_graph, steps, torch):
+    """Per-kernel launch duration: K times, replay lead_graph (so the host runs
+    ahead), then for each kernel issue all of its launches of the step back to
+    back, in step order, between two HIP events on the launch stream.  Returns
+    {kernel: mean ms per launch}.  (The launches of one kernel run without the
+    other stage in between; the fold's values are not used after this.)"""
+    names = []
+    for c in step.calls:
+        if c[1] not in names:
+            names.append(c[1])
+    out = {}
+    for kn in names:
+        idx = [i for i, c in enumerate(step.calls) if c[1] == kn]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            lead_graph.replay()
+            e0.record()
+            for i in idx:
+                if step.calls[i][2]() != 0:
+                    raise RuntimeError(step.calls[i][0])
+            e1.record()
+        torch.cuda.synchronize()
+        out[kn] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs])) / len(idx)
+    return out
+
+
+COPY_BYTES = 256 << 20  # bytes read (and written) by one calibration copy
+
+
+def copy_calibration(torch, dev):
+    """Plain device-to-device copies of COPY_BYTES: the kernel reads and writes
+    exactly that many bytes, so the ratio of a traffic counter's reading to
+    COPY_BYTES calibrates that counter."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device=dev).fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def run_gpu(args):
     import torch
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if getattr(args, "copy_calibration", False):
+        copy_calibration(torch, dev)
     wls = select_workloads(args.workload)
     step = Step(dev, wls)
     ncalls = len(step.calls)
@@ -308,23 +470,25 @@ def run_gpu(args):
         per_call_ms[other] = _timed_eager(step, other, lead, args.steps, torch)
     segs = [(i, i + 1) for i in range(ncalls)]
     seg_ms = per_call_ms
+    # timed region D: each kernel's launches back to back (per-launch durations
+    # for the kernel table and the roofline)
+    kernel_ms = _timed_by_kernel(step, full, args.steps, torch)
 
     ms_per_step = wall * 1e3 / args.steps
-    # launches timed one by one (single-call segments), grouped by kernel
+    # per kernel: launches, algorithmic bytes and flops per step, mean launch time
     kernels = {}
-    for (a, b), ms in zip(segs, seg_ms):
-        if b - a != 1:
-            continue
-        _, kname, _, by, fl, _ = step.calls[a]
-        k = kernels.setdefault(kname, {"launches": 0, "ms": 0.0, "bytes": 0, "flops": 0.0})
+    for c in step.calls:
+        k = kernels.setdefault(c[1], {"launches": 0, "bytes": 0, "flops": 0.0})
         k["launches"] += 1
-        k["ms"] += float(ms)
-        k["bytes"] += int(by)
-        k["flops"] += float(fl)
+        k["bytes"] += int(c[3])
+        k["flops"] += float(c[4])
+    for kn, k in kernels.items():
+        k["ms"] = kernel_ms[kn] * k["launches"]
     dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["ms"])
     avg_launch_s = dom["ms"] / dom["launches"] * 1e-3
     bytes_per_launch = dom["bytes"] / dom["launches"]
     achieved = bytes_per_launch / avg_launch_s / 1e9
+    traffic = measured_traffic(dom_name)
 
     per_workload = {}
     for tag, _ in wls:
@@ -354,7 +518,7 @@ def run_gpu(args):
         "flops": step.flops,
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algo_bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "launches_per_step": dom["launches"]},
@@ -423,7 +587,16 @@ def main():
                     help="sorted rows per grouped projection in the cpu_baseline sample "
                          "(the default covers the whole step)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print a markdown summary of rocprofv3 output directories and exit")
+    ap.add_argument("--bench-json", help="with --summarize: a bench.py output line to include")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run plain device copies of COPY_BYTES (256 MiB) each, so that "
+                         "a counter run sees the counters of a copy of known size")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize(args.summarize, args.bench_json))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the routed fold has no multi-GPU path in this "
               "library (run with --gpus 1).", file=sys.stderr)
