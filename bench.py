@@ -285,7 +285,12 @@ class Step:
                 stid = i32(wl.sorted_token_ids)
                 rad = i32(wl.row_adapter)
                 xa = torch.zeros(wl.cap * wl.max_rank + 8, dtype=torch.int16, device=dev)
-                keep += [off, stid, rad, xa]
+                # one workspace for every projection and window (sized for the largest)
+                wsb = max(R.rld_moe_grouped_workspace_bytes(wl.cap, p.k_in, wl.max_rank,
+                                                            wl.max_loras, wl.num_experts)
+                          for p in wl.projections)
+                ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+                keep += [off, stid, rad, xa, ws]
                 wins = [(k * wl.cap, min((k + 1) * wl.cap, wl.te))
                         for k in range(-(-wl.te // wl.cap))]
                 for p in wl.projections:
@@ -298,10 +303,11 @@ class Step:
                         sb, eb, fl, _ = grouped_window_bytes(wl, p, lo, hi)
 
                         def shrink(rt=rt, x=x, p=p, lo=lo, hi=hi, off=off, stid=stid, rad=rad,
-                                   xa=xa, wl=wl):
+                                   xa=xa, wl=wl, ws=ws, wsb=wsb):
                             return R.rld_moe_grouped_shrink(rt.route, x, p.k_in, p.x_gather,
                                                             wl.num_tokens, off, wl.num_experts,
-                                                            stid, rad, lo, hi, xa, wl.cap)
+                                                            stid, rad, lo, hi, xa, wl.cap, ws,
+                                                            wsb)
 
                         def expand(rt=rt, base=base, p=p, lo=lo, hi=hi, off=off, stid=stid,
                                    rad=rad, xa=xa, wl=wl):

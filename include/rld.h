@@ -225,6 +225,18 @@ int rld_moe_gather(const rld_moe_route* route, const void* x, uint32_t x_row_str
                    uint32_t n_rows, void* base_out, uint32_t out_row_stride, void* xa,
                    void* stream);
 
+/* Bytes of workspace rld_moe_grouped_shrink needs for a window of window_rows
+ * rows: the fp32 partial sums of its k_in split ([chunks][window_rows]
+ * [max_rank], chunks = ceil(k_in / 256) up to k_in = 1024, ceil(k_in / 512)
+ * above) plus 16 bytes of counter per (slot, expert) pair.  Returns 0 when
+ * k_in fits one chunk (no workspace needed; NULL may be passed) or when any
+ * size is 0.  The workspace contract of rld_bgmv_workspace_bytes applies
+ * (16-byte aligned, zero-filled once, counters at the end of the buffer keyed
+ * by pair, calls sharing it must not overlap); one buffer sized for the
+ * largest window serves every window of a route. */
+size_t rld_moe_grouped_workspace_bytes(uint32_t window_rows, uint32_t k_in, uint32_t max_rank,
+                                       uint32_t max_loras, uint32_t num_experts);
+
 /* MoE grouped fold shrink for ONE chunk window [row_offset, row_end) of the
  * expert-sorted rows (moe_lora_grouped_down):
  *   expert_offsets   device int32 [num_experts_off + 1], non-decreasing prefix
@@ -238,17 +250,24 @@ int rld_moe_gather(const rld_moe_route* route, const void* x, uint32_t x_row_str
  *                    x_gather != 0: token-major rows, x + t*x_row_stride with
  *                    t = sorted_token_ids[r]
  *   xa               device BF16 [xa_rows_cap, max_rank]; row r is written at
- *                    the window-local row r - row_offset
+ *                    the window-local row r - row_offset; rows that do not
+ *                    fold are written as zeros
+ *   workspace        see rld_moe_grouped_workspace_bytes (RLD_ENOSPACE if
+ *                    workspace_bytes is smaller than it for this window)
  * The launch shape depends only on the host arguments (route sizes and the
  * window), so a captured call replays with new routing contents; an empty
- * window (row_end == row_offset) launches nothing and returns RLD_OK.
+ * window (row_end == row_offset) launches nothing and returns RLD_OK.  A
+ * row's xa depends only on its own x row, so a full-window call and the union
+ * of its chunk windows are bit-identical.
  * RLD_EUNSUPPORTED if max_loras * num_experts > 2048 (the per-launch pair
- * list); RLD_ENOSPACE if row_end - row_offset > xa_rows_cap. */
+ * list) or num_experts_off >= 1024 (offsets staged on chip); RLD_ENOSPACE if
+ * row_end - row_offset > xa_rows_cap. */
 int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x, uint32_t x_row_stride,
                            int x_gather, uint32_t num_tokens, const int32_t* expert_offsets,
                            uint32_t num_experts_off, const int32_t* sorted_token_ids,
                            const int32_t* row_adapter, uint32_t row_offset, uint32_t row_end,
-                           void* xa, uint32_t xa_rows_cap, void* stream);
+                           void* xa, uint32_t xa_rows_cap, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* MoE grouped fold expand + fold of the same window into the sorted base_out
  * ([te, out_row_stride] BF16, row r folded in place). */
@@ -264,7 +283,7 @@ int rld_moe_grouped(const rld_moe_route* route, const void* x, uint32_t x_row_st
                     uint32_t num_experts_off, const int32_t* sorted_token_ids,
                     const int32_t* row_adapter, uint32_t row_offset, uint32_t row_end,
                     void* base_out, uint32_t out_row_stride, void* xa, uint32_t xa_rows_cap,
-                    void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------ diagnostics -- */
 

@@ -92,12 +92,15 @@ _SIGS = {
                                            _P]),
     "rld_moe_gather": (c_int, [_M, _P, c_uint32, _P, _P, c_uint32, c_uint32, _P, c_uint32, _P,
                                _P]),
+    "rld_moe_grouped_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32, c_uint32,
+                                                   c_uint32]),
     "rld_moe_grouped_shrink": (c_int, [_M, _P, c_uint32, c_int, c_uint32, _P, c_uint32, _P, _P,
-                                       c_uint32, c_uint32, _P, c_uint32, _P]),
+                                       c_uint32, c_uint32, _P, c_uint32, _P, c_size_t, _P]),
     "rld_moe_grouped_expand_fold": (c_int, [_M, _P, c_uint32, _P, c_uint32, _P, _P, c_uint32,
                                             c_uint32, _P, c_uint32, _P]),
     "rld_moe_grouped": (c_int, [_M, _P, c_uint32, c_int, c_uint32, _P, c_uint32, _P, _P,
-                                c_uint32, c_uint32, _P, c_uint32, _P, c_uint32, _P]),
+                                c_uint32, c_uint32, _P, c_uint32, _P, c_uint32, _P, c_size_t,
+                                _P]),
     "rld_status_string": (ctypes.c_char_p, [c_int]),
     "rld_last_hip_error": (c_int, []),
     "rld_version": (ctypes.c_char_p, []),
@@ -245,13 +248,19 @@ def rld_moe_gather(route, x, x_row_stride, indices, row_adapter, top_k, n_rows, 
                                ptr(xa), stream_handle(stream))
 
 
+def rld_moe_grouped_workspace_bytes(window_rows, k_in, max_rank, max_loras, num_experts):
+    return _lib.rld_moe_grouped_workspace_bytes(window_rows, k_in, max_rank, max_loras,
+                                                num_experts)
+
+
 def rld_moe_grouped_shrink(route, x, x_row_stride, x_gather, num_tokens, expert_offsets,
                            num_experts_off, sorted_token_ids, row_adapter, row_offset, row_end,
-                           xa, xa_rows_cap, stream=None):
+                           xa, xa_rows_cap, workspace, workspace_bytes, stream=None):
     return _lib.rld_moe_grouped_shrink(ctypes.byref(route), ptr(x), x_row_stride, int(x_gather),
                                        num_tokens, ptr(expert_offsets), num_experts_off,
                                        ptr(sorted_token_ids), ptr(row_adapter), row_offset,
-                                       row_end, ptr(xa), xa_rows_cap, stream_handle(stream))
+                                       row_end, ptr(xa), xa_rows_cap, ptr(workspace),
+                                       workspace_bytes, stream_handle(stream))
 
 
 def rld_moe_grouped_expand_fold(route, xa, num_tokens, expert_offsets, num_experts_off,
@@ -266,12 +275,12 @@ def rld_moe_grouped_expand_fold(route, xa, num_tokens, expert_offsets, num_exper
 
 def rld_moe_grouped(route, x, x_row_stride, x_gather, num_tokens, expert_offsets,
                     num_experts_off, sorted_token_ids, row_adapter, row_offset, row_end, base_out,
-                    out_row_stride, xa, xa_rows_cap, stream=None):
+                    out_row_stride, xa, xa_rows_cap, workspace, workspace_bytes, stream=None):
     return _lib.rld_moe_grouped(ctypes.byref(route), ptr(x), x_row_stride, int(x_gather),
                                 num_tokens, ptr(expert_offsets), num_experts_off,
                                 ptr(sorted_token_ids), ptr(row_adapter), row_offset, row_end,
                                 ptr(base_out), out_row_stride, ptr(xa), xa_rows_cap,
-                                stream_handle(stream))
+                                ptr(workspace), workspace_bytes, stream_handle(stream))
 
 
 def library_path() -> str:

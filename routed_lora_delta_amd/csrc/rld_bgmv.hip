@@ -131,19 +131,6 @@ __device__ __forceinline__ SlotEntry slot_entry(const BgmvArgs& a, int s) {
   return e;
 }
 
-// Block-wide: this thread's stores have completed, then the block meets, then
-// thread 0 adds 1 to *ctr (agent scope) and every thread gets the old value.
-__device__ __forceinline__ uint32_t block_signal(RLD_GLOBAL uint32_t* ctr, int* slot) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *slot = (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const uint32_t old = (uint32_t)*slot;
-  __syncthreads();
-  return old;
-}
-
 // Shrink item w (slot-major over (slot, chunk, 16 columns)).
 __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, ShrinkSmem& sm) {
   const uint32_t n = a.n, R = a.R, nchunks = a.nch, ntr = a.ntr;

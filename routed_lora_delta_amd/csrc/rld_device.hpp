@@ -147,6 +147,22 @@ __device__ __forceinline__ int expert_of_row(P off, int E, int r) {
   return r < off[lo + 1] ? lo : -1;
 }
 
+// Block-wide arrival on a counter shared by the blocks that each produce part
+// of a result: this thread's stores have completed (the partial results were
+// written with agent-scope stores, which other XCDs see), then the block
+// meets, then thread 0 adds 1 to *ctr (agent scope) and every thread gets the
+// old value in *slot (LDS).  The block that sees (arrivals - 1) is the last.
+__device__ __forceinline__ uint32_t block_signal(RLD_GLOBAL uint32_t* ctr, int* slot) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *slot = (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t old = (uint32_t)*slot;
+  __syncthreads();
+  return old;
+}
+
 // Block index remap so that consecutive work items land on the same XCD
 // (workgroups are dispatched round-robin over the 8 XCDs).  gridDim.x must be
 // a multiple of 8; returns >= total for padding blocks.

@@ -9,25 +9,29 @@
 //
 // Work is keyed on the pair, not on fixed row tiles: the work item of pair
 // (s, e) reads the window part of expert e's span, keeps the rows whose slot is
-// s, and streams A_{s,e} (shrink) or a column slice of B_{s,e} (expand) exactly
-// once for all of them.  Every x row and every base row is touched by the one
-// item of its pair, and the MFMA jobs are as tall as the pair's row count.
+// s, and streams a k chunk of A_{s,e} (shrink) or a column slice of B_{s,e}
+// (expand) exactly once for all of them.  Every piece of an x row or a base
+// row is touched by one item, and the MFMA jobs are as tall as the pair's row
+// count.
 // Launches are persistent: a fixed number of blocks (host constant, so a
 // captured launch keeps its shape), each of which lists the window's active
 // pairs (adapter present, rows in the window) from the offsets and the tables
 // in one round of loads, then takes its share of the items.  No block is spent
 // on a pair that has nothing to do.
 //
-// Summation order.  The shrink splits k_in into 8 fixed ranges, one per wave
-// (range length a function of k_in only); each wave sums its range in one MFMA
-// chain, the 8 partial sums are added in wave order.  The expand is one MFMA
-// chain over max_rank.  A row's result therefore never depends on which other
-// rows share its block or window: a full-window call and the union of chunk
-// windows are bit-identical.
+// The shrink spreads each pair over the whole chip: its items are (pair, k
+// chunk), so the pair's A_{s,e} and x rows are streamed by several blocks at
+// once, and fp32 partial sums per chunk meet in a workspace (see GsArgs).
 //
-// xa rows of window rows that do not fold are written as zeros, expert by
-// expert (items after the pair items), and by block 0 for rows that no expert
-// of the table owns.
+// Summation order.  The shrink cuts k_in into chunks of a length fixed by k_in
+// alone, each chunk into four wave ranges; a wave sums its range in one MFMA
+// chain, the wave sums are added in wave order and the chunk sums in chunk
+// order.  The expand is one MFMA chain over max_rank.  A row's result
+// therefore never depends on which other rows share its block or window: a
+// full-window call and the union of chunk windows are bit-identical.
+//
+// xa rows of window rows that do not fold are written as zeros by row-block
+// items of the shrink.
 #include "rld_device.hpp"
 #include "rld_internal.hpp"
 
@@ -37,9 +41,6 @@ constexpr int kOffCap = 1024;    // expert_offsets entries staged in LDS (num_ex
 constexpr int kPairCap = 2048;   // max_loras * num_experts held in the LDS worklist
 constexpr int kListCap = 512;    // rows of a pair collected per scan
 constexpr int kBatch = 64;       // rows of a pair per MFMA pass (4 subtiles of 16)
-constexpr int kPsThreads = 512;  // shrink block: 8 waves, one k_in range each
-constexpr int kPsWaves = kPsThreads / kWave;
-constexpr int kPsSplit = 1;      // shrink blocks per pair (row subtiles split between them)
 constexpr int kPeThreads = 512;  // expand block: 8 waves x 64 columns
 constexpr int kPeCols = 512;     // output columns per expand item
 constexpr int kPeGrid = 512;     // expand blocks per launch
@@ -61,13 +62,6 @@ struct GroupedRows {
   __device__ const RLD_GLOBAL uint64_t* b_table() const { return gp<const uint64_t>(btab_); }
 };
 
-// All threads: expert_offsets into LDS (the launchers require E_off < kOffCap).
-__device__ __forceinline__ const int* stage_offsets(const GroupedRows& g, int* off_s) {
-  for (uint32_t i = threadIdx.x; i <= g.E_off; i += blockDim.x) off_s[i] = g.off()[i];
-  __syncthreads();
-  return off_s;
-}
-
 // Window part [lo, hi) of expert e's span (empty when e has no offsets entry).
 __device__ __forceinline__ void span_in_window(const int* off, const GroupedRows& g, int e,
                                                uint32_t row_offset, uint32_t row_end,
@@ -80,8 +74,14 @@ __device__ __forceinline__ void span_in_window(const int* off, const GroupedRows
   if (hi < lo) hi = lo;
 }
 
-// Adapter slot of sorted row r (slot 0 without row_adapter), or -1 when its
-// token is out of range; the token goes to *tok.
+// Adapter slot of token t (in range): slot 0 without row_adapter, else its
+// row_adapter entry.
+__device__ __forceinline__ int token_slot(const GroupedRows& g, int t) {
+  return g.radapt_ ? g.radapt()[t] : 0;
+}
+
+// Adapter slot of sorted row r, or -1 when its token is out of range; the
+// token goes to *tok.
 __device__ __forceinline__ int row_slot(const GroupedRows& g, uint32_t r, int* tok) {
   int t = 0;
   if (g.need_tok) {
@@ -89,7 +89,7 @@ __device__ __forceinline__ int row_slot(const GroupedRows& g, uint32_t r, int* t
     if (t < 0 || (uint32_t)t >= g.num_tokens) return -1;
   }
   *tok = t;
-  return g.radapt_ ? g.radapt()[t] : 0;
+  return token_slot(g, t);
 }
 
 // Appends to list/toks (LDS) the rows of [c0, c1) (c1 - c0 <= blockDim) that
@@ -128,26 +128,49 @@ __device__ __forceinline__ void zero_xa_row(RLD_GLOBAL uint16_t* xa, uint32_t lo
   for (uint32_t i = 0; i < R / 8; ++i) store16(xa + (size_t)local_row * R + 8 * i, zero16());
 }
 
-// Every thread: stage expert_offsets, read the A/B table entries of every pair
+// Every thread (NTH of them): stage expert_offsets in LDS, read the A/B table entries of every pair
 // (valid[p] = both present), and list in LDS, ascending, the pairs that are
-// valid and own rows of [row_offset, row_end).  The offsets and table reads go
-// out together, so this costs one round of loads.  Returns the pair count.
+// valid and own rows of [row_offset, row_end).  All these loads go out
+// together, so this costs one round of loads.  Returns the pair count.
+template <int NTH>
 __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row_offset,
                                               uint32_t row_end, int* off_s, uint8_t* valid,
                                               int16_t* apairs, int* wcount) {
+  constexpr int kOffPer = kOffCap / NTH;
+  constexpr int kPairPer = kPairCap / NTH;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  constexpr int nw = NTH / kWave;
   const uint32_t np = g.max_loras * g.E;
-  for (uint32_t i = threadIdx.x; i <= g.E_off; i += blockDim.x) off_s[i] = g.off()[i];
-  for (uint32_t p = threadIdx.x; p < np; p += blockDim.x) {
-    const uint64_t ta = g.a_table()[p], tb = g.b_table()[p];
-    valid[p] = (ta != 0ull && tb != 0ull) ? 1 : 0;
+  int ov[kOffPer];
+  uint64_t ta[kPairPer], tb[kPairPer];
+#pragma unroll
+  for (int i = 0; i < kOffPer; ++i) {
+    const uint32_t j = threadIdx.x + i * NTH;
+    ov[i] = g.off()[j <= g.E_off ? j : 0];
+  }
+  // unconditional loads at clamped indices: a load under a branch gets a wait
+  // of its own, which would serialise this round
+#pragma unroll
+  for (int i = 0; i < kPairPer; ++i) {
+    const uint32_t p = threadIdx.x + i * NTH;
+    ta[i] = g.a_table()[p < np ? p : 0];
+    tb[i] = g.b_table()[p < np ? p : 0];
+  }
+#pragma unroll
+  for (int i = 0; i < kOffPer; ++i) {
+    const uint32_t j = threadIdx.x + i * NTH;
+    if (j <= g.E_off) off_s[j] = ov[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kPairPer; ++i) {
+    const uint32_t p = threadIdx.x + i * NTH;
+    if (p < np) valid[p] = (ta[i] != 0ull && tb[i] != 0ull) ? 1 : 0;
   }
   __syncthreads();
   const int* off = off_s;
   int na = 0;
-  for (uint32_t c0 = 0; c0 < np; c0 += blockDim.x) {
+  for (uint32_t c0 = 0; c0 < np; c0 += NTH) {
     const uint32_t p = c0 + threadIdx.x;
     bool act = false;
     if (p < np && valid[p]) {
@@ -160,6 +183,7 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
     __syncthreads();
     int pos = na;
     int tot = 0;
+#pragma unroll
     for (int v = 0; v < nw; ++v) {
       pos += v < wave ? wcount[v] : 0;
       tot += wcount[v];
@@ -171,165 +195,322 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
   return na;
 }
 
-// Block = (pair (s, e), part h of kPsSplit).  Part h takes the 16-row subtiles
-// q of the pair's row list with q % kPsSplit == h, so a pair's rows spread over
-// kPsSplit blocks (placed on one XCD, where they share A_{s,e} in L2).  Wave
-// w sums k_in range [w*kw, (w+1)*kw) for up to 4 subtiles at a time, loading
-// that range of A once per pass and of each x row once; the 8 partial sums
-// meet in LDS in wave order.
-__global__ __launch_bounds__(kPsThreads) void grouped_shrink_kernel(
-    uint64_t x_addr, uint32_t xs, int x_gather, GroupedRows gr, uint32_t k_in, uint32_t R,
-    uint32_t row_offset, uint32_t row_end, uint32_t kw, uint32_t total, uint64_t xa_addr) {
-  const RLD_GLOBAL uint16_t* x = gp<const uint16_t>(x_addr);
-  RLD_GLOBAL uint16_t* xa = gp<uint16_t>(xa_addr);
-  __shared__ int off_s[kOffCap];
-  __shared__ int list[kListCap];
-  __shared__ int toks[kListCap];
-  __shared__ int wcount[kPsWaves];
-  __shared__ floatx4 red[kPsWaves][8][kWave];
-
-  const uint32_t w = xcd_work_item(total);
-  if (w >= total) return;
-  const int pair = (int)(w / kPsSplit);
-  const int h = (int)(w % kPsSplit);
-  const int s = pair / (int)gr.E;
-  const int e = pair % (int)gr.E;
-  const uint64_t ta = gr.a_table()[pair], tb = gr.b_table()[pair];  // with the offsets
-  const int* off = stage_offsets(gr, off_s);
-  const bool pair_ok = ta != 0ull && tb != 0ull;
-  uint32_t lo, hi;
-  span_in_window(off, gr, e, row_offset, row_end, lo, hi);
-
-  if (s == 0 && h == 0) {
-    // rows of e's span that no pair folds
-    for (uint32_t r = lo + threadIdx.x; r < hi; r += blockDim.x) {
-      if (expert_of_row(off, (int)gr.E_off, (int)r) != e) continue;
-      int t = 0;
-      const int sr = row_slot(gr, r, &t);
-      bool act = sr >= 0 && (uint32_t)sr < gr.max_loras;
-      if (act) {
-        const int pr = sr * (int)gr.E + e;
-        const uint64_t pa = gr.a_table()[pr], pb = gr.b_table()[pr];
-        act = pa != 0ull && pb != 0ull;
-      }
-      if (!act) zero_xa_row(xa, r - row_offset, R);
-    }
-    if (e == 0) {
-      // rows that no expert of the table owns
-      for (uint32_t r = row_offset + threadIdx.x; r < row_end; r += blockDim.x) {
-        const int o = expert_of_row(off, (int)gr.E_off, (int)r);
-        if (o < 0 || (uint32_t)o >= gr.E) zero_xa_row(xa, r - row_offset, R);
-      }
-    }
+// Shrink work items, in this order:
+//   (active pair p, k chunk c, column group cg)  for p < na, c < nch, cg < ncg
+//   row block z of the window (256 rows)         for z < nz
+// A pair item streams chunk c of x and of A_{s,e} for the pair's rows: wave w
+// of the block sums k range [c*kc + w*kc/4, c*kc + (w+1)*kc/4) (KS MFMA steps
+// of 32) for up to 64 rows at a time, and the four wave sums meet in LDS in
+// wave order.  With one chunk that sum is rounded to xa right away; otherwise
+// it goes to the fp32 partials part[c][local row][column], and the block that
+// completes the pair's last item (a per-pair counter at the end of the
+// workspace) adds the chunks in chunk order and writes xa.  An item covers
+// NT*16 xa columns (column group cg).  A row-block item zeroes the xa rows of
+// its 256 rows that no pair folds.
+struct GsArgs {
+  uint64_t x_, xa_, part_, ctr_;
+  GroupedRows gr;
+  uint32_t xs, x_gather, k_in, R, row_offset, row_end;
+  uint32_t kc;   // k chunk: 4 waves x 32*KS
+  uint32_t nch;  // chunks, ceil(k_in / kc)
+  uint32_t ncg;  // column groups, ceil(R / (16*NT))
+  uint32_t nz;   // row blocks of the window
+  __device__ const RLD_GLOBAL uint16_t* x() const { return gp<const uint16_t>(x_); }
+  __device__ RLD_GLOBAL uint16_t* xa() const { return gp<uint16_t>(xa_); }
+  __device__ RLD_GLOBAL float* part() const { return gp<float>(part_); }
+  // 16 bytes per pair, below the end of the workspace
+  __device__ RLD_GLOBAL uint32_t* ctr(int pair) const {
+    return gp<uint32_t>(ctr_) - 4 * (pair + 1);
   }
-  if (!pair_ok || hi <= lo) return;
+};
 
-  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ta);
+constexpr int kGsThreads = 256;
+constexpr int kGsWaves = kGsThreads / kWave;
+constexpr int kGsListCap = 512;  // rows of a pair held per scan segment
+
+struct GsSmem {
+  int off[kOffCap];
+  uint8_t valid[kPairCap];
+  int16_t apairs[kPairCap];
+  int list[kGsListCap];  // sorted rows of the pair
+  int xrow[kGsListCap];  // their x rows (token, or the sorted row)
+  int wcount[kGsWaves];
+  int flag;
+};
+
+// One round of gs_scan: the rows of [c0, min(c0 + kGsThreads, hi)) that expert
+// e owns and whose adapter slot is s are appended at sm.list[cnt..] in row
+// order.  Returns the rows appended.
+__device__ __forceinline__ int gs_round(const GroupedRows& g, GsSmem& sm, int e, int s,
+                                        uint32_t c0, uint32_t hi, uint32_t x_gather, int cnt) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t r = c0 + threadIdx.x;
+  const bool inr = r < hi && expert_of_row(sm.off, (int)g.E_off, (int)r) == e;
+  int t = (int)r;
+  if (g.need_tok) t = inr ? g.stid()[r] : 0;
+  bool hit = inr;
+  if (g.need_tok) hit = inr && t >= 0 && (uint32_t)t < g.num_tokens;
+  int sr = -1;
+  if (hit) sr = token_slot(g, t);
+  hit = hit && sr == s;
+  const uint64_t m = __ballot(hit);
+  if (lane == 0) sm.wcount[wave] = __popcll(m);
+  __syncthreads();
+  int pos = cnt;
+  int tot = 0;
+#pragma unroll
+  for (int v = 0; v < kGsWaves; ++v) {
+    pos += v < wave ? sm.wcount[v] : 0;
+    tot += sm.wcount[v];
+  }
+  if (hit) {
+    const int p = pos + __popcll(m & lanemask_lt(lane));
+    sm.list[p] = (int)r;
+    sm.xrow[p] = x_gather ? t : (int)r;
+  }
+  __syncthreads();
+  return tot;
+}
+
+// Collects into sm.list / sm.xrow the rows of [*c0, hi) that expert e owns and
+// whose adapter slot is s, until the segment holds more than
+// kGsListCap - kGsThreads rows, and advances *c0 past the rows scanned
+// (*c0 < hi on entry).  Every thread calls it; returns the row count.
+__device__ __forceinline__ int gs_scan(const GroupedRows& g, GsSmem& sm, int e, int s,
+                                       uint32_t* c0, uint32_t hi, uint32_t x_gather) {
+  int cnt = 0;
+  do {
+    cnt += gs_round(g, sm, e, s, *c0, hi, x_gather, cnt);
+    *c0 += kGsThreads;
+  } while (*c0 < hi && cnt + kGsThreads <= kGsListCap);
+  return cnt;
+}
+
+// Last block of a pair: xa[row, :] = bf16(sum over chunks, in chunk order, of
+// the partials) for the cnt rows in sm.list.  Each thread takes up to 4 column
+// pairs; all their chunk loads (up to 8 chunks at a time) go out before the
+// adds.
+__device__ __forceinline__ void gs_reduce_rows(const GsArgs& a, const GsSmem& sm, int cnt) {
+  const uint32_t R = a.R;
+  const uint32_t half = R / 2;
+  const size_t W = a.row_end - a.row_offset;
+  const size_t cstride = W * R / 2;  // uint64 per chunk
+  const uint32_t tot = (uint32_t)cnt * half;
+  const RLD_GLOBAL uint64_t* part = reinterpret_cast<const RLD_GLOBAL uint64_t*>(a.part());
+  for (uint32_t base = 0; base < tot; base += 4 * kGsThreads) {
+    uint32_t off[4];
+    bool ok[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t ei = base + threadIdx.x + u * kGsThreads;
+      ok[u] = ei < tot;
+      const uint32_t li = ok[u] ? ei / half : 0;
+      const uint32_t lr = (uint32_t)sm.list[li] - a.row_offset;
+      off[u] = lr * half + (ok[u] ? ei % half : 0);
+    }
+    float s0[4], s1[4];
+    for (uint32_t cb = 0; cb < a.nch; cb += 8) {
+      uint64_t v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[u][j] = (ok[u] && cb + j < a.nch)
+                        ? __hip_atomic_load(part + (cb + j) * cstride + off[u], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : 0ull;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float f0 = __uint_as_float((uint32_t)v[u][j]);
+          const float f1 = __uint_as_float((uint32_t)(v[u][j] >> 32));
+          if (cb + j == 0) {
+            s0[u] = f0;
+            s1[u] = f1;
+          } else if (cb + j < a.nch) {
+            s0[u] += f0;
+            s1[u] += f1;
+          }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (ok[u])
+        *reinterpret_cast<RLD_GLOBAL uint32_t*>(a.xa() + 2 * (size_t)off[u]) =
+            pack_bf16x2(s0[u], s1[u]);
+  }
+}
+
+// Pair item (pair, chunk c, column group cg); see GsArgs.
+template <int KS, int NT>
+__device__ void gs_pair_item(const GsArgs& a, GsSmem& sm, floatx4 (*red)[4 * NT][kWave], int pair,
+                             uint32_t c, uint32_t cg) {
+  const GroupedRows& g = a.gr;
+  const uint32_t R = a.R, k_in = a.k_in;
+  const int s = pair / (int)g.E;
+  const int e = pair % (int)g.E;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lg = lane >> 4;
   const int cl = lane & 15;
-  const uint32_t kb = min(wave * kw, k_in);
-  const uint32_t ke = min(kb + kw, k_in);
-  const int ntn = (int)((R + 15) / 16);
+  const uint32_t kw0 = c * a.kc + (uint32_t)wave * (32u * KS);
+  const uint32_t col0 = cg * 16u * NT;
+  uint32_t lo, hi;
+  span_in_window(sm.off, g, e, a.row_offset, a.row_end, lo, hi);
 
+  const uint64_t ta = g.a_table()[pair];  // goes out with the scan's row loads
   uint32_t c0 = lo;
-  while (c0 < hi) {
-    int cnt = 0;
-    while (c0 < hi && cnt + (int)blockDim.x <= kListCap) {
-      cnt += append_pair_rows(gr, off, e, s, c0, min(c0 + blockDim.x, hi), list, toks, cnt,
-                              wcount);
-      c0 += blockDim.x;
+  int cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
+  // Every item of the pair finds the same rows; a pair without rows (no row
+  // of e's span is on slot s) has nothing to write or count.
+  if (cnt == 0) return;
+  const bool multi = c0 < hi;
+
+  const RLD_GLOBAL uint16_t* x = a.x();
+  const bool one_chunk = a.nch == 1;
+  const size_t W = a.row_end - a.row_offset;
+  // up to 64 rows of the segment, starting at b0
+  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ta);
+  auto batch = [&](int b0) {
+    const int nb = min(cnt - b0, 64);
+    // Rows col0.. of A_{s,e} over this wave's k range (MFMA B operands) and the
+    // x rows of the batch's four 16-row subtiles, all in one round of loads
+    // (clamped in-bounds addresses).
+    uint4 bop[NT][KS];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const uint32_t col = col0 + 16u * j + cl;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t kk = kw0 + 32u * ks + 8u * lg;
+        bop[j][ks] = load16(A + (col < R && kk < k_in ? (size_t)col * k_in + kk : 0));
+      }
     }
-    // this block's subtiles: q = h, h + kPsSplit, ... of the (cnt+15)/16
-    const int nsub = (cnt + 15) >> 4;
-    for (int q0 = h; q0 < nsub; q0 += 4 * kPsSplit) {
-      const RLD_GLOBAL uint16_t* xr[4];
-      bool rok[4];
-      int nq = 0;
+    uint4 aop[4][KS];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int qs = q0 + q * kPsSplit;
-        nq += qs < nsub ? 1 : 0;
-        const int li = qs * 16 + cl;
-        rok[q] = qs < nsub && li < cnt;
-        const int src = rok[q] ? (x_gather ? toks[li] : list[li]) : 0;
-        xr[q] = x + (size_t)src * xs;
+    for (int q = 0; q < 4; ++q) {
+      const int li = q * 16 + cl;
+      const RLD_GLOBAL uint16_t* xr = x + (size_t)sm.xrow[b0 + (li < nb ? li : 0)] * a.xs;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t kk = kw0 + 32u * ks + 8u * lg;
+        aop[q][ks] = load16(xr + (kk < k_in ? kk : 0));
       }
-      for (int n0 = 0; n0 < ntn; n0 += 2) {
-        floatx4 acc[4][2];
+    }
+    issue_point();
+    // k past k_in contributes nothing (both operands zeroed); columns past
+    // max_rank are computed from clamped reads and never stored
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+    for (int ks = 0; ks < KS; ++ks)
+      if (kw0 + 32u * ks + 8u * lg >= k_in) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[q][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (uint32_t k = kb; k < ke; k += 256) {
-          uint4 bop[2][8];
+        for (int q = 0; q < 4; ++q) aop[q][ks] = zero16();
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint32_t col = (n0 + j) * 16 + cl;
+        for (int j = 0; j < NT; ++j) bop[j][ks] = zero16();
+      }
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-              const uint32_t kk = k + ks * 32 + lg * 8;
-              bop[j][ks] = (col < R && kk < ke) ? load16(A + (size_t)col * k_in + kk) : zero16();
-            }
-          }
-          // x rows of the four subtiles: two in flight ahead of the MFMAs
-          uint4 aop[4][8];
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (q < 2) {
+      for (int j = 0; j < NT; ++j) {
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int ks = 0; ks < 8; ++ks) {
-                const uint32_t kk = k + ks * 32 + lg * 8;
-                aop[q][ks] = (q < nq && rok[q] && kk < ke) ? load16(xr[q] + kk) : zero16();
-              }
-            }
-          }
+        for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(aop[q][ks], bop[j][ks], acc);
+        red[wave][q * NT + j][lane] = acc;
+      }
+    __syncthreads();
+    {
+      // one thread per (subtile, lane): the wave sums in wave order
+      const int q = threadIdx.x >> 6;
+      const int ln = threadIdx.x & 63;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (q + 2 < 4) {
+      for (int j = 0; j < NT; ++j) {
+        const uint32_t col = col0 + 16u * j + (ln & 15);
+        floatx4 sum = red[0][q * NT + j][ln];
 #pragma unroll
-              for (int ks = 0; ks < 8; ++ks) {
-                const uint32_t kk = k + ks * 32 + lg * 8;
-                aop[q + 2][ks] =
-                    (q + 2 < nq && rok[q + 2] && kk < ke) ? load16(xr[q + 2] + kk) : zero16();
-              }
-            }
-            if (q < nq) {
+        for (int v = 1; v < kGsWaves; ++v) sum += red[v][q * NT + j][ln];
+        if (col < R) {
 #pragma unroll
-              for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                  acc[q][j] = mfma_bf16_16x16x32(aop[q][ks], bop[j][ks], acc[q][j]);
+          for (int i = 0; i < 4; ++i) {
+            const int li = q * 16 + 4 * (ln >> 4) + i;
+            if (li < nb) {
+              const uint32_t lr = (uint32_t)sm.list[b0 + li] - a.row_offset;
+              if (one_chunk)
+                a.xa()[(size_t)lr * R + col] = (uint16_t)f32_to_bf16(sum[i]);
+              else
+                __hip_atomic_store(a.part() + ((size_t)c * W + lr) * R + col, sum[i],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
           }
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) red[wave][q * 2 + j][lane] = acc[q][j];
-        __syncthreads();
-        {
-          // one thread per (subtile, column tile, lane): partial sums in wave order
-          const int q = threadIdx.x >> 7;
-          const int j = (threadIdx.x >> 6) & 1;
-          const int ln = threadIdx.x & 63;
-          const uint32_t col = (n0 + j) * 16 + (ln & 15);
-          if (q < nq && col < R) {
-            floatx4 sum = red[0][q * 2 + j][ln];
-#pragma unroll
-            for (int v = 1; v < kPsWaves; ++v) sum += red[v][q * 2 + j][ln];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int li = (q0 + q * kPsSplit) * 16 + 4 * (ln >> 4) + i;
-              if (li < cnt)
-                xa[(size_t)((uint32_t)list[li] - row_offset) * R + col] =
-                    (uint16_t)f32_to_bf16(sum[i]);
-            }
-          }
-        }
-        __syncthreads();
       }
+    }
+    __syncthreads();
+  };
+  if (!multi && cnt <= 64) {
+    batch(0);  // the usual case
+  } else {
+    for (;;) {
+      for (int b0 = 0; b0 < cnt; b0 += 64) batch(b0);
+      if (c0 >= hi) break;
+      cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
+    }
+  }
+  if (one_chunk) return;
+
+  // The block that completes the pair adds the chunks.
+  RLD_GLOBAL uint32_t* ctr = a.ctr(pair);
+  if (block_signal(ctr, &sm.flag) != a.nch * a.ncg - 1) return;
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!multi) {  // sm.list still holds the pair's rows
+    gs_reduce_rows(a, sm, cnt);
+    return;
+  }
+  c0 = lo;
+  while (c0 < hi) {
+    cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
+    gs_reduce_rows(a, sm, cnt);
+  }
+}
+
+// Row-block item z: zero the xa rows of [row_offset + 256z, +256) that no pair
+// folds (no owner expert, token out of range, slot out of range or not
+// adapted for the expert).
+__device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem& sm, uint32_t z) {
+  const GroupedRows& g = a.gr;
+  const uint32_t r = a.row_offset + z * kGsThreads + threadIdx.x;
+  if (r >= a.row_end) return;
+  const int e = expert_of_row(sm.off, (int)g.E_off, (int)r);
+  bool fold = e >= 0 && (uint32_t)e < g.E;
+  int t = 0;
+  if (fold && g.need_tok) {
+    t = g.stid()[r];
+    fold = t >= 0 && (uint32_t)t < g.num_tokens;
+  }
+  int s = 0;
+  if (fold) s = token_slot(g, t);
+  fold = fold && s >= 0 && (uint32_t)s < g.max_loras && sm.valid[s * (int)g.E + e];
+  if (!fold) zero_xa_row(a.xa(), r - a.row_offset, a.R);
+}
+
+// Persistent: every block lists the window's active pairs, then takes items
+// blockIdx.x, blockIdx.x + gridDim.x, ...
+template <int KS, int NT>
+__global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
+  __shared__ GsSmem sm;
+  __shared__ floatx4 red[kGsWaves][4 * NT][kWave];
+  const int na = build_worklist<kGsThreads>(a.gr, a.row_offset, a.row_end, sm.off, sm.valid,
+                                            sm.apairs, sm.wcount);
+  const uint32_t per = a.nch * a.ncg;
+  const uint32_t npi = (uint32_t)na * per;
+  const uint32_t total = npi + a.nz;
+  for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
+    if (it < npi) {
+      const uint32_t rem = it % per;
+      gs_pair_item<KS, NT>(a, sm, red, sm.apairs[it / per], rem / a.ncg, rem % a.ncg);
+    } else {
+      gs_zero_item(a, sm, it - npi);
     }
   }
 }
@@ -355,7 +536,7 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
   __shared__ int wcount[kPeThreads / kWave];
   __shared__ __attribute__((aligned(16))) uint16_t dl[kBatch * kDlStride];
 
-  const int na = build_worklist(gr, row_offset, row_end, off_s, valid, apairs, wcount);
+  const int na = build_worklist<kPeThreads>(gr, row_offset, row_end, off_s, valid, apairs, wcount);
   const int* off = off_s;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -485,13 +666,20 @@ static GroupedRows make_rows(const rld_moe_route* route, int x_gather, uint32_t 
   return g;
 }
 
-// Length of the k_in range of one shrink wave: the 8 ranges cover k_in, in
-// multiples of 32.  A function of k_in only.
-static uint32_t shrink_range(uint32_t k_in) { return 32u * div_ceil(k_in, 32u * kPsWaves); }
+template <int KS, int NT>
+static void launch_gs(const GsArgs& a, uint32_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((grouped_shrink_kernel<KS, NT>), dim3(grid), dim3(kGsThreads), 0, st, a);
+}
 
 }  // namespace rld
 
 using namespace rld;
+
+extern "C" size_t rld_moe_grouped_workspace_bytes(uint32_t window_rows, uint32_t k_in,
+                                                  uint32_t max_rank, uint32_t max_loras,
+                                                  uint32_t num_experts) {
+  return grouped_workspace(window_rows, k_in, max_rank, max_loras, num_experts);
+}
 
 extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
                                       uint32_t x_row_stride, int x_gather, uint32_t num_tokens,
@@ -499,7 +687,7 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
                                       const int32_t* sorted_token_ids,
                                       const int32_t* row_adapter, uint32_t row_offset,
                                       uint32_t row_end, void* xa, uint32_t xa_rows_cap,
-                                      void* stream) {
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_grouped(route, x_gather, expert_offsets, num_experts_off, sorted_token_ids,
                          row_adapter, row_offset, row_end);
   if (st) return st;
@@ -508,14 +696,42 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
   if (!aligned16(xa)) return RLD_EALIGN;
   if (row_end - row_offset > xa_rows_cap) return RLD_ENOSPACE;
   if (row_end == row_offset) return RLD_OK;
-  GroupedRows gr = make_rows(route, x_gather, num_tokens, expert_offsets, num_experts_off,
-                             sorted_token_ids, row_adapter);
-  const uint32_t total = route->max_loras * route->num_experts * kPsSplit;
-  hipLaunchKernelGGL(grouped_shrink_kernel, dim3(xcd_grid(total)), dim3(kPsThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<uint64_t>(x),
-                     x_row_stride, x_gather ? 1 : 0, gr, route->k_in, route->max_rank,
-                     row_offset, row_end, shrink_range(route->k_in), total,
-                     reinterpret_cast<uint64_t>(xa));
+  const uint32_t W = row_end - row_offset;
+  const size_t need =
+      grouped_workspace(W, route->k_in, route->max_rank, route->max_loras, route->num_experts);
+  if (need) {
+    if (!workspace) return RLD_EINVAL;
+    if (!aligned16(workspace)) return RLD_EALIGN;
+    if (workspace_bytes < need) return RLD_ENOSPACE;
+  }
+  GsArgs a;
+  a.x_ = reinterpret_cast<uint64_t>(x);
+  a.xa_ = reinterpret_cast<uint64_t>(xa);
+  a.part_ = reinterpret_cast<uint64_t>(workspace);
+  a.ctr_ = reinterpret_cast<uint64_t>(workspace) + (workspace_bytes & ~(size_t)15);
+  a.gr = make_rows(route, x_gather, num_tokens, expert_offsets, num_experts_off,
+                   sorted_token_ids, row_adapter);
+  a.xs = x_row_stride;
+  a.x_gather = x_gather ? 1u : 0u;
+  a.k_in = route->k_in;
+  a.R = route->max_rank;
+  a.row_offset = row_offset;
+  a.row_end = row_end;
+  a.kc = grouped_chunk(route->k_in);
+  a.nch = div_ceil(route->k_in, a.kc);
+  const uint32_t nt = grouped_nt(route->max_rank);
+  a.ncg = div_ceil(div_ceil(route->max_rank, 16u), nt);
+  a.nz = div_ceil(W, (uint32_t)kGsThreads);
+  const uint64_t items =
+      (uint64_t)route->max_loras * route->num_experts * a.nch * a.ncg + a.nz;
+  const uint32_t grid = (uint32_t)(items < kGsGrid ? items : kGsGrid);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const bool k4 = a.kc == 512u;
+  switch (nt) {
+    case 1: k4 ? launch_gs<4, 1>(a, grid, hs) : launch_gs<2, 1>(a, grid, hs); break;
+    case 2: k4 ? launch_gs<4, 2>(a, grid, hs) : launch_gs<2, 2>(a, grid, hs); break;
+    default: k4 ? launch_gs<4, 4>(a, grid, hs) : launch_gs<2, 4>(a, grid, hs); break;
+  }
   return launch_status();
 }
 
@@ -556,14 +772,15 @@ extern "C" int rld_moe_grouped(const rld_moe_route* route, const void* x, uint32
                                uint32_t num_experts_off, const int32_t* sorted_token_ids,
                                const int32_t* row_adapter, uint32_t row_offset, uint32_t row_end,
                                void* base_out, uint32_t out_row_stride, void* xa,
-                               uint32_t xa_rows_cap, void* stream) {
+                               uint32_t xa_rows_cap, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   int st = check_grouped(route, x_gather, expert_offsets, num_experts_off, sorted_token_ids,
                          row_adapter, row_offset, row_end);
   if (st) return st;
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
   st = rld_moe_grouped_shrink(route, x, x_row_stride, x_gather, num_tokens, expert_offsets,
                               num_experts_off, sorted_token_ids, row_adapter, row_offset,
-                              row_end, xa, xa_rows_cap, stream);
+                              row_end, xa, xa_rows_cap, workspace, workspace_bytes, stream);
   if (st) return st;
   return rld_moe_grouped_expand_fold(route, xa, num_tokens, expert_offsets, num_experts_off,
                                      sorted_token_ids, row_adapter, row_offset, row_end,

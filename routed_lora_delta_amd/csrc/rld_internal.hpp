@@ -63,6 +63,33 @@ inline uint32_t xcd_group_grid(uint32_t total, uint32_t group) {
   return 8u * group * div_ceil(div_ceil(total, group), 8u);
 }
 
+// k chunk of the MoE grouped shrink, a function of k_in only (so a row's
+// summation order never depends on its window): four waves x 64 k (256) up to
+// k_in = 1024, four waves x 128 k (512) above.
+inline uint32_t grouped_chunk(uint32_t k_in) { return k_in <= 1024u ? 256u : 512u; }
+
+// 16-column MFMA tiles of xa held by one grouped shrink item (1, 2 or 4).
+inline uint32_t grouped_nt(uint32_t max_rank) {
+  const uint32_t t = div_ceil(max_rank, 16u);
+  return t <= 1u ? 1u : (t <= 2u ? 2u : 4u);
+}
+
+// Workspace of a grouped shrink window of `rows` rows: fp32 partials
+// [chunks][rows][max_rank] (16-byte rounded) plus 16 bytes of counter per
+// (slot, expert) pair; none when k_in fits one chunk.
+inline size_t grouped_workspace(uint32_t rows, uint32_t k_in, uint32_t max_rank,
+                                uint32_t max_loras, uint32_t num_experts) {
+  if (k_in == 0 || max_rank == 0 || max_loras == 0 || num_experts == 0) return 0;
+  const uint32_t nch = div_ceil(k_in, grouped_chunk(k_in));
+  if (nch == 1) return 0;
+  const size_t part = ((size_t)nch * rows * max_rank * 4 + 15) & ~(size_t)15;
+  return part + (size_t)16 * max_loras * num_experts;
+}
+
+// Blocks of the persistent grouped shrink launch (fewer when there are fewer
+// possible items).
+constexpr uint32_t kGsGrid = 512;
+
 // Output columns per block of the gather expand (two per thread).
 constexpr uint32_t kGatherCols = 512;
 

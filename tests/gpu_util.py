@@ -71,7 +71,8 @@ def shrink_depth(path: str, k_in: int, max_rank: int) -> int:
         steps = -(-kc // 32)
         return 32 + -(-steps // 4) + 4 + nch
     if path == "grouped":
-        return 32 + -(-k_in // 32)
+        kc = 256 if k_in <= 1024 else 512
+        return 32 + kc // 128 + 4 + -(-k_in // kc)
     if path == "gather":
         return 8 * -(-k_in // 512) + 6
     raise ValueError(path)
@@ -363,6 +364,9 @@ class GroupedRun:
         self.stid = dev_i32(wl.sorted_token_ids, device)
         self.rad = dev_i32(self.ra, device) if self.ra is not None else None
         self.xa = torch.zeros(self.cap * wl.max_rank + 8, dtype=torch.int16, device=device)
+        self.ws_bytes = R.rld_moe_grouped_workspace_bytes(self.cap, proj.k_in, wl.max_rank,
+                                                          wl.max_loras, wl.num_experts)
+        self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
 
     def run(self, windows=None, keep_xa=True):
         wl, p = self.wl, self.p
@@ -371,7 +375,8 @@ class GroupedRun:
         for lo, hi in windows:
             R.check(R.rld_moe_grouped(self.route.route, self.x, p.k_in, p.x_gather, wl.num_tokens,
                                       self.off, wl.num_experts, self.stid, self.rad, lo, hi,
-                                      self.base.ptr(), p.n_out, self.xa, self.cap),
+                                      self.base.ptr(), p.n_out, self.xa, self.cap, self.ws,
+                                      self.ws_bytes),
                     "rld_moe_grouped")
             if keep_xa:
                 torch.cuda.synchronize()

@@ -253,7 +253,7 @@ def test_empty_batches_are_noops():
     assert R.rld_moe_gather(mr, FAKE, 256, FAKE, FAKE, 8, 0, FAKE, 256, FAKE, 0) == R.RLD_OK
     # empty grouped window: validated, then nothing to launch
     assert R.rld_moe_grouped(mr, FAKE, 256, 1, 64, FAKE, 8, FAKE, FAKE, 100, 100, FAKE, 256,
-                             FAKE, 0, 0) == R.RLD_OK
+                             FAKE, 0, 0, 0, 0) == R.RLD_OK
 
 
 def test_moe_rejects_bad_arguments():
@@ -261,7 +261,7 @@ def test_moe_rejects_bad_arguments():
     g = lambda **k: R.rld_moe_grouped_shrink(  # noqa: E731
         k.get("rt", mr), FAKE, 256, k.get("xg", 1), 64, k.get("off", FAKE), k.get("Eo", 8),
         k.get("stid", FAKE), FAKE, k.get("lo", 0), k.get("hi", 64), k.get("xa", FAKE),
-        k.get("cap", 64), 0)
+        k.get("cap", 64), k.get("ws", 0), k.get("wsb", 0), 0)
     assert g(off=0) == R.RLD_EINVAL
     assert g(Eo=0) == R.RLD_EINVAL
     assert g(lo=10, hi=5) == R.RLD_EINVAL         # row_end < row_offset
@@ -278,6 +278,34 @@ def test_moe_rejects_bad_arguments():
     assert ga(xs=8) == R.RLD_EINVAL
     assert ga(xa=0) == R.RLD_EINVAL
     assert ga(xa=FAKE + 2) == R.RLD_EALIGN
+
+
+def test_grouped_workspace_contract():
+    # k_in = 2048 splits into 4 chunks of 512: fp32 partials per window row, then
+    # 16 bytes of counter per (slot, expert) pair; short or missing workspaces
+    # are refused before any launch
+    need = R.rld_moe_grouped_workspace_bytes(8192, 2048, 32, 4, 128)
+    assert need == 4 * 8192 * 32 * 4 + 16 * 4 * 128
+    mr = R.rld_moe_route(FAKE, FAKE, FAKE, 4, 128, 2048, 768, 32)
+    g = lambda ws, wsb, hi=8192: R.rld_moe_grouped_shrink(  # noqa: E731
+        mr, FAKE, 2048, 1, 4096, FAKE, 128, FAKE, FAKE, 0, hi, FAKE, 8192, ws, wsb, 0)
+    for short in (need - 16, need // 2, 16):
+        assert g(FAKE, short) == R.RLD_ENOSPACE
+    assert g(0, need) == R.RLD_EINVAL
+    assert g(FAKE + 8, need) == R.RLD_EALIGN
+    # a smaller window needs less: the buffer of the largest window serves all
+    assert R.rld_moe_grouped_workspace_bytes(100, 2048, 32, 4, 128) == \
+        4 * 100 * 32 * 4 + 16 * 4 * 128
+    assert g(FAKE, R.rld_moe_grouped_workspace_bytes(100, 2048, 32, 4, 128) - 16, hi=100) == \
+        R.RLD_ENOSPACE
+    assert R.rld_moe_grouped(mr, FAKE, 2048, 1, 4096, FAKE, 128, FAKE, FAKE, 0, 8192, FAKE, 768,
+                             FAKE, 8192, FAKE, need - 16, 0) == R.RLD_ENOSPACE
+    # up to k_in = 1024 the chunks are 256 wide; one chunk needs no workspace
+    assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 4, 128) == \
+        3 * 8192 * 32 * 4 + 16 * 4 * 128
+    assert R.rld_moe_grouped_workspace_bytes(64, 4096, 16, 2, 8) == 8 * 64 * 16 * 4 + 16 * 2 * 8
+    assert R.rld_moe_grouped_workspace_bytes(8192, 256, 32, 4, 128) == 0
+    assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 0, 128) == 0
 
 
 def test_scale_table_values_are_exact_closed_forms():
