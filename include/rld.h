@@ -162,17 +162,15 @@ int rld_gather_grids(uint32_t max_rank, uint32_t n_out, uint32_t n_rows, uint32_
 /* -------------------------------------------------------------- device ---- */
 
 /* Bytes of workspace the BGMV entry points need for a call with these sizes:
- * the fp32 partial sums of the k_in split ([chunks][n][max_rank], none when
- * k_in fits one chunk) plus 32 * max_loras bytes of chunk counters.  Returns
- * 0 if k_in, max_rank or max_loras is 0.
+ * the fp32 partial sums of the k_in split ([chunks][n][max_rank], chunks of
+ * 256 for max_rank <= 16 and 512 above); 0 when k_in fits one chunk (then no
+ * workspace is needed and NULL may be passed) or when k_in, max_rank or
+ * max_loras is 0.
  *
  * Workspace contract (rld_bgmv_shrink and rld_bgmv):
  *   - device memory, 16-byte aligned, of workspace_bytes >= the size above;
- *     one buffer may serve calls of different shapes if it is as large as the
- *     largest of them and the same workspace_bytes is passed every time (the
- *     counters sit at the end of the buffer, keyed by slot);
- *   - zero-filled once before its first use (e.g. hipMemset at allocation);
- *     every call leaves the counters at zero again; do not write them;
+ *     one buffer as large as the largest call serves calls of every shape;
+ *   - its contents need no initialisation and carry nothing between calls;
  *   - calls that share a workspace must not run at the same time (same stream,
  *     or otherwise ordered). */
 size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank,
@@ -180,7 +178,9 @@ size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank,
 
 /* Routed BGMV shrink (apply_lora_bgmv, kernel 1): for every row i < n with an
  * active slot s = seq_slot[i], xa[i, k] = bf16(sum_c x[i*x_row_stride + c] *
- * A_s[k, c]) for k < max_rank; xa rows of base rows are zeros.
+ * A_s[k, c]) for k < max_rank; xa rows of base rows are zeros.  With a k_in
+ * split this is two launches on the stream (the shrink, then the chunk
+ * reduce).
  *   x        device BF16, row i at x + i*x_row_stride, k_in elements read
  *   seq_slot device int32 [n], contents may change between calls
  *   xa       device BF16 [n, max_rank] (row stride max_rank), written
@@ -230,10 +230,14 @@ int rld_moe_gather(const rld_moe_route* route, const void* x, uint32_t x_row_str
  * [max_rank], chunks = ceil(k_in / 256) up to k_in = 1024, ceil(k_in / 512)
  * above) plus 16 bytes of counter per (slot, expert) pair.  Returns 0 when
  * k_in fits one chunk (no workspace needed; NULL may be passed) or when any
- * size is 0.  The workspace contract of rld_bgmv_workspace_bytes applies
- * (16-byte aligned, zero-filled once, counters at the end of the buffer keyed
- * by pair, calls sharing it must not overlap); one buffer sized for the
- * largest window serves every window of a route. */
+ * size is 0.  Workspace contract:
+ *   - device memory, 16-byte aligned, of workspace_bytes >= the size above;
+ *     one buffer as large as the largest call needs serves every window and
+ *     route, if the same workspace_bytes is passed every time (the counters
+ *     sit at the end of the buffer, keyed by pair);
+ *   - zero-filled once before its first use (e.g. hipMemset at allocation);
+ *     every call leaves the counters at zero again; do not write them;
+ *   - calls that share a workspace must not run at the same time. */
 size_t rld_moe_grouped_workspace_bytes(uint32_t window_rows, uint32_t k_in, uint32_t max_rank,
                                        uint32_t max_loras, uint32_t num_experts);
 

@@ -8,35 +8,34 @@
 // per row.  The row list of a slot is rebuilt by every item from seq_slot (no
 // host read), in ascending row order.
 //
-//   shrink item  (slot, k_in chunk, 16 columns of xa).  Each of the four waves
-//                owns every fourth 32-wide K step of the chunk and issues all
-//                of its A fragments at once, then the x fragments of up to 64
-//                rows at once.  The waves'
-//                partial sums are added in wave order.  With several chunks,
-//                each item writes fp32 partials, and the item that finishes
-//                the last chunk of a (slot, 16 columns) pair adds the chunks in
-//                chunk order and writes xa (a counter per pair in the
-//                workspace).  The chunk length depends only on (k_in,
-//                max_rank), so a row's summation order is the same whatever
-//                the batch holds: a batched call is bit-identical to one-row
-//                calls.
+//   shrink item  (slot, k_in chunk, up to 64 columns of xa).  Each of the four
+//                waves owns every fourth 32-wide K step of the chunk and issues
+//                all of its A fragments at once, then the x fragments of up to
+//                64 rows at once.  The waves' partial sums are added in wave
+//                order.  With one chunk the sum is rounded to xa right away;
+//                otherwise it is stored as an fp32 partial [chunk][row][col]
+//                in the workspace, and a second, small kernel adds each row's
+//                chunks in chunk order and writes xa (and the zero rows of base
+//                rows).  The chunk length depends only on (k_in, max_rank), so
+//                a row's summation order is the same whatever the batch holds:
+//                a batched call is bit-identical to one-row calls.
 //   expand item  (slot, 256 output columns).  B_s rows of the tile stay in
 //                registers as MFMA A operands; rows of the slot stream through
 //                as the B operand (16 rows per MFMA).  The base values of a
 //                64-row pass are loaded before its MFMAs, deltas are rounded to
 //                BF16 into LDS, and the fold writes 16-byte coalesced vectors.
 //
-// k-split partials move between blocks with agent-scope (L2-coherent across
-// XCDs) stores and loads, and each block's stores have completed before it
-// raises its group's counter, so no whole-cache writeback or invalidate is
-// needed.  rld_bgmv launches the shrink, then the expand, on the caller's
-// stream.
+// rld_bgmv launches the shrink (and its reduce), then the expand, on the
+// caller's stream.
+#include <type_traits>
+
 #include "rld_device.hpp"
 #include "rld_internal.hpp"
 
 namespace rld {
 
 constexpr int kShrinkMT = 4;     // 16-row M-subtiles per shrink pass
+constexpr int kReduceThreads = 256;
 constexpr int kShrinkSteps = 4;  // K steps per wave per chunk (chunk <= 512 = 4 waves x 4 x 32)
 constexpr int kListCap = 512;    // rows collected per pass over seq_slot
 constexpr int kJT = 256;         // output columns per expand item
@@ -50,27 +49,26 @@ static_assert(kShrinkSteps * 4 * 32 >= 512, "a chunk is at most 512 elements");
 // the global-pointer accessors.
 struct BgmvArgs {
   uint64_t x_, seq_, atab_, btab_, stab_;
-  uint64_t partial_;  // [nch][n][R] fp32 (k split only), at the start of the workspace
-  uint64_t book_;     // end of the workspace: slot s's 8 chunk counters (one per
-                      // 16-column group of xa) are the 8 words at book - 8 (s + 1)
+  uint64_t partial_;  // [nch][n][R] fp32 (k split only): the workspace
   uint64_t xa_, out_;
-  uint32_t xs, n, max_loras, k_in, n_out, R, kc, nch, ntr, os;
+  uint32_t xs, n, max_loras, k_in, n_out, R, kc, nch;
+  uint32_t ncg;  // shrink column groups of 16*NT xa columns
+  uint32_t os;
   __device__ const RLD_GLOBAL uint16_t* x() const { return gp<const uint16_t>(x_); }
   __device__ const RLD_GLOBAL int32_t* seq_slot() const { return gp<const int32_t>(seq_); }
   __device__ const RLD_GLOBAL uint64_t* a_table() const { return gp<const uint64_t>(atab_); }
   __device__ const RLD_GLOBAL uint64_t* b_table() const { return gp<const uint64_t>(btab_); }
   __device__ const RLD_GLOBAL float* scale_table() const { return gp<const float>(stab_); }
   __device__ RLD_GLOBAL float* partial() const { return gp<float>(partial_); }
-  __device__ RLD_GLOBAL uint32_t* book() const { return gp<uint32_t>(book_); }
   __device__ RLD_GLOBAL uint16_t* xa() const { return gp<uint16_t>(xa_); }
   __device__ RLD_GLOBAL uint16_t* out() const { return gp<uint16_t>(out_); }
 };
 
+template <int NT>
 struct ShrinkSmem {
   int rows[kListCap];
   int wcount[4];
-  floatx4 red[4][kShrinkMT][kWave];
-  int flag;
+  floatx4 red[4][kShrinkMT * NT][kWave];
 };
 
 struct ExpandSmem {
@@ -78,10 +76,6 @@ struct ExpandSmem {
   int wcount[4];
   __attribute__((aligned(16))) uint16_t dl[kExpRows * kDlStride];
 };
-
-__device__ __forceinline__ RLD_GLOBAL uint32_t* slot_counters(const BgmvArgs& a, int s) {
-  return a.book() - 8 * ((size_t)s + 1);
-}
 
 __device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
   if (s < 0 || (uint32_t)s >= a.max_loras) return false;
@@ -131,12 +125,14 @@ __device__ __forceinline__ SlotEntry slot_entry(const BgmvArgs& a, int s) {
   return e;
 }
 
-// Shrink item w (slot-major over (slot, chunk, 16 columns)).
-__device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, ShrinkSmem& sm) {
-  const uint32_t n = a.n, R = a.R, nchunks = a.nch, ntr = a.ntr;
-  const uint32_t rt = w % ntr;
-  const uint32_t c = (w / ntr) % nchunks;
-  const int s = (int)(w / (ntr * nchunks));
+// Shrink item w (slot-major over (slot, chunk, column group)); the group
+// covers xa columns [16*NT*cg, 16*NT*(cg+1)).
+template <int NT>
+__device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, ShrinkSmem<NT>& sm) {
+  const uint32_t n = a.n, R = a.R, nchunks = a.nch, ncg = a.ncg;
+  const uint32_t cg = w % ncg;
+  const uint32_t c = (w / ncg) % nchunks;
+  const int s = (int)(w / (ncg * nchunks));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
@@ -144,9 +140,10 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, Shrin
   const int key0 = first_key(a.seq_slot(), n);
   const SlotEntry ent = slot_entry(a, s);
 
-  // The last item (a slot of the last index, usually cold) also writes the
-  // zero xa rows of base rows.
-  if (w == total - 1) {
+  // Without a k split, the last item (a slot of the last index, usually cold)
+  // also writes the zero xa rows of base rows (the reduce kernel does it
+  // otherwise).
+  if (nchunks == 1 && w == total - 1) {
     const uint32_t r8 = R / 8;
     for (uint32_t e = threadIdx.x; e < n * r8; e += 256) {
       const uint32_t row = e / r8;
@@ -159,86 +156,97 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, Shrin
   const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ent.a);
   const int lg = lane >> 4;
   const int cl = lane & 15;
-  const uint32_t col = rt * 16 + cl;  // xa column = A_s row served by this lane
-  const bool col_ok = col < R;
-  const RLD_GLOBAL uint16_t* Arow = A + (size_t)(col_ok ? col : 0) * a.k_in;
+  const uint32_t col0 = cg * 16u * NT;
   const uint32_t kb = c * a.kc;
   const uint32_t ke = min(kb + a.kc, a.k_in);
   const uint32_t nsteps = (ke - kb + 31) / 32;
 
-  // Every A fragment of this wave's K steps (wave, wave + 4, ...) is issued
-  // before the row scan, which needs only the seq_slot entries already in
-  // flight; the x loads the scan enables then overlap the A tile's arrival.
-  // The loads are unconditional (out-of-range lanes read the chunk's first
-  // element of row 0 and drop it) so they stay here in the prologue.
-  uint4 bop[kShrinkSteps];
+  // K steps of this wave: wave, wave + 4, ... of the chunk
   uint32_t kof[kShrinkSteps];
   bool kok[kShrinkSteps];
 #pragma unroll
   for (int i = 0; i < kShrinkSteps; ++i) {
     const uint32_t st = wave + 4 * i;
     kof[i] = kb + st * 32 + lg * 8;
-    kok[i] = col_ok && st < nsteps && kof[i] < ke;
-    bop[i] = load16(kok[i] ? Arow + kof[i] : A + kb);
+    kok[i] = st < nsteps && kof[i] < ke;
   }
-  issue_point();
-#pragma unroll
-  for (int i = 0; i < kShrinkSteps; ++i)
-    if (!kok[i]) bop[i] = zero16();
 
-  uint32_t pos = 0;
-  int first_row = -1;
-  int scans = 0, last_cnt = 0;
-  while (pos < n) {
-    const int cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
-    ++scans;
-    last_cnt = cnt;
-    if (first_row < 0 && cnt > 0) first_row = sm.rows[0];
-    for (int b0 = 0; b0 < cnt; b0 += kShrinkMT * 16) {
-      const int nb = min(cnt - b0, kShrinkMT * 16);
-      const int nmt = (nb + 15) >> 4;
-      floatx4 acc[kShrinkMT];
+  // Rows b0 .. b0 + 16*QT - 1 of the slot's list: the A fragments of this
+  // wave's K steps for the NT column tiles, then the x fragments of all QT
+  // subtiles, in one round of loads (unconditional A loads: out-of-range
+  // lanes read the chunk's first element of row 0).  The slot's table entry
+  // arrived with its seq_slot entries, so nothing is gained by issuing A
+  // before the row scan.  Subtiles go through the wave reduce kShrinkMT at a
+  // time.
+  auto batch = [&](auto qt_tag, int b0, int cnt) {
+    constexpr int QT = decltype(qt_tag)::value;
+    const int nb = min(cnt - b0, QT * 16);
+    const int nmt = (nb + 15) >> 4;
+    uint4 bop[NT][kShrinkSteps];
 #pragma unroll
-      for (int q = 0; q < kShrinkMT; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-      // x fragments of every subtile of the pass, all in flight together
-      uint4 xf[kShrinkMT][kShrinkSteps];
+    for (int j = 0; j < NT; ++j) {
+      const uint32_t col = col0 + 16u * j + cl;
+      const RLD_GLOBAL uint16_t* Arow = A + (size_t)(col < R ? col : 0) * a.k_in;
 #pragma unroll
-      for (int q = 0; q < kShrinkMT; ++q) {
-        const int li = q * 16 + cl;
-        const bool ok = li < nb;
-        const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)(ok ? sm.rows[b0 + li] : 0) * a.xs;
+      for (int i = 0; i < kShrinkSteps; ++i)
+        bop[j][i] = load16((col < R && kok[i]) ? Arow + kof[i] : A + kb);
+    }
+    uint4 xf[QT][kShrinkSteps];
 #pragma unroll
-        for (int i = 0; i < kShrinkSteps; ++i)
-          xf[q][i] = (q < nmt && ok && kof[i] < ke) ? load16(xr + kof[i]) : zero16();
-      }
+    for (int q = 0; q < QT; ++q) {
+      const int li = q * 16 + cl;
+      const bool ok = li < nb;
+      const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)(ok ? sm.rows[b0 + li] : 0) * a.xs;
 #pragma unroll
-      for (int q = 0; q < kShrinkMT; ++q) {
+      for (int i = 0; i < kShrinkSteps; ++i)
+        xf[q][i] = (q < nmt && ok && kok[i]) ? load16(xr + kof[i]) : zero16();
+    }
+    issue_point();
+    // k past the chunk contributes nothing; columns past max_rank are
+    // computed from clamped reads and never stored
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < kShrinkSteps; ++i)
+        if (!kok[i]) bop[j][i] = zero16();
+#pragma unroll
+    for (int h = 0; h < QT / kShrinkMT; ++h) {
+      if (h * kShrinkMT >= nmt) break;
+#pragma unroll
+      for (int qq = 0; qq < kShrinkMT; ++qq) {
+        const int q = h * kShrinkMT + qq;
         if (q < nmt) {
 #pragma unroll
-          for (int i = 0; i < kShrinkSteps; ++i)
-            acc[q] = mfma_bf16_16x16x32(xf[q][i], bop[i], acc[q]);
+          for (int j = 0; j < NT; ++j) {
+            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < kShrinkSteps; ++i)
+              acc = mfma_bf16_16x16x32(xf[q][i], bop[j][i], acc);
+            sm.red[wave][qq * NT + j][lane] = acc;
+          }
         }
       }
-#pragma unroll
-      for (int q = 0; q < kShrinkMT; ++q)
-        if (q < nmt) sm.red[wave][q][lane] = acc[q];
       __syncthreads();
-      for (int q = wave; q < nmt; q += 4) {
-        floatx4 sum = sm.red[0][q][lane];
-        sum += sm.red[1][q][lane];
-        sum += sm.red[2][q][lane];
-        sum += sm.red[3][q][lane];
-        if (col_ok) {
+      const int qq = wave;  // this wave adds subtile h*kShrinkMT + wave
+      const int q = h * kShrinkMT + qq;
+      if (q < nmt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int li = q * 16 + 4 * lg + i;
-            if (li < nb) {
-              const uint32_t row = (uint32_t)sm.rows[b0 + li];
-              if (nchunks == 1) {
-                a.xa()[(size_t)row * R + col] = (uint16_t)f32_to_bf16(sum[i]);
-              } else {  // agent-scope store: written through to where every XCD reads it
-                __hip_atomic_store(a.partial() + ((size_t)c * n + row) * R + col, sum[i],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int j = 0; j < NT; ++j) {
+          const uint32_t col = col0 + 16u * j + cl;
+          floatx4 sum = sm.red[0][qq * NT + j][lane];
+          sum += sm.red[1][qq * NT + j][lane];
+          sum += sm.red[2][qq * NT + j][lane];
+          sum += sm.red[3][qq * NT + j][lane];
+          if (col < R) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int li = q * 16 + 4 * lg + i;
+              if (li < nb) {
+                const uint32_t row = (uint32_t)sm.rows[b0 + li];
+                if (nchunks == 1)
+                  a.xa()[(size_t)row * R + col] = (uint16_t)f32_to_bf16(sum[i]);
+                else
+                  a.partial()[((size_t)c * n + row) * R + col] = sum[i];
               }
             }
           }
@@ -246,63 +254,30 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, Shrin
       }
       __syncthreads();
     }
+  };
+  using Q4 = std::integral_constant<int, kShrinkMT>;
+  using Q8 = std::integral_constant<int, 2 * kShrinkMT>;
+
+  // The usual case, straight-line: at most 256 rows (their seq_slot entries
+  // are key0, so the scan issues no load that would wait behind the A tile)
+  // and at most 128 of them on this slot.
+  if (n <= 256) {
+    const int cnt = append_hits(key0 == s, threadIdx.x, sm.rows, 0, sm.wcount);
+    if (cnt <= kShrinkMT * 16) {
+      if (cnt > 0) batch(Q4{}, 0, cnt);
+      return;
+    }
+    if (cnt <= 2 * kShrinkMT * 16) {
+      batch(Q8{}, 0, cnt);
+      return;
+    }
   }
-  if (first_row < 0 || nchunks == 1) return;
-
-  // k split: the item that completes the last chunk of its (slot, 16 xa
-  // columns) adds the chunks in chunk order and writes xa.  The group's
-  // counter is left at zero.
-  RLD_GLOBAL uint32_t* ctr = slot_counters(a, s) + rt;
-  if (block_signal(ctr, &sm.flag) != nchunks - 1) return;
-  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  const int rl = threadIdx.x >> 4;  // 16 rows x 16 columns per step
-  const uint32_t rcol = rt * 16 + (threadIdx.x & 15);
-  uint32_t rpos = 0;
-  for (int batch = 0;; ++batch) {
-    int cnt;
-    if (scans == 1) {  // rows[] still holds the slot's whole list
-      if (batch > 0) break;
-      cnt = last_cnt;
-    } else {
-      if (rpos >= n) break;
-      cnt = collect_slot_rows(a.seq_slot(), n, &rpos, s, sm.rows, sm.wcount, key0);
-    }
-    if (rcol < R) {
-      const size_t cstride = (size_t)n * R;
-      // two rows per thread per step, 16 chunks of each in flight
-      for (int li = rl; li < cnt; li += 32) {
-        const bool two = li + 16 < cnt;
-        const uint32_t r0 = (uint32_t)sm.rows[li];
-        const uint32_t r1 = two ? (uint32_t)sm.rows[li + 16] : r0;
-        RLD_GLOBAL float* p0 = a.partial() + (size_t)r0 * R + rcol;
-        RLD_GLOBAL float* p1 = a.partial() + (size_t)r1 * R + rcol;
-        float s0 = 0.f, s1 = 0.f;
-        for (uint32_t c0 = 0; c0 < nchunks; c0 += 16) {
-          float v0[16], v1[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const bool ok = c0 + j < nchunks;
-            v0[j] = ok ? __hip_atomic_load(p0 + (c0 + j) * cstride, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT)
-                       : 0.f;
-            v1[j] = (ok && two) ? __hip_atomic_load(p1 + (c0 + j) * cstride, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT)
-                                : 0.f;
-          }
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            if (c0 + j < nchunks) {  // chunk order
-              s0 = (c0 + j == 0) ? v0[j] : s0 + v0[j];
-              s1 = (c0 + j == 0) ? v1[j] : s1 + v1[j];
-            }
-          }
-        }
-        a.xa()[(size_t)r0 * R + rcol] = (uint16_t)f32_to_bf16(s0);
-        if (two) a.xa()[(size_t)r1 * R + rcol] = (uint16_t)f32_to_bf16(s1);
-      }
-    }
-    __syncthreads();
+  uint32_t pos = 0;
+  int cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
+  for (;;) {
+    for (int b0 = 0; b0 < cnt; b0 += kShrinkMT * 16) batch(Q4{}, b0, cnt);
+    if (pos >= n) break;
+    cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
   }
 }
 
@@ -399,12 +374,42 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
   }
 }
 
+template <int NT>
 __global__ __launch_bounds__(256) void bgmv_shrink_kernel(BgmvArgs a, uint32_t total) {
-  __shared__ ShrinkSmem sm;
-  // the ntr items of one (slot, chunk) share an XCD, and so the x rows in its L2
-  const uint32_t w = xcd_group_item(a.ntr);
+  __shared__ ShrinkSmem<NT> sm;
+  // the column groups of one (slot, chunk) share an XCD, and so the x rows in
+  // its L2
+  const uint32_t w = xcd_group_item(a.ncg);
   if (w >= total) return;
-  shrink_item(a, w, total, sm);
+  shrink_item<NT>(a, w, total, sm);
+}
+
+// k split: xa[row, 4 columns] = bf16(sum over chunks, in chunk order, of the
+// partials); zero rows for base rows.  One thread per (row, 4 columns); the
+// chunk loads of a thread go out 8 at a time, ahead of their adds.
+__global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a) {
+  const uint32_t q4 = a.R / 4;
+  const uint32_t t = blockIdx.x * kReduceThreads + threadIdx.x;
+  if (t >= a.n * q4) return;
+  const uint32_t row = t / q4;
+  const uint32_t col = (t % q4) * 4;
+  const int s = a.seq_slot()[row];
+  const RLD_GLOBAL floatx4* p =
+      reinterpret_cast<const RLD_GLOBAL floatx4*>(a.partial() + (size_t)row * a.R + col);
+  const size_t cstride = (size_t)a.n * a.R / 4;  // floatx4 per chunk
+  floatx4 sum = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (uint32_t c0 = 0; c0 < a.nch; c0 += 8) {
+    floatx4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = p[(c0 + j < a.nch ? c0 + j : c0) * cstride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < a.nch) sum = (c0 + j == 0) ? v[j] : sum + v[j];
+  }
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 o = {0u, 0u};
+  if (slot_active(a, s)) o = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+  *reinterpret_cast<RLD_GLOBAL u32x2*>(a.xa() + (size_t)row * a.R + col) = o;
 }
 
 template <int NKS>
@@ -413,12 +418,7 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(BgmvArgs a) {
   expand_item<NKS>(a, (int)blockIdx.y, blockIdx.x * kJT, sm);
 }
 
-// Workspace: fp32 partials [nch][n][R] from the start (k split only), and at
-// the end of the caller's buffer (its size rounded down to 16 bytes) 8 chunk
-// counters per slot.  Keying the counters to the end of the buffer and to
-// slots keeps them in one place for every call that shares the buffer,
-// whatever their shapes.  They must be zero before the first call and are zero
-// after every call.
+// Workspace: fp32 partials [nch][n][R] (k split only).
 static size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 static size_t partial_bytes(uint32_t n, uint32_t k_in, uint32_t R) {
@@ -426,17 +426,16 @@ static size_t partial_bytes(uint32_t n, uint32_t k_in, uint32_t R) {
   return nch > 1 ? round16((size_t)nch * n * R * sizeof(float)) : 0;
 }
 
-static size_t book_bytes(uint32_t max_loras) { return (size_t)max_loras * 32; }
-
 static int make_args(const rld_route* route, const void* x, uint32_t x_row_stride,
                      const int32_t* seq_slot, uint32_t n, void* xa, void* workspace,
                      size_t workspace_bytes, void* base_out, uint32_t out_row_stride,
                      BgmvArgs* a) {
   const uint32_t R = route->max_rank, k_in = route->k_in;
-  const size_t end = workspace_bytes & ~(size_t)15;
-  if (!workspace || end < partial_bytes(n, k_in, R) + book_bytes(route->max_loras))
-    return RLD_ENOSPACE;
-  if (!aligned16(workspace)) return RLD_EALIGN;
+  const size_t need = partial_bytes(n, k_in, R);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return RLD_ENOSPACE;
+    if (!aligned16(workspace)) return RLD_EALIGN;
+  }
   char* ws = static_cast<char*>(workspace);
   a->x_ = reinterpret_cast<uint64_t>(x);
   a->seq_ = reinterpret_cast<uint64_t>(seq_slot);
@@ -444,7 +443,6 @@ static int make_args(const rld_route* route, const void* x, uint32_t x_row_strid
   a->btab_ = reinterpret_cast<uint64_t>(route->b_table);
   a->stab_ = reinterpret_cast<uint64_t>(route->scale_table);
   a->partial_ = reinterpret_cast<uint64_t>(ws);
-  a->book_ = reinterpret_cast<uint64_t>(ws + end);
   a->xa_ = reinterpret_cast<uint64_t>(xa);
   a->out_ = reinterpret_cast<uint64_t>(base_out);
   a->xs = x_row_stride;
@@ -455,7 +453,7 @@ static int make_args(const rld_route* route, const void* x, uint32_t x_row_strid
   a->R = R;
   a->kc = bgmv_chunk(k_in, R);
   a->nch = div_ceil(k_in, a->kc);
-  a->ntr = div_ceil(R, 16);
+  a->ncg = div_ceil(R, 16u * bgmv_nt(R));
   a->os = out_row_stride;
   return RLD_OK;
 }
@@ -478,7 +476,7 @@ using namespace rld;
 extern "C" size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank,
                                            uint32_t max_loras) {
   if (k_in == 0 || max_rank == 0 || max_loras == 0) return 0;
-  return partial_bytes(n, k_in, max_rank) + book_bytes(max_loras);
+  return partial_bytes(n, k_in, max_rank);
 }
 
 extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x_row_stride,
@@ -495,10 +493,21 @@ extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x
   if ((st = make_args(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
                       nullptr, 0, &a)))
     return st;
-  const uint32_t total = route->max_loras * a.nch * a.ntr;
-  hipLaunchKernelGGL(bgmv_shrink_kernel, dim3(xcd_group_grid(total, a.ntr)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), a, total);
-  return launch_status();
+  const uint32_t total = route->max_loras * a.nch * a.ncg;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid(xcd_group_grid(total, a.ncg));
+  switch (bgmv_nt(a.R)) {
+    case 1: hipLaunchKernelGGL(bgmv_shrink_kernel<1>, grid, dim3(256), 0, hs, a, total); break;
+    case 2: hipLaunchKernelGGL(bgmv_shrink_kernel<2>, grid, dim3(256), 0, hs, a, total); break;
+    default: hipLaunchKernelGGL(bgmv_shrink_kernel<4>, grid, dim3(256), 0, hs, a, total); break;
+  }
+  if ((st = launch_status())) return st;
+  if (a.nch > 1) {
+    hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(n * (a.R / 4), kReduceThreads)),
+                       dim3(kReduceThreads), 0, hs, a);
+    return launch_status();
+  }
+  return RLD_OK;
 }
 
 extern "C" int rld_bgmv_expand_fold(const rld_route* route, const void* xa,
@@ -523,7 +532,6 @@ extern "C" int rld_bgmv_expand_fold(const rld_route* route, const void* xa,
   a.k_in = route->k_in;
   a.n_out = route->n_out;
   a.R = route->max_rank;
-  a.ntr = div_ceil(a.R, 16);
   a.os = out_row_stride;
   hipLaunchKernelGGL(pick_expand(a.R), dim3(div_ceil(route->n_out, kJT), route->max_loras),
                      dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);

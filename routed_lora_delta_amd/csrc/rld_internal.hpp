@@ -58,6 +58,12 @@ inline uint32_t bgmv_chunk(uint32_t k_in, uint32_t max_rank) {
   return k_in <= kc ? k_in : kc;
 }
 
+// 16-column MFMA tiles of xa per BGMV shrink item (1, 2 or 4).
+inline uint32_t bgmv_nt(uint32_t max_rank) {
+  const uint32_t t = div_ceil(max_rank, 16u);
+  return t <= 1u ? 1u : (t <= 2u ? 2u : 4u);
+}
+
 // Grid of xcd_group_item: 8 XCDs x whole groups, covering `total` items.
 inline uint32_t xcd_group_grid(uint32_t total, uint32_t group) {
   return 8u * group * div_ceil(div_ceil(total, group), 8u);

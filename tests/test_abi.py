@@ -228,8 +228,8 @@ def test_bgmv_workspace_contract():
     # one is refused before any launch, by every entry point that takes one
     rt = _route(k_in=12288, n_out=4096, max_rank=64, max_loras=32)
     need = R.rld_bgmv_workspace_bytes(256, 12288, 64, 32)
-    # 24 chunks of 512 fp32 partials, then 8 chunk counters per slot
-    assert need == 24 * 256 * 64 * 4 + 32 * 32
+    # 24 chunks of 512: fp32 partials per row and xa column
+    assert need == 24 * 256 * 64 * 4
     for short in (need - 32, need // 2, 16, 0):
         assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, FAKE, short, 0) == \
             R.RLD_ENOSPACE
@@ -238,8 +238,8 @@ def test_bgmv_workspace_contract():
     assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, 0, need, 0) == R.RLD_ENOSPACE
     assert R.rld_bgmv_shrink(rt, FAKE, 12288, FAKE, 256, FAKE, FAKE + 8, need, 0) == \
         R.RLD_EALIGN
-    # a single chunk needs no partials, only the counters
-    assert R.rld_bgmv_workspace_bytes(4, 256, 64, 2) == 2 * 32
+    # a single chunk needs no workspace at all
+    assert R.rld_bgmv_workspace_bytes(4, 256, 64, 2) == 0
     assert R.rld_bgmv_workspace_bytes(256, 0, 64, 32) == 0
     assert R.rld_bgmv_workspace_bytes(256, 4096, 64, 0) == 0
 

@@ -127,10 +127,9 @@ def test_bgmv_batched_equals_single_rows():
 
 
 def test_bgmv_graph_replays():
-    """rld_bgmv captured in a HIP graph (k split over 4 chunks): every replay,
-    with eager work and synchronisations between replays, gives the eager
-    call's bits, and the chunk counters at the end of the workspace are back at
-    zero after each."""
+    """rld_bgmv captured in a HIP graph (k split over 8 chunks: shrink, chunk
+    reduce and expand): every replay, with eager work and synchronisations
+    between replays, gives the eager call's bits."""
     dev = require_gpu()
     wl = W.bgmv_custom(22, 256, 4096, 2048, 64, 16, (16, 64), base_frac=0.05, zipf=1.1)
     say("case: graph replays")
@@ -144,15 +143,12 @@ def test_bgmv_graph_replays():
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(g, stream=s):
         run.run_call(0, stream=s)
-    end = run.ws_bytes // 16 * 16
     for rep in range(4):
         run.bufs["out"].t.copy_(pristine)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(run.outputs()["out"], want), f"replay {rep}"
-        counters = run.ws.view(torch.int32).cpu().numpy()[(end - 32 * 16) // 4: end // 4]
-        assert np.all(counters == 0), f"replay {rep}: counters {np.flatnonzero(counters)[:8]}"
         _ = torch.ones(1 << 20, device=dev).sum().item()  # eager work between replays
 
 
@@ -210,7 +206,7 @@ def test_bgmv_shared_workspace_second_pass():
     4 chunks, down in 12), used for a second pass after the first: the second
     pass (outputs restored to the base values first, now through the separate
     shrink and expand entry points) still meets the oracle, so no call's scratch
-    disturbs another's counters."""
+    disturbs another's."""
     dev = require_gpu()
     wl = W.bgmv_ffn_decode()
     say(f"case: shared workspace, second pass, {wl.name}")
@@ -332,6 +328,68 @@ def test_moe_grouped_edge_windows():
     assert_out_close(run2.base.body(), out_o2, "rows outside spans")
     tail = slice((wl.te - 40) * p.n_out, wl.te * p.n_out)
     assert np.array_equal(run2.base.body()[tail], p.base.ravel()[tail])
+
+
+@pytest.mark.parametrize("max_loras", [1, 2])
+def test_moe_grouped_long_pairs(max_loras):
+    """Pairs with hundreds of rows in one window: 64-row batches, and with one
+    slot more than one scan segment (the chunk reduce rescans the span), in
+    one full window and in windows of 700 rows."""
+    dev = require_gpu()
+    wl = W.moe_grouped(9, num_tokens=1200, top_k=2, num_experts=4, hidden=520, inter=264,
+                       max_loras=max_loras, n_adapted=4, ranks=(8, 16, 32), max_rank=32,
+                       cap=2400, projections=("down", "gate"))
+    ra = None if max_loras == 1 else "wl"
+    for p in wl.projections:
+        say(f"case: grouped long pairs {p.name} max_loras={max_loras}")
+        full = GroupedRun(wl, p, dev, cap=wl.te, row_adapter=ra)
+        xa_full = full.run([(0, wl.te)])[0]
+        xa_o, out_o = oracle_grouped_window(wl, p, 0, wl.te, p.base.ravel().copy(), ra)
+        assert_xa_close(xa_full, xa_o, f"long pairs xa {p.name}",
+                        abs_sums_grouped(wl, p, 0, wl.te, ra),
+                        shrink_depth("grouped", p.k_in, wl.max_rank))
+        assert_out_close(full.base.body(), out_o, f"long pairs out {p.name}")
+        part = GroupedRun(wl, p, dev, cap=700, row_adapter=ra)
+        xas = part.run(O.grouped_down_windows(wl.te, 700))
+        assert np.array_equal(np.concatenate(xas), xa_full)
+        assert np.array_equal(part.base.body(), full.base.body())
+
+
+def test_moe_grouped_graph_replays():
+    """Every window of a projection (k split over 3 chunks) captured in one HIP
+    graph: each replay, with eager work and synchronisations between, gives
+    the eager calls' bits, and the per-pair counters at the end of the
+    workspace are back at zero after each."""
+    dev = require_gpu()
+    wl = _small_grouped(projections=("gate",))
+    p = wl.projections[0]
+    say("case: grouped graph replays")
+    eager = GroupedRun(wl, p, dev)
+    eager.run(keep_xa=False)
+    want = eager.base.body()
+    run = GroupedRun(wl, p, dev)
+    pristine = run.base.t.clone()
+    wins = O.grouped_down_windows(wl.te, wl.cap)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        for lo, hi in wins:
+            R.check(R.rld_moe_grouped(run.route.route, run.x, p.k_in, p.x_gather, wl.num_tokens,
+                                      run.off, wl.num_experts, run.stid, run.rad, lo, hi,
+                                      run.base.ptr(), p.n_out, run.xa, run.cap, run.ws,
+                                      run.ws_bytes, s), "captured rld_moe_grouped")
+    end = run.ws_bytes // 16 * 16
+    npairs = wl.max_loras * wl.num_experts
+    for rep in range(4):
+        run.base.t.copy_(pristine)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(run.base.body(), want), f"replay {rep}"
+        counters = run.ws.view(torch.int32).cpu().numpy()[(end - 16 * npairs) // 4: end // 4]
+        assert np.all(counters == 0), f"replay {rep}: counters {np.flatnonzero(counters)[:8]}"
+        _ = torch.ones(1 << 20, device=dev).sum().item()  # eager work between replays
 
 
 def test_determinism_repeat_runs():
