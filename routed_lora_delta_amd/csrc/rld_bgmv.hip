@@ -19,11 +19,12 @@
 //                rows).  The chunk length depends only on (k_in, max_rank), so
 //                a row's summation order is the same whatever the batch holds:
 //                a batched call is bit-identical to one-row calls.
-//   expand item  (slot, 256 output columns).  B_s rows of the tile stay in
-//                registers as MFMA A operands; rows of the slot stream through
-//                as the B operand (16 rows per MFMA).  The base values of a
-//                64-row pass are loaded before its MFMAs, deltas are rounded to
-//                BF16 into LDS, and the fold writes 16-byte coalesced vectors.
+//   expand item  (slot, 256 output columns).  B_s rows of the tile are
+//                the MFMA A operands; rows of the slot stream through as the B
+//                operand (16 rows per MFMA).  The B tile, the base values and
+//                the xa rows of a 64-row pass go out in one round of loads,
+//                deltas are rounded to BF16 into LDS, and the fold writes
+//                16-byte coalesced vectors.
 //
 // rld_bgmv launches the shrink (and its reduce), then the expand, on the
 // caller's stream.
@@ -38,10 +39,7 @@ constexpr int kShrinkMT = 4;     // 16-row M-subtiles per shrink pass
 constexpr int kReduceThreads = 256;
 constexpr int kShrinkSteps = 4;  // K steps per wave per chunk (chunk <= 512 = 4 waves x 4 x 32)
 constexpr int kListCap = 512;    // rows collected per pass over seq_slot
-constexpr int kJT = 256;         // output columns per expand item
 constexpr int kExpRows = 64;     // rows per fold pass of the expand
-constexpr int kDlStride = kJT + 8;
-constexpr int kFoldVecs = kExpRows * (kJT / 8) / 256;  // base vectors per thread per pass
 
 static_assert(kShrinkSteps * 4 * 32 >= 512, "a chunk is at most 512 elements");
 
@@ -71,10 +69,14 @@ struct ShrinkSmem {
   floatx4 red[4][kShrinkMT * NT][kWave];
 };
 
+// Expand item of 64*MT output columns (16*MT per wave).
+template <int MT>
 struct ExpandSmem {
+  static constexpr int kCols = 64 * MT;
+  static constexpr int kStride = kCols + 8;  // LDS row stride of the delta tile
   int rows[kListCap];
   int wcount[4];
-  __attribute__((aligned(16))) uint16_t dl[kExpRows * kDlStride];
+  __attribute__((aligned(16))) uint16_t dl[kExpRows * kStride];
 };
 
 __device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
@@ -281,9 +283,14 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, Shrin
   }
 }
 
-// Expand item (slot s, 256 output columns from j0).  NKS = ceil(max_rank/32).
-template <int NKS>
-__device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& sm) {
+// Expand item (slot s, 64*MT output columns from j0).  NKS = ceil(max_rank/32).
+template <int NKS, int MT>
+__device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem<MT>& sm) {
+  constexpr int kCols = ExpandSmem<MT>::kCols;
+  constexpr int kStride = ExpandSmem<MT>::kStride;
+  constexpr int kRowVecs = kCols / 8;            // 16-byte vectors per row of the tile
+  constexpr int kRowsPerPass = 256 / kRowVecs;   // rows the block folds per pass
+  constexpr int kFoldVecs = kExpRows / kRowsPerPass;
   const uint32_t n = a.n, R = a.R, n_out = a.n_out, os = a.os;
   // seq_slot entries and the slot's table entries first (one round trip)
   const int key0 = first_key(a.seq_slot(), n);
@@ -295,82 +302,99 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem& s
   const int wave = threadIdx.x >> 6;
   const int lg = lane >> 4;
   const int cl = lane & 15;
-
-  // B_s rows of this wave's 64 columns, as MFMA A operands for every K step,
-  // issued before the row scan (unconditional loads: out-of-range lanes read
-  // B's first element and drop it).
-  uint4 aop[4][NKS];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint32_t col = j0 + wave * 64 + m * 16 + cl;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const uint32_t k = ks * 32 + lg * 8;
-      const bool ok = col < n_out && k < R;
-      aop[m][ks] = load16(ok ? B + (size_t)col * R + k : B);
-      if (!ok) aop[m][ks] = zero16();
-    }
-  }
-  issue_point();
-
-  // fold mapping: vector i of a thread is row (tid / 32) + 8 i, columns c8 .. c8+7
-  const int frow = threadIdx.x >> 5;
-  const int c8 = (threadIdx.x & 31) * 8;
+  // fold mapping: vector i of a thread is row frow + kRowsPerPass*i, columns c8 .. c8+7
+  const int frow = threadIdx.x / kRowVecs;
+  const int c8 = (threadIdx.x % kRowVecs) * 8;
   const bool fcol_ok = j0 + c8 < n_out;
 
+  // rows b0 .. b0+63 of the slot's list
+  auto batch = [&](int b0, int cnt) {
+    const int nb = min(cnt - b0, kExpRows);
+    // One round of loads: the B_s rows of this wave's 16*MT columns as MFMA A
+    // operands (unconditional: out-of-range lanes read B's first element),
+    // the batch's base values and its xa rows.  The slot's table entry came
+    // with its seq_slot entries, so B gains nothing by going out before the
+    // row scan.
+    uint4 aop[MT][NKS];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint32_t col = j0 + wave * 16 * MT + m * 16 + cl;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint32_t k = ks * 32 + lg * 8;
+        aop[m][ks] = load16((col < n_out && k < R) ? B + (size_t)col * R + k : B);
+      }
+    }
+    uint4 bv[kFoldVecs];
+#pragma unroll
+    for (int i = 0; i < kFoldVecs; ++i) {
+      const int rl = frow + kRowsPerPass * i;
+      bv[i] = (rl < nb && fcol_ok) ? load16(a.out() + (size_t)sm.rows[b0 + rl] * os + j0 + c8)
+                                   : zero16();
+    }
+    uint4 bop[4][NKS];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int li = p * 16 + cl;
+      const bool ok = li < nb;
+      const RLD_GLOBAL uint16_t* xr = a.xa() + (size_t)(ok ? sm.rows[b0 + li] : 0) * R;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint32_t k = ks * 32 + lg * 8;
+        bop[p][ks] = (p * 16 < nb && ok && k < R) ? load16(xr + k) : zero16();
+      }
+    }
+    issue_point();
+    // k past max_rank contributes nothing (xa operand already zero there);
+    // columns past n_out are computed from clamped reads and never stored
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        if (ks * 32 + lg * 8 >= (int)R) aop[m][ks] = zero16();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (p * 16 < nb) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) acc = mfma_bf16_16x16x32(aop[m][ks], bop[p][ks], acc);
+          // lane holds delta[row p*16+cl][cols m*16 + 4*lg .. +3] of this wave's slice
+          const uint32_t d01 = pack_bf16x2(acc[0], acc[1]);
+          const uint32_t d23 = pack_bf16x2(acc[2], acc[3]);
+          *reinterpret_cast<uint2*>(
+              &sm.dl[(p * 16 + cl) * kStride + wave * 16 * MT + m * 16 + 4 * lg]) =
+              make_uint2(d01, d23);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kFoldVecs; ++i) {
+      const int rl = frow + kRowsPerPass * i;
+      if (rl < nb && fcol_ok) {
+        const uint4 dv = *reinterpret_cast<const uint4*>(&sm.dl[rl * kStride + c8]);
+        store16(a.out() + (size_t)sm.rows[b0 + rl] * os + j0 + c8, fold8(bv[i], dv, scale));
+      }
+    }
+    __syncthreads();
+  };
+
+  // The usual case, straight-line: at most 256 rows (their seq_slot entries
+  // are key0) and at most 128 of them on this slot.
+  if (n <= 256) {
+    const int cnt = append_hits(key0 == s, threadIdx.x, sm.rows, 0, sm.wcount);
+    if (cnt <= 2 * kExpRows) {
+      if (cnt > 0) batch(0, cnt);
+      if (cnt > kExpRows) batch(kExpRows, cnt);
+      return;
+    }
+  }
   uint32_t pos = 0;
   while (pos < n) {
     const int cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
-    for (int b0 = 0; b0 < cnt; b0 += kExpRows) {
-      const int nb = min(cnt - b0, kExpRows);
-      // base values of the pass, issued before the MFMAs
-      uint4 bv[kFoldVecs];
-#pragma unroll
-      for (int i = 0; i < kFoldVecs; ++i) {
-        const int rl = frow + 8 * i;
-        bv[i] = (rl < nb && fcol_ok)
-                    ? load16(a.out() + (size_t)sm.rows[b0 + rl] * os + j0 + c8)
-                    : zero16();
-      }
-      uint4 bop[4][NKS];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int li = p * 16 + cl;
-        const bool ok = li < nb;
-        const RLD_GLOBAL uint16_t* xr = a.xa() + (size_t)(ok ? sm.rows[b0 + li] : 0) * R;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const uint32_t k = ks * 32 + lg * 8;
-          bop[p][ks] = (p * 16 < nb && ok && k < R) ? load16(xr + k) : zero16();
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        if (p * 16 < nb) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) acc = mfma_bf16_16x16x32(aop[m][ks], bop[p][ks], acc);
-            // lane holds delta[row p*16+cl][cols m*16 + 4*lg .. +3] of this wave's slice
-            const uint32_t d01 = pack_bf16x2(acc[0], acc[1]);
-            const uint32_t d23 = pack_bf16x2(acc[2], acc[3]);
-            *reinterpret_cast<uint2*>(&sm.dl[(p * 16 + cl) * kDlStride + wave * 64 + m * 16 +
-                                             4 * lg]) = make_uint2(d01, d23);
-          }
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kFoldVecs; ++i) {
-        const int rl = frow + 8 * i;
-        if (rl < nb && fcol_ok) {
-          const uint4 dv = *reinterpret_cast<const uint4*>(&sm.dl[rl * kDlStride + c8]);
-          store16(a.out() + (size_t)sm.rows[b0 + rl] * os + j0 + c8, fold8(bv[i], dv, scale));
-        }
-      }
-      __syncthreads();
-    }
+    for (int b0 = 0; b0 < cnt; b0 += kExpRows) batch(b0, cnt);
   }
 }
 
@@ -412,10 +436,10 @@ __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a)
   *reinterpret_cast<RLD_GLOBAL u32x2*>(a.xa() + (size_t)row * a.R + col) = o;
 }
 
-template <int NKS>
+template <int NKS, int MT>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(BgmvArgs a) {
-  __shared__ ExpandSmem sm;
-  expand_item<NKS>(a, (int)blockIdx.y, blockIdx.x * kJT, sm);
+  __shared__ ExpandSmem<MT> sm;
+  expand_item<NKS, MT>(a, (int)blockIdx.y, blockIdx.x * ExpandSmem<MT>::kCols, sm);
 }
 
 // Workspace: fp32 partials [nch][n][R] (k split only).
@@ -460,12 +484,16 @@ static int make_args(const rld_route* route, const void* x, uint32_t x_row_strid
 
 typedef void (*BgmvKernel)(BgmvArgs);
 
+// Expand items of 256 output columns (16*4 per wave).  (512-column items,
+// half the blocks, measured slower on the decode FFN shapes.)
+constexpr int kExpMT = 4;
+
 static BgmvKernel pick_expand(uint32_t R) {
   switch (div_ceil(R, 32)) {
-    case 1: return bgmv_expand_kernel<1>;
-    case 2: return bgmv_expand_kernel<2>;
-    case 3: return bgmv_expand_kernel<3>;
-    default: return bgmv_expand_kernel<4>;
+    case 1: return bgmv_expand_kernel<1, kExpMT>;
+    case 2: return bgmv_expand_kernel<2, kExpMT>;
+    case 3: return bgmv_expand_kernel<3, kExpMT>;
+    default: return bgmv_expand_kernel<4, kExpMT>;
   }
 }
 
@@ -533,7 +561,7 @@ extern "C" int rld_bgmv_expand_fold(const rld_route* route, const void* xa,
   a.n_out = route->n_out;
   a.R = route->max_rank;
   a.os = out_row_stride;
-  hipLaunchKernelGGL(pick_expand(a.R), dim3(div_ceil(route->n_out, kJT), route->max_loras),
+  hipLaunchKernelGGL(pick_expand(a.R), dim3(div_ceil(route->n_out, 64 * kExpMT), route->max_loras),
                      dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
   return launch_status();
 }
