@@ -20,6 +20,11 @@ What it computes, and where the pages say so:
   ``[n_out, max_rank]``, both row-major BF16 with zero rows/columns past the
   adapter's rank; scale = alpha/r, or alpha/sqrt(r) with use_rslora, kept out
   of B.
+* "Module lora_delta" and the lora_delta.rs listing (apply_lora_delta doc
+  comment): the unrouted single-adapter delta, base_out[m, n_out] +=
+  scale * (x @ a^T) @ b^T for one LoraPair, with the same rounding points as
+  the routed fold (the pages state that the routed path is byte-identical to
+  row-by-row calls of this one).
 * "Module moe_lora_grouped" (moe_lora_grouped_down, moe_lora_gather_bgmv,
   pack_expert_tables, grouped_down_wc, grouped_down_windows,
   gather_row_token): the same fold for MoE experts, over expert-sorted rows of
@@ -267,6 +272,28 @@ def bgmv(slots: List[Optional[SlotWeights]], k_in: int, n_out: int, max_rank: in
         o0 = out_offset + i * out_row_stride
         xa[i], out[o0: o0 + n_out] = fold_row(xrow, slots[s], out[o0: o0 + n_out])
     return xa, out
+
+
+def lora_delta(w: SlotWeights, k_in: int, n_out: int, max_rank: int, x: np.ndarray,
+               x_row_stride: int, m: int, base_out: np.ndarray, out_offset: int,
+               out_row_stride: int):
+    """Unrouted delta of one adapter pair over m rows (apply_lora_delta), written
+    as matrices: XA = bf16(X @ A^T) [m, max_rank], D = bf16(XA @ B^T) [m, n_out],
+    OUT = bf16(f32(OUT) + f32(scale * f32(D))).  Row i of x starts at
+    i*x_row_stride, row i of the output region at out_offset + i*out_row_stride.
+    Returns (xa [m, max_rank] BF16 bits, folded copy of base_out)."""
+    out = np.array(base_out, dtype=np.uint16, copy=True)
+    if m == 0:
+        return np.zeros((0, max_rank), np.uint16), out
+    rows_x = np.arange(m)[:, None] * x_row_stride + np.arange(k_in)[None, :]
+    X = bf16_to_f64(np.asarray(x)[rows_x])                       # [m, k_in]
+    XA = round_bf16(X @ w.a64().T)                                # [m, max_rank]
+    D = round_bf16(bf16_to_f64(XA) @ w.b64().T)                   # [m, n_out]
+    rows_o = out_offset + np.arange(m)[:, None] * out_row_stride + np.arange(n_out)[None, :]
+    T = np.float32(w.scale) * bf16_to_f32(D)                      # float32 products
+    S = bf16_to_f32(out[rows_o]) + T                              # float32 sums
+    out[rows_o] = round_bf16(S)
+    return XA, out
 
 
 def moe_gather(pairs, num_experts: int, k_in: int, n_out: int, max_rank: int,

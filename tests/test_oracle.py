@@ -488,11 +488,81 @@ def pin_helpers(o):
     assert [float(v) for v in sc] == [0.0, 2.0, 0.0, 4.0]
 
 
+def _one_pair(o, rng, k_in, n_out, rank, max_rank, rslora=False):
+    ad = W.make_adapter(rng, 0, rank, k_in, n_out, 16.0, rslora)
+    return ad, o.pack_slots([ad], 1, max_rank)[0]
+
+
+def pin_lora_delta_brute_force(o):
+    """Unrouted delta (apply_lora_delta) on tiny inputs against exact rationals,
+    rounding only where the pages do; rank padded, rsLoRA scale."""
+    rng = W.rng_for(0, salt=21)
+    k_in, n_out, max_rank, m = 20, 12, 8, 3
+    ad, w = _one_pair(o, rng, k_in, n_out, 5, max_rank, rslora=True)
+    x = W.bf16_trunc(rng.standard_normal((m, k_in)).astype(np.float32)).ravel()
+    base = W.bf16_trunc(rng.standard_normal((m, n_out)).astype(np.float32)).ravel()
+    xa, out = o.lora_delta(w, k_in, n_out, max_rank, x, k_in, m, base, 0, n_out)
+    for i in range(m):
+        exa, eout = exact_fold_row(x[i * k_in:(i + 1) * k_in], w.A, w.B, w.scale,
+                                   base[i * n_out:(i + 1) * n_out])
+        assert np.array_equal(xa[i], exa)
+        assert np.array_equal(out[i * n_out:(i + 1) * n_out], eout)
+
+
+def pin_lora_delta_textbook(o):
+    """Integer-exact values: the unrouted delta is standard LoRA
+    y = W0 x + (alpha/r) B (A x), A [r, k_in], B [n_out, r]."""
+    rng = np.random.default_rng(23)
+    for k_in, n_out, rank, max_rank, m in ((8, 8, 8, 8, 1), (16, 12, 4, 8, 6), (12, 20, 3, 16, 9)):
+        x = rng.integers(-1, 2, size=(m, k_in))
+        A = rng.integers(-1, 2, size=(rank, k_in))
+        B = rng.integers(-1, 2, size=(n_out, rank))
+        base = 2 * rng.integers(-4, 5, size=(m, n_out))
+        ad = W.Adapter(0, rank, 4.0 * rank, False, _int_bits(A), _int_bits(B))  # scale 4
+        w = o.pack_slots([ad], 1, max_rank)[0]
+        xa, out = o.lora_delta(w, k_in, n_out, max_rank, _int_bits(x).ravel(), k_in, m,
+                               _int_bits(base).ravel(), 0, n_out)
+        y = base + 4 * (x @ A.T) @ B.T
+        assert np.array_equal(o.bf16_to_f64(out).reshape(m, n_out), y.astype(np.float64))
+        assert np.array_equal(o.bf16_to_f64(xa)[:, :rank], (x @ A.T).astype(np.float64))
+        assert np.all(xa[:, rank:] == 0)
+
+
+def pin_lora_delta_matches_routed(o):
+    """The pages: the routed fold is byte-identical to row-by-row unrouted calls
+    of the same pair.  The matrix form here against the per-row routed oracle with
+    every row on one slot, and m rows against m one-row calls, with row strides and
+    an output region inside wider rows left untouched outside [0, n_out)."""
+    rng = W.rng_for(0, salt=22)
+    k_in, n_out, max_rank, m = 72, 40, 16, 11
+    ad, w = _one_pair(o, rng, k_in, n_out, 12, max_rank)
+    xs, os_, off = k_in + 8, 2 * n_out + 8, n_out
+    x = W.bf16_trunc(rng.standard_normal(m * xs).astype(np.float32))
+    base = W.bf16_trunc(rng.standard_normal(m * os_).astype(np.float32))
+    xa, out = o.lora_delta(w, k_in, n_out, max_rank, x, xs, m, base, off, os_)
+    xa_r, out_r = o.bgmv([w], k_in, n_out, max_rank, x, xs, np.zeros(m, np.int32), m, base,
+                         off, os_)
+    assert np.array_equal(xa, xa_r) and np.array_equal(out, out_r)
+    changed = out != base
+    inside = np.zeros(m * os_, bool)
+    for i in range(m):
+        inside[i * os_ + off: i * os_ + off + n_out] = True
+        xa1, out1 = o.lora_delta(w, k_in, n_out, max_rank, x[i * xs:], xs, 1,
+                                 base[i * os_:(i + 1) * os_], off, os_)
+        assert np.array_equal(xa1[0], xa[i])
+        assert np.array_equal(out1, out[i * os_:(i + 1) * os_])
+    assert np.any(changed) and not np.any(changed & ~inside)
+    # m = 0 changes nothing
+    xa0, out0 = o.lora_delta(w, k_in, n_out, max_rank, x, xs, 0, base, off, os_)
+    assert xa0.shape == (0, max_rank) and np.array_equal(out0, base)
+
+
 PINS = [pin_bf16_known, pin_bf16_roundtrip, pin_bf16_midpoints, pin_bf16_vs_torch,
         pin_scale_closed_forms, pin_brute_force_bgmv, pin_textbook_lora, pin_pad_invariant,
         pin_inactive_and_strides, pin_batched_equals_rows, pin_fold_order,
         pin_routing_probe_grouped, pin_routing_probe_gather, pin_window_union, pin_cross_path,
-        pin_helpers]
+        pin_helpers, pin_lora_delta_brute_force, pin_lora_delta_textbook,
+        pin_lora_delta_matches_routed]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)

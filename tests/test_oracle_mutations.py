@@ -146,10 +146,51 @@ def _mut_pack_first_wins(m):
     m.pack_expert_tables = pet
 
 
+def _lora_variant(m, *, b_orient="ok", fused=False, round_xa=True, x_stride_ok=True):
+    """A re-implementation of the matrix-form unrouted delta with one mistake."""
+    def lora_delta(w, k_in, n_out, max_rank, x, xs, rows, base, off, os_):
+        out = np.array(base, dtype=np.uint16, copy=True)
+        if rows == 0:
+            return np.zeros((0, max_rank), np.uint16), out
+        st = xs if x_stride_ok else k_in
+        X = m.bf16_to_f64(np.asarray(x)[np.arange(rows)[:, None] * st + np.arange(k_in)])
+        XA64 = X @ w.a64().T
+        XA = m.round_bf16(XA64)
+        Bm = w.b64() if b_orient == "ok" else w.b64().reshape(max_rank, n_out).T
+        D64 = (m.bf16_to_f64(XA) if round_xa else XA64) @ Bm.T
+        D = m.round_bf16(D64)
+        ro = off + np.arange(rows)[:, None] * os_ + np.arange(n_out)
+        if fused:
+            S = m.bf16_to_f64(out[ro]) + np.float64(w.scale) * m.bf16_to_f64(D)
+        else:
+            S = m.bf16_to_f32(out[ro]) + np.float32(w.scale) * m.bf16_to_f32(D)
+        out[ro] = m.round_bf16(S)
+        return XA, out
+    m.lora_delta = lora_delta
+
+
+def _mut_lora_transposed_B(m):
+    _lora_variant(m, b_orient="transposed")
+
+
+def _mut_lora_fused_fold(m):
+    _lora_variant(m, fused=True)
+
+
+def _mut_lora_unrounded_xa(m):
+    _lora_variant(m, round_xa=False)
+
+
+def _mut_lora_ignores_x_stride(m):
+    _lora_variant(m, x_stride_ok=False)
+
+
 MUTANTS = [_mut_truncating_round, _mut_fused_fold, _mut_transposed_A, _mut_dropped_term,
            _mut_scale_before_round, _mut_unrounded_xa, _mut_sign, _mut_rslora_always,
            _mut_gather_token_mod, _mut_owner_off_by_one, _mut_grouped_adapter_by_row,
-           _mut_ignore_out_offset, _mut_xa_not_zeroed, _mut_wc_floor, _mut_pack_first_wins]
+           _mut_ignore_out_offset, _mut_xa_not_zeroed, _mut_wc_floor, _mut_pack_first_wins,
+           _mut_lora_transposed_B, _mut_lora_fused_fold, _mut_lora_unrounded_xa,
+           _mut_lora_ignores_x_stride]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
