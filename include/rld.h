@@ -75,6 +75,19 @@ typedef struct rld_route {
   uint32_t max_rank;
 } rld_route;
 
+/* One adapted module without routing (LoraPair, "Module lora_delta"): device
+ * addresses of A ([max_rank, k_in] row-major BF16, zero rows past the
+ * adapter's rank) and B ([n_out, max_rank] row-major BF16, zero columns past
+ * the rank), and the fp32 scale. */
+typedef struct rld_pair {
+  const void* a;
+  const void* b;
+  float scale;
+  uint32_t k_in;
+  uint32_t n_out;
+  uint32_t max_rank;
+} rld_pair;
+
 /* Expert routing tables of one MoE projection (MoeExpertRoute, widened to a
  * [max_loras][num_experts] table so a mixed batch can name its adapter per
  * row): entry s*num_experts + e holds adapter slot s's pair for expert e. */
@@ -205,6 +218,38 @@ int rld_bgmv_expand_fold(const rld_route* route, const void* xa, const int32_t* 
 int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_stride,
              const int32_t* seq_slot, uint32_t n, void* base_out, uint32_t out_row_stride,
              void* xa, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace the unrouted entry points need for m rows: the same k_in
+ * split as the BGMV path (rld_bgmv_workspace_bytes(m, k_in, max_rank, 1)),
+ * under the same contract.  0 when k_in fits one chunk. */
+size_t rld_lora_workspace_bytes(uint32_t m, uint32_t k_in, uint32_t max_rank);
+
+/* Unrouted single-adapter shrink (apply_lora_delta, lora_delta.rs): for every
+ * row i < m, xa[i, k] = bf16(sum_c x[i*x_row_stride + c] * A[k, c]) for
+ * k < max_rank.
+ *   x   device BF16, row i at x + i*x_row_stride (the page asks for
+ *       contiguous rows; any stride >= k_in works here)
+ *   xa  device BF16 [m, max_rank], written
+ * One launch shape serves every m (the page's m == 1 GEMV pair, its row loop
+ * up to lora_gemv_max_m rows and its GEMM path are one path here).  A row's
+ * summation order depends only on (k_in, max_rank) and is the same as in the
+ * routed BGMV shrink, so m rows are bit-identical to m one-row calls and to a
+ * routed call with every row on a slot holding this pair. */
+int rld_lora_shrink(const rld_pair* pair, const void* x, uint32_t x_row_stride, uint32_t m,
+                    void* xa, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Unrouted expand + fold (apply_lora_delta's expand and bf16_scaled_add, fused):
+ * delta = bf16(xa[i,:] @ B^T) and base_out[i*out_row_stride + j] =
+ * bf16(f32(base) + scale * f32(delta_j)) for j < n_out, every row i < m.
+ * Nothing outside [0, n_out) of a row is touched. */
+int rld_lora_expand_fold(const rld_pair* pair, const void* xa, uint32_t m, void* base_out,
+                         uint32_t out_row_stride, void* stream);
+
+/* apply_lora_delta: rld_lora_shrink then rld_lora_expand_fold on the same
+ * stream.  m == 0 is a no-op. */
+int rld_lora_delta(const rld_pair* pair, const void* x, uint32_t x_row_stride, uint32_t m,
+                   void* base_out, uint32_t out_row_stride, void* xa, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* MoE decode gather-fold shrink (moe_lora_gather_bgmv): flat row rho < n_rows
  * (rho = token*top_k + position) uses expert e = indices[rho] and adapter slot

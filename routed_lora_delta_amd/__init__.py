@@ -55,6 +55,11 @@ class rld_route(ctypes.Structure):
                 ("max_rank", c_uint32)]
 
 
+class rld_pair(ctypes.Structure):
+    _fields_ = [("a", c_void_p), ("b", c_void_p), ("scale", c_float), ("k_in", c_uint32),
+                ("n_out", c_uint32), ("max_rank", c_uint32)]
+
+
 class rld_moe_route(ctypes.Structure):
     _fields_ = [("a_table", c_void_p), ("b_table", c_void_p), ("scale_table", c_void_p),
                 ("max_loras", c_uint32), ("num_experts", c_uint32), ("k_in", c_uint32),
@@ -70,6 +75,7 @@ class rld_adapter_entry(ctypes.Structure):
 _P = c_void_p
 _R = POINTER(rld_route)
 _M = POINTER(rld_moe_route)
+_L = POINTER(rld_pair)
 _E = POINTER(rld_adapter_entry)
 _u32p = POINTER(c_uint32)
 
@@ -87,6 +93,10 @@ _SIGS = {
     "rld_bgmv_shrink": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
     "rld_bgmv_expand_fold": (c_int, [_R, _P, _P, c_uint32, _P, c_uint32, _P]),
     "rld_bgmv": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
+    "rld_lora_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32]),
+    "rld_lora_shrink": (c_int, [_L, _P, c_uint32, c_uint32, _P, _P, c_size_t, _P]),
+    "rld_lora_expand_fold": (c_int, [_L, _P, c_uint32, _P, c_uint32, _P]),
+    "rld_lora_delta": (c_int, [_L, _P, c_uint32, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
     "rld_moe_gather_shrink": (c_int, [_M, _P, c_uint32, _P, _P, c_uint32, c_uint32, _P, _P]),
     "rld_moe_gather_expand_fold": (c_int, [_M, _P, _P, _P, c_uint32, c_uint32, _P, c_uint32,
                                            _P]),
@@ -225,6 +235,27 @@ def rld_bgmv(route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, xa, 
     return _lib.rld_bgmv(ctypes.byref(route), ptr(x), x_row_stride, ptr(seq_slot), n,
                          ptr(base_out), out_row_stride, ptr(xa), ptr(workspace), workspace_bytes,
                          stream_handle(stream))
+
+
+def rld_lora_workspace_bytes(m, k_in, max_rank):
+    return _lib.rld_lora_workspace_bytes(m, k_in, max_rank)
+
+
+def rld_lora_shrink(pair, x, x_row_stride, m, xa, workspace, workspace_bytes, stream=None):
+    return _lib.rld_lora_shrink(ctypes.byref(pair), ptr(x), x_row_stride, m, ptr(xa),
+                                ptr(workspace), workspace_bytes, stream_handle(stream))
+
+
+def rld_lora_expand_fold(pair, xa, m, base_out, out_row_stride, stream=None):
+    return _lib.rld_lora_expand_fold(ctypes.byref(pair), ptr(xa), m, ptr(base_out),
+                                     out_row_stride, stream_handle(stream))
+
+
+def rld_lora_delta(pair, x, x_row_stride, m, base_out, out_row_stride, xa, workspace,
+                   workspace_bytes, stream=None):
+    return _lib.rld_lora_delta(ctypes.byref(pair), ptr(x), x_row_stride, m, ptr(base_out),
+                               out_row_stride, ptr(xa), ptr(workspace), workspace_bytes,
+                               stream_handle(stream))
 
 
 def rld_moe_gather_shrink(route, x, x_row_stride, indices, row_adapter, top_k, n_rows, xa,

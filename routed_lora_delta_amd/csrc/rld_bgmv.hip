@@ -49,6 +49,11 @@ struct BgmvArgs {
   uint64_t x_, seq_, atab_, btab_, stab_;
   uint64_t partial_;  // [nch][n][R] fp32 (k split only): the workspace
   uint64_t xa_, out_;
+  // Unrouted mode (dense != 0): one pair for every row; items take contiguous
+  // row tiles instead of a slot's rows, and seq_slot and the tables are unused.
+  uint64_t a_dense, b_dense;
+  float scale_dense;
+  uint32_t dense;
   uint32_t xs, n, max_loras, k_in, n_out, R, kc, nch;
   uint32_t ncg;  // shrink column groups of 16*NT xa columns
   uint32_t os;
@@ -127,6 +132,18 @@ __device__ __forceinline__ SlotEntry slot_entry(const BgmvArgs& a, int s) {
   return e;
 }
 
+// Rows of the shrink / expand tiles of the unrouted mode.
+constexpr int kDenseShrinkRows = 64;
+constexpr int kDenseExpandRows = 128;
+
+// Unrouted mode: rows [r0, r0 + cnt) of a tile into the LDS row list.
+__device__ __forceinline__ int dense_tile_rows(uint32_t r0, uint32_t n, int tile, int* rows) {
+  const int cnt = (int)min((uint32_t)tile, n - r0);
+  for (int i = threadIdx.x; i < cnt; i += 256) rows[i] = (int)(r0 + i);
+  __syncthreads();
+  return cnt;
+}
+
 // Shrink item w (slot-major over (slot, chunk, column group)); the group
 // covers xa columns [16*NT*cg, 16*NT*(cg+1)).
 template <int NT>
@@ -134,18 +151,26 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, Shrin
   const uint32_t n = a.n, R = a.R, nchunks = a.nch, ncg = a.ncg;
   const uint32_t cg = w % ncg;
   const uint32_t c = (w / ncg) % nchunks;
-  const int s = (int)(w / (ncg * nchunks));
+  const int s = (int)(w / (ncg * nchunks));  // slot, or row tile in the unrouted mode
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
   // The block's seq_slot entries and the slot's table entries go out first.
-  const int key0 = first_key(a.seq_slot(), n);
-  const SlotEntry ent = slot_entry(a, s);
+  int key0 = -1;
+  SlotEntry ent;
+  if (a.dense) {
+    ent.a = a.a_dense;
+    ent.b = a.b_dense;
+    ent.scale = a.scale_dense;
+  } else {
+    key0 = first_key(a.seq_slot(), n);
+    ent = slot_entry(a, s);
+  }
 
   // Without a k split, the last item (a slot of the last index, usually cold)
   // also writes the zero xa rows of base rows (the reduce kernel does it
   // otherwise).
-  if (nchunks == 1 && w == total - 1) {
+  if (!a.dense && nchunks == 1 && w == total - 1) {
     const uint32_t r8 = R / 8;
     for (uint32_t e = threadIdx.x; e < n * r8; e += 256) {
       const uint32_t row = e / r8;
@@ -260,6 +285,11 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, Shrin
   using Q4 = std::integral_constant<int, kShrinkMT>;
   using Q8 = std::integral_constant<int, 2 * kShrinkMT>;
 
+  if (a.dense) {
+    const int cnt = dense_tile_rows((uint32_t)s * kDenseShrinkRows, n, kDenseShrinkRows, sm.rows);
+    batch(Q4{}, 0, cnt);
+    return;
+  }
   // The usual case, straight-line: at most 256 rows (their seq_slot entries
   // are key0, so the scan issues no load that would wait behind the A tile)
   // and at most 128 of them on this slot.
@@ -293,8 +323,16 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem<MT
   constexpr int kFoldVecs = kExpRows / kRowsPerPass;
   const uint32_t n = a.n, R = a.R, n_out = a.n_out, os = a.os;
   // seq_slot entries and the slot's table entries first (one round trip)
-  const int key0 = first_key(a.seq_slot(), n);
-  const SlotEntry ent = slot_entry(a, s);
+  int key0 = -1;
+  SlotEntry ent;
+  if (a.dense) {
+    ent.a = a.a_dense;
+    ent.b = a.b_dense;
+    ent.scale = a.scale_dense;
+  } else {
+    key0 = first_key(a.seq_slot(), n);
+    ent = slot_entry(a, s);
+  }
   if (!ent.active()) return;
   const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(ent.b);
   const float scale = ent.scale;
@@ -381,6 +419,12 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem<MT
     __syncthreads();
   };
 
+  if (a.dense) {  // s is the row tile
+    const int cnt = dense_tile_rows((uint32_t)s * kDenseExpandRows, n, kDenseExpandRows, sm.rows);
+    batch(0, cnt);
+    if (cnt > kExpRows) batch(kExpRows, cnt);
+    return;
+  }
   // The usual case, straight-line: at most 256 rows (their seq_slot entries
   // are key0) and at most 128 of them on this slot.
   if (n <= 256) {
@@ -417,7 +461,7 @@ __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a)
   if (t >= a.n * q4) return;
   const uint32_t row = t / q4;
   const uint32_t col = (t % q4) * 4;
-  const int s = a.seq_slot()[row];
+  const int s = a.dense ? 0 : a.seq_slot()[row];
   const RLD_GLOBAL floatx4* p =
       reinterpret_cast<const RLD_GLOBAL floatx4*>(a.partial() + (size_t)row * a.R + col);
   const size_t cstride = (size_t)a.n * a.R / 4;  // floatx4 per chunk
@@ -432,7 +476,8 @@ __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a)
   }
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   u32x2 o = {0u, 0u};
-  if (slot_active(a, s)) o = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+  if (a.dense || slot_active(a, s))
+    o = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
   *reinterpret_cast<RLD_GLOBAL u32x2*>(a.xa() + (size_t)row * a.R + col) = o;
 }
 
@@ -454,6 +499,7 @@ static int make_args(const rld_route* route, const void* x, uint32_t x_row_strid
                      const int32_t* seq_slot, uint32_t n, void* xa, void* workspace,
                      size_t workspace_bytes, void* base_out, uint32_t out_row_stride,
                      BgmvArgs* a) {
+  *a = BgmvArgs{};
   const uint32_t R = route->max_rank, k_in = route->k_in;
   const size_t need = partial_bytes(n, k_in, R);
   if (need) {
@@ -578,4 +624,105 @@ extern "C" int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_st
                        stream);
   if (st) return st;
   return rld_bgmv_expand_fold(route, xa, seq_slot, n, base_out, out_row_stride, stream);
+}
+
+// ------------------------------------------------------------ unrouted ----
+
+static int check_pair(const rld_pair* p) {
+  if (!p || !p->a || !p->b) return RLD_EINVAL;
+  int st = check_dims(p->k_in, p->n_out, p->max_rank);
+  if (st) return st;
+  if (!aligned16(p->a) || !aligned16(p->b)) return RLD_EALIGN;
+  return RLD_OK;
+}
+
+static void dense_args(const rld_pair* pair, uint32_t m, BgmvArgs* a) {
+  *a = BgmvArgs{};
+  a->dense = 1;
+  a->a_dense = reinterpret_cast<uint64_t>(pair->a);
+  a->b_dense = reinterpret_cast<uint64_t>(pair->b);
+  a->scale_dense = pair->scale;
+  a->n = m;
+  a->max_loras = 1;
+  a->k_in = pair->k_in;
+  a->n_out = pair->n_out;
+  a->R = pair->max_rank;
+  a->kc = bgmv_chunk(pair->k_in, pair->max_rank);
+  a->nch = div_ceil(pair->k_in, a->kc);
+  a->ncg = div_ceil(pair->max_rank, 16u * bgmv_nt(pair->max_rank));
+}
+
+extern "C" size_t rld_lora_workspace_bytes(uint32_t m, uint32_t k_in, uint32_t max_rank) {
+  if (k_in == 0 || max_rank == 0) return 0;
+  return partial_bytes(m, k_in, max_rank);
+}
+
+extern "C" int rld_lora_shrink(const rld_pair* pair, const void* x, uint32_t x_row_stride,
+                               uint32_t m, void* xa, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  int st = check_pair(pair);
+  if (st) return st;
+  if (m == 0) return RLD_OK;
+  if (!xa) return RLD_EINVAL;
+  if ((st = check_rows(x, x_row_stride, pair->k_in))) return st;
+  if (!aligned16(xa)) return RLD_EALIGN;
+  const size_t need = partial_bytes(m, pair->k_in, pair->max_rank);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return RLD_ENOSPACE;
+    if (!aligned16(workspace)) return RLD_EALIGN;
+  }
+  BgmvArgs a;
+  dense_args(pair, m, &a);
+  a.x_ = reinterpret_cast<uint64_t>(x);
+  a.xs = x_row_stride;
+  a.xa_ = reinterpret_cast<uint64_t>(xa);
+  a.partial_ = reinterpret_cast<uint64_t>(workspace);
+  const uint32_t total = div_ceil(m, (uint32_t)kDenseShrinkRows) * a.nch * a.ncg;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid(xcd_group_grid(total, a.ncg));
+  switch (bgmv_nt(a.R)) {
+    case 1: hipLaunchKernelGGL(bgmv_shrink_kernel<1>, grid, dim3(256), 0, hs, a, total); break;
+    case 2: hipLaunchKernelGGL(bgmv_shrink_kernel<2>, grid, dim3(256), 0, hs, a, total); break;
+    default: hipLaunchKernelGGL(bgmv_shrink_kernel<4>, grid, dim3(256), 0, hs, a, total); break;
+  }
+  if ((st = launch_status())) return st;
+  if (a.nch > 1) {
+    hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(m * (a.R / 4), kReduceThreads)),
+                       dim3(kReduceThreads), 0, hs, a);
+    return launch_status();
+  }
+  return RLD_OK;
+}
+
+extern "C" int rld_lora_expand_fold(const rld_pair* pair, const void* xa, uint32_t m,
+                                    void* base_out, uint32_t out_row_stride, void* stream) {
+  int st = check_pair(pair);
+  if (st) return st;
+  if (m == 0) return RLD_OK;
+  if (!xa) return RLD_EINVAL;
+  if (!aligned16(xa)) return RLD_EALIGN;
+  if ((st = check_rows(base_out, out_row_stride, pair->n_out))) return st;
+  const uint32_t tiles = div_ceil(m, (uint32_t)kDenseExpandRows);
+  if (tiles > 65535u) return RLD_EUNSUPPORTED;
+  BgmvArgs a;
+  dense_args(pair, m, &a);
+  a.xa_ = reinterpret_cast<uint64_t>(xa);
+  a.out_ = reinterpret_cast<uint64_t>(base_out);
+  a.os = out_row_stride;
+  hipLaunchKernelGGL(pick_expand(a.R), dim3(div_ceil(pair->n_out, 64 * kExpMT), tiles), dim3(256),
+                     0, reinterpret_cast<hipStream_t>(stream), a);
+  return launch_status();
+}
+
+extern "C" int rld_lora_delta(const rld_pair* pair, const void* x, uint32_t x_row_stride,
+                              uint32_t m, void* base_out, uint32_t out_row_stride, void* xa,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_pair(pair);
+  if (st) return st;
+  if (m == 0) return RLD_OK;
+  if ((st = check_rows(base_out, out_row_stride, pair->n_out))) return st;
+  if (div_ceil(m, (uint32_t)kDenseExpandRows) > 65535u) return RLD_EUNSUPPORTED;
+  st = rld_lora_shrink(pair, x, x_row_stride, m, xa, workspace, workspace_bytes, stream);
+  if (st) return st;
+  return rld_lora_expand_fold(pair, xa, m, base_out, out_row_stride, stream);
 }

@@ -15,7 +15,7 @@ from typing import Sequence
 import numpy as np
 import torch
 
-from . import (check, rld_adapter_entry, rld_moe_route, rld_moe_tables_pack,
+from . import (check, rld_adapter_entry, rld_moe_route, rld_moe_tables_pack, rld_pair,
                rld_pad_adapter_host, rld_route, rld_route_pack)
 
 _ALIGN_ELEMS = 128  # 256 bytes of BF16
@@ -91,6 +91,18 @@ class DenseRoute:
             self.a_table[slot] = int(np.int64(np.uint64(a_addr)))
         if b_addr is not None:
             self.b_table[slot] = int(np.int64(np.uint64(b_addr)))
+
+
+class SinglePair:
+    """One adapter module without routing (LoraPair): the pair packed on slot 0 of
+    a one-slot route, so the same pool serves the unrouted and the routed calls."""
+
+    def __init__(self, adapter, max_rank: int, k_in: int, n_out: int, device="cuda"):
+        assert adapter.slot == 0
+        self.route = DenseRoute([adapter], 1, max_rank, k_in, n_out, device)
+        r = self.route
+        self.pair = rld_pair(int(r.a_host[0]), int(r.b_host[0]), float(r.scale_host[0]), k_in,
+                             n_out, max_rank)
 
 
 class MoeRoute:

@@ -308,6 +308,37 @@ def test_grouped_workspace_contract():
     assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 0, 128) == 0
 
 
+def test_lora_rejects_bad_arguments():
+    # the unrouted entry points: every argument error is found before a launch
+    P = lambda **k: R.rld_pair(k.get("a", FAKE), k.get("b", FAKE), 0.5,  # noqa: E731
+                               k.get("k_in", 4096), k.get("n_out", 1024), k.get("r", 16))
+    ws = R.rld_lora_workspace_bytes(64, 4096, 16)
+    d = lambda p, **k: R.rld_lora_delta(  # noqa: E731
+        p, k.get("x", FAKE), k.get("xs", 4096), k.get("m", 64), k.get("out", FAKE),
+        k.get("os", 1024), k.get("xa", FAKE), k.get("ws", FAKE), k.get("wsb", ws), 0)
+    assert d(P(a=0)) == R.RLD_EINVAL
+    assert d(P(b=0)) == R.RLD_EINVAL
+    assert d(P(k_in=0)) == R.RLD_EINVAL
+    assert d(P(r=136)) == R.RLD_EUNSUPPORTED
+    assert d(P(k_in=4092)) == R.RLD_EALIGN
+    assert d(P(a=FAKE + 8)) == R.RLD_EALIGN          # A must be 16-byte aligned
+    assert d(P(), x=0) == R.RLD_EINVAL
+    assert d(P(), xs=1024) == R.RLD_EINVAL            # stride < k_in
+    assert d(P(), out=FAKE + 2) == R.RLD_EALIGN
+    assert d(P(), os=512) == R.RLD_EINVAL             # stride < n_out
+    assert d(P(), xa=0) == R.RLD_EINVAL
+    assert d(P(), wsb=ws - 16) == R.RLD_ENOSPACE
+    assert d(P(), ws=0) == R.RLD_ENOSPACE
+    assert d(P(), m=0) == R.RLD_OK                    # no-op, nothing launched
+    assert R.rld_lora_shrink(P(), FAKE, 4096, 0, FAKE, 0, 0, 0) == R.RLD_OK
+    assert R.rld_lora_expand_fold(P(), FAKE, 0, FAKE, 1024, 0) == R.RLD_OK
+    assert R.rld_lora_expand_fold(P(), 0, 4, FAKE, 1024, 0) == R.RLD_EINVAL
+    # the same k split as the routed path, so the same partials
+    assert ws == R.rld_bgmv_workspace_bytes(64, 4096, 16, 1) == 16 * 64 * 16 * 4
+    assert R.rld_lora_workspace_bytes(64, 256, 16) == 0
+    assert R.rld_lora_workspace_bytes(64, 0, 16) == 0
+
+
 def test_scale_table_values_are_exact_closed_forms():
     # the fp32 scales of the decode workloads: alpha/r and alpha/sqrt(r), rounded once
     for alpha, r in ((32.0, 8), (32.0, 32), (16.0, 16)):

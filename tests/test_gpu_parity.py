@@ -13,11 +13,12 @@ import torch
 import oracle as O
 import routed_lora_delta_amd as R
 import workloads as W
-from gpu_util import (BgmvRun, GroupedRun, abs_sums_bgmv, abs_sums_gather, abs_sums_grouped,
-                      abs_sums_rows, assert_out_close, assert_xa_close, compare_bgmv, dev_i32,
+from gpu_util import (BgmvRun, GroupedRun, Guarded, abs_sums_bgmv, abs_sums_gather,
+                      abs_sums_grouped, abs_sums_rows, assert_out_close, assert_xa_close,
+                      compare_bgmv, dev_i32,
                       expand_depth, oracle_gather, oracle_grouped_window, require_gpu,
                       run_gather, say, shrink_depth)
-from routed_lora_delta_amd.pool import DenseRoute, from_device_u16, to_device_u16
+from routed_lora_delta_amd.pool import DenseRoute, SinglePair, from_device_u16, to_device_u16
 
 pytestmark = pytest.mark.gpu
 
@@ -410,3 +411,124 @@ def test_determinism_repeat_runs():
         r.run_all()
         o2.append(r.outputs()["out"])
     assert np.array_equal(o2[0], o2[1])
+
+
+# --------------------------------------------------------------- unrouted ---
+
+class LoraRun:
+    """Device state of one unrouted case: the pair (on slot 0 of a one-slot route,
+    so the routed entry points can run on the same pool), guarded x and output
+    buffers, xa and workspace."""
+
+    def __init__(self, ad, m, k_in, n_out, max_rank, x, base, dev):
+        self.sp = SinglePair(ad, max_rank, k_in, n_out, dev)
+        self.m, self.k_in, self.n_out, self.R = m, k_in, n_out, max_rank
+        self.x = Guarded(x, dev)
+        self.base = Guarded(base, dev)
+        self.xa = torch.zeros(max(m, 1) * max_rank + 8, dtype=torch.int16, device=dev)
+        self.ws_bytes = R.rld_lora_workspace_bytes(m, k_in, max_rank)
+        self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def xa_host(self, rows=None):
+        rows = self.m if rows is None else rows
+        return from_device_u16(self.xa)[: rows * self.R].reshape(rows, self.R).copy()
+
+
+def _lora_inputs(seed, m, k_in, n_out, rank, xs, os_, rslora=False):
+    rng = W.rng_for(5, salt=seed)
+    ad = W.make_adapter(rng, 0, rank, k_in, n_out, 16.0, rslora)
+    x = W.bf16_trunc(rng.standard_normal(max(m, 1) * xs).astype(np.float32))
+    base = W.bf16_trunc(rng.standard_normal(max(m, 1) * os_).astype(np.float32))
+    return ad, x, base
+
+
+def _check_lora(run, ad, x, xs, base, off, os_, label):
+    """xa and the folded region against the oracle; everything else bit-exact."""
+    m, k_in, n_out, Rk = run.m, run.k_in, run.n_out, run.R
+    w = O.pack_slots([ad], 1, Rk)[0]
+    xa_o, out_o = O.lora_delta(w, k_in, n_out, Rk, x, xs, m, base, off, os_)
+    X = x[np.arange(m)[:, None] * xs + np.arange(k_in)]
+    assert_xa_close(run.xa_host(), xa_o, f"{label} xa", abs_sums_rows(X, w.A),
+                    shrink_depth("bgmv", k_in, Rk))
+    out_g = run.base.body()
+    rows_o = off + np.arange(m)[:, None] * os_ + np.arange(n_out)
+    xa64 = O.bf16_to_f64(xa_o)
+    delta = O.round_bf16(xa64 @ w.b64().T)
+    sabs = np.abs(xa64) @ np.abs(w.b64()).T
+    assert_out_close(out_g[rows_o], out_o[rows_o], f"{label} out", delta=delta,
+                     scale=float(w.scale), sabs_d=sabs, depth_d=expand_depth("bgmv", Rk))
+    outside = np.ones(out_g.size, bool)
+    outside[rows_o.ravel()] = False
+    assert np.array_equal(out_g[outside], base[outside]), f"{label}: outside [0, n_out) changed"
+
+
+@pytest.mark.parametrize("m,k_in,n_out,max_rank,rank", [
+    (1, 4096, 4096, 16, 8),        # the pages' m == 1 GEMV pair
+    (2, 256, 264, 8, 8),
+    (48, 1000, 520, 24, 20),       # up to the pages' row-loop threshold
+    (49, 2056, 264, 32, 32),       # just past it: their GEMM path
+    (130, 512, 768, 128, 100),     # rank 128, ragged tiles
+    (1000, 12288, 1032, 64, 64),   # k split over 24 chunks
+    (4096, 4096, 4096, 16, 16),    # a prefill-sized batch
+], ids=lambda v: str(v))
+def test_lora_delta_shapes(m, k_in, n_out, max_rank, rank):
+    dev = require_gpu()
+    say(f"case: unrouted m={m} k_in={k_in} n_out={n_out} r={max_rank}")
+    ad, x, base = _lora_inputs(m % 97, m, k_in, n_out, rank, k_in, n_out, rslora=m % 2 == 1)
+    run = LoraRun(ad, m, k_in, n_out, max_rank, x, base, dev)
+    R.check(R.rld_lora_delta(run.sp.pair, run.x.ptr(), k_in, m, run.base.ptr(), n_out, run.xa,
+                             run.ws, run.ws_bytes), "rld_lora_delta")
+    torch.cuda.synchronize()
+    _check_lora(run, ad, x, k_in, base, 0, n_out, f"unrouted m={m}")
+
+
+def test_lora_delta_strided_two_stage():
+    """Padded x rows, the output region inside wider rows (as the K region of a
+    [Q|K|V] row), through the separate shrink and expand entry points."""
+    dev = require_gpu()
+    m, k_in, n_out, Rk = 77, 1536, 264, 32
+    xs, os_, off = k_in + 8, 3 * n_out, n_out
+    say("case: unrouted strided")
+    ad, x, base = _lora_inputs(3, m, k_in, n_out, 24, xs, os_)
+    run = LoraRun(ad, m, k_in, n_out, Rk, x, base, dev)
+    R.check(R.rld_lora_shrink(run.sp.pair, run.x.ptr(), xs, m, run.xa, run.ws, run.ws_bytes),
+            "rld_lora_shrink")
+    R.check(R.rld_lora_expand_fold(run.sp.pair, run.xa, m, run.base.ptr(off), os_),
+            "rld_lora_expand_fold")
+    torch.cuda.synchronize()
+    _check_lora(run, ad, x, xs, base, off, os_, "unrouted strided")
+
+
+def test_lora_delta_equals_routed_and_single_rows():
+    """The pages: the routed fold is byte-identical to row-by-row unrouted calls.
+    Here m rows of rld_lora_delta == m one-row rld_lora_delta calls == rld_bgmv
+    with every row on the slot holding the same pair, bit for bit (xa and out),
+    with and without a k split."""
+    dev = require_gpu()
+    for m, k_in, n_out, Rk in ((150, 12288, 520, 64), (70, 512, 1032, 16)):
+        say(f"case: unrouted vs routed vs single rows k_in={k_in}")
+        ad, x, base = _lora_inputs(7, m, k_in, n_out, Rk, k_in, n_out)
+        full = LoraRun(ad, m, k_in, n_out, Rk, x, base, dev)
+        R.check(R.rld_lora_delta(full.sp.pair, full.x.ptr(), k_in, m, full.base.ptr(), n_out,
+                                 full.xa, full.ws, full.ws_bytes), "rld_lora_delta")
+        torch.cuda.synchronize()
+        xa_full, out_full = full.xa_host(), full.base.body()
+        rows = LoraRun(ad, m, k_in, n_out, Rk, x, base, dev)
+        xa1s = []
+        for i in range(m):
+            R.check(R.rld_lora_delta(rows.sp.pair, rows.x.ptr(i * k_in), k_in, 1,
+                                     rows.base.ptr(i * n_out), n_out, rows.xa, rows.ws,
+                                     rows.ws_bytes), "one-row rld_lora_delta")
+            torch.cuda.synchronize()
+            xa1s.append(rows.xa_host(1)[0])
+        assert np.array_equal(np.stack(xa1s), xa_full)
+        assert np.array_equal(rows.base.body(), out_full)
+        routed = LoraRun(ad, m, k_in, n_out, Rk, x, base, dev)
+        seq = dev_i32(np.zeros(m, np.int32), dev)
+        wsb = R.rld_bgmv_workspace_bytes(m, k_in, Rk, 1)
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+        R.check(R.rld_bgmv(routed.sp.route.route, routed.x.ptr(), k_in, seq, m,
+                           routed.base.ptr(), n_out, routed.xa, ws, wsb), "rld_bgmv")
+        torch.cuda.synchronize()
+        assert np.array_equal(routed.xa_host(), xa_full)
+        assert np.array_equal(routed.base.body(), out_full)
