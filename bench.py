@@ -220,7 +220,7 @@ class Step:
         import torch
 
         import routed_lora_delta_amd as R
-        from routed_lora_delta_amd.pool import DenseRoute, MoeRoute, to_device_u16
+        from routed_lora_delta_amd.pool import DenseRoute, MoeRoute, SinglePair, to_device_u16
 
         self.R, self.torch = R, torch
         self.calls = []  # (label, kernel name, fn, algorithmic bytes, flops, rows)
@@ -253,9 +253,34 @@ class Step:
                     def expand(rt=rt, c=c, out=out, seq=seq, xa=xa, n=wl.n):
                         return R.rld_bgmv_expand_fold(rt.route, xa, seq, n, out, c.out_row_stride)
 
-                    self.calls.append((f"{tag}.{c.module}.shrink", "bgmv_shrink_kernel", shrink,
+                    self.calls.append((f"{tag}.{c.module}.shrink", BGMV_SHRINK, shrink,
                                        sb, fl / 2, wl.n))
                     self.calls.append((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", expand,
+                                       eb, fl / 2, 0))
+                    self.rows += wl.n
+            elif tag == "lora":
+                bufs = {k: to_device_u16(v, dev) for k, v in wl.buffers.items()}
+                rmax = max(c.max_rank for c in wl.calls)
+                xa = torch.zeros(wl.n * rmax + 8, dtype=torch.int16, device=dev)
+                wsb = max(R.rld_lora_workspace_bytes(wl.n, c.k_in, c.max_rank) for c in wl.calls)
+                ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+                keep += [bufs, xa, ws]
+                for c in wl.calls:
+                    sp = SinglePair(c.adapters[0], c.max_rank, c.k_in, c.n_out, dev)
+                    keep.append(sp)
+                    sb, eb, fl, _ = bgmv_bytes(wl, c)
+                    x = bufs[c.x_buf].data_ptr()
+                    out = bufs[c.out_buf].data_ptr() + 2 * c.out_offset
+
+                    def lshrink(sp=sp, c=c, x=x, xa=xa, ws=ws, wsb=wsb, m=wl.n):
+                        return R.rld_lora_shrink(sp.pair, x, c.x_row_stride, m, xa, ws, wsb)
+
+                    def lexpand(sp=sp, c=c, out=out, xa=xa, m=wl.n):
+                        return R.rld_lora_expand_fold(sp.pair, xa, m, out, c.out_row_stride)
+
+                    self.calls.append((f"{tag}.{c.module}.shrink", BGMV_SHRINK, lshrink, sb,
+                                       fl / 2, wl.n))
+                    self.calls.append((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", lexpand,
                                        eb, fl / 2, 0))
                     self.rows += wl.n
             elif tag == "gather":
@@ -348,6 +373,8 @@ def select_workloads(name):
         out.append(("gather", W.moe_gather()))
     if name in ("step", "grouped"):
         out.append(("grouped", W.moe_grouped()))
+    if name == "lora":
+        out.append(("lora", W.lora_prefill()))
     return out
 
 
@@ -359,7 +386,13 @@ WORKLOAD_NAMES = {
     "ffn": "ffn-decode BGMV gate/up/down n=256 4096x12288 r64 L32",
     "gather": "MoE gather down 32 tokens top8 E128 768->2048 r16 L8",
     "grouped": "MoE grouped down/gate/up 4096 tokens top8 E128 te=32768 cap=8192 r32 L4",
+    "lora": "unrouted single adapter, prefill m=4096, FFN gate/up 4096->12288, down "
+            "12288->4096, r64",
 }
+
+# The BGMV shrink entry point is two launches when k_in is split (the shrink,
+# then the chunk reduce); the bench times the pair as one entry.
+BGMV_SHRINK = "bgmv_shrink_kernel+bgmv_reduce_kernel"
 
 
 def _timed_eager(step, idx, lead_graph, steps, torch):
@@ -425,7 +458,7 @@ def copy_calibration(torch, dev):
     torch.cuda.empty_cache()
 
 
-def run_gpu(args):
+def run_gpu(args, traffic=True):
     import torch
 
     dev = torch.device("cuda:0")
@@ -494,7 +527,7 @@ def run_gpu(args):
     avg_launch_s = dom["ms"] / dom["launches"] * 1e-3
     bytes_per_launch = dom["bytes"] / dom["launches"]
     achieved = bytes_per_launch / avg_launch_s / 1e9
-    traffic = measured_traffic(dom_name)
+    traffic = measured_traffic(dom_name) if traffic else None
 
     per_workload = {}
     for tag, _ in wls:
@@ -593,6 +626,8 @@ def main():
                     help="sorted rows per grouped projection in the cpu_baseline sample "
                          "(the default covers the whole step)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-unrouted", action="store_true",
+                    help="with the default step: skip the separate unrouted-path measurement")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="print a markdown summary of rocprofv3 output directories and exit")
     ap.add_argument("--bench-json", help="with --summarize: a bench.py output line to include")
@@ -634,6 +669,20 @@ def main():
         "kernels": g["kernels"],
         "per_workload": g["per_workload"],
     }
+    if args.workload == "step" and not args.no_unrouted:
+        # The unrouted single-adapter path (apply_lora_delta), measured the same
+        # way on its own prefill workload; not part of the step or of `value`.
+        ua = argparse.Namespace(**{**vars(args), "workload": "lora", "copy_calibration": False})
+        u = run_gpu(ua, traffic=False)
+        ugbs = u["bytes"] / (u["ms_per_step"] * 1e-3) / 1e9
+        line["unrouted"] = {
+            "workload": WORKLOAD_NAMES["lora"], "ms_per_pass": round(u["ms_per_step"], 5),
+            "rows_per_pass": u["rows"], "rows_per_s": round(u["rows"] / (u["ms_per_step"] * 1e-3), 1),
+            "algo_bytes_per_pass": int(u["bytes"]), "hbm_gbs": round(ugbs, 1),
+            "hbm_frac": round(ugbs / HBM_PEAK_GBS, 4),
+            "mfma_util": round(u["flops"] / (u["ms_per_step"] * 1e-3) / 1e12
+                               / BF16_MFMA_PEAK_TFLOPS, 5),
+            "roofline": u["roofline"], "kernels": u["kernels"]}
     print(json.dumps(line), flush=True)
 
 

@@ -276,6 +276,32 @@ def bgmv_ffn_decode(seed_index: int = 2, n: int = 256, hidden: int = 4096,
                         buffers, calls)
 
 
+def lora_prefill(seed_index: int = 5, m: int = 4096, hidden: int = 4096, inter: int = 12288,
+                 rank: int = 64, alpha: float = 32.0) -> BgmvWorkload:
+    """Unrouted single adapter over a prefill batch (the apply_lora_delta path):
+    m tokens through the FFN of Qwen3-8B shapes, gate/up hidden->inter and down
+    inter->hidden, one adapter of rank 64 (scale alpha/r) on slot 0.  Every row
+    uses the adapter (seq_slot is all zero, for the routed comparison)."""
+    rng = rng_for(seed_index)
+    calls = []
+    for module, k_in, n_out, xbuf, obuf in (
+        ("gate", hidden, inter, "h", "gate_out"),
+        ("up", hidden, inter, "h", "up_out"),
+        ("down", inter, hidden, "act", "down_out"),
+    ):
+        ad = [make_adapter(rng, 0, rank, k_in, n_out, alpha, False)]
+        calls.append(BgmvCall(module, k_in, n_out, rank, 1, ad, xbuf, k_in, obuf, 0, n_out))
+    buffers = {
+        "h": _normal(rng, (m, hidden)).ravel(),
+        "act": _normal(rng, (m, inter)).ravel(),
+        "gate_out": _normal(rng, (m, inter)).ravel(),
+        "up_out": _normal(rng, (m, inter)).ravel(),
+        "down_out": _normal(rng, (m, hidden)).ravel(),
+    }
+    return BgmvWorkload(f"unrouted prefill m={m} {hidden}->{inter}->{hidden} r{rank}", m,
+                        np.zeros(m, np.int32), buffers, calls)
+
+
 # ---------------------------------------------------------------------------
 # MoE workloads
 # ---------------------------------------------------------------------------
