@@ -671,6 +671,25 @@ static void launch_gs(const GsArgs& a, uint32_t grid, hipStream_t st) {
   hipLaunchKernelGGL((grouped_shrink_kernel<KS, NT>), dim3(grid), dim3(kGsThreads), 0, st, a);
 }
 
+template <int KS>
+static void launch_gs_nt(uint32_t nt, const GsArgs& a, uint32_t grid, hipStream_t st) {
+  switch (nt) {
+    case 1: launch_gs<KS, 1>(a, grid, st); break;
+    case 2: launch_gs<KS, 2>(a, grid, st); break;
+    default: launch_gs<KS, 4>(a, grid, st); break;
+  }
+}
+
+// KS = chunk / 128 (MFMA steps per wave), one of the chunk lengths grouped_chunk gives.
+static void launch_gs_ks(uint32_t ks, uint32_t nt, const GsArgs& a, uint32_t grid, hipStream_t st) {
+  switch (ks) {
+    case 2: launch_gs_nt<2>(nt, a, grid, st); break;
+    case 4: launch_gs_nt<4>(nt, a, grid, st); break;
+    case 6: launch_gs_nt<6>(nt, a, grid, st); break;
+    default: launch_gs_nt<8>(nt, a, grid, st); break;
+  }
+}
+
 }  // namespace rld
 
 using namespace rld;
@@ -726,12 +745,7 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
       (uint64_t)route->max_loras * route->num_experts * a.nch * a.ncg + a.nz;
   const uint32_t grid = (uint32_t)(items < kGsGrid ? items : kGsGrid);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const bool k4 = a.kc == 512u;
-  switch (nt) {
-    case 1: k4 ? launch_gs<4, 1>(a, grid, hs) : launch_gs<2, 1>(a, grid, hs); break;
-    case 2: k4 ? launch_gs<4, 2>(a, grid, hs) : launch_gs<2, 2>(a, grid, hs); break;
-    default: k4 ? launch_gs<4, 4>(a, grid, hs) : launch_gs<2, 4>(a, grid, hs); break;
-  }
+  launch_gs_ks(a.kc / 128u, nt, a, grid, hs);
   return launch_status();
 }
 

@@ -70,9 +70,13 @@ inline uint32_t xcd_group_grid(uint32_t total, uint32_t group) {
 }
 
 // k chunk of the MoE grouped shrink, a function of k_in only (so a row's
-// summation order never depends on its window): four waves x 64 k (256) up to
-// k_in = 1024, four waves x 128 k (512) above.
-inline uint32_t grouped_chunk(uint32_t k_in) { return k_in <= 1024u ? 256u : 512u; }
+// summation order never depends on its window): up to k_in = 1024 the whole of
+// k_in in one chunk of 512, 768 or 1024 (no partials, no reduce), above that
+// chunks of 512 (four waves x 128 k).
+inline uint32_t grouped_chunk(uint32_t k_in) {
+  if (k_in > 1024u) return 512u;
+  return k_in <= 512u ? 512u : (k_in <= 768u ? 768u : 1024u);
+}
 
 // 16-column MFMA tiles of xa held by one grouped shrink item (1, 2 or 4).
 inline uint32_t grouped_nt(uint32_t max_rank) {

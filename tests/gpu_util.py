@@ -71,7 +71,7 @@ def shrink_depth(path: str, k_in: int, max_rank: int) -> int:
         steps = -(-kc // 32)
         return 32 + -(-steps // 4) + 4 + nch
     if path == "grouped":
-        kc = 256 if k_in <= 1024 else 512
+        kc = 512 if k_in > 1024 else (512 if k_in <= 512 else (768 if k_in <= 768 else 1024))
         return 32 + kc // 128 + 4 + -(-k_in // kc)
     if path == "gather":
         return 8 * -(-k_in // 512) + 6

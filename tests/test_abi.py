@@ -300,9 +300,10 @@ def test_grouped_workspace_contract():
         R.RLD_ENOSPACE
     assert R.rld_moe_grouped(mr, FAKE, 2048, 1, 4096, FAKE, 128, FAKE, FAKE, 0, 8192, FAKE, 768,
                              FAKE, 8192, FAKE, need - 16, 0) == R.RLD_ENOSPACE
-    # up to k_in = 1024 the chunks are 256 wide; one chunk needs no workspace
-    assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 4, 128) == \
-        3 * 8192 * 32 * 4 + 16 * 4 * 128
+    # up to k_in = 1024 the whole of k_in is one chunk: no workspace
+    assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 4, 128) == 0
+    assert R.rld_moe_grouped_workspace_bytes(8192, 1024, 32, 4, 128) == 0
+    assert R.rld_moe_grouped_workspace_bytes(64, 1032, 16, 2, 8) == 3 * 64 * 16 * 4 + 16 * 2 * 8
     assert R.rld_moe_grouped_workspace_bytes(64, 4096, 16, 2, 8) == 8 * 64 * 16 * 4 + 16 * 2 * 8
     assert R.rld_moe_grouped_workspace_bytes(8192, 256, 32, 4, 128) == 0
     assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 0, 128) == 0

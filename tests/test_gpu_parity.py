@@ -334,10 +334,11 @@ def test_moe_grouped_edge_windows():
 @pytest.mark.parametrize("max_loras", [1, 2])
 def test_moe_grouped_long_pairs(max_loras):
     """Pairs with hundreds of rows in one window: 64-row batches, and with one
-    slot more than one scan segment (the chunk reduce rescans the span), in
-    one full window and in windows of 700 rows."""
+    slot more than one scan segment (the chunk reduce rescans the span; gate's
+    k_in = 2056 splits into 5 chunks), in one full window and in windows of 700
+    rows."""
     dev = require_gpu()
-    wl = W.moe_grouped(9, num_tokens=1200, top_k=2, num_experts=4, hidden=520, inter=264,
+    wl = W.moe_grouped(9, num_tokens=1200, top_k=2, num_experts=4, hidden=2056, inter=264,
                        max_loras=max_loras, n_adapted=4, ranks=(8, 16, 32), max_rank=32,
                        cap=2400, projections=("down", "gate"))
     ra = None if max_loras == 1 else "wl"
@@ -357,12 +358,12 @@ def test_moe_grouped_long_pairs(max_loras):
 
 
 def test_moe_grouped_graph_replays():
-    """Every window of a projection (k split over 3 chunks) captured in one HIP
-    graph: each replay, with eager work and synchronisations between, gives
-    the eager calls' bits, and the per-pair counters at the end of the
-    workspace are back at zero after each."""
+    """Every window of a projection (k split over 5 chunks, the last one ragged)
+    captured in one HIP graph: each replay, with eager work and
+    synchronisations between, gives the eager calls' bits, and the per-pair
+    counters at the end of the workspace are back at zero after each."""
     dev = require_gpu()
-    wl = _small_grouped(projections=("gate",))
+    wl = _small_grouped(projections=("gate",), hidden=2056)
     p = wl.projections[0]
     say("case: grouped graph replays")
     eager = GroupedRun(wl, p, dev)
