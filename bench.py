@@ -9,9 +9,15 @@ inputs shaped like the routed-LoRA workloads:
                           8192; down 768->2048 and gate/up 2048->768 (x gather)
 Every call goes through librld.so's C ABI on torch's current stream.
 
+The step graph keeps a layer's dependencies: the q, k and v folds (and the gate
+and up folds, dense or MoE) read the same input and write different outputs,
+so they are captured on parallel branches (each with its own xa and
+workspace); o follows q/k/v and down follows gate/up.
+
 Timing.  The step is captured once as a HIP graph; timed region A replays it K
 times back to back and its wall clock gives ms_per_step and the value.  Timed
-regions B and C time every call with HIP events on the launch stream: the
+regions B and C time every call, one at a time, with HIP events on the launch
+stream (their sum is ms_per_step_calls): the
 grouped-window calls are issued eagerly, each between two events, right after
 a replay of the captured BGMV+gather part (region B), and the BGMV and gather
 calls the same way after a replay of the captured grouped part (region C), so
@@ -213,8 +219,21 @@ def summarize(dirs, bench_json=None):
 
 # ------------------------------------------------------------------ GPU side --
 
+# Independent calls of one step and the order of their groups: in a layer, the
+# q, k and v folds (and the gate and up folds) read the same input and write
+# different outputs, so they run on parallel branches of the step's graph; o
+# follows q/k/v, down follows gate/up.  Module -> (group within its workload,
+# lane).  Calls of one module keep one lane (its shrink feeds its expand).
+LANES = {"q": (0, 0), "k": (0, 1), "v": (0, 2), "o": (1, 0),
+         "gate": (0, 0), "up": (0, 1), "down": (1, 0)}
+MAX_LANES = 3
+
+
 class Step:
-    """Device state of the whole step and the ordered list of its calls."""
+    """Device state of the whole step and the ordered list of its calls.  Every
+    call has a (group, lane): calls of one group on different lanes are
+    independent and run on parallel branches of the captured step (each lane
+    has its own xa and workspace); groups run in order."""
 
     def __init__(self, dev, workloads):
         import torch
@@ -224,64 +243,63 @@ class Step:
 
         self.R, self.torch = R, torch
         self.calls = []  # (label, kernel name, fn, algorithmic bytes, flops, rows)
+        self.sched = []  # (group, lane) of each call
         self.rows = 0
         keep = []
+        group0 = 0
 
         def i32(a):
             return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
 
+        def add(call, module):
+            g, lane = LANES.get(module, (0, 0))
+            self.calls.append(call)
+            self.sched.append((group0 + g, lane))
+
         for tag, wl in workloads:
-            if tag in ("attn", "ffn"):
+            if tag in ("attn", "ffn", "lora"):
                 seq = i32(wl.seq_slot)
                 bufs = {k: to_device_u16(v, dev) for k, v in wl.buffers.items()}
                 rmax = max(c.max_rank for c in wl.calls)
-                xa = torch.zeros(wl.n * rmax + 8, dtype=torch.int16, device=dev)
-                wsb = max(R.rld_bgmv_workspace_bytes(wl.n, c.k_in, c.max_rank, c.max_loras)
-                          for c in wl.calls)
-                ws = torch.zeros(max(wsb, 16) // 4 + 4, dtype=torch.float32, device=dev)
-                keep += [seq, bufs, xa, ws]
+                if tag == "lora":
+                    wsb = max(R.rld_lora_workspace_bytes(wl.n, c.k_in, c.max_rank)
+                              for c in wl.calls)
+                else:
+                    wsb = max(R.rld_bgmv_workspace_bytes(wl.n, c.k_in, c.max_rank, c.max_loras)
+                              for c in wl.calls)
+                lanes = [(torch.zeros(wl.n * rmax + 8, dtype=torch.int16, device=dev),
+                          torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev))
+                         for _ in range(MAX_LANES)]
+                keep += [seq, bufs, lanes]
                 for c in wl.calls:
-                    rt = DenseRoute(c.adapters, c.max_loras, c.max_rank, c.k_in, c.n_out, dev)
-                    keep.append(rt)
+                    xa, ws = lanes[LANES.get(c.module, (0, 0))[1]]
                     sb, eb, fl, _ = bgmv_bytes(wl, c)
                     x = bufs[c.x_buf].data_ptr()
                     out = bufs[c.out_buf].data_ptr() + 2 * c.out_offset
+                    if tag == "lora":
+                        sp = SinglePair(c.adapters[0], c.max_rank, c.k_in, c.n_out, dev)
+                        keep.append(sp)
 
-                    def shrink(rt=rt, c=c, x=x, seq=seq, xa=xa, ws=ws, wsb=wsb, n=wl.n):
-                        return R.rld_bgmv_shrink(rt.route, x, c.x_row_stride, seq, n, xa, ws, wsb)
+                        def shrink(sp=sp, c=c, x=x, xa=xa, ws=ws, wsb=wsb, m=wl.n):
+                            return R.rld_lora_shrink(sp.pair, x, c.x_row_stride, m, xa, ws, wsb)
 
-                    def expand(rt=rt, c=c, out=out, seq=seq, xa=xa, n=wl.n):
-                        return R.rld_bgmv_expand_fold(rt.route, xa, seq, n, out, c.out_row_stride)
+                        def expand(sp=sp, c=c, out=out, xa=xa, m=wl.n):
+                            return R.rld_lora_expand_fold(sp.pair, xa, m, out, c.out_row_stride)
+                    else:
+                        rt = DenseRoute(c.adapters, c.max_loras, c.max_rank, c.k_in, c.n_out, dev)
+                        keep.append(rt)
 
-                    self.calls.append((f"{tag}.{c.module}.shrink", BGMV_SHRINK, shrink,
-                                       sb, fl / 2, wl.n))
-                    self.calls.append((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", expand,
-                                       eb, fl / 2, 0))
-                    self.rows += wl.n
-            elif tag == "lora":
-                bufs = {k: to_device_u16(v, dev) for k, v in wl.buffers.items()}
-                rmax = max(c.max_rank for c in wl.calls)
-                xa = torch.zeros(wl.n * rmax + 8, dtype=torch.int16, device=dev)
-                wsb = max(R.rld_lora_workspace_bytes(wl.n, c.k_in, c.max_rank) for c in wl.calls)
-                ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
-                keep += [bufs, xa, ws]
-                for c in wl.calls:
-                    sp = SinglePair(c.adapters[0], c.max_rank, c.k_in, c.n_out, dev)
-                    keep.append(sp)
-                    sb, eb, fl, _ = bgmv_bytes(wl, c)
-                    x = bufs[c.x_buf].data_ptr()
-                    out = bufs[c.out_buf].data_ptr() + 2 * c.out_offset
+                        def shrink(rt=rt, c=c, x=x, seq=seq, xa=xa, ws=ws, wsb=wsb, n=wl.n):
+                            return R.rld_bgmv_shrink(rt.route, x, c.x_row_stride, seq, n, xa, ws,
+                                                     wsb)
 
-                    def lshrink(sp=sp, c=c, x=x, xa=xa, ws=ws, wsb=wsb, m=wl.n):
-                        return R.rld_lora_shrink(sp.pair, x, c.x_row_stride, m, xa, ws, wsb)
-
-                    def lexpand(sp=sp, c=c, out=out, xa=xa, m=wl.n):
-                        return R.rld_lora_expand_fold(sp.pair, xa, m, out, c.out_row_stride)
-
-                    self.calls.append((f"{tag}.{c.module}.shrink", BGMV_SHRINK, lshrink, sb,
-                                       fl / 2, wl.n))
-                    self.calls.append((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", lexpand,
-                                       eb, fl / 2, 0))
+                        def expand(rt=rt, c=c, out=out, seq=seq, xa=xa, n=wl.n):
+                            return R.rld_bgmv_expand_fold(rt.route, xa, seq, n, out,
+                                                          c.out_row_stride)
+                    add((f"{tag}.{c.module}.shrink", BGMV_SHRINK, shrink, sb, fl / 2, wl.n),
+                        c.module)
+                    add((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", expand, eb, fl / 2, 0),
+                        c.module)
                     self.rows += wl.n
             elif tag == "gather":
                 rt = MoeRoute(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank, wl.k_in,
@@ -293,6 +311,7 @@ class Step:
                 xa = torch.zeros(wl.n_rows * wl.max_rank + 8, dtype=torch.int16, device=dev)
                 keep += [rt, x, base, idx, rad, xa]
                 sb, eb, fl, _ = gather_bytes(wl)
+
                 def gshrink(rt=rt, x=x, idx=idx, rad=rad, xa=xa, wl=wl):
                     return R.rld_moe_gather_shrink(rt.route, x, wl.k_in, idx, rad, wl.top_k,
                                                    wl.n_rows, xa)
@@ -300,30 +319,33 @@ class Step:
                 def gexpand(rt=rt, base=base, idx=idx, rad=rad, xa=xa, wl=wl):
                     return R.rld_moe_gather_expand_fold(rt.route, xa, idx, rad, wl.top_k,
                                                         wl.n_rows, base, wl.n_out)
-                self.calls.append(("gather.down.shrink", "gather_shrink_kernel", gshrink, sb,
-                                   fl / 2, wl.n_rows))
-                self.calls.append(("gather.down.expand", "gather_expand_kernel", gexpand, eb,
-                                   fl / 2, 0))
+                add(("gather.down.shrink", "gather_shrink_kernel", gshrink, sb, fl / 2,
+                     wl.n_rows), "")
+                add(("gather.down.expand", "gather_expand_kernel", gexpand, eb, fl / 2, 0), "")
                 self.rows += wl.n_rows
             elif tag == "grouped":
                 off = i32(wl.expert_offsets)
                 stid = i32(wl.sorted_token_ids)
                 rad = i32(wl.row_adapter)
-                xa = torch.zeros(wl.cap * wl.max_rank + 8, dtype=torch.int16, device=dev)
-                # one workspace for every projection and window (sized for the largest)
+                # per lane: xa, and a workspace for every projection and window of
+                # the lane (sized for the largest)
                 wsb = max(R.rld_moe_grouped_workspace_bytes(wl.cap, p.k_in, wl.max_rank,
                                                             wl.max_loras, wl.num_experts)
                           for p in wl.projections)
-                ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
-                keep += [off, stid, rad, xa, ws]
+                lanes = [(torch.zeros(wl.cap * wl.max_rank + 8, dtype=torch.int16, device=dev),
+                          torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev))
+                         for _ in range(MAX_LANES)]
+                keep += [off, stid, rad, lanes]
                 wins = [(k * wl.cap, min((k + 1) * wl.cap, wl.te))
                         for k in range(-(-wl.te // wl.cap))]
-                for p in wl.projections:
+                order = {"gate": 0, "up": 1, "down": 2}
+                for p in sorted(wl.projections, key=lambda q: order.get(q.name, 3)):
                     rt = MoeRoute(p.adapters, wl.max_loras, wl.num_experts, wl.max_rank, p.k_in,
                                   p.n_out, dev)
                     x = to_device_u16(p.x.ravel(), dev)
                     base = to_device_u16(p.base.ravel(), dev)
                     keep += [rt, x, base]
+                    xa, ws = lanes[LANES.get(p.name, (0, 0))[1]]
                     for lo, hi in wins:
                         sb, eb, fl, _ = grouped_window_bytes(wl, p, lo, hi)
 
@@ -340,14 +362,48 @@ class Step:
                                                                  wl.num_experts, stid, rad, lo,
                                                                  hi, base, p.n_out)
 
-                        self.calls.append((f"grouped.{p.name}.[{lo},{hi}).shrink",
-                                           "grouped_shrink_kernel", shrink, sb, fl / 2, hi - lo))
-                        self.calls.append((f"grouped.{p.name}.[{lo},{hi}).expand",
-                                           "grouped_expand_kernel", expand, eb, fl / 2, 0))
+                        add((f"grouped.{p.name}.[{lo},{hi}).shrink", "grouped_shrink_kernel",
+                             shrink, sb, fl / 2, hi - lo), p.name)
+                        add((f"grouped.{p.name}.[{lo},{hi}).expand", "grouped_expand_kernel",
+                             expand, eb, fl / 2, 0), p.name)
                     self.rows += wl.te
+            group0 = max((g for g, _ in self.sched), default=-1) + 1
         self._keep = keep
         self.bytes = sum(c[3] for c in self.calls)
         self.flops = sum(c[4] for c in self.calls)
+
+    def capture(self, idx, stream, parallel=True):
+        """One HIP graph of the calls idx (in order), captured on `stream`: each
+        group forks its lanes onto side streams and joins them before the next
+        group starts (parallel=False: every call on `stream`, in order)."""
+        torch = self.torch
+        side = [None] + [torch.cuda.Stream() for _ in range(MAX_LANES - 1)]
+        idx = list(idx)
+        g = torch.cuda.CUDAGraph()
+        if not parallel:
+            with torch.cuda.graph(g, stream=stream):
+                for i in idx:
+                    if self.calls[i][2]() != 0:
+                        raise RuntimeError("call failed during capture: " + self.calls[i][0])
+            return g
+        with torch.cuda.graph(g, stream=stream):
+            groups = sorted({self.sched[i][0] for i in idx})
+            for grp in groups:
+                members = [i for i in idx if self.sched[i][0] == grp]
+                lanes = sorted({self.sched[i][1] for i in members})
+                for ln in lanes:
+                    if ln:
+                        side[ln].wait_stream(stream)
+                for ln in lanes:
+                    with torch.cuda.stream(stream if ln == 0 else side[ln]):
+                        for i in members:
+                            if self.sched[i][1] == ln and self.calls[i][2]() != 0:
+                                raise RuntimeError("call failed during capture: "
+                                                   + self.calls[i][0])
+                for ln in lanes:
+                    if ln:
+                        stream.wait_stream(side[ln])
+        return g
 
     def enqueue(self, events=None):
         """Issue every call on the current stream; events[i] is recorded before
@@ -477,19 +533,18 @@ def run_gpu(args, traffic=True):
 
     cap_stream = torch.cuda.Stream()
 
-    def capture(idx):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap_stream):
-            for i in idx:
-                if step.calls[i][2]() != 0:
-                    raise RuntimeError("call failed during capture")
-        return g
+    def capture(idx, parallel=False):
+        return step.capture(idx, cap_stream, parallel)
 
-    full = capture(range(ncalls))
+    # the step as timed (independent calls on parallel branches), and sequential
+    # captures that keep the GPU busy ahead of the per-call and per-kernel timing
+    full = capture(range(ncalls), parallel=True)
+    full_seq = capture(range(ncalls))
     g_other = capture(other) if other else None
     g_grouped = capture(grouped) if grouped else None
     for _ in range(3):
         full.replay()
+        full_seq.replay()
     torch.cuda.synchronize()
 
     # timed region A: K replays of the whole step, back to back
@@ -511,7 +566,7 @@ def run_gpu(args, traffic=True):
     seg_ms = per_call_ms
     # timed region D: each kernel's launches back to back (per-launch durations
     # for the kernel table and the roofline)
-    kernel_ms = _timed_by_kernel(step, full, args.steps, torch)
+    kernel_ms = _timed_by_kernel(step, full_seq, args.steps, torch)
 
     ms_per_step = wall * 1e3 / args.steps
     # per kernel: launches, algorithmic bytes and flops per step, mean launch time
