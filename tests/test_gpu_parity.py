@@ -533,3 +533,76 @@ def test_lora_delta_equals_routed_and_single_rows():
         torch.cuda.synchronize()
         assert np.array_equal(routed.xa_host(), xa_full)
         assert np.array_equal(routed.base.body(), out_full)
+
+
+# ------------------------------------------------------------ graph safety ---
+
+def test_bgmv_graph_new_routing_each_replay():
+    """The graph-safe contract: rld_bgmv is captured once, and before every
+    replay new seq_slot contents (including out-of-range slots) are written into
+    the same device buffer.  Each replay meets the oracle for its own routing."""
+    dev = require_gpu()
+    import dataclasses
+    wl = W.bgmv_custom(31, 96, 4096, 1032, 16, 8, (8, 16), base_frac=0.1)
+    say("case: bgmv graph, new seq_slot per replay")
+    run = BgmvRun(wl, dev)
+    pristine = run.bufs["out"].t.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run.run_call(0, stream=s)
+    rng = np.random.default_rng(77)
+    for rep in range(4):
+        seq = rng.integers(-2, 10, size=wl.n).astype(np.int32)  # 8, 9: beyond max_loras
+        run.seq.copy_(torch.from_numpy(seq))
+        run.bufs["out"].t.copy_(pristine)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        run.wl = dataclasses.replace(wl, seq_slot=seq)
+        run.xa_by_call = [from_device_u16(run.xa)[: wl.n * 16].reshape(wl.n, 16).copy()]
+        compare_bgmv(run, f"replay {rep}")
+        _base_rows_xa_zero(run.wl, run)
+
+
+def test_grouped_graph_new_routing_each_replay():
+    """The same for the grouped fold: every window of a projection (k split)
+    captured once; before every replay the device expert_offsets,
+    sorted_token_ids and row_adapter buffers get the routing of a different
+    batch of the same size.  Each replay meets the oracle for its routing."""
+    dev = require_gpu()
+    wl = _small_grouped(projections=("gate",), hidden=2056)
+    p = wl.projections[0]
+    say("case: grouped graph, new routing per replay")
+    run = GroupedRun(wl, p, dev)
+    pristine = run.base.t.clone()
+    wins = O.grouped_down_windows(wl.te, wl.cap)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for lo, hi in wins:
+            R.check(R.rld_moe_grouped(run.route.route, run.x, p.k_in, p.x_gather, wl.num_tokens,
+                                      run.off, wl.num_experts, run.stid, run.rad, lo, hi,
+                                      run.base.ptr(), p.n_out, run.xa, run.cap, run.ws,
+                                      run.ws_bytes, s), "captured rld_moe_grouped")
+    for rep, seed in enumerate((41, 42, 43)):
+        other = _small_grouped(seed=seed, projections=("gate",), hidden=2056)
+        assert other.te == wl.te and other.num_experts == wl.num_experts
+        run.off.copy_(torch.from_numpy(other.expert_offsets.astype(np.int32)))
+        run.stid.copy_(torch.from_numpy(other.sorted_token_ids.astype(np.int32)))
+        run.rad.copy_(torch.from_numpy(other.row_adapter.astype(np.int32)))
+        run.base.t.copy_(pristine)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        # the new routing over this workload's adapters, x and base rows
+        wl2 = W.MoeGroupedWorkload(**{**wl.__dict__, "expert_offsets": other.expert_offsets,
+                                      "sorted_token_ids": other.sorted_token_ids,
+                                      "row_adapter": other.row_adapter,
+                                      "sorted_expert": other.sorted_expert})
+        base = p.base.ravel().copy()
+        for lo, hi in wins:
+            _, base = oracle_grouped_window(wl2, p, lo, hi, base)
+        assert_out_close(run.base.body(), base, f"grouped replay {rep}")
