@@ -120,6 +120,14 @@ typedef struct rld_adapter_entry {
  * float.  RLD_EINVAL if rank == 0 or out is NULL. */
 int rld_scale(float alpha, uint32_t rank, int use_rslora, float* out);
 
+/* Adapter install, PEFT tensors stored as F16 ("Module lora_delta": A/B kept
+ * verbatim, converted F16 -> BF16 on the host at load): dst[i] = the BF16
+ * value nearest to the F16 value src[i], ties to even.  Every F16 value is in
+ * BF16's normal range, so only the significand is rounded; +-0 and +-Inf are
+ * kept, a NaN becomes a quiet NaN with its sign.  Host memory, bit patterns;
+ * src and dst may be the same array.  RLD_EINVAL on NULL with n > 0. */
+int rld_f16_to_bf16_host(const uint16_t* src, uint16_t* dst, size_t n);
+
 /* Pool layout of one PEFT pair ("Module lora_delta", LoraPair; lora_delta.rs
  * header invariants): a [rank, k_in] -> a_pad [max_rank, k_in] with zero rows
  * after rank; b [n_out, rank] -> b_pad [n_out, max_rank] with zero columns

@@ -119,6 +119,13 @@ def round_bf16(v) -> np.ndarray:
 # adapter pack (install time)
 # ---------------------------------------------------------------------------
 
+def f16_to_bf16(bits) -> np.ndarray:
+    """Adapter install ("Module lora_delta": PEFT tensors converted F16 -> BF16 on
+    the host): the F16 value (numpy's float16 decoding, exact in float64)
+    rounded to BF16 by round_bf16."""
+    return round_bf16(np.asarray(bits, np.uint16).view(np.float16).astype(np.float64))
+
+
 def scale_for(alpha: float, rank: int, use_rslora: bool) -> np.float32:
     """LoraPair scale: lora_alpha / r, or lora_alpha / sqrt(r) under use_rslora
     (lora_delta.rs listing, LoraPair doc comment).  Computed in double and

@@ -93,6 +93,7 @@ _SIGS = {
     "rld_bgmv_shrink": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
     "rld_bgmv_expand_fold": (c_int, [_R, _P, _P, c_uint32, _P, c_uint32, _P]),
     "rld_bgmv": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
+    "rld_f16_to_bf16_host": (c_int, [_P, _P, c_size_t]),
     "rld_lora_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32]),
     "rld_lora_shrink": (c_int, [_L, _P, c_uint32, c_uint32, _P, _P, c_size_t, _P]),
     "rld_lora_expand_fold": (c_int, [_L, _P, c_uint32, _P, c_uint32, _P]),
@@ -235,6 +236,11 @@ def rld_bgmv(route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, xa, 
     return _lib.rld_bgmv(ctypes.byref(route), ptr(x), x_row_stride, ptr(seq_slot), n,
                          ptr(base_out), out_row_stride, ptr(xa), ptr(workspace), workspace_bytes,
                          stream_handle(stream))
+
+
+def rld_f16_to_bf16_host(src, dst, n):
+    """src, dst: host uint16 numpy arrays (F16 bits in, BF16 bits out)."""
+    return _lib.rld_f16_to_bf16_host(src.ctypes.data, dst.ctypes.data, n)
 
 
 def rld_lora_workspace_bytes(m, k_in, max_rank):

@@ -31,6 +31,39 @@ extern "C" int rld_scale(float alpha, uint32_t rank, int use_rslora, float* out)
   return RLD_OK;
 }
 
+// F16 -> F32, exact: F32 has more exponent and significand bits than F16,
+// and F16 subnormals are F32 normals.
+static uint32_t f16_bits_to_f32_bits(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1fu;
+  uint32_t m = h & 0x3ffu;
+  if (e == 0x1fu) return sign | 0x7f800000u | (m << 13);  // Inf, NaN (payload kept)
+  if (e != 0) return sign | ((e + 112u) << 23) | (m << 13);
+  if (m == 0) return sign;  // +-0
+  // subnormal m * 2^-24: shift the leading one to bit 10
+  int p = 0;
+  while (!(m & 0x400u)) {
+    m <<= 1;
+    ++p;
+  }
+  return sign | ((uint32_t)(113 - p) << 23) | ((m & 0x3ffu) << 13);
+}
+
+// F32 bits -> BF16 bits, round to nearest on the 16 dropped bits, ties to
+// even; NaN -> quiet NaN with the sign kept.
+static uint16_t f32_bits_to_bf16(uint32_t u) {
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu))
+    return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+  const uint32_t lsb = (u >> 16) & 1u;
+  return (uint16_t)((u + 0x7fffu + lsb) >> 16);
+}
+
+extern "C" int rld_f16_to_bf16_host(const uint16_t* src, uint16_t* dst, size_t n) {
+  if (n && (!src || !dst)) return RLD_EINVAL;
+  for (size_t i = 0; i < n; ++i) dst[i] = f32_bits_to_bf16(f16_bits_to_f32_bits(src[i]));
+  return RLD_OK;
+}
+
 extern "C" int rld_pad_adapter_host(const uint16_t* a, const uint16_t* b, uint32_t rank,
                                     uint32_t k_in, uint32_t n_out, uint32_t max_rank,
                                     uint16_t* a_pad, uint16_t* b_pad) {

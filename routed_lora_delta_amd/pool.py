@@ -15,14 +15,35 @@ from typing import Sequence
 import numpy as np
 import torch
 
-from . import (check, rld_adapter_entry, rld_moe_route, rld_moe_tables_pack, rld_pair,
-               rld_pad_adapter_host, rld_route, rld_route_pack)
+from . import (check, rld_adapter_entry, rld_f16_to_bf16_host, rld_moe_route,
+               rld_moe_tables_pack, rld_pad_adapter_host, rld_pair, rld_route, rld_route_pack,
+               rld_scale)
 
 _ALIGN_ELEMS = 128  # 256 bytes of BF16
 
 
 def _round_up(v: int, a: int) -> int:
     return (v + a - 1) // a * a
+
+
+def install_peft_pair(a_f16: np.ndarray, b_f16: np.ndarray, rank: int, k_in: int, n_out: int,
+                      max_rank: int, alpha: float, use_rslora: bool):
+    """Host side of installing one PEFT module stored as F16 (lora_A [rank,
+    k_in], lora_B [n_out, rank]): F16 -> BF16 (rld_f16_to_bf16_host), padded to
+    the pool layout (rld_pad_adapter_host) and the fp32 scale (rld_scale).
+    Returns (A [max_rank, k_in], B [n_out, max_rank] BF16 bits, scale)."""
+    a16 = np.ascontiguousarray(a_f16, np.uint16).reshape(rank, k_in)
+    b16 = np.ascontiguousarray(b_f16, np.uint16).reshape(n_out, rank)
+    a_bf, b_bf = np.empty_like(a16), np.empty_like(b16)
+    check(rld_f16_to_bf16_host(a16.ravel(), a_bf.ravel(), a16.size), "rld_f16_to_bf16_host")
+    check(rld_f16_to_bf16_host(b16.ravel(), b_bf.ravel(), b16.size), "rld_f16_to_bf16_host")
+    a_pad = np.empty((max_rank, k_in), np.uint16)
+    b_pad = np.empty((n_out, max_rank), np.uint16)
+    check(rld_pad_adapter_host(a_bf, b_bf, rank, k_in, n_out, max_rank, a_pad, b_pad),
+          "rld_pad_adapter_host")
+    sc = ctypes.c_float()
+    check(rld_scale(alpha, rank, use_rslora, ctypes.byref(sc)), "rld_scale")
+    return a_pad, b_pad, np.float32(sc.value)
 
 
 def to_device_u16(arr: np.ndarray, device) -> torch.Tensor:

@@ -340,6 +340,33 @@ def test_lora_rejects_bad_arguments():
     assert R.rld_lora_workspace_bytes(64, 0, 16) == 0
 
 
+def test_f16_to_bf16_host_matches_oracle_on_every_pattern():
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    out = np.zeros_like(allh)
+    assert R.rld_f16_to_bf16_host(allh, out, allh.size) == R.RLD_OK
+    want = O.f16_to_bf16(allh)
+    assert np.array_equal(out, want)
+    inplace = allh.copy()                       # src and dst may be the same array
+    assert R.rld_f16_to_bf16_host(inplace, inplace, inplace.size) == R.RLD_OK
+    assert np.array_equal(inplace, want)
+    assert R._lib.rld_f16_to_bf16_host(None, None, 4) == R.RLD_EINVAL
+    assert R._lib.rld_f16_to_bf16_host(None, None, 0) == R.RLD_OK
+
+
+def test_install_peft_f16_pair_matches_oracle():
+    # PEFT F16 tensors -> BF16 -> pool layout, and the scale, against the
+    # oracle's conversion, padding and scale
+    from routed_lora_delta_amd.pool import install_peft_pair
+    rng = np.random.default_rng(5)
+    rank, k_in, n_out, max_rank = 12, 40, 24, 16
+    a16 = (rng.standard_normal((rank, k_in)) * 0.1).astype(np.float16).view(np.uint16)
+    b16 = (rng.standard_normal((n_out, rank)) * 0.02).astype(np.float16).view(np.uint16)
+    a_pad, b_pad, sc = install_peft_pair(a16, b16, rank, k_in, n_out, max_rank, 32.0, True)
+    wa, wb = O.pad_adapter(O.f16_to_bf16(a16), O.f16_to_bf16(b16), max_rank)
+    assert np.array_equal(a_pad, wa) and np.array_equal(b_pad, wb)
+    assert sc == O.scale_for(32.0, rank, True)
+
+
 def test_scale_table_values_are_exact_closed_forms():
     # the fp32 scales of the decode workloads: alpha/r and alpha/sqrt(r), rounded once
     for alpha, r in ((32.0, 8), (32.0, 32), (16.0, 16)):

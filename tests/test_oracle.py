@@ -557,12 +557,42 @@ def pin_lora_delta_matches_routed(o):
     assert xa0.shape == (0, max_rank) and np.array_equal(out0, base)
 
 
+def pin_f16_to_bf16(o):
+    """Install-time F16 -> BF16: hand-derived cases, then every F16 pattern
+    against torch's float16 -> bfloat16 conversion (NaN: quiet, sign kept)."""
+    known = [
+        (0x3C00, 0x3F80),  # 1.0
+        (0x3C01, 0x3F80),  # 1 + 2^-10: below half a BF16 ulp
+        (0x3C04, 0x3F80),  # 1 + 2^-8: tie between 0x3F80 and 0x3F81 -> even
+        (0x3C0C, 0x3F82),  # 1 + 3*2^-8: tie between 0x3F81 and 0x3F82 -> even
+        (0x3C05, 0x3F81),  # 1 + 2^-8 + 2^-10: just above the tie
+        (0x0001, 0x3380),  # smallest subnormal 2^-24, exact in BF16
+        (0x03FF, 0x3880),  # largest subnormal (1 - 2^-10) 2^-14 rounds up to 2^-14
+        (0x7BFF, 0x4780),  # largest finite 65504 rounds up to 65536
+        (0xC000, 0xC000),  # -2
+        (0x8000, 0x8000),  # -0
+        (0x7C00, 0x7F80),  # +inf
+        (0xFC00, 0xFF80),  # -inf
+    ]
+    for h, b in known:
+        assert int(o.f16_to_bf16(np.array([h], np.uint16))[0]) == b, hex(h)
+    allh = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = o.f16_to_bf16(allh)
+    ref = torch.from_numpy(allh.view(np.float16).copy()).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+    f = allh.view(np.float16)
+    nan = np.isnan(f)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.all((mine[nan] & 0x7FC0) == 0x7FC0)
+    assert np.array_equal(mine[nan] >> 15, allh[nan] >> 15)
+
+
 PINS = [pin_bf16_known, pin_bf16_roundtrip, pin_bf16_midpoints, pin_bf16_vs_torch,
         pin_scale_closed_forms, pin_brute_force_bgmv, pin_textbook_lora, pin_pad_invariant,
         pin_inactive_and_strides, pin_batched_equals_rows, pin_fold_order,
         pin_routing_probe_grouped, pin_routing_probe_gather, pin_window_union, pin_cross_path,
         pin_helpers, pin_lora_delta_brute_force, pin_lora_delta_textbook,
-        pin_lora_delta_matches_routed]
+        pin_lora_delta_matches_routed, pin_f16_to_bf16]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
