@@ -71,6 +71,23 @@ def test_bgmv_shapes(shape):
     _base_rows_xa_zero(wl, run)
 
 
+def test_bgmv_gated_q_fold():
+    """A gated model's q projection writes [Q | gate] rows; the q delta folds into
+    the Q half (offset 0, row stride 2*n_out) before the two are de-interleaved,
+    and the gate half stays bit-identical (compare_bgmv checks every element of
+    the buffer outside the folded regions)."""
+    dev = require_gpu()
+    n, k_in, n_out = 48, 4096, 4096
+    wl = W.bgmv_custom(12, n, k_in, n_out, 16, 16, (8, 16), base_frac=0.1,
+                       out_row_stride=2 * n_out, out_offset=0)
+    say("case: gated q fold into [Q|gate] rows")
+    run = BgmvRun(wl, dev)
+    run.run_all()
+    compare_bgmv(run, "gated q")
+    out = run.outputs()["out"].reshape(n, 2 * n_out)
+    assert np.array_equal(out[:, n_out:], wl.buffers["out"].reshape(n, 2 * n_out)[:, n_out:])
+
+
 def test_bgmv_out_of_range_slots_and_missing_tables():
     """Slots >= max_loras, negative slots and slots whose A or B entry is 0
     leave their rows untouched and write zero xa."""
