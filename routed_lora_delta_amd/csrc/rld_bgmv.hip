@@ -14,9 +14,9 @@
 //                64 rows at once.  The waves' partial sums are added in wave
 //                order.  With one chunk the sum is rounded to xa right away;
 //                otherwise it is stored as an fp32 partial [chunk][row][col]
-//                in the workspace, and a second, small kernel adds each row's
-//                chunks in chunk order and writes xa (and the zero rows of base
-//                rows).  The chunk length depends only on (k_in, max_rank), so
+//                in the workspace (zeros for base rows), and a second, small
+//                kernel adds each row's chunks in chunk order and writes xa.
+//                The chunk length depends only on (k_in, max_rank), so
 //                a row's summation order is the same whatever the batch holds:
 //                a batched call is bit-identical to one-row calls.
 //   expand item  (slot, 256 output columns).  B_s rows of the tile are
@@ -147,13 +147,14 @@ __device__ __forceinline__ int dense_tile_rows(uint32_t r0, uint32_t n, int tile
 // Shrink item w (slot-major over (slot, chunk, column group)); the group
 // covers xa columns [16*NT*cg, 16*NT*(cg+1)).
 template <int NT>
-__device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, ShrinkSmem<NT>& sm) {
+__device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
   const uint32_t n = a.n, R = a.R, nchunks = a.nch, ncg = a.ncg;
   const uint32_t cg = w % ncg;
   const uint32_t c = (w / ncg) % nchunks;
   const int s = (int)(w / (ncg * nchunks));  // slot, or row tile in the unrouted mode
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const uint32_t col0 = cg * 16u * NT;
 
   // The block's seq_slot entries and the slot's table entries go out first.
   int key0 = -1;
@@ -167,15 +168,24 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, Shrin
     ent = slot_entry(a, s);
   }
 
-  // Without a k split, the last item (a slot of the last index, usually cold)
-  // also writes the zero xa rows of base rows (the reduce kernel does it
-  // otherwise).
-  if (!a.dense && nchunks == 1 && w == total - 1) {
-    const uint32_t r8 = R / 8;
-    for (uint32_t e = threadIdx.x; e < n * r8; e += 256) {
-      const uint32_t row = e / r8;
-      if (!slot_active(a, a.seq_slot()[row]))
-        store16(a.xa() + (size_t)row * R + (e % r8) * 8, zero16());
+  // Zeros for base rows, by the items of the last slot (usually cold, so these
+  // blocks have nothing else to do): the item of chunk c and column group cg
+  // writes the base rows' xa columns of the group (no k split) or their
+  // partials of chunk c (so the chunk reduce needs no routing).  One row per
+  // thread; the first 256 rows' slots are key0.
+  if (!a.dense && (uint32_t)s == a.max_loras - 1) {
+    const uint32_t c1 = min(col0 + 16u * NT, R);
+    for (uint32_t r0 = 0; r0 < n; r0 += 256) {
+      const uint32_t row = r0 + threadIdx.x;
+      const int key = r0 == 0 ? key0 : (row < n ? a.seq_slot()[row] : 0);
+      if (row >= n || slot_active(a, key)) continue;
+      if (nchunks == 1) {
+        for (uint32_t cc = col0; cc < c1; cc += 8) store16(a.xa() + (size_t)row * R + cc, zero16());
+      } else {
+        RLD_GLOBAL float* pp = a.partial() + ((size_t)c * n + row) * R;
+        for (uint32_t cc = col0; cc < c1; cc += 4)
+          store16(reinterpret_cast<RLD_GLOBAL uint16_t*>(pp + cc), zero16());
+      }
     }
   }
   if (!ent.active()) return;
@@ -183,7 +193,6 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, uint32_t total, Shrin
   const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ent.a);
   const int lg = lane >> 4;
   const int cl = lane & 15;
-  const uint32_t col0 = cg * 16u * NT;
   const uint32_t kb = c * a.kc;
   const uint32_t ke = min(kb + a.kc, a.k_in);
   const uint32_t nsteps = (ke - kb + 31) / 32;
@@ -449,35 +458,38 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(BgmvArgs a, uint32_t t
   // its L2
   const uint32_t w = xcd_group_item(a.ncg);
   if (w >= total) return;
-  shrink_item<NT>(a, w, total, sm);
+  shrink_item<NT>(a, w, sm);
 }
 
 // k split: xa[row, 4 columns] = bf16(sum over chunks, in chunk order, of the
-// partials); zero rows for base rows.  One thread per (row, 4 columns); the
-// chunk loads of a thread go out 8 at a time, ahead of their adds.
+// partials).  Base rows have zero partials (written by the shrink), so every
+// row is handled alike and no routing is read.  One thread per (row, 4
+// columns); up to kReduceBatch chunk loads go out before their adds.
+constexpr int kReduceBatch = 24;
+
 __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a) {
   const uint32_t q4 = a.R / 4;
   const uint32_t t = blockIdx.x * kReduceThreads + threadIdx.x;
   if (t >= a.n * q4) return;
   const uint32_t row = t / q4;
   const uint32_t col = (t % q4) * 4;
-  const int s = a.dense ? 0 : a.seq_slot()[row];
   const RLD_GLOBAL floatx4* p =
       reinterpret_cast<const RLD_GLOBAL floatx4*>(a.partial() + (size_t)row * a.R + col);
   const size_t cstride = (size_t)a.n * a.R / 4;  // floatx4 per chunk
   floatx4 sum = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (uint32_t c0 = 0; c0 < a.nch; c0 += 8) {
-    floatx4 v[8];
+  for (uint32_t c0 = 0; c0 < a.nch; c0 += kReduceBatch) {
+    floatx4 v[kReduceBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = p[(c0 + j < a.nch ? c0 + j : c0) * cstride];
+    for (int j = 0; j < kReduceBatch; ++j) v[j] = p[(c0 + j < a.nch ? c0 + j : c0) * cstride];
+    // every load of the batch goes out before the first add (no instruction
+    // is scheduled across this point)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kReduceBatch; ++j)
       if (c0 + j < a.nch) sum = (c0 + j == 0) ? v[j] : sum + v[j];
   }
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 o = {0u, 0u};
-  if (a.dense || slot_active(a, s))
-    o = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+  const u32x2 o = {pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
   *reinterpret_cast<RLD_GLOBAL u32x2*>(a.xa() + (size_t)row * a.R + col) = o;
 }
 
