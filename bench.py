@@ -223,7 +223,10 @@ def summarize(dirs, bench_json=None):
 # q, k and v folds (and the gate and up folds) read the same input and write
 # different outputs, so they run on parallel branches of the step's graph; o
 # follows q/k/v, down follows gate/up.  Module -> (group within its workload,
-# lane).  Calls of one module keep one lane (its shrink feeds its expand).
+# lane).  Calls of one module keep one lane (its shrink feeds its expand).  The
+# windows of a grouped projection write disjoint rows of its output, so with an
+# xa arena and a workspace each they are independent too: window k of a module
+# on lane `lane * windows + k`.
 LANES = {"q": (0, 0), "k": (0, 1), "v": (0, 2), "o": (1, 0),
          "gate": (0, 0), "up": (0, 1), "down": (1, 0)}
 MAX_LANES = 3
@@ -251,10 +254,10 @@ class Step:
         def i32(a):
             return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
 
-        def add(call, module):
-            g, lane = LANES.get(module, (0, 0))
+        def add(call, module, lane=None):
+            g, ln = LANES.get(module, (0, 0))
             self.calls.append(call)
-            self.sched.append((group0 + g, lane))
+            self.sched.append((group0 + g, ln if lane is None else lane))
 
         for tag, wl in workloads:
             if tag in ("attn", "ffn", "lora"):
@@ -327,17 +330,18 @@ class Step:
                 off = i32(wl.expert_offsets)
                 stid = i32(wl.sorted_token_ids)
                 rad = i32(wl.row_adapter)
-                # per lane: xa, and a workspace for every projection and window of
-                # the lane (sized for the largest)
+                wins = [(k * wl.cap, min((k + 1) * wl.cap, wl.te))
+                        for k in range(-(-wl.te // wl.cap))]
+                # per lane (module lane x window): xa, and a workspace sized for
+                # the largest projection
                 wsb = max(R.rld_moe_grouped_workspace_bytes(wl.cap, p.k_in, wl.max_rank,
                                                             wl.max_loras, wl.num_experts)
                           for p in wl.projections)
                 lanes = [(torch.zeros(wl.cap * wl.max_rank + 8, dtype=torch.int16, device=dev),
                           torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev))
-                         for _ in range(MAX_LANES)]
+                         for _ in range(len(wins) * (1 + max(LANES.get(p.name, (0, 0))[1]
+                                                             for p in wl.projections)))]
                 keep += [off, stid, rad, lanes]
-                wins = [(k * wl.cap, min((k + 1) * wl.cap, wl.te))
-                        for k in range(-(-wl.te // wl.cap))]
                 order = {"gate": 0, "up": 1, "down": 2}
                 for p in sorted(wl.projections, key=lambda q: order.get(q.name, 3)):
                     rt = MoeRoute(p.adapters, wl.max_loras, wl.num_experts, wl.max_rank, p.k_in,
@@ -345,8 +349,9 @@ class Step:
                     x = to_device_u16(p.x.ravel(), dev)
                     base = to_device_u16(p.base.ravel(), dev)
                     keep += [rt, x, base]
-                    xa, ws = lanes[LANES.get(p.name, (0, 0))[1]]
-                    for lo, hi in wins:
+                    for k, (lo, hi) in enumerate(wins):
+                        lane = LANES.get(p.name, (0, 0))[1] * len(wins) + k
+                        xa, ws = lanes[lane]
                         sb, eb, fl, _ = grouped_window_bytes(wl, p, lo, hi)
 
                         def shrink(rt=rt, x=x, p=p, lo=lo, hi=hi, off=off, stid=stid, rad=rad,
@@ -363,9 +368,9 @@ class Step:
                                                                  hi, base, p.n_out)
 
                         add((f"grouped.{p.name}.[{lo},{hi}).shrink", "grouped_shrink_kernel",
-                             shrink, sb, fl / 2, hi - lo), p.name)
+                             shrink, sb, fl / 2, hi - lo), p.name, lane)
                         add((f"grouped.{p.name}.[{lo},{hi}).expand", "grouped_expand_kernel",
-                             expand, eb, fl / 2, 0), p.name)
+                             expand, eb, fl / 2, 0), p.name, lane)
                     self.rows += wl.te
             group0 = max((g for g, _ in self.sched), default=-1) + 1
         self._keep = keep
@@ -377,7 +382,8 @@ class Step:
         group forks its lanes onto side streams and joins them before the next
         group starts (parallel=False: every call on `stream`, in order)."""
         torch = self.torch
-        side = [None] + [torch.cuda.Stream() for _ in range(MAX_LANES - 1)]
+        nlanes = 1 + max(ln for _, ln in self.sched)
+        side = [None] + [torch.cuda.Stream() for _ in range(nlanes - 1)]
         idx = list(idx)
         g = torch.cuda.CUDAGraph()
         if not parallel:
