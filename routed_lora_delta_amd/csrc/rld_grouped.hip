@@ -37,8 +37,15 @@
 
 namespace rld {
 
-constexpr int kOffCap = 1024;    // expert_offsets entries staged in LDS (num_experts_off < kOffCap)
-constexpr int kPairCap = 2048;   // max_loras * num_experts held in the LDS worklist
+// LDS worklist capacities of a launch: PC pairs (max_loras * num_experts) and
+// off_cap<PC>() staged expert_offsets entries (num_experts_off < off_cap).  A
+// launch uses the small instantiation whenever the route fits it: its prologue
+// issues a quarter of the loads and its block holds less LDS, which shortens
+// both the first round trip and the launch ramp.
+constexpr int kPairCapSmall = 512;
+constexpr int kPairCapLarge = 2048;
+template <int PC>
+constexpr int off_cap() { return PC < 1024 ? PC : 1024; }
 constexpr int kListCap = 512;    // rows of a pair collected per scan
 constexpr int kBatch = 64;       // rows of a pair per MFMA pass (4 subtiles of 16)
 constexpr int kPeThreads = 512;  // expand block: 8 waves x 64 columns
@@ -132,12 +139,13 @@ __device__ __forceinline__ void zero_xa_row(RLD_GLOBAL uint16_t* xa, uint32_t lo
 // (valid[p] = both present), and list in LDS, ascending, the pairs that are
 // valid and own rows of [row_offset, row_end).  All these loads go out
 // together, so this costs one round of loads.  Returns the pair count.
-template <int NTH>
+template <int NTH, int PC>
 __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row_offset,
                                               uint32_t row_end, int* off_s, uint8_t* valid,
                                               int16_t* apairs, int* wcount) {
-  constexpr int kOffPer = kOffCap / NTH;
-  constexpr int kPairPer = kPairCap / NTH;
+  constexpr int kOffPer = off_cap<PC>() / NTH;
+  constexpr int kPairPer = PC / NTH;
+  static_assert(kOffPer >= 1 && kPairPer >= 1, "capacity below one entry per thread");
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   constexpr int nw = NTH / kWave;
@@ -228,62 +236,93 @@ constexpr int kGsThreads = 256;
 constexpr int kGsWaves = kGsThreads / kWave;
 constexpr int kGsListCap = 512;  // rows of a pair held per scan segment
 
+template <int PC>
 struct GsSmem {
-  int off[kOffCap];
-  uint8_t valid[kPairCap];
-  int16_t apairs[kPairCap];
+  int off[off_cap<PC>()];
+  uint8_t valid[PC];
+  int16_t apairs[PC];
   int list[kGsListCap];  // sorted rows of the pair
   int xrow[kGsListCap];  // their x rows (token, or the sorted row)
-  int wcount[kGsWaves];
+  int wcount[2 * kGsWaves];
   int flag;
 };
 
-// One round of gs_scan: the rows of [c0, min(c0 + kGsThreads, hi)) that expert
-// e owns and whose adapter slot is s are appended at sm.list[cnt..] in row
-// order.  Returns the rows appended.
-__device__ __forceinline__ int gs_round(const GroupedRows& g, GsSmem& sm, int e, int s,
+// Rows of one gs_scan round: two per thread, so that an expert's span of the
+// window (about te / num_experts rows) is usually one round.
+constexpr int kGsRoundRows = 2 * kGsThreads;
+
+// One round of gs_scan: the rows of [c0, min(c0 + kGsRoundRows, hi)) that
+// expert e owns and whose adapter slot is s are appended at sm.list[cnt..] in
+// row order.  A thread takes rows c0 + tid and c0 + kGsThreads + tid; the loads
+// of both go out together (clamped, in-bounds indices), so a round is two
+// dependent loads whatever its length.  Returns the rows appended.
+template <int PC>
+__device__ __forceinline__ int gs_round(const GroupedRows& g, GsSmem<PC>& sm, int e, int s,
                                         uint32_t c0, uint32_t hi, uint32_t x_gather, int cnt) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const uint32_t r = c0 + threadIdx.x;
-  const bool inr = r < hi && expert_of_row(sm.off, (int)g.E_off, (int)r) == e;
-  int t = (int)r;
-  if (g.need_tok) t = inr ? g.stid()[r] : 0;
-  bool hit = inr;
-  if (g.need_tok) hit = inr && t >= 0 && (uint32_t)t < g.num_tokens;
-  int sr = -1;
-  if (hit) sr = token_slot(g, t);
-  hit = hit && sr == s;
-  const uint64_t m = __ballot(hit);
-  if (lane == 0) sm.wcount[wave] = __popcll(m);
+  uint32_t r[2];
+  bool hit[2];
+  int t[2], sr[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    r[h] = c0 + (uint32_t)(h * kGsThreads) + threadIdx.x;
+    hit[h] = r[h] < hi && expert_of_row(sm.off, (int)g.E_off, (int)r[h]) == e;
+    t[h] = (int)r[h];
+  }
+  if (g.need_tok) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) t[h] = g.stid()[r[h] < hi ? r[h] : c0];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) hit[h] = hit[h] && t[h] >= 0 && (uint32_t)t[h] < g.num_tokens;
+  }
+  sr[0] = sr[1] = 0;
+  if (g.radapt_ && g.num_tokens > 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sr[h] = g.radapt()[hit[h] ? t[h] : 0];
+  }
+  uint64_t m[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    hit[h] = hit[h] && sr[h] == s;
+    m[h] = __ballot(hit[h]);
+    if (lane == 0) sm.wcount[h * kGsWaves + wave] = __popcll(m[h]);
+  }
   __syncthreads();
-  int pos = cnt;
+  int pos[2] = {cnt, cnt};
   int tot = 0;
 #pragma unroll
-  for (int v = 0; v < kGsWaves; ++v) {
-    pos += v < wave ? sm.wcount[v] : 0;
-    tot += sm.wcount[v];
-  }
-  if (hit) {
-    const int p = pos + __popcll(m & lanemask_lt(lane));
-    sm.list[p] = (int)r;
-    sm.xrow[p] = x_gather ? t : (int)r;
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int v = 0; v < kGsWaves; ++v) {
+      const int wc = sm.wcount[h * kGsWaves + v];
+      pos[h] += (v < wave ? wc : 0);
+      if (h == 0) pos[1] += wc;
+      tot += wc;
+    }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (hit[h]) {
+      const int p = pos[h] + __popcll(m[h] & lanemask_lt(lane));
+      sm.list[p] = (int)r[h];
+      sm.xrow[p] = x_gather ? t[h] : (int)r[h];
+    }
   __syncthreads();
   return tot;
 }
 
 // Collects into sm.list / sm.xrow the rows of [*c0, hi) that expert e owns and
-// whose adapter slot is s, until the segment holds more than
-// kGsListCap - kGsThreads rows, and advances *c0 past the rows scanned
-// (*c0 < hi on entry).  Every thread calls it; returns the row count.
-__device__ __forceinline__ int gs_scan(const GroupedRows& g, GsSmem& sm, int e, int s,
+// whose adapter slot is s, until the segment could not take another round, and
+// advances *c0 past the rows scanned (*c0 < hi on entry).  Every thread calls
+// it; returns the row count.
+template <int PC>
+__device__ __forceinline__ int gs_scan(const GroupedRows& g, GsSmem<PC>& sm, int e, int s,
                                        uint32_t* c0, uint32_t hi, uint32_t x_gather) {
   int cnt = 0;
   do {
     cnt += gs_round(g, sm, e, s, *c0, hi, x_gather, cnt);
-    *c0 += kGsThreads;
-  } while (*c0 < hi && cnt + kGsThreads <= kGsListCap);
+    *c0 += kGsRoundRows;
+  } while (*c0 < hi && cnt + kGsRoundRows <= kGsListCap);
   return cnt;
 }
 
@@ -291,7 +330,8 @@ __device__ __forceinline__ int gs_scan(const GroupedRows& g, GsSmem& sm, int e, 
 // the partials) for the cnt rows in sm.list.  Each thread takes up to 4 column
 // pairs; all their chunk loads (up to 8 chunks at a time) go out before the
 // adds.
-__device__ __forceinline__ void gs_reduce_rows(const GsArgs& a, const GsSmem& sm, int cnt) {
+template <int PC>
+__device__ __forceinline__ void gs_reduce_rows(const GsArgs& a, const GsSmem<PC>& sm, int cnt) {
   const uint32_t R = a.R;
   const uint32_t half = R / 2;
   const size_t W = a.row_end - a.row_offset;
@@ -344,8 +384,8 @@ __device__ __forceinline__ void gs_reduce_rows(const GsArgs& a, const GsSmem& sm
 }
 
 // Pair item (pair, chunk c, column group cg); see GsArgs.
-template <int KS, int NT>
-__device__ void gs_pair_item(const GsArgs& a, GsSmem& sm, floatx4 (*red)[4 * NT][kWave], int pair,
+template <int KS, int NT, int PC>
+__device__ void gs_pair_item(const GsArgs& a, GsSmem<PC>& sm, floatx4 (*red)[4 * NT][kWave], int pair,
                              uint32_t c, uint32_t cg) {
   const GroupedRows& g = a.gr;
   const uint32_t R = a.R, k_in = a.k_in;
@@ -477,7 +517,8 @@ __device__ void gs_pair_item(const GsArgs& a, GsSmem& sm, floatx4 (*red)[4 * NT]
 // Row-block item z: zero the xa rows of [row_offset + 256z, +256) that no pair
 // folds (no owner expert, token out of range, slot out of range or not
 // adapted for the expert).
-__device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem& sm, uint32_t z) {
+template <int PC>
+__device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem<PC>& sm, uint32_t z) {
   const GroupedRows& g = a.gr;
   const uint32_t r = a.row_offset + z * kGsThreads + threadIdx.x;
   if (r >= a.row_end) return;
@@ -496,11 +537,11 @@ __device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem& sm, 
 
 // Persistent: every block lists the window's active pairs, then takes items
 // blockIdx.x, blockIdx.x + gridDim.x, ...
-template <int KS, int NT>
+template <int KS, int NT, int PC>
 __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
-  __shared__ GsSmem sm;
+  __shared__ GsSmem<PC> sm;
   __shared__ floatx4 red[kGsWaves][4 * NT][kWave];
-  const int na = build_worklist<kGsThreads>(a.gr, a.row_offset, a.row_end, sm.off, sm.valid,
+  const int na = build_worklist<kGsThreads, PC>(a.gr, a.row_offset, a.row_end, sm.off, sm.valid,
                                             sm.apairs, sm.wcount);
   const uint32_t per = a.nch * a.ncg;
   const uint32_t npi = (uint32_t)na * per;
@@ -508,7 +549,7 @@ __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
   for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
     if (it < npi) {
       const uint32_t rem = it % per;
-      gs_pair_item<KS, NT>(a, sm, red, sm.apairs[it / per], rem / a.ncg, rem % a.ncg);
+      gs_pair_item<KS, NT, PC>(a, sm, red, sm.apairs[it / per], rem / a.ncg, rem % a.ncg);
     } else {
       gs_zero_item(a, sm, it - npi);
     }
@@ -520,7 +561,7 @@ __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
 // in batches of 64: their base values are prefetched, their xa rows are the B
 // operand, deltas go to LDS as BF16 and are folded back in 16-byte pieces.
 // NKS = ceil(max_rank / 32) K steps.
-template <int NKS>
+template <int NKS, int PC>
 __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
     uint64_t xa_addr, GroupedRows gr, uint64_t scale_addr,
     uint32_t n_out, uint32_t R, uint32_t row_offset, uint32_t row_end, uint32_t nct,
@@ -528,15 +569,15 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
   const RLD_GLOBAL uint16_t* xa = gp<const uint16_t>(xa_addr);
   const RLD_GLOBAL float* scale_table = gp<const float>(scale_addr);
   RLD_GLOBAL uint16_t* out = gp<uint16_t>(out_addr);
-  __shared__ int off_s[kOffCap];
-  __shared__ uint8_t valid[kPairCap];
-  __shared__ int16_t apairs[kPairCap];
+  __shared__ int off_s[off_cap<PC>()];
+  __shared__ uint8_t valid[PC];
+  __shared__ int16_t apairs[PC];
   __shared__ int list[kListCap];
   __shared__ int toks[kListCap];
   __shared__ int wcount[kPeThreads / kWave];
   __shared__ __attribute__((aligned(16))) uint16_t dl[kBatch * kDlStride];
 
-  const int na = build_worklist<kPeThreads>(gr, row_offset, row_end, off_s, valid, apairs, wcount);
+  const int na = build_worklist<kPeThreads, PC>(gr, row_offset, row_end, off_s, valid, apairs, wcount);
   const int* off = off_s;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -641,12 +682,19 @@ static int check_grouped(const rld_moe_route* route, int x_gather, const int32_t
                          const int32_t* row_adapter, uint32_t row_offset, uint32_t row_end) {
   int st = check_moe_route(route);
   if (st) return st;
-  if ((uint64_t)route->max_loras * route->num_experts > (uint64_t)kPairCap) return RLD_EUNSUPPORTED;
+  if ((uint64_t)route->max_loras * route->num_experts > (uint64_t)kPairCapLarge)
+    return RLD_EUNSUPPORTED;
   if (!expert_offsets || num_experts_off == 0) return RLD_EINVAL;
-  if (num_experts_off >= (uint32_t)kOffCap) return RLD_EUNSUPPORTED;
+  if (num_experts_off >= (uint32_t)off_cap<kPairCapLarge>()) return RLD_EUNSUPPORTED;
   if (row_end < row_offset || row_end > 0x7fffffffu) return RLD_EINVAL;
   if ((x_gather || row_adapter) && !sorted_token_ids) return RLD_EINVAL;
   return RLD_OK;
+}
+
+// The route and offsets fit the small worklist instantiation.
+static bool small_caps(const rld_moe_route* route, uint32_t num_experts_off) {
+  return (uint64_t)route->max_loras * route->num_experts <= (uint64_t)kPairCapSmall &&
+         num_experts_off < (uint32_t)off_cap<kPairCapSmall>();
 }
 
 static GroupedRows make_rows(const rld_moe_route* route, int x_gather, uint32_t num_tokens,
@@ -666,27 +714,28 @@ static GroupedRows make_rows(const rld_moe_route* route, int x_gather, uint32_t 
   return g;
 }
 
-template <int KS, int NT>
+template <int KS, int NT, int PC>
 static void launch_gs(const GsArgs& a, uint32_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((grouped_shrink_kernel<KS, NT>), dim3(grid), dim3(kGsThreads), 0, st, a);
+  hipLaunchKernelGGL((grouped_shrink_kernel<KS, NT, PC>), dim3(grid), dim3(kGsThreads), 0, st, a);
 }
 
-template <int KS>
+template <int KS, int PC>
 static void launch_gs_nt(uint32_t nt, const GsArgs& a, uint32_t grid, hipStream_t st) {
   switch (nt) {
-    case 1: launch_gs<KS, 1>(a, grid, st); break;
-    case 2: launch_gs<KS, 2>(a, grid, st); break;
-    default: launch_gs<KS, 4>(a, grid, st); break;
+    case 1: launch_gs<KS, 1, PC>(a, grid, st); break;
+    case 2: launch_gs<KS, 2, PC>(a, grid, st); break;
+    default: launch_gs<KS, 4, PC>(a, grid, st); break;
   }
 }
 
 // KS = chunk / 128 (MFMA steps per wave), one of the chunk lengths grouped_chunk gives.
+template <int PC>
 static void launch_gs_ks(uint32_t ks, uint32_t nt, const GsArgs& a, uint32_t grid, hipStream_t st) {
   switch (ks) {
-    case 2: launch_gs_nt<2>(nt, a, grid, st); break;
-    case 4: launch_gs_nt<4>(nt, a, grid, st); break;
-    case 6: launch_gs_nt<6>(nt, a, grid, st); break;
-    default: launch_gs_nt<8>(nt, a, grid, st); break;
+    case 2: launch_gs_nt<2, PC>(nt, a, grid, st); break;
+    case 4: launch_gs_nt<4, PC>(nt, a, grid, st); break;
+    case 6: launch_gs_nt<6, PC>(nt, a, grid, st); break;
+    default: launch_gs_nt<8, PC>(nt, a, grid, st); break;
   }
 }
 
@@ -745,7 +794,10 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
       (uint64_t)route->max_loras * route->num_experts * a.nch * a.ncg + a.nz;
   const uint32_t grid = (uint32_t)(items < kGsGrid ? items : kGsGrid);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  launch_gs_ks(a.kc / 128u, nt, a, grid, hs);
+  if (small_caps(route, num_experts_off))
+    launch_gs_ks<kPairCapSmall>(a.kc / 128u, nt, a, grid, hs);
+  else
+    launch_gs_ks<kPairCapLarge>(a.kc / 128u, nt, a, grid, hs);
   return launch_status();
 }
 
@@ -766,12 +818,13 @@ extern "C" int rld_moe_grouped_expand_fold(const rld_moe_route* route, const voi
   const uint32_t nct = div_ceil(route->n_out, kPeCols);
   GroupedRows gr = make_rows(route, 0, num_tokens, expert_offsets, num_experts_off,
                              sorted_token_ids, row_adapter);
-  auto kern = grouped_expand_kernel<1>;
+  const bool sm = small_caps(route, num_experts_off);
+  auto kern = grouped_expand_kernel<1, kPairCapLarge>;
   switch (div_ceil(route->max_rank, 32)) {
-    case 1: kern = grouped_expand_kernel<1>; break;
-    case 2: kern = grouped_expand_kernel<2>; break;
-    case 3: kern = grouped_expand_kernel<3>; break;
-    default: kern = grouped_expand_kernel<4>; break;
+    case 1: kern = sm ? grouped_expand_kernel<1, kPairCapSmall> : grouped_expand_kernel<1, kPairCapLarge>; break;
+    case 2: kern = sm ? grouped_expand_kernel<2, kPairCapSmall> : grouped_expand_kernel<2, kPairCapLarge>; break;
+    case 3: kern = sm ? grouped_expand_kernel<3, kPairCapSmall> : grouped_expand_kernel<3, kPairCapLarge>; break;
+    default: kern = sm ? grouped_expand_kernel<4, kPairCapSmall> : grouped_expand_kernel<4, kPairCapLarge>; break;
   }
   hipLaunchKernelGGL(kern, dim3(kPeGrid), dim3(kPeThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), reinterpret_cast<uint64_t>(xa), gr,

@@ -348,6 +348,29 @@ def test_moe_grouped_edge_windows():
     assert np.array_equal(run2.base.body()[tail], p.base.ravel()[tail])
 
 
+@pytest.mark.parametrize("max_loras,num_experts", [(5, 128), (1, 600)])
+def test_moe_grouped_large_route(max_loras, num_experts):
+    """Routes past the small worklist capacity (more than 512 (slot, expert)
+    pairs, or 512 or more offsets entries) take the large-capacity kernels;
+    both projections against the oracle, in windows."""
+    dev = require_gpu()
+    wl = _small_grouped(seed=6, num_tokens=400, num_experts=num_experts, max_loras=max_loras,
+                        n_adapted=num_experts * 3 // 4, projections=("down", "gate"), cap=700)
+    assert wl.max_loras * wl.num_experts > 512
+    ra = "wl" if max_loras > 1 else None
+    for p in wl.projections:
+        say(f"case: grouped large route {p.name} max_loras={max_loras} E={num_experts}")
+        run = GroupedRun(wl, p, dev, cap=wl.cap, row_adapter=ra)
+        xas = run.run()
+        base = p.base.ravel().copy()
+        for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
+            xa_o, base = oracle_grouped_window(wl, p, lo, hi, base, ra)
+            assert_xa_close(xa_g, xa_o, f"large route xa [{lo},{hi})",
+                            abs_sums_grouped(wl, p, lo, hi, ra),
+                            shrink_depth("grouped", p.k_in, wl.max_rank))
+        assert_out_close(run.base.body(), base, "large route out")
+
+
 @pytest.mark.parametrize("max_loras", [1, 2])
 def test_moe_grouped_long_pairs(max_loras):
     """Pairs with hundreds of rows in one window: 64-row batches, and with one
