@@ -348,6 +348,32 @@ def test_moe_grouped_edge_windows():
     assert np.array_equal(run2.base.body()[tail], p.base.ravel()[tail])
 
 
+def test_moe_grouped_full_config_sampled():
+    """The MoE grouped prefill at full size (4096 tokens, top-8 of 128 experts,
+    te = 32768 sorted rows in windows of 8192, down 768 -> 2048 and gate/up
+    2048 -> 768 gathered, rank 32, 4 slots), each projection window by window
+    as the step issues it; in every window three random 64-row blocks and the
+    last one against the oracle, rows computed one by one."""
+    dev = require_gpu()
+    wl = W.moe_grouped()
+    rng = np.random.default_rng(11)
+    for p in wl.projections:
+        say(f"case: grouped full config {p.name} k_in={p.k_in} n_out={p.n_out}")
+        run = GroupedRun(wl, p, dev)
+        xas = run.run()
+        out_g = run.base.body().reshape(wl.te, p.n_out)
+        for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
+            starts = sorted(rng.choice(np.arange(lo, hi - 64, 64), 3, replace=False)) + [hi - 64]
+            for a in starts:
+                xa_o, out_o = oracle_grouped_window(wl, p, a, a + 64, p.base.ravel().copy())
+                assert_xa_close(xa_g[a - lo: a - lo + 64], xa_o, f"full {p.name} xa [{a},+64)",
+                                abs_sums_grouped(wl, p, a, a + 64),
+                                shrink_depth("grouped", p.k_in, wl.max_rank))
+                assert_out_close(out_g[a: a + 64].ravel(),
+                                 out_o.reshape(wl.te, p.n_out)[a: a + 64].ravel(),
+                                 f"full {p.name} out [{a},+64)")
+
+
 @pytest.mark.parametrize("max_loras,num_experts", [(5, 128), (1, 600)])
 def test_moe_grouped_large_route(max_loras, num_experts):
     """Routes past the small worklist capacity (more than 512 (slot, expert)
