@@ -280,9 +280,10 @@ int rld_moe_gather(const rld_moe_route* route, const void* x, uint32_t x_row_str
 
 /* Bytes of workspace rld_moe_grouped_shrink needs for a window of window_rows
  * rows: the fp32 partial sums of its k_in split ([chunks][window_rows]
- * [max_rank], chunks = ceil(k_in / 512) for k_in > 1024) plus 16 bytes of
- * counter per (slot, expert) pair.  Returns 0 for k_in <= 1024 (one chunk: no
- * workspace needed, NULL may be passed) or when any size is 0.  Workspace contract:
+ * [max_rank], chunks = ceil(k_in / 512)) plus 16 bytes of counter per (slot,
+ * expert) pair.  Returns 0 when k_in is one chunk -- k_in <= 1024, or
+ * k_in <= 2048 with max_rank <= 32 -- (no workspace needed, NULL may be
+ * passed) or when any size is 0.  Workspace contract:
  *   - device memory, 16-byte aligned, of workspace_bytes >= the size above;
  *     one buffer as large as the largest call needs serves every window and
  *     route, if the same workspace_bytes is passed every time (the counters

@@ -23,10 +23,10 @@
 // chunk), so the pair's A_{s,e} and x rows are streamed by several blocks at
 // once, and fp32 partial sums per chunk meet in a workspace (see GsArgs).
 //
-// Summation order.  The shrink cuts k_in into chunks of a length fixed by k_in
-// alone, each chunk into four wave ranges; a wave sums its range in one MFMA
-// chain, the wave sums are added in wave order and the chunk sums in chunk
-// order.  The expand is one MFMA chain over max_rank.  A row's result
+// Summation order.  The shrink cuts k_in into chunks of a length fixed by
+// (k_in, max_rank) alone, each chunk into four (sixteen in the wide case) wave
+// ranges; a wave sums its range in one MFMA chain, the wave sums are added in
+// wave order and the chunk sums in chunk order.  The expand is one MFMA chain over max_rank.  A row's result
 // therefore never depends on which other rows share its block or window: a
 // full-window call and the union of chunk windows are bit-identical.
 //
@@ -143,9 +143,8 @@ template <int NTH, int PC>
 __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row_offset,
                                               uint32_t row_end, int* off_s, uint8_t* valid,
                                               int16_t* apairs, int* wcount) {
-  constexpr int kOffPer = off_cap<PC>() / NTH;
-  constexpr int kPairPer = PC / NTH;
-  static_assert(kOffPer >= 1 && kPairPer >= 1, "capacity below one entry per thread");
+  constexpr int kOffPer = (off_cap<PC>() + NTH - 1) / NTH;
+  constexpr int kPairPer = (PC + NTH - 1) / NTH;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   constexpr int nw = NTH / kWave;
@@ -203,7 +202,7 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
   return na;
 }
 
-// Shrink work items, in this order:
+// Shrink work items of the chunked kernel (256-thread blocks), in this order:
 //   (active pair p, k chunk c, column group cg)  for p < na, c < nch, cg < ncg
 //   row block z of the window (256 rows)         for z < nz
 // A pair item streams chunk c of x and of A_{s,e} for the pair's rows: wave w
@@ -214,15 +213,16 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
 // completes the pair's last item (a per-pair counter at the end of the
 // workspace) adds the chunks in chunk order and writes xa.  An item covers
 // NT*16 xa columns (column group cg).  A row-block item zeroes the xa rows of
-// its 256 rows that no pair folds.
+// its 256 rows that no pair folds.  The wide kernel's items are listed with it
+// below.
 struct GsArgs {
   uint64_t x_, xa_, part_, ctr_;
   GroupedRows gr;
   uint32_t xs, x_gather, k_in, R, row_offset, row_end;
-  uint32_t kc;   // k chunk: 4 waves x 32*KS
+  uint32_t kc;   // k chunk: 4 waves x 32*KS (16 waves x 128 in the wide kernel)
   uint32_t nch;  // chunks, ceil(k_in / kc)
   uint32_t ncg;  // column groups, ceil(R / (16*NT))
-  uint32_t nz;   // row blocks of the window
+  uint32_t nz;   // row blocks of the window (of blockDim rows)
   __device__ const RLD_GLOBAL uint16_t* x() const { return gp<const uint16_t>(x_); }
   __device__ RLD_GLOBAL uint16_t* xa() const { return gp<uint16_t>(xa_); }
   __device__ RLD_GLOBAL float* part() const { return gp<float>(part_); }
@@ -232,97 +232,105 @@ struct GsArgs {
   }
 };
 
-constexpr int kGsThreads = 256;
+constexpr int kGsThreads = 256;   // block of the chunked kernel
 constexpr int kGsWaves = kGsThreads / kWave;
-constexpr int kGsListCap = 512;  // rows of a pair held per scan segment
+constexpr int kGwThreads = 1024;  // block of the wide kernel
+constexpr int kGwWaves = kGwThreads / kWave;
 
-template <int PC>
+// LDS of a shrink block of NTH threads.  A gs_scan round takes RPT rows per
+// thread (at least 512 rows a round, so that an expert's span of the window,
+// about te / num_experts rows, is usually one round), and the row list holds
+// one round.
+template <int PC, int NTH>
 struct GsSmem {
+  static constexpr int kNW = NTH / kWave;
+  static constexpr int kRPT = NTH >= 512 ? 1 : 512 / NTH;
+  static constexpr int kRound = NTH * kRPT;
   int off[off_cap<PC>()];
   uint8_t valid[PC];
   int16_t apairs[PC];
-  int list[kGsListCap];  // sorted rows of the pair
-  int xrow[kGsListCap];  // their x rows (token, or the sorted row)
-  int wcount[2 * kGsWaves];
+  int list[kRound];  // sorted rows of the pair
+  int xrow[kRound];  // their x rows (token, or the sorted row)
+  int wcount[kRPT * kNW];
   int flag;
 };
 
-// Rows of one gs_scan round: two per thread, so that an expert's span of the
-// window (about te / num_experts rows) is usually one round.
-constexpr int kGsRoundRows = 2 * kGsThreads;
-
-// One round of gs_scan: the rows of [c0, min(c0 + kGsRoundRows, hi)) that
+// One round of gs_scan: the rows of [c0, min(c0 + SM::kRound, hi)) that
 // expert e owns and whose adapter slot is s are appended at sm.list[cnt..] in
-// row order.  A thread takes rows c0 + tid and c0 + kGsThreads + tid; the loads
-// of both go out together (clamped, in-bounds indices), so a round is two
+// row order.  A thread takes rows c0 + tid, c0 + NTH + tid, ...; the loads of
+// all of them go out together (clamped, in-bounds indices), so a round is two
 // dependent loads whatever its length.  Returns the rows appended.
-template <int PC>
-__device__ __forceinline__ int gs_round(const GroupedRows& g, GsSmem<PC>& sm, int e, int s,
-                                        uint32_t c0, uint32_t hi, uint32_t x_gather, int cnt) {
+template <class SM>
+__device__ __forceinline__ int gs_round(const GroupedRows& g, SM& sm, int e, int s, uint32_t c0,
+                                        uint32_t hi, uint32_t x_gather, int cnt) {
+  constexpr int RPT = SM::kRPT, NW = SM::kNW, NTH = NW * kWave;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t r[2];
-  bool hit[2];
-  int t[2], sr[2];
+  uint32_t r[RPT];
+  bool hit[RPT];
+  int t[RPT], sr[RPT];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    r[h] = c0 + (uint32_t)(h * kGsThreads) + threadIdx.x;
+  for (int h = 0; h < RPT; ++h) {
+    r[h] = c0 + (uint32_t)(h * NTH) + threadIdx.x;
     hit[h] = r[h] < hi && expert_of_row(sm.off, (int)g.E_off, (int)r[h]) == e;
     t[h] = (int)r[h];
+    sr[h] = 0;
   }
   if (g.need_tok) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) t[h] = g.stid()[r[h] < hi ? r[h] : c0];
+    for (int h = 0; h < RPT; ++h) t[h] = g.stid()[r[h] < hi ? r[h] : c0];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) hit[h] = hit[h] && t[h] >= 0 && (uint32_t)t[h] < g.num_tokens;
+    for (int h = 0; h < RPT; ++h) hit[h] = hit[h] && t[h] >= 0 && (uint32_t)t[h] < g.num_tokens;
   }
-  sr[0] = sr[1] = 0;
   if (g.radapt_ && g.num_tokens > 0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) sr[h] = g.radapt()[hit[h] ? t[h] : 0];
+    for (int h = 0; h < RPT; ++h) sr[h] = g.radapt()[hit[h] ? t[h] : 0];
   }
-  uint64_t m[2];
+  uint64_t m[RPT];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < RPT; ++h) {
     hit[h] = hit[h] && sr[h] == s;
     m[h] = __ballot(hit[h]);
-    if (lane == 0) sm.wcount[h * kGsWaves + wave] = __popcll(m[h]);
+    if (lane == 0) sm.wcount[h * NW + wave] = __popcll(m[h]);
   }
   __syncthreads();
-  int pos[2] = {cnt, cnt};
-  int tot = 0;
+  int pos[RPT];
+  int acc = cnt;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < RPT; ++h) {
+    int before = 0, all = 0;
 #pragma unroll
-    for (int v = 0; v < kGsWaves; ++v) {
-      const int wc = sm.wcount[h * kGsWaves + v];
-      pos[h] += (v < wave ? wc : 0);
-      if (h == 0) pos[1] += wc;
-      tot += wc;
+    for (int v = 0; v < NW; ++v) {
+      const int wc = sm.wcount[h * NW + v];
+      before += v < wave ? wc : 0;
+      all += wc;
     }
+    pos[h] = acc + before;
+    acc += all;
+  }
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < RPT; ++h)
     if (hit[h]) {
       const int p = pos[h] + __popcll(m[h] & lanemask_lt(lane));
       sm.list[p] = (int)r[h];
       sm.xrow[p] = x_gather ? t[h] : (int)r[h];
     }
   __syncthreads();
-  return tot;
+  return acc - cnt;
 }
 
 // Collects into sm.list / sm.xrow the rows of [*c0, hi) that expert e owns and
-// whose adapter slot is s, until the segment could not take another round, and
-// advances *c0 past the rows scanned (*c0 < hi on entry).  Every thread calls
-// it; returns the row count.
-template <int PC>
-__device__ __forceinline__ int gs_scan(const GroupedRows& g, GsSmem<PC>& sm, int e, int s,
-                                       uint32_t* c0, uint32_t hi, uint32_t x_gather) {
+// whose adapter slot is s, up to one round's worth (rounds that find nothing
+// do not end the segment), and advances *c0 past the rows scanned (*c0 < hi on
+// entry).  Every thread calls it; returns the row count.
+template <class SM>
+__device__ __forceinline__ int gs_scan(const GroupedRows& g, SM& sm, int e, int s, uint32_t* c0,
+                                       uint32_t hi, uint32_t x_gather) {
   int cnt = 0;
   do {
     cnt += gs_round(g, sm, e, s, *c0, hi, x_gather, cnt);
-    *c0 += kGsRoundRows;
-  } while (*c0 < hi && cnt + kGsRoundRows <= kGsListCap);
+    *c0 += SM::kRound;
+  } while (*c0 < hi && cnt == 0);
   return cnt;
 }
 
@@ -331,7 +339,8 @@ __device__ __forceinline__ int gs_scan(const GroupedRows& g, GsSmem<PC>& sm, int
 // pairs; all their chunk loads (up to 8 chunks at a time) go out before the
 // adds.
 template <int PC>
-__device__ __forceinline__ void gs_reduce_rows(const GsArgs& a, const GsSmem<PC>& sm, int cnt) {
+__device__ __forceinline__ void gs_reduce_rows(const GsArgs& a, const GsSmem<PC, kGsThreads>& sm,
+                                               int cnt) {
   const uint32_t R = a.R;
   const uint32_t half = R / 2;
   const size_t W = a.row_end - a.row_offset;
@@ -385,7 +394,7 @@ __device__ __forceinline__ void gs_reduce_rows(const GsArgs& a, const GsSmem<PC>
 
 // Pair item (pair, chunk c, column group cg); see GsArgs.
 template <int KS, int NT, int PC>
-__device__ void gs_pair_item(const GsArgs& a, GsSmem<PC>& sm, floatx4 (*red)[4 * NT][kWave], int pair,
+__device__ void gs_pair_item(const GsArgs& a, GsSmem<PC, kGsThreads>& sm, floatx4 (*red)[4 * NT][kWave], int pair,
                              uint32_t c, uint32_t cg) {
   const GroupedRows& g = a.gr;
   const uint32_t R = a.R, k_in = a.k_in;
@@ -514,13 +523,14 @@ __device__ void gs_pair_item(const GsArgs& a, GsSmem<PC>& sm, floatx4 (*red)[4 *
   }
 }
 
-// Row-block item z: zero the xa rows of [row_offset + 256z, +256) that no pair
-// folds (no owner expert, token out of range, slot out of range or not
-// adapted for the expert).
-template <int PC>
-__device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem<PC>& sm, uint32_t z) {
+// Row-block item z of a block of NTH threads: zero the xa rows of
+// [row_offset + NTH z, +NTH) that no pair folds (no owner expert, token out of
+// range, slot out of range or not adapted for the expert).
+template <int PC, int NTH>
+__device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem<PC, NTH>& sm,
+                                             uint32_t z) {
   const GroupedRows& g = a.gr;
-  const uint32_t r = a.row_offset + z * kGsThreads + threadIdx.x;
+  const uint32_t r = a.row_offset + z * NTH + threadIdx.x;
   if (r >= a.row_end) return;
   const int e = expert_of_row(sm.off, (int)g.E_off, (int)r);
   bool fold = e >= 0 && (uint32_t)e < g.E;
@@ -539,7 +549,7 @@ __device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem<PC>& 
 // blockIdx.x, blockIdx.x + gridDim.x, ...
 template <int KS, int NT, int PC>
 __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
-  __shared__ GsSmem<PC> sm;
+  __shared__ GsSmem<PC, kGsThreads> sm;
   __shared__ floatx4 red[kGsWaves][4 * NT][kWave];
   const int na = build_worklist<kGsThreads, PC>(a.gr, a.row_offset, a.row_end, sm.off, sm.valid,
                                             sm.apairs, sm.wcount);
@@ -550,6 +560,144 @@ __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
     if (it < npi) {
       const uint32_t rem = it % per;
       gs_pair_item<KS, NT, PC>(a, sm, red, sm.apairs[it / per], rem / a.ncg, rem % a.ncg);
+    } else {
+      gs_zero_item(a, sm, it - npi);
+    }
+  }
+}
+
+// Wide kernel (1024 < k_in <= 2048, max_rank <= 32): blocks of 16 waves, one
+// chunk.  Items, in this order:
+//   (active pair p, row half h)  for p < na, h < 2, ordered so that both halves
+//                                of a pair have the same blockIdx % 8 (so the
+//                                same XCD, whose L2 then serves the second read
+//                                of A_{s,e})
+//   row block z of the window (1024 rows)
+// Item (p, h) takes the pair's rows 32h + 64i, i = 0, 1, ... in batches of 32:
+// wave w sums k range [128w, 128w + 128) in one MFMA chain of four steps for
+// all NT*16 xa columns, the 16 wave sums meet in LDS in wave order, and the sum
+// is rounded to xa.  A batch's x rows, and A_{s,e} over the wave's range, are
+// one round of loads: 16 x 128 KB of A and 32 x 4 KB of x rows in flight per
+// block.
+template <int NT, int PC>
+__device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
+                             floatx4 (*red)[2 * NT][kWave], int pair, int h) {
+  constexpr int KS = 4;   // MFMA steps per wave: 128 k
+  constexpr int QB = 2;   // 16-row subtiles per batch
+  constexpr int kRows = 16 * QB;
+  const GroupedRows& g = a.gr;
+  const uint32_t R = a.R, k_in = a.k_in;
+  const int s = pair / (int)g.E;
+  const int e = pair % (int)g.E;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lg = lane >> 4;
+  const int cl = lane & 15;
+  const uint32_t kw0 = (uint32_t)wave * (32u * KS);
+  uint32_t lo, hi;
+  span_in_window(sm.off, g, e, a.row_offset, a.row_end, lo, hi);
+  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(g.a_table()[pair]);
+  const RLD_GLOBAL uint16_t* x = a.x();
+  // The wave's k range lies inside k_in (every wave when k_in is a multiple of
+  // 128): one pointer per operand row, the steps at immediate offsets.
+  // Otherwise clamped in-bounds addresses, and k past k_in zeroed once loaded.
+  const bool full = kw0 + 32u * KS <= k_in;
+  // A_{s,e} over the wave's k range serves every batch of the item: it goes
+  // out before the row scan, whose first wait covers it.
+  uint4 bop[NT][KS];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const uint32_t col = 16u * j + cl;
+    const RLD_GLOBAL uint16_t* ar = A + (size_t)(col < R ? col : 0) * k_in;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t kk = kw0 + 32u * ks + 8u * lg;
+      bop[j][ks] = load16(full ? ar + kk : ar + (kk < k_in ? kk : 0));
+    }
+  }
+  issue_point();
+  bool masked = full;
+  uint32_t c0 = lo;
+  while (c0 < hi) {
+    const int cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
+    if (!masked) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        if (kw0 + 32u * ks + 8u * lg >= k_in) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) bop[j][ks] = zero16();
+        }
+      masked = true;
+    }
+    for (int b0 = kRows * h; b0 < cnt; b0 += 2 * kRows) {
+      const int nb = min(cnt - b0, kRows);
+      uint4 aop[QB][KS];
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const int li = q * 16 + cl;
+        const RLD_GLOBAL uint16_t* xr = x + (size_t)sm.xrow[b0 + (li < nb ? li : 0)] * a.xs;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint32_t kk = kw0 + 32u * ks + 8u * lg;
+          aop[q][ks] = load16(full ? xr + kk : xr + (kk < k_in ? kk : 0));
+        }
+      }
+      issue_point();
+      if (!full) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          if (kw0 + 32u * ks + 8u * lg >= k_in) {
+#pragma unroll
+            for (int q = 0; q < QB; ++q) aop[q][ks] = zero16();
+          }
+      }
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(aop[q][ks], bop[j][ks], acc);
+          red[wave][q * NT + j][lane] = acc;
+        }
+      __syncthreads();
+      // one thread per (subtile, column tile, lane): the 16 wave sums in wave order
+      if (threadIdx.x < QB * NT * kWave) {
+        const int q = threadIdx.x / (NT * kWave);
+        const int j = (threadIdx.x / kWave) % NT;
+        const int ln = threadIdx.x & 63;
+        const uint32_t col = 16u * j + (ln & 15);
+        floatx4 sum = red[0][q * NT + j][ln];
+#pragma unroll
+        for (int v = 1; v < kGwWaves; ++v) sum += red[v][q * NT + j][ln];
+        if (col < R) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int li = q * 16 + 4 * (ln >> 4) + i;
+            if (li < nb) {
+              const uint32_t lr = (uint32_t)sm.list[b0 + li] - a.row_offset;
+              a.xa()[(size_t)lr * R + col] = (uint16_t)f32_to_bf16(sum[i]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <int NT, int PC>
+__global__ __launch_bounds__(kGwThreads) void grouped_shrink_wide_kernel(GsArgs a) {
+  __shared__ GsSmem<PC, kGwThreads> sm;
+  __shared__ floatx4 red[kGwWaves][2 * NT][kWave];
+  const int na = build_worklist<kGwThreads, PC>(a.gr, a.row_offset, a.row_end, sm.off, sm.valid,
+                                                sm.apairs, sm.wcount);
+  const uint32_t npi = 16u * (((uint32_t)na + 7u) / 8u);  // pair halves, in groups of 8 pairs
+  const uint32_t total = npi + a.nz;
+  for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
+    if (it < npi) {
+      const uint32_t p = (it / 16u) * 8u + it % 8u;
+      if (p < (uint32_t)na) gs_wide_item<NT, PC>(a, sm, red, sm.apairs[p], (int)((it / 8u) % 2u));
     } else {
       gs_zero_item(a, sm, it - npi);
     }
@@ -785,15 +933,27 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
   a.R = route->max_rank;
   a.row_offset = row_offset;
   a.row_end = row_end;
-  a.kc = grouped_chunk(route->k_in);
+  a.kc = grouped_chunk(route->k_in, route->max_rank);
   a.nch = div_ceil(route->k_in, a.kc);
   const uint32_t nt = grouped_nt(route->max_rank);
   a.ncg = div_ceil(div_ceil(route->max_rank, 16u), nt);
-  a.nz = div_ceil(W, (uint32_t)kGsThreads);
-  const uint64_t items =
-      (uint64_t)route->max_loras * route->num_experts * a.nch * a.ncg + a.nz;
-  const uint32_t grid = (uint32_t)(items < kGsGrid ? items : kGsGrid);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const uint64_t np = (uint64_t)route->max_loras * route->num_experts;
+  if (grouped_wide(route->k_in, route->max_rank)) {
+    a.nz = div_ceil(W, (uint32_t)kGwThreads);
+    const uint64_t items = 16u * ((np + 7u) / 8u) + a.nz;
+    const uint32_t grid = (uint32_t)(items < kGwGrid ? items : kGwGrid);
+    const bool sm = small_caps(route, num_experts_off);
+    auto kern = nt == 1 ? (sm ? grouped_shrink_wide_kernel<1, kPairCapSmall>
+                              : grouped_shrink_wide_kernel<1, kPairCapLarge>)
+                        : (sm ? grouped_shrink_wide_kernel<2, kPairCapSmall>
+                              : grouped_shrink_wide_kernel<2, kPairCapLarge>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kGwThreads), 0, hs, a);
+    return launch_status();
+  }
+  a.nz = div_ceil(W, (uint32_t)kGsThreads);
+  const uint64_t items = np * a.nch * a.ncg + a.nz;
+  const uint32_t grid = (uint32_t)(items < kGsGrid ? items : kGsGrid);
   if (small_caps(route, num_experts_off))
     launch_gs_ks<kPairCapSmall>(a.kc / 128u, nt, a, grid, hs);
   else

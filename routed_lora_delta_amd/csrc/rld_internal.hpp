@@ -69,11 +69,20 @@ inline uint32_t xcd_group_grid(uint32_t total, uint32_t group) {
   return 8u * group * div_ceil(div_ceil(total, group), 8u);
 }
 
-// k chunk of the MoE grouped shrink, a function of k_in only (so a row's
-// summation order never depends on its window): up to k_in = 1024 the whole of
-// k_in in one chunk of 512, 768 or 1024 (no partials, no reduce), above that
+// Wide MoE grouped shrink: for 1024 < k_in <= 2048 and max_rank <= 32 one
+// block of 16 waves covers the whole of k_in (128 k per wave), so no partials
+// and no second pass are needed.
+inline bool grouped_wide(uint32_t k_in, uint32_t max_rank) {
+  return k_in > 1024u && k_in <= 2048u && max_rank <= 32u;
+}
+
+// k chunk of the MoE grouped shrink, a function of (k_in, max_rank) only (so a
+// row's summation order never depends on its window): up to k_in = 1024 the
+// whole of k_in in one chunk of 512, 768 or 1024 (four waves, no partials, no
+// reduce); the wide case above in one chunk of 2048 (sixteen waves); otherwise
 // chunks of 512 (four waves x 128 k).
-inline uint32_t grouped_chunk(uint32_t k_in) {
+inline uint32_t grouped_chunk(uint32_t k_in, uint32_t max_rank) {
+  if (grouped_wide(k_in, max_rank)) return 2048u;
   if (k_in > 1024u) return 512u;
   return k_in <= 512u ? 512u : (k_in <= 768u ? 768u : 1024u);
 }
@@ -90,15 +99,16 @@ inline uint32_t grouped_nt(uint32_t max_rank) {
 inline size_t grouped_workspace(uint32_t rows, uint32_t k_in, uint32_t max_rank,
                                 uint32_t max_loras, uint32_t num_experts) {
   if (k_in == 0 || max_rank == 0 || max_loras == 0 || num_experts == 0) return 0;
-  const uint32_t nch = div_ceil(k_in, grouped_chunk(k_in));
+  const uint32_t nch = div_ceil(k_in, grouped_chunk(k_in, max_rank));
   if (nch == 1) return 0;
   const size_t part = ((size_t)nch * rows * max_rank * 4 + 15) & ~(size_t)15;
   return part + (size_t)16 * max_loras * num_experts;
 }
 
 // Blocks of the persistent grouped shrink launch (fewer when there are fewer
-// possible items).
+// possible items): 256-thread blocks, or 1024-thread blocks of the wide case.
 constexpr uint32_t kGsGrid = 512;
+constexpr uint32_t kGwGrid = 256;
 
 // Output columns per block of the gather expand (two per thread).
 constexpr uint32_t kGatherCols = 512;

@@ -71,6 +71,8 @@ def shrink_depth(path: str, k_in: int, max_rank: int) -> int:
         steps = -(-kc // 32)
         return 32 + -(-steps // 4) + 4 + nch
     if path == "grouped":
+        if 1024 < k_in <= 2048 and max_rank <= 32:
+            return 32 + 4 + 16 + 1  # one chunk over sixteen waves of four steps
         kc = 512 if k_in > 1024 else (512 if k_in <= 512 else (768 if k_in <= 768 else 1024))
         return 32 + kc // 128 + 4 + -(-k_in // kc)
     if path == "gather":

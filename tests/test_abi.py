@@ -281,29 +281,34 @@ def test_moe_rejects_bad_arguments():
 
 
 def test_grouped_workspace_contract():
-    # k_in = 2048 splits into 4 chunks of 512: fp32 partials per window row, then
+    # k_in = 4096 splits into 8 chunks of 512: fp32 partials per window row, then
     # 16 bytes of counter per (slot, expert) pair; short or missing workspaces
     # are refused before any launch
-    need = R.rld_moe_grouped_workspace_bytes(8192, 2048, 32, 4, 128)
-    assert need == 4 * 8192 * 32 * 4 + 16 * 4 * 128
-    mr = R.rld_moe_route(FAKE, FAKE, FAKE, 4, 128, 2048, 768, 32)
+    need = R.rld_moe_grouped_workspace_bytes(8192, 4096, 32, 4, 128)
+    assert need == 8 * 8192 * 32 * 4 + 16 * 4 * 128
+    mr = R.rld_moe_route(FAKE, FAKE, FAKE, 4, 128, 4096, 768, 32)
     g = lambda ws, wsb, hi=8192: R.rld_moe_grouped_shrink(  # noqa: E731
-        mr, FAKE, 2048, 1, 4096, FAKE, 128, FAKE, FAKE, 0, hi, FAKE, 8192, ws, wsb, 0)
+        mr, FAKE, 4096, 1, 4096, FAKE, 128, FAKE, FAKE, 0, hi, FAKE, 8192, ws, wsb, 0)
     for short in (need - 16, need // 2, 16):
         assert g(FAKE, short) == R.RLD_ENOSPACE
     assert g(0, need) == R.RLD_EINVAL
     assert g(FAKE + 8, need) == R.RLD_EALIGN
     # a smaller window needs less: the buffer of the largest window serves all
-    assert R.rld_moe_grouped_workspace_bytes(100, 2048, 32, 4, 128) == \
-        4 * 100 * 32 * 4 + 16 * 4 * 128
-    assert g(FAKE, R.rld_moe_grouped_workspace_bytes(100, 2048, 32, 4, 128) - 16, hi=100) == \
+    assert R.rld_moe_grouped_workspace_bytes(100, 4096, 32, 4, 128) == \
+        8 * 100 * 32 * 4 + 16 * 4 * 128
+    assert g(FAKE, R.rld_moe_grouped_workspace_bytes(100, 4096, 32, 4, 128) - 16, hi=100) == \
         R.RLD_ENOSPACE
-    assert R.rld_moe_grouped(mr, FAKE, 2048, 1, 4096, FAKE, 128, FAKE, FAKE, 0, 8192, FAKE, 768,
+    assert R.rld_moe_grouped(mr, FAKE, 4096, 1, 4096, FAKE, 128, FAKE, FAKE, 0, 8192, FAKE, 768,
                              FAKE, 8192, FAKE, need - 16, 0) == R.RLD_ENOSPACE
-    # up to k_in = 1024 the whole of k_in is one chunk: no workspace
+    # up to k_in = 1024 the whole of k_in is one chunk of four waves, and up to
+    # 2048 at max_rank <= 32 one chunk of sixteen waves: no workspace
     assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 4, 128) == 0
     assert R.rld_moe_grouped_workspace_bytes(8192, 1024, 32, 4, 128) == 0
-    assert R.rld_moe_grouped_workspace_bytes(64, 1032, 16, 2, 8) == 3 * 64 * 16 * 4 + 16 * 2 * 8
+    assert R.rld_moe_grouped_workspace_bytes(8192, 2048, 32, 4, 128) == 0
+    assert R.rld_moe_grouped_workspace_bytes(64, 1032, 16, 2, 8) == 0
+    # past those: chunks of 512
+    assert R.rld_moe_grouped_workspace_bytes(64, 1032, 48, 2, 8) == 3 * 64 * 48 * 4 + 16 * 2 * 8
+    assert R.rld_moe_grouped_workspace_bytes(64, 2056, 16, 2, 8) == 5 * 64 * 16 * 4 + 16 * 2 * 8
     assert R.rld_moe_grouped_workspace_bytes(64, 4096, 16, 2, 8) == 8 * 64 * 16 * 4 + 16 * 2 * 8
     assert R.rld_moe_grouped_workspace_bytes(8192, 256, 32, 4, 128) == 0
     assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 0, 128) == 0

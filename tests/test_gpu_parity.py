@@ -397,19 +397,51 @@ def test_moe_grouped_large_route(max_loras, num_experts):
         assert_out_close(run.base.body(), base, "large route out")
 
 
+@pytest.mark.parametrize("k_in,max_rank,proj", [(2048, 32, "gate"), (1032, 16, "gate"),
+                                                (1544, 32, "down"), (2048, 24, "down"),
+                                                (1160, 32, "gate")])
+def test_moe_grouped_wide(k_in, max_rank, proj):
+    """1024 < k_in <= 2048 at max_rank <= 32: one sixteen-wave block per pair
+    half covers all of k_in; k_in not a multiple of 128 leaves one wave's range
+    partly past k_in and later ones wholly past it.  Pairs of up to ~100 rows
+    (both halves, several batches each), windows of 333 rows against the oracle,
+    and the full window bit-identical to their union."""
+    dev = require_gpu()
+    sizes = dict(hidden=k_in, inter=264) if proj == "gate" else dict(hidden=264, inter=k_in)
+    wl = _small_grouped(seed=7, num_experts=4, n_adapted=3, max_rank=max_rank,
+                        ranks=(8, max_rank), cap=333, projections=(proj,), **sizes)
+    p = wl.projections[0]
+    say(f"case: grouped wide {proj} k_in={k_in} max_rank={max_rank}")
+    run = GroupedRun(wl, p, dev, cap=wl.cap)
+    xas = run.run()
+    base = p.base.ravel().copy()
+    for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
+        xa_o, base = oracle_grouped_window(wl, p, lo, hi, base)
+        assert_xa_close(xa_g, xa_o, f"wide xa [{lo},{hi})", abs_sums_grouped(wl, p, lo, hi),
+                        shrink_depth("grouped", p.k_in, wl.max_rank))
+        assert np.all(xa_g[np.all(xa_o == 0, axis=1)] == 0)
+    assert_out_close(run.base.body(), base, "wide out")
+    full = GroupedRun(wl, p, dev, cap=wl.te)
+    xa_full = full.run([(0, wl.te)])[0]
+    assert np.array_equal(np.concatenate(xas), xa_full)
+    assert np.array_equal(full.base.body(), run.base.body())
+
+
+@pytest.mark.parametrize("hidden,num_tokens", [(2056, 1200), (2048, 2400)])
 @pytest.mark.parametrize("max_loras", [1, 2])
-def test_moe_grouped_long_pairs(max_loras):
-    """Pairs with hundreds of rows in one window: 64-row batches, and with one
-    slot more than one scan segment (the chunk reduce rescans the span; gate's
-    k_in = 2056 splits into 5 chunks), in one full window and in windows of 700
+def test_moe_grouped_long_pairs(max_loras, hidden, num_tokens):
+    """Pairs with hundreds of rows in one window: many row batches, and with one
+    slot more than one scan segment (gate's k_in = 2056 splits into 5 chunks and
+    the chunk reduce rescans the span; k_in = 2048 is the sixteen-wave kernel,
+    whose segments hold 1024 rows), in one full window and in windows of 700
     rows."""
     dev = require_gpu()
-    wl = W.moe_grouped(9, num_tokens=1200, top_k=2, num_experts=4, hidden=2056, inter=264,
-                       max_loras=max_loras, n_adapted=4, ranks=(8, 16, 32), max_rank=32,
-                       cap=2400, projections=("down", "gate"))
+    wl = W.moe_grouped(9, num_tokens=num_tokens, top_k=2, num_experts=4, hidden=hidden,
+                       inter=264, max_loras=max_loras, n_adapted=4, ranks=(8, 16, 32),
+                       max_rank=32, cap=2 * num_tokens, projections=("down", "gate"))
     ra = None if max_loras == 1 else "wl"
     for p in wl.projections:
-        say(f"case: grouped long pairs {p.name} max_loras={max_loras}")
+        say(f"case: grouped long pairs {p.name} k_in={p.k_in} max_loras={max_loras}")
         full = GroupedRun(wl, p, dev, cap=wl.te, row_adapter=ra)
         xa_full = full.run([(0, wl.te)])[0]
         xa_o, out_o = oracle_grouped_window(wl, p, 0, wl.te, p.base.ravel().copy(), ra)
