@@ -137,12 +137,18 @@ __device__ __forceinline__ void zero_xa_row(RLD_GLOBAL uint16_t* xa, uint32_t lo
 
 // Every thread (NTH of them): stage expert_offsets in LDS, read the A/B table entries of every pair
 // (valid[p] = both present), and list in LDS, ascending, the pairs that are
-// valid and own rows of [row_offset, row_end).  All these loads go out
-// together, so this costs one round of loads.  Returns the pair count.
-template <int NTH, int PC>
+// valid and own rows of [row_offset, row_end).  KEEP = 1 also keeps every
+// pair's A table entry in keep_tab, KEEP = 2 its B entry in keep_tab and its
+// scale (scale_table) in keep_scale, so that an item has its operand address
+// without a round trip of its own.  All these loads go out together, so this
+// costs one round of loads.  Returns the pair count.
+template <int NTH, int PC, int KEEP = 0>
 __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row_offset,
                                               uint32_t row_end, int* off_s, uint8_t* valid,
-                                              int16_t* apairs, int* wcount) {
+                                              int16_t* apairs, int* wcount,
+                                              uint64_t* keep_tab = nullptr,
+                                              float* keep_scale = nullptr,
+                                              const RLD_GLOBAL float* scale_table = nullptr) {
   constexpr int kOffPer = (off_cap<PC>() + NTH - 1) / NTH;
   constexpr int kPairPer = (PC + NTH - 1) / NTH;
   const int lane = threadIdx.x & 63;
@@ -151,6 +157,7 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
   const uint32_t np = g.max_loras * g.E;
   int ov[kOffPer];
   uint64_t ta[kPairPer], tb[kPairPer];
+  float sv[kPairPer];
 #pragma unroll
   for (int i = 0; i < kOffPer; ++i) {
     const uint32_t j = threadIdx.x + i * NTH;
@@ -163,6 +170,7 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
     const uint32_t p = threadIdx.x + i * NTH;
     ta[i] = g.a_table()[p < np ? p : 0];
     tb[i] = g.b_table()[p < np ? p : 0];
+    if (KEEP == 2) sv[i] = scale_table[p < np ? p : 0];
   }
 #pragma unroll
   for (int i = 0; i < kOffPer; ++i) {
@@ -172,7 +180,14 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
 #pragma unroll
   for (int i = 0; i < kPairPer; ++i) {
     const uint32_t p = threadIdx.x + i * NTH;
-    if (p < np) valid[p] = (ta[i] != 0ull && tb[i] != 0ull) ? 1 : 0;
+    if (p < np) {
+      valid[p] = (ta[i] != 0ull && tb[i] != 0ull) ? 1 : 0;
+      if (KEEP == 1) keep_tab[p] = ta[i];
+      if (KEEP == 2) {
+        keep_tab[p] = tb[i];
+        keep_scale[p] = sv[i];
+      }
+    }
   }
   __syncthreads();
   const int* off = off_s;
@@ -246,6 +261,7 @@ struct GsSmem {
   static constexpr int kNW = NTH / kWave;
   static constexpr int kRPT = NTH >= 512 ? 1 : 512 / NTH;
   static constexpr int kRound = NTH * kRPT;
+  uint64_t atab[PC];  // A table entry of every pair
   int off[off_cap<PC>()];
   uint8_t valid[PC];
   int16_t apairs[PC];
@@ -409,7 +425,7 @@ __device__ void gs_pair_item(const GsArgs& a, GsSmem<PC, kGsThreads>& sm, floatx
   uint32_t lo, hi;
   span_in_window(sm.off, g, e, a.row_offset, a.row_end, lo, hi);
 
-  const uint64_t ta = g.a_table()[pair];  // goes out with the scan's row loads
+  const uint64_t ta = sm.atab[pair];
   uint32_t c0 = lo;
   int cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
   // Every item of the pair finds the same rows; a pair without rows (no row
@@ -551,8 +567,8 @@ template <int KS, int NT, int PC>
 __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
   __shared__ GsSmem<PC, kGsThreads> sm;
   __shared__ floatx4 red[kGsWaves][4 * NT][kWave];
-  const int na = build_worklist<kGsThreads, PC>(a.gr, a.row_offset, a.row_end, sm.off, sm.valid,
-                                            sm.apairs, sm.wcount);
+  const int na = build_worklist<kGsThreads, PC, 1>(a.gr, a.row_offset, a.row_end, sm.off,
+                                               sm.valid, sm.apairs, sm.wcount, sm.atab);
   const uint32_t per = a.nch * a.ncg;
   const uint32_t npi = (uint32_t)na * per;
   const uint32_t total = npi + a.nz;
@@ -596,7 +612,7 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
   const uint32_t kw0 = (uint32_t)wave * (32u * KS);
   uint32_t lo, hi;
   span_in_window(sm.off, g, e, a.row_offset, a.row_end, lo, hi);
-  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(g.a_table()[pair]);
+  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(sm.atab[pair]);
   const RLD_GLOBAL uint16_t* x = a.x();
   // The wave's k range lies inside k_in (every wave when k_in is a multiple of
   // 128): one pointer per operand row, the steps at immediate offsets.
@@ -690,8 +706,8 @@ template <int NT, int PC>
 __global__ __launch_bounds__(kGwThreads) void grouped_shrink_wide_kernel(GsArgs a) {
   __shared__ GsSmem<PC, kGwThreads> sm;
   __shared__ floatx4 red[kGwWaves][2 * NT][kWave];
-  const int na = build_worklist<kGwThreads, PC>(a.gr, a.row_offset, a.row_end, sm.off, sm.valid,
-                                                sm.apairs, sm.wcount);
+  const int na = build_worklist<kGwThreads, PC, 1>(a.gr, a.row_offset, a.row_end, sm.off,
+                                                   sm.valid, sm.apairs, sm.wcount, sm.atab);
   const uint32_t npi = 16u * (((uint32_t)na + 7u) / 8u);  // pair halves, in groups of 8 pairs
   const uint32_t total = npi + a.nz;
   for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
@@ -717,6 +733,8 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
   const RLD_GLOBAL uint16_t* xa = gp<const uint16_t>(xa_addr);
   const RLD_GLOBAL float* scale_table = gp<const float>(scale_addr);
   RLD_GLOBAL uint16_t* out = gp<uint16_t>(out_addr);
+  __shared__ uint64_t btab[PC];
+  __shared__ float bscale[PC];
   __shared__ int off_s[off_cap<PC>()];
   __shared__ uint8_t valid[PC];
   __shared__ int16_t apairs[PC];
@@ -725,7 +743,8 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
   __shared__ int wcount[kPeThreads / kWave];
   __shared__ __attribute__((aligned(16))) uint16_t dl[kBatch * kDlStride];
 
-  const int na = build_worklist<kPeThreads, PC>(gr, row_offset, row_end, off_s, valid, apairs, wcount);
+  const int na = build_worklist<kPeThreads, PC, 2>(gr, row_offset, row_end, off_s, valid, apairs,
+                                                   wcount, btab, bscale, scale_table);
   const int* off = off_s;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -738,8 +757,8 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
     const uint32_t j0 = (uint32_t)(it % (int)nct) * kPeCols;
     const int s = pair / (int)gr.E;
     const int e = pair % (int)gr.E;
-    const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(gr.b_table()[pair]);
-    const float scale = scale_table[pair];
+    const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(btab[pair]);
+    const float scale = bscale[pair];
     uint4 aop[4][NKS];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
