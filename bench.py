@@ -126,10 +126,10 @@ def _kernel_key(name):
     return n.split("::")[-1].strip()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary in
-    profiles/ (calibrated FETCH_SIZE + WRITE_SIZE), or None when there is none
-    for the current kernel sources."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` in `workload` from the committed
+    counter summary in profiles/ (calibrated FETCH_SIZE + WRITE_SIZE), or None
+    when there is none for this workload and the current kernel sources."""
     import glob
     digest = source_digest()
     for f in sorted(glob.glob(os.path.join(PROFILES, "*counters*.md"))):
@@ -140,12 +140,13 @@ def measured_traffic(kernel):
                 d = json.loads(block.split("```")[0])
             except ValueError:
                 continue
-            if d.get("source_digest") == digest and kernel in d.get("kernels", {}):
+            if (d.get("source_digest") == digest and d.get("workload") == workload
+                    and kernel in d.get("kernels", {})):
                 return int(d["kernels"][kernel]["traffic_bytes_per_launch"])
     return None
 
 
-def summarize(dirs, bench_json=None):
+def summarize(dirs, bench_json=None, workload="step"):
     """Markdown summary of rocprofv3 output directories: kernel-trace stats
     (*_kernel_stats.csv) and FETCH_SIZE / WRITE_SIZE counter runs
     (*_counter_collection.csv) calibrated on the COPY_BYTES copy of
@@ -189,8 +190,8 @@ def summarize(dirs, bench_json=None):
         lines.append("| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
                      "HBM MB/dispatch (calibrated) |")
         lines.append("|---|---|---|---|---|")
-        out = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES,
-               "factors": factor, "kernels": {}}
+        out = {"source_digest": source_digest(), "workload": workload,
+               "copy_bytes": COPY_BYTES, "factors": factor, "kernels": {}}
         for k, v in sorted(per.items()):
             fk = float(np.mean(v.get("FETCH_SIZE", [0.0])))
             wk = float(np.mean(v.get("WRITE_SIZE", [0.0])))
@@ -230,6 +231,13 @@ def summarize(dirs, bench_json=None):
 LANES = {"q": (0, 0), "k": (0, 1), "v": (0, 2), "o": (1, 0),
          "gate": (0, 0), "up": (0, 1), "down": (1, 0)}
 MAX_LANES = 3
+
+
+def grouped_shrink_kernel(k_in, max_rank):
+    """Kernel that rld_moe_grouped_shrink launches: the sixteen-wave one for
+    1024 < k_in <= 2048 at max_rank <= 32, the chunked one otherwise."""
+    wide = 1024 < k_in <= 2048 and max_rank <= 32
+    return "grouped_shrink_wide_kernel" if wide else "grouped_shrink_kernel"
 
 
 class Step:
@@ -367,8 +375,9 @@ class Step:
                                                                  wl.num_experts, stid, rad, lo,
                                                                  hi, base, p.n_out)
 
-                        add((f"grouped.{p.name}.[{lo},{hi}).shrink", "grouped_shrink_kernel",
-                             shrink, sb, fl / 2, hi - lo), p.name, lane)
+                        add((f"grouped.{p.name}.[{lo},{hi}).shrink",
+                             grouped_shrink_kernel(p.k_in, wl.max_rank), shrink, sb, fl / 2,
+                             hi - lo), p.name, lane)
                         add((f"grouped.{p.name}.[{lo},{hi}).expand", "grouped_expand_kernel",
                              expand, eb, fl / 2, 0), p.name, lane)
                     self.rows += wl.te
@@ -588,7 +597,7 @@ def run_gpu(args, traffic=True):
     avg_launch_s = dom["ms"] / dom["launches"] * 1e-3
     bytes_per_launch = dom["bytes"] / dom["launches"]
     achieved = bytes_per_launch / avg_launch_s / 1e9
-    traffic = measured_traffic(dom_name) if traffic else None
+    traffic = measured_traffic(dom_name, args.workload) if traffic else None
 
     per_workload = {}
     for tag, _ in wls:
@@ -697,7 +706,7 @@ def main():
                          "a counter run sees the counters of a copy of known size")
     args = ap.parse_args()
     if args.summarize:
-        print(summarize(args.summarize, args.bench_json))
+        print(summarize(args.summarize, args.bench_json, args.workload))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the routed fold has no multi-GPU path in this "
