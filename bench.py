@@ -240,6 +240,12 @@ def grouped_shrink_kernel(k_in, max_rank):
     return "grouped_shrink_wide_kernel" if wide else "grouped_shrink_kernel"
 
 
+def grouped_fused(k_in, max_rank, n_out):
+    """rld_moe_grouped runs the shrink and the fold of a window as one kernel
+    when the wide shrink applies and n_out <= 768."""
+    return grouped_shrink_kernel(k_in, max_rank) == "grouped_shrink_wide_kernel" and n_out <= 768
+
+
 class Step:
     """Device state of the whole step and the ordered list of its calls.  Every
     call has a (group, lane): calls of one group on different lanes are
@@ -375,6 +381,19 @@ class Step:
                                                                  wl.num_experts, stid, rad, lo,
                                                                  hi, base, p.n_out)
 
+                        if grouped_fused(p.k_in, wl.max_rank, p.n_out):
+                            # one call: shrink and fold of the window in one kernel
+                            def fold(rt=rt, x=x, base=base, p=p, lo=lo, hi=hi, off=off,
+                                     stid=stid, rad=rad, xa=xa, wl=wl, ws=ws, wsb=wsb):
+                                return R.rld_moe_grouped(rt.route, x, p.k_in, p.x_gather,
+                                                         wl.num_tokens, off, wl.num_experts,
+                                                         stid, rad, lo, hi, base, p.n_out, xa,
+                                                         wl.cap, ws, wsb)
+
+                            add((f"grouped.{p.name}.[{lo},{hi}).fold",
+                                 "grouped_fold_wide_kernel", fold, sb + eb, fl, hi - lo),
+                                p.name, lane)
+                            continue
                         add((f"grouped.{p.name}.[{lo},{hi}).shrink",
                              grouped_shrink_kernel(p.k_in, wl.max_rank), shrink, sb, fl / 2,
                              hi - lo), p.name, lane)

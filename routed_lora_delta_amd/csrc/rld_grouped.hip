@@ -137,16 +137,17 @@ __device__ __forceinline__ void zero_xa_row(RLD_GLOBAL uint16_t* xa, uint32_t lo
 
 // Every thread (NTH of them): stage expert_offsets in LDS, read the A/B table entries of every pair
 // (valid[p] = both present), and list in LDS, ascending, the pairs that are
-// valid and own rows of [row_offset, row_end).  KEEP = 1 also keeps every
-// pair's A table entry in keep_tab, KEEP = 2 its B entry in keep_tab and its
-// scale (scale_table) in keep_scale, so that an item has its operand address
-// without a round trip of its own.  All these loads go out together, so this
-// costs one round of loads.  Returns the pair count.
+// valid and own rows of [row_offset, row_end).  With KEEP & 1 it also keeps
+// every pair's A table entry in keep_a, with KEEP & 2 its B entry in keep_b and
+// its scale (scale_table) in keep_scale, so that an item has its operand
+// addresses without a round trip of its own.  All these loads go out
+// together, so this costs one round of loads.  Returns the pair count.
 template <int NTH, int PC, int KEEP = 0>
 __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row_offset,
                                               uint32_t row_end, int* off_s, uint8_t* valid,
                                               int16_t* apairs, int* wcount,
-                                              uint64_t* keep_tab = nullptr,
+                                              uint64_t* keep_a = nullptr,
+                                              uint64_t* keep_b = nullptr,
                                               float* keep_scale = nullptr,
                                               const RLD_GLOBAL float* scale_table = nullptr) {
   constexpr int kOffPer = (off_cap<PC>() + NTH - 1) / NTH;
@@ -170,7 +171,7 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
     const uint32_t p = threadIdx.x + i * NTH;
     ta[i] = g.a_table()[p < np ? p : 0];
     tb[i] = g.b_table()[p < np ? p : 0];
-    if (KEEP == 2) sv[i] = scale_table[p < np ? p : 0];
+    if (KEEP & 2) sv[i] = scale_table[p < np ? p : 0];
   }
 #pragma unroll
   for (int i = 0; i < kOffPer; ++i) {
@@ -182,9 +183,9 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
     const uint32_t p = threadIdx.x + i * NTH;
     if (p < np) {
       valid[p] = (ta[i] != 0ull && tb[i] != 0ull) ? 1 : 0;
-      if (KEEP == 1) keep_tab[p] = ta[i];
-      if (KEEP == 2) {
-        keep_tab[p] = tb[i];
+      if (KEEP & 1) keep_a[p] = ta[i];
+      if (KEEP & 2) {
+        keep_b[p] = tb[i];
         keep_scale[p] = sv[i];
       }
     }
@@ -232,6 +233,8 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
 // below.
 struct GsArgs {
   uint64_t x_, xa_, part_, ctr_;
+  uint64_t out_, scale_;  // fused kernel: base_out and the scale table
+  uint32_t n_out, os;     // fused kernel: output width and row stride
   GroupedRows gr;
   uint32_t xs, x_gather, k_in, R, row_offset, row_end;
   uint32_t kc;   // k chunk: 4 waves x 32*KS (16 waves x 128 in the wide kernel)
@@ -241,6 +244,8 @@ struct GsArgs {
   __device__ const RLD_GLOBAL uint16_t* x() const { return gp<const uint16_t>(x_); }
   __device__ RLD_GLOBAL uint16_t* xa() const { return gp<uint16_t>(xa_); }
   __device__ RLD_GLOBAL float* part() const { return gp<float>(part_); }
+  __device__ RLD_GLOBAL uint16_t* out() const { return gp<uint16_t>(out_); }
+  __device__ const RLD_GLOBAL float* scale_table() const { return gp<const float>(scale_); }
   // 16 bytes per pair, below the end of the workspace
   __device__ RLD_GLOBAL uint32_t* ctr(int pair) const {
     return gp<uint32_t>(ctr_) - 4 * (pair + 1);
@@ -595,9 +600,104 @@ __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
 // is rounded to xa.  A batch's x rows, and A_{s,e} over the wave's range, are
 // one round of loads: 16 x 128 KB of A and 32 x 4 KB of x rows in flight per
 // block.
-template <int NT, int PC>
+//
+// FUSE (grouped_fold_wide_kernel, n_out <= kFuseCols): the block then folds the
+// batch's rows right away, the expand of the same pair on the xa it has just
+// rounded: each wave's kFuseTiles 16-column tiles of B_{s,e} (MFMA A operands,
+// one k step of 32 covers max_rank), the batch's base rows and the xa tile
+// (from LDS) in one round, deltas -> LDS (over the wave-sum buffer) -> 16-byte
+// fold of the base rows.  The expand's own launch, row scan and xa round trip
+// through memory are saved.
+constexpr int kFuseTiles = 3;
+constexpr int kFuseCols = kGwWaves * kFuseTiles * 16;  // 768
+constexpr int kFuseStride = kFuseCols + 8;             // LDS row stride of the delta tile
+constexpr int kXlStride = 32 + 8;                       // LDS row stride of the xa tile
+
+// Fused fold of one batch (see gs_wide_item): rows[0, nb) of the sorted rows,
+// their xa (BF16, max_rank <= 32 columns) in xl, deltas staged in dl, n_out <=
+// kFuseCols.  Every thread of the 1024 calls it.
+__device__ __forceinline__ void wide_fold_batch(const GsArgs& a, const int* rows, int nb,
+                                                uint64_t b_addr, float scale, const uint16_t* xl,
+                                                uint16_t* dl) {
+  constexpr int kPieces = 32 * (kFuseCols / 8) / kGwThreads;  // 16-byte base pieces per thread
+  const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(b_addr);
+  RLD_GLOBAL uint16_t* out = a.out();
+  const uint32_t R = a.R, n_out = a.n_out;
+  // The thread index passes through an empty asm: the fold's per-thread
+  // offsets are then computed here, not hoisted to the kernel's start where
+  // they would hold registers through the shrink.
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lg = lane >> 4;
+  const int cl = lane & 15;
+  const bool kin = (uint32_t)(8 * lg) < R;  // this lane's 8 k of the 32-wide step hold rank
+  // One column chunk (n_out <= kFuseCols), in straight-line code: a loop over
+  // chunks, entered with the xa stores outstanding, waits for them before the
+  // chunk's loads.
+  {
+    constexpr uint32_t cc = 0;
+    // one round: B tiles, base pieces, xa fragments (clamped in-bounds addresses)
+    uint4 bt[kFuseTiles];
+#pragma unroll
+    for (int t = 0; t < kFuseTiles; ++t) {
+      const uint32_t col = cc + (uint32_t)(wave * kFuseTiles + t) * 16u + cl;
+      bt[t] = load16(B + (size_t)(col < n_out ? col : 0) * R + (kin ? 8 * lg : 0));
+    }
+    uint4 bv[kPieces];
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int ei = tid + kGwThreads * j;
+      const int rl = ei / (kFuseCols / 8);
+      const uint32_t col = cc + (uint32_t)(ei % (kFuseCols / 8)) * 8u;
+      bv[j] = load16(out + (size_t)rows[rl < nb ? rl : 0] * a.os + (col < n_out ? col : cc));
+    }
+    uint4 xf[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      xf[q] = kin ? *reinterpret_cast<const uint4*>(&xl[(q * 16 + cl) * kXlStride + 8 * lg])
+                  : zero16();
+    issue_point();
+    // k past max_rank and columns past n_out contribute nothing
+#pragma unroll
+    for (int t = 0; t < kFuseTiles; ++t) {
+      const uint32_t col = cc + (uint32_t)(wave * kFuseTiles + t) * 16u + cl;
+      if (!kin || col >= n_out) bt[t] = zero16();
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (q * 16 >= nb) continue;
+#pragma unroll
+      for (int t = 0; t < kFuseTiles; ++t) {
+        const floatx4 acc = mfma_bf16_16x16x32(bt[t], xf[q], floatx4{0.f, 0.f, 0.f, 0.f});
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2*>(
+            &dl[(q * 16 + cl) * kFuseStride + (wave * kFuseTiles + t) * 16 + 4 * lg]) =
+            u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int ei = tid + kGwThreads * j;
+      const int rl = ei / (kFuseCols / 8);
+      const int c8 = (ei % (kFuseCols / 8)) * 8;
+      const uint32_t col = cc + (uint32_t)c8;
+      if (rl < nb && col < n_out) {
+        const uint4 dv = *reinterpret_cast<const uint4*>(&dl[rl * kFuseStride + c8]);
+        store16(out + (size_t)rows[rl] * a.os + col, fold8(bv[j], dv, scale));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int NT, int PC, bool FUSE>
 __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
-                             floatx4 (*red)[2 * NT][kWave], int pair, int h) {
+                             floatx4 (*red)[2 * NT][kWave], int pair, int h,
+                             const uint64_t* btab = nullptr, const float* bscale = nullptr,
+                             uint16_t* xl = nullptr) {
   constexpr int KS = 4;   // MFMA steps per wave: 128 k
   constexpr int QB = 2;   // 16-row subtiles per batch
   constexpr int kRows = 16 * QB;
@@ -612,41 +712,54 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
   const uint32_t kw0 = (uint32_t)wave * (32u * KS);
   uint32_t lo, hi;
   span_in_window(sm.off, g, e, a.row_offset, a.row_end, lo, hi);
-  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(sm.atab[pair]);
   const RLD_GLOBAL uint16_t* x = a.x();
   // The wave's k range lies inside k_in (every wave when k_in is a multiple of
   // 128): one pointer per operand row, the steps at immediate offsets.
   // Otherwise clamped in-bounds addresses, and k past k_in zeroed once loaded.
   const bool full = kw0 + 32u * KS <= k_in;
   // A_{s,e} over the wave's k range serves every batch of the item: it goes
-  // out before the row scan, whose first wait covers it.
+  // out before the row scan, whose first wait covers it.  The fused kernel
+  // loads it with each batch's x rows instead, so that it is not held through
+  // the fold (which needs those registers).
   uint4 bop[NT][KS];
+  auto load_a = [&]() {
+    // the address is read from LDS at each call: computed once and kept, the
+    // eight row addresses would hold registers through the fold
+    const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(sm.atab[pair]);
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const uint32_t col = 16u * j + cl;
-    const RLD_GLOBAL uint16_t* ar = A + (size_t)(col < R ? col : 0) * k_in;
+    for (int j = 0; j < NT; ++j) {
+      const uint32_t col = 16u * j + cl;
+      const RLD_GLOBAL uint16_t* ar = A + (size_t)(col < R ? col : 0) * k_in;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t kk = kw0 + 32u * ks + 8u * lg;
-      bop[j][ks] = load16(full ? ar + kk : ar + (kk < k_in ? kk : 0));
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t kk = kw0 + 32u * ks + 8u * lg;
+        bop[j][ks] = load16(full ? ar + kk : ar + (kk < k_in ? kk : 0));
+      }
     }
+  };
+  auto mask_a = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      if (kw0 + 32u * ks + 8u * lg >= k_in) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) bop[j][ks] = zero16();
+      }
+  };
+  if (!FUSE) {
+    load_a();
+    issue_point();
   }
-  issue_point();
-  bool masked = full;
+  bool masked = full || FUSE;
   uint32_t c0 = lo;
   while (c0 < hi) {
     const int cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
     if (!masked) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        if (kw0 + 32u * ks + 8u * lg >= k_in) {
-#pragma unroll
-          for (int j = 0; j < NT; ++j) bop[j][ks] = zero16();
-        }
+      mask_a();
       masked = true;
     }
     for (int b0 = kRows * h; b0 < cnt; b0 += 2 * kRows) {
       const int nb = min(cnt - b0, kRows);
+      if (FUSE) load_a();
       uint4 aop[QB][KS];
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
@@ -660,6 +773,7 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
       }
       issue_point();
       if (!full) {
+        if (FUSE) mask_a();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           if (kw0 + 32u * ks + 8u * lg >= k_in) {
@@ -690,14 +804,38 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int li = q * 16 + 4 * (ln >> 4) + i;
+            const uint16_t v = (uint16_t)f32_to_bf16(sum[i]);
+            if (FUSE) xl[li * kXlStride + col] = v;
             if (li < nb) {
               const uint32_t lr = (uint32_t)sm.list[b0 + li] - a.row_offset;
-              a.xa()[(size_t)lr * R + col] = (uint16_t)f32_to_bf16(sum[i]);
+              a.xa()[(size_t)lr * R + col] = v;
             }
           }
         }
       }
       __syncthreads();
+      if (FUSE) wide_fold_batch(a, sm.list + b0, nb, btab[pair], bscale[pair], xl,
+                                reinterpret_cast<uint16_t*>(&red[0][0][0]));
+    }
+  }
+}
+
+// Items of the wide kernels: pair halves in groups of 8 pairs, then row blocks.
+template <int NT, int PC, bool FUSE>
+__device__ __forceinline__ void wide_items(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
+                                           floatx4 (*red)[2 * NT][kWave], int na,
+                                           const uint64_t* btab, const float* bscale,
+                                           uint16_t* xl) {
+  const uint32_t npi = 16u * (((uint32_t)na + 7u) / 8u);
+  const uint32_t total = npi + a.nz;
+  for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
+    if (it < npi) {
+      const uint32_t p = (it / 16u) * 8u + it % 8u;
+      if (p < (uint32_t)na)
+        gs_wide_item<NT, PC, FUSE>(a, sm, red, sm.apairs[p], (int)((it / 8u) % 2u), btab, bscale,
+                                   xl);
+    } else {
+      gs_zero_item(a, sm, it - npi);
     }
   }
 }
@@ -708,16 +846,26 @@ __global__ __launch_bounds__(kGwThreads) void grouped_shrink_wide_kernel(GsArgs 
   __shared__ floatx4 red[kGwWaves][2 * NT][kWave];
   const int na = build_worklist<kGwThreads, PC, 1>(a.gr, a.row_offset, a.row_end, sm.off,
                                                    sm.valid, sm.apairs, sm.wcount, sm.atab);
-  const uint32_t npi = 16u * (((uint32_t)na + 7u) / 8u);  // pair halves, in groups of 8 pairs
-  const uint32_t total = npi + a.nz;
-  for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
-    if (it < npi) {
-      const uint32_t p = (it / 16u) * 8u + it % 8u;
-      if (p < (uint32_t)na) gs_wide_item<NT, PC>(a, sm, red, sm.apairs[p], (int)((it / 8u) % 2u));
-    } else {
-      gs_zero_item(a, sm, it - npi);
-    }
-  }
+  wide_items<NT, PC, false>(a, sm, red, na, nullptr, nullptr, nullptr);
+}
+
+// Shrink and fold of a window in one launch (rld_moe_grouped in the wide case).
+// The wave-sum buffer doubles as the delta tile of the fold.
+template <int NT, int PC>
+__global__ __launch_bounds__(kGwThreads) void grouped_fold_wide_kernel(GsArgs a) {
+  constexpr size_t kRedBytes = sizeof(floatx4) * kGwWaves * 2 * NT * kWave;
+  constexpr size_t kDlBytes = sizeof(uint16_t) * 32 * kFuseStride;
+  __shared__ GsSmem<PC, kGwThreads> sm;
+  __shared__ uint64_t btab[PC];
+  __shared__ float bscale[PC];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[32 * kXlStride];
+  __shared__ __attribute__((aligned(16))) unsigned char buf[kRedBytes > kDlBytes ? kRedBytes
+                                                                                : kDlBytes];
+  auto red = reinterpret_cast<floatx4 (*)[2 * NT][kWave]>(buf);
+  const int na = build_worklist<kGwThreads, PC, 3>(a.gr, a.row_offset, a.row_end, sm.off,
+                                                   sm.valid, sm.apairs, sm.wcount, sm.atab, btab,
+                                                   bscale, a.scale_table());
+  wide_items<NT, PC, true>(a, sm, red, na, btab, bscale, xl);
 }
 
 // Item: (pair, 512 output columns).  The pair's B rows for the columns go to
@@ -744,7 +892,7 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t dl[kBatch * kDlStride];
 
   const int na = build_worklist<kPeThreads, PC, 2>(gr, row_offset, row_end, off_s, valid, apairs,
-                                                   wcount, btab, bscale, scale_table);
+                                                   wcount, nullptr, btab, bscale, scale_table);
   const int* off = off_s;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -916,13 +1064,16 @@ extern "C" size_t rld_moe_grouped_workspace_bytes(uint32_t window_rows, uint32_t
   return grouped_workspace(window_rows, k_in, max_rank, max_loras, num_experts);
 }
 
-extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
-                                      uint32_t x_row_stride, int x_gather, uint32_t num_tokens,
-                                      const int32_t* expert_offsets, uint32_t num_experts_off,
-                                      const int32_t* sorted_token_ids,
-                                      const int32_t* row_adapter, uint32_t row_offset,
-                                      uint32_t row_end, void* xa, uint32_t xa_rows_cap,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+// The shrink of a window; with fold_out (rld_moe_grouped) in the wide case
+// the fused kernel also folds the window into fold_out and *folded is set.
+static int grouped_shrink(const rld_moe_route* route, const void* x, uint32_t x_row_stride,
+                          int x_gather, uint32_t num_tokens, const int32_t* expert_offsets,
+                          uint32_t num_experts_off, const int32_t* sorted_token_ids,
+                          const int32_t* row_adapter, uint32_t row_offset, uint32_t row_end,
+                          void* xa, uint32_t xa_rows_cap, void* workspace,
+                          size_t workspace_bytes, void* stream, void* fold_out,
+                          uint32_t fold_os, bool* folded) {
+  *folded = false;
   int st = check_grouped(route, x_gather, expert_offsets, num_experts_off, sorted_token_ids,
                          row_adapter, row_offset, row_end);
   if (st) return st;
@@ -939,7 +1090,7 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
     if (!aligned16(workspace)) return RLD_EALIGN;
     if (workspace_bytes < need) return RLD_ENOSPACE;
   }
-  GsArgs a;
+  GsArgs a = GsArgs{};
   a.x_ = reinterpret_cast<uint64_t>(x);
   a.xa_ = reinterpret_cast<uint64_t>(xa);
   a.part_ = reinterpret_cast<uint64_t>(workspace);
@@ -967,6 +1118,17 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
                               : grouped_shrink_wide_kernel<1, kPairCapLarge>)
                         : (sm ? grouped_shrink_wide_kernel<2, kPairCapSmall>
                               : grouped_shrink_wide_kernel<2, kPairCapLarge>);
+    if (fold_out && route->n_out <= (uint32_t)kFuseCols) {
+      a.out_ = reinterpret_cast<uint64_t>(fold_out);
+      a.os = fold_os;
+      a.n_out = route->n_out;
+      a.scale_ = reinterpret_cast<uint64_t>(route->scale_table);
+      kern = nt == 1 ? (sm ? grouped_fold_wide_kernel<1, kPairCapSmall>
+                           : grouped_fold_wide_kernel<1, kPairCapLarge>)
+                     : (sm ? grouped_fold_wide_kernel<2, kPairCapSmall>
+                           : grouped_fold_wide_kernel<2, kPairCapLarge>);
+      *folded = true;
+    }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kGwThreads), 0, hs, a);
     return launch_status();
   }
@@ -978,6 +1140,19 @@ extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
   else
     launch_gs_ks<kPairCapLarge>(a.kc / 128u, nt, a, grid, hs);
   return launch_status();
+}
+
+extern "C" int rld_moe_grouped_shrink(const rld_moe_route* route, const void* x,
+                                      uint32_t x_row_stride, int x_gather, uint32_t num_tokens,
+                                      const int32_t* expert_offsets, uint32_t num_experts_off,
+                                      const int32_t* sorted_token_ids,
+                                      const int32_t* row_adapter, uint32_t row_offset,
+                                      uint32_t row_end, void* xa, uint32_t xa_rows_cap,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  bool folded;
+  return grouped_shrink(route, x, x_row_stride, x_gather, num_tokens, expert_offsets,
+                        num_experts_off, sorted_token_ids, row_adapter, row_offset, row_end, xa,
+                        xa_rows_cap, workspace, workspace_bytes, stream, nullptr, 0, &folded);
 }
 
 extern "C" int rld_moe_grouped_expand_fold(const rld_moe_route* route, const void* xa,
@@ -1024,10 +1199,12 @@ extern "C" int rld_moe_grouped(const rld_moe_route* route, const void* x, uint32
                          row_adapter, row_offset, row_end);
   if (st) return st;
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
-  st = rld_moe_grouped_shrink(route, x, x_row_stride, x_gather, num_tokens, expert_offsets,
-                              num_experts_off, sorted_token_ids, row_adapter, row_offset,
-                              row_end, xa, xa_rows_cap, workspace, workspace_bytes, stream);
-  if (st) return st;
+  bool folded = false;
+  st = grouped_shrink(route, x, x_row_stride, x_gather, num_tokens, expert_offsets,
+                      num_experts_off, sorted_token_ids, row_adapter, row_offset, row_end, xa,
+                      xa_rows_cap, workspace, workspace_bytes, stream, base_out, out_row_stride,
+                      &folded);
+  if (st || folded) return st;
   return rld_moe_grouped_expand_fold(route, xa, num_tokens, expert_offsets, num_experts_off,
                                      sorted_token_ids, row_adapter, row_offset, row_end,
                                      base_out, out_row_stride, stream);

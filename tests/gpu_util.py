@@ -370,16 +370,31 @@ class GroupedRun:
                                                           wl.max_loras, wl.num_experts)
         self.ws = torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
 
-    def run(self, windows=None, keep_xa=True):
+    def run(self, windows=None, keep_xa=True, separate=False):
+        """Every window through rld_moe_grouped (which may fuse the two
+        stages), or with separate=True through rld_moe_grouped_shrink then
+        rld_moe_grouped_expand_fold."""
         wl, p = self.wl, self.p
         windows = windows if windows is not None else O.grouped_down_windows(wl.te, self.cap)
         xas = []
         for lo, hi in windows:
-            R.check(R.rld_moe_grouped(self.route.route, self.x, p.k_in, p.x_gather, wl.num_tokens,
-                                      self.off, wl.num_experts, self.stid, self.rad, lo, hi,
-                                      self.base.ptr(), p.n_out, self.xa, self.cap, self.ws,
-                                      self.ws_bytes),
-                    "rld_moe_grouped")
+            if separate:
+                R.check(R.rld_moe_grouped_shrink(self.route.route, self.x, p.k_in, p.x_gather,
+                                                 wl.num_tokens, self.off, wl.num_experts,
+                                                 self.stid, self.rad, lo, hi, self.xa, self.cap,
+                                                 self.ws, self.ws_bytes),
+                        "rld_moe_grouped_shrink")
+                R.check(R.rld_moe_grouped_expand_fold(self.route.route, self.xa, wl.num_tokens,
+                                                      self.off, wl.num_experts, self.stid,
+                                                      self.rad, lo, hi, self.base.ptr(),
+                                                      p.n_out),
+                        "rld_moe_grouped_expand_fold")
+            else:
+                R.check(R.rld_moe_grouped(self.route.route, self.x, p.k_in, p.x_gather,
+                                          wl.num_tokens, self.off, wl.num_experts, self.stid,
+                                          self.rad, lo, hi, self.base.ptr(), p.n_out, self.xa,
+                                          self.cap, self.ws, self.ws_bytes),
+                        "rld_moe_grouped")
             if keep_xa:
                 torch.cuda.synchronize()
                 xas.append(from_device_u16(self.xa)[: (hi - lo) * wl.max_rank]

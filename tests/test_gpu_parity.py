@@ -400,20 +400,23 @@ def test_moe_grouped_large_route(max_loras, num_experts):
 @pytest.mark.parametrize("k_in,max_rank,proj", [(2048, 32, "gate"), (1032, 16, "gate"),
                                                 (1544, 32, "down"), (2048, 24, "down"),
                                                 (1160, 32, "gate")])
-def test_moe_grouped_wide(k_in, max_rank, proj):
+@pytest.mark.parametrize("separate", [False, True])
+def test_moe_grouped_wide(k_in, max_rank, proj, separate):
     """1024 < k_in <= 2048 at max_rank <= 32: one sixteen-wave block per pair
     half covers all of k_in; k_in not a multiple of 128 leaves one wave's range
-    partly past k_in and later ones wholly past it.  Pairs of up to ~100 rows
-    (both halves, several batches each), windows of 333 rows against the oracle,
-    and the full window bit-identical to their union."""
+    partly past k_in and later ones wholly past it.  Through rld_moe_grouped
+    (the shrink and fold in one kernel, n_out <= 768 here) or the two stages
+    separately.  Pairs of up to ~100 rows (both halves, several batches each),
+    windows of 333 rows against the oracle, and the full window bit-identical
+    to their union."""
     dev = require_gpu()
     sizes = dict(hidden=k_in, inter=264) if proj == "gate" else dict(hidden=264, inter=k_in)
     wl = _small_grouped(seed=7, num_experts=4, n_adapted=3, max_rank=max_rank,
                         ranks=(8, max_rank), cap=333, projections=(proj,), **sizes)
     p = wl.projections[0]
-    say(f"case: grouped wide {proj} k_in={k_in} max_rank={max_rank}")
+    say(f"case: grouped wide {proj} k_in={k_in} max_rank={max_rank} separate={separate}")
     run = GroupedRun(wl, p, dev, cap=wl.cap)
-    xas = run.run()
+    xas = run.run(separate=separate)
     base = p.base.ravel().copy()
     for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
         xa_o, base = oracle_grouped_window(wl, p, lo, hi, base)
@@ -422,7 +425,7 @@ def test_moe_grouped_wide(k_in, max_rank, proj):
         assert np.all(xa_g[np.all(xa_o == 0, axis=1)] == 0)
     assert_out_close(run.base.body(), base, "wide out")
     full = GroupedRun(wl, p, dev, cap=wl.te)
-    xa_full = full.run([(0, wl.te)])[0]
+    xa_full = full.run([(0, wl.te)], separate=not separate)[0]
     assert np.array_equal(np.concatenate(xas), xa_full)
     assert np.array_equal(full.base.body(), run.base.body())
 
