@@ -334,7 +334,11 @@ int rld_moe_grouped_expand_fold(const rld_moe_route* route, const void* xa, uint
                                 uint32_t row_offset, uint32_t row_end, void* base_out,
                                 uint32_t out_row_stride, void* stream);
 
-/* moe_lora_grouped_down for one window: shrink then expand + fold. */
+/* moe_lora_grouped_down for one window: shrink then expand + fold, with the
+ * results of the two calls above (xa written the same way, base_out folded
+ * bit-identically).  When 1024 < k_in <= 2048, max_rank <= 32 and
+ * n_out <= 768 both stages run in one launch, each block folding the rows it
+ * has just contracted; otherwise it is the two launches. */
 int rld_moe_grouped(const rld_moe_route* route, const void* x, uint32_t x_row_stride,
                     int x_gather, uint32_t num_tokens, const int32_t* expert_offsets,
                     uint32_t num_experts_off, const int32_t* sorted_token_ids,
