@@ -166,6 +166,33 @@ def summarize(dirs, bench_json=None, workload="step"):
                          f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
                          f"{float(r['Percentage']):.1f}% |")
         lines.append("")
+    traces = [f for d in dirs for f in glob.glob(os.path.join(d, "**", "*_kernel_trace.csv"),
+                                                  recursive=True)]
+    for f in traces:
+        # launches that overlapped no other launch, against all of them: the
+        # step graph runs independent calls on parallel branches, and a kernel
+        # sharing the chip with another takes longer than one running alone
+        ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                    for r in csv.DictReader(open(f)))
+        alone = {}
+        last_end = -1
+        for i, (t0, t1, name) in enumerate(ev):
+            nxt = ev[i + 1][0] if i + 1 < len(ev) else None
+            solo = t0 >= last_end and (nxt is None or nxt >= t1)
+            last_end = max(last_end, t1)
+            if "rld::" not in name:
+                continue
+            k = alone.setdefault(_kernel_key(name), [[], []])
+            k[0].append((t1 - t0) / 1e3)
+            if solo:
+                k[1].append((t1 - t0) / 1e3)
+        lines.append(f"Launches that ran alone ({os.path.relpath(f)}):\n")
+        lines.append("| kernel | launches | alone | mean us, all | mean us, alone |")
+        lines.append("|---|---|---|---|---|")
+        for k, (al, so) in sorted(alone.items()):
+            lines.append(f"| {k} | {len(al)} | {len(so)} | {np.mean(al):.3f} | "
+                         f"{(np.mean(so) if so else float('nan')):.3f} |")
+        lines.append("")
     counters = {}
     for d in dirs:
         for f in glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True):
