@@ -273,6 +273,15 @@ def grouped_fused(k_in, max_rank, n_out):
     return grouped_shrink_kernel(k_in, max_rank) == "grouped_shrink_wide_kernel" and n_out <= 768
 
 
+def grouped_pair_fused(pa, pb, wl):
+    """rld_moe_grouped_pair folds the two projections in one launch (the same
+    input rows, both fusable, at most 512 (slot, expert) pairs)."""
+    return (pa.x is pb.x and pa.k_in == pb.k_in
+            and grouped_fused(pa.k_in, wl.max_rank, pa.n_out)
+            and grouped_fused(pb.k_in, wl.max_rank, pb.n_out)
+            and wl.max_loras * wl.num_experts <= 512 and wl.num_experts < 511)
+
+
 class Step:
     """Device state of the whole step and the ordered list of its calls.  Every
     call has a (group, lane): calls of one group on different lanes are
@@ -384,16 +393,43 @@ class Step:
                                                              for p in wl.projections)))]
                 keep += [off, stid, rad, lanes]
                 order = {"gate": 0, "up": 1, "down": 2}
-                for p in sorted(wl.projections, key=lambda q: order.get(q.name, 3)):
+                projs = sorted(wl.projections, key=lambda q: order.get(q.name, 3))
+                dev_p = {}
+                for p in projs:
                     rt = MoeRoute(p.adapters, wl.max_loras, wl.num_experts, wl.max_rank, p.k_in,
                                   p.n_out, dev)
                     x = to_device_u16(p.x.ravel(), dev)
                     base = to_device_u16(p.base.ravel(), dev)
                     keep += [rt, x, base]
+                    dev_p[p.name] = (rt, x, base)
+                byname = {p.name: p for p in projs}
+                paired = ("gate" in byname and "up" in byname
+                          and grouped_pair_fused(byname["gate"], byname["up"], wl))
+                for p in projs:
+                    rt, x, base = dev_p[p.name]
+                    if paired and p.name == "up":
+                        continue  # folded with gate, one call per window
                     for k, (lo, hi) in enumerate(wins):
                         lane = LANES.get(p.name, (0, 0))[1] * len(wins) + k
                         xa, ws = lanes[lane]
                         sb, eb, fl, _ = grouped_window_bytes(wl, p, lo, hi)
+                        if paired and p.name == "gate":
+                            q = byname["up"]
+                            rt_b, _, base_b = dev_p["up"]
+                            xa_b = lanes[LANES["up"][1] * len(wins) + k][0]
+                            sb2, eb2, fl2, _ = grouped_window_bytes(wl, q, lo, hi)
+
+                            def pair(rt=rt, rt_b=rt_b, x=x, base=base, base_b=base_b, p=p, q=q,
+                                     lo=lo, hi=hi, off=off, stid=stid, rad=rad, xa=xa, xa_b=xa_b,
+                                     wl=wl, ws=ws, wsb=wsb):
+                                return R.rld_moe_grouped_pair(
+                                    rt.route, rt_b.route, x, p.k_in, p.x_gather, wl.num_tokens,
+                                    off, wl.num_experts, stid, rad, lo, hi, base, p.n_out,
+                                    base_b, q.n_out, xa, xa_b, wl.cap, ws, wsb)
+
+                            add((f"grouped.gate+up.[{lo},{hi}).fold", "grouped_fold_pair_kernel",
+                                 pair, sb + eb + sb2 + eb2, fl + fl2, 2 * (hi - lo)), p.name, lane)
+                            continue
 
                         def shrink(rt=rt, x=x, p=p, lo=lo, hi=hi, off=off, stid=stid, rad=rad,
                                    xa=xa, wl=wl, ws=ws, wsb=wsb):
@@ -426,7 +462,7 @@ class Step:
                              hi - lo), p.name, lane)
                         add((f"grouped.{p.name}.[{lo},{hi}).expand", "grouped_expand_kernel",
                              expand, eb, fl / 2, 0), p.name, lane)
-                    self.rows += wl.te
+                self.rows += wl.te * len(projs)
             group0 = max((g for g, _ in self.sched), default=-1) + 1
         self._keep = keep
         self.bytes = sum(c[3] for c in self.calls)

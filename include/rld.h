@@ -346,6 +346,25 @@ int rld_moe_grouped(const rld_moe_route* route, const void* x, uint32_t x_row_st
                     void* base_out, uint32_t out_row_stride, void* xa, uint32_t xa_rows_cap,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Two projections that read the same x rows under the same routing -- a gated
+ * FFN's gate and up -- over one window: the results of rld_moe_grouped(route_a,
+ * ..., base_a, os_a, xa_a, ...) followed by rld_moe_grouped(route_b, ...,
+ * base_b, os_b, xa_b, ...), bit for bit.  When both routes have the same k_in,
+ * max_rank, max_loras and num_experts, 1024 < k_in <= 2048, max_rank <= 32,
+ * both n_out <= 768 and max_loras * num_experts <= 512, it is one launch that
+ * shares the row scan between the projections; otherwise it is those two
+ * calls (the workspace then serves them in turn).  A (slot, expert) pair that
+ * only one route adapts folds in that projection alone; xa rows of the other
+ * are written as zeros.  Errors as rld_moe_grouped for either route. */
+int rld_moe_grouped_pair(const rld_moe_route* route_a, const rld_moe_route* route_b,
+                         const void* x, uint32_t x_row_stride, int x_gather, uint32_t num_tokens,
+                         const int32_t* expert_offsets, uint32_t num_experts_off,
+                         const int32_t* sorted_token_ids, const int32_t* row_adapter,
+                         uint32_t row_offset, uint32_t row_end, void* base_a, uint32_t os_a,
+                         void* base_b, uint32_t os_b, void* xa_a, void* xa_b,
+                         uint32_t xa_rows_cap, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* ------------------------------------------------------------ diagnostics -- */
 
 const char* rld_status_string(int status);

@@ -112,6 +112,9 @@ _SIGS = {
     "rld_moe_grouped": (c_int, [_M, _P, c_uint32, c_int, c_uint32, _P, c_uint32, _P, _P,
                                 c_uint32, c_uint32, _P, c_uint32, _P, c_uint32, _P, c_size_t,
                                 _P]),
+    "rld_moe_grouped_pair": (c_int, [_M, _M, _P, c_uint32, c_int, c_uint32, _P, c_uint32, _P,
+                                     _P, c_uint32, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P,
+                                     c_uint32, _P, c_size_t, _P]),
     "rld_status_string": (ctypes.c_char_p, [c_int]),
     "rld_last_hip_error": (c_int, []),
     "rld_version": (ctypes.c_char_p, []),
@@ -318,6 +321,19 @@ def rld_moe_grouped(route, x, x_row_stride, x_gather, num_tokens, expert_offsets
                                 ptr(sorted_token_ids), ptr(row_adapter), row_offset, row_end,
                                 ptr(base_out), out_row_stride, ptr(xa), xa_rows_cap,
                                 ptr(workspace), workspace_bytes, stream_handle(stream))
+
+
+def rld_moe_grouped_pair(route_a, route_b, x, x_row_stride, x_gather, num_tokens,
+                         expert_offsets, num_experts_off, sorted_token_ids, row_adapter,
+                         row_offset, row_end, base_a, os_a, base_b, os_b, xa_a, xa_b,
+                         xa_rows_cap, workspace, workspace_bytes, stream=None):
+    return _lib.rld_moe_grouped_pair(ctypes.byref(route_a), ctypes.byref(route_b), ptr(x),
+                                     x_row_stride, int(x_gather), num_tokens,
+                                     ptr(expert_offsets), num_experts_off,
+                                     ptr(sorted_token_ids), ptr(row_adapter), row_offset,
+                                     row_end, ptr(base_a), os_a, ptr(base_b), os_b, ptr(xa_a),
+                                     ptr(xa_b), xa_rows_cap, ptr(workspace), workspace_bytes,
+                                     stream_handle(stream))
 
 
 def library_path() -> str:

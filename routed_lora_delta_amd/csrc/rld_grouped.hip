@@ -138,18 +138,29 @@ __device__ __forceinline__ void zero_xa_row(RLD_GLOBAL uint16_t* xa, uint32_t lo
 // Every thread (NTH of them): stage expert_offsets in LDS, read the A/B table entries of every pair
 // (valid[p] = both present), and list in LDS, ascending, the pairs that are
 // valid and own rows of [row_offset, row_end).  With KEEP & 1 it also keeps
-// every pair's A table entry in keep_a, with KEEP & 2 its B entry in keep_b and
-// its scale (scale_table) in keep_scale, so that an item has its operand
-// addresses without a round trip of its own.  All these loads go out
-// together, so this costs one round of loads.  Returns the pair count.
-template <int NTH, int PC, int KEEP = 0>
+// every pair's A table entry in k0.a, with KEEP & 2 its B entry in k0.b and its
+// scale (k0.scale_table) in k0.scale, so that an item has its operand addresses
+// without a round trip of its own.  NR = 2 (a launch folding two routes that
+// share the routing) reads the second route's tables k1.at, k1.bt and
+// k1.scale_table too and keeps them in k1.a, k1.b, k1.scale; valid[p] then has
+// bit r set when route r adapts pair p, and a pair is listed when either does.
+// All these loads go out together, so this costs one round of loads.  Returns
+// the pair count.
+struct PairKeep {
+  uint64_t* a = nullptr;
+  uint64_t* b = nullptr;
+  float* scale = nullptr;
+  const RLD_GLOBAL float* scale_table = nullptr;
+  const RLD_GLOBAL uint64_t* at = nullptr;  // second route's tables (NR = 2)
+  const RLD_GLOBAL uint64_t* bt = nullptr;
+};
+
+template <int NTH, int PC, int KEEP = 0, int NR = 1>
 __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row_offset,
                                               uint32_t row_end, int* off_s, uint8_t* valid,
                                               int16_t* apairs, int* wcount,
-                                              uint64_t* keep_a = nullptr,
-                                              uint64_t* keep_b = nullptr,
-                                              float* keep_scale = nullptr,
-                                              const RLD_GLOBAL float* scale_table = nullptr) {
+                                              const PairKeep& k0 = PairKeep{},
+                                              const PairKeep& k1 = PairKeep{}) {
   constexpr int kOffPer = (off_cap<PC>() + NTH - 1) / NTH;
   constexpr int kPairPer = (PC + NTH - 1) / NTH;
   const int lane = threadIdx.x & 63;
@@ -159,6 +170,8 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
   int ov[kOffPer];
   uint64_t ta[kPairPer], tb[kPairPer];
   float sv[kPairPer];
+  uint64_t ta2[NR == 2 ? kPairPer : 1], tb2[NR == 2 ? kPairPer : 1];
+  float sv2[NR == 2 ? kPairPer : 1];
 #pragma unroll
   for (int i = 0; i < kOffPer; ++i) {
     const uint32_t j = threadIdx.x + i * NTH;
@@ -169,9 +182,15 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
 #pragma unroll
   for (int i = 0; i < kPairPer; ++i) {
     const uint32_t p = threadIdx.x + i * NTH;
-    ta[i] = g.a_table()[p < np ? p : 0];
-    tb[i] = g.b_table()[p < np ? p : 0];
-    if (KEEP & 2) sv[i] = scale_table[p < np ? p : 0];
+    const uint32_t pc = p < np ? p : 0;
+    ta[i] = g.a_table()[pc];
+    tb[i] = g.b_table()[pc];
+    if (KEEP & 2) sv[i] = k0.scale_table[pc];
+    if (NR == 2) {
+      ta2[i] = k1.at[pc];
+      tb2[i] = k1.bt[pc];
+      sv2[i] = k1.scale_table[pc];
+    }
   }
 #pragma unroll
   for (int i = 0; i < kOffPer; ++i) {
@@ -182,11 +201,18 @@ __device__ __forceinline__ int build_worklist(const GroupedRows& g, uint32_t row
   for (int i = 0; i < kPairPer; ++i) {
     const uint32_t p = threadIdx.x + i * NTH;
     if (p < np) {
-      valid[p] = (ta[i] != 0ull && tb[i] != 0ull) ? 1 : 0;
-      if (KEEP & 1) keep_a[p] = ta[i];
+      uint8_t v = (ta[i] != 0ull && tb[i] != 0ull) ? 1 : 0;
+      if (NR == 2) v |= (ta2[i] != 0ull && tb2[i] != 0ull) ? 2 : 0;
+      valid[p] = v;
+      if (KEEP & 1) k0.a[p] = ta[i];
       if (KEEP & 2) {
-        keep_b[p] = tb[i];
-        keep_scale[p] = sv[i];
+        k0.b[p] = tb[i];
+        k0.scale[p] = sv[i];
+      }
+      if (NR == 2) {
+        k1.a[p] = ta2[i];
+        k1.b[p] = tb2[i];
+        k1.scale[p] = sv2[i];
       }
     }
   }
@@ -235,6 +261,9 @@ struct GsArgs {
   uint64_t x_, xa_, part_, ctr_;
   uint64_t out_, scale_;  // fused kernel: base_out and the scale table
   uint32_t n_out, os;     // fused kernel: output width and row stride
+  // pair kernel: the second projection's xa, output, tables
+  uint64_t xa2_, out2_, scale2_, atab2_, btab2_;
+  uint32_t n_out2, os2;
   GroupedRows gr;
   uint32_t xs, x_gather, k_in, R, row_offset, row_end;
   uint32_t kc;   // k chunk: 4 waves x 32*KS (16 waves x 128 in the wide kernel)
@@ -549,7 +578,7 @@ __device__ void gs_pair_item(const GsArgs& a, GsSmem<PC, kGsThreads>& sm, floatx
 // range, slot out of range or not adapted for the expert).
 template <int PC, int NTH>
 __device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem<PC, NTH>& sm,
-                                             uint32_t z) {
+                                             uint32_t z, uint64_t xa2 = 0) {
   const GroupedRows& g = a.gr;
   const uint32_t r = a.row_offset + z * NTH + threadIdx.x;
   if (r >= a.row_end) return;
@@ -563,7 +592,10 @@ __device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem<PC, N
   int s = 0;
   if (fold) s = token_slot(g, t);
   fold = fold && s >= 0 && (uint32_t)s < g.max_loras && sm.valid[s * (int)g.E + e];
-  if (!fold) zero_xa_row(a.xa(), r - a.row_offset, a.R);
+  if (!fold) {
+    zero_xa_row(a.xa(), r - a.row_offset, a.R);
+    if (xa2) zero_xa_row(gp<uint16_t>(xa2), r - a.row_offset, a.R);
+  }
 }
 
 // Persistent: every block lists the window's active pairs, then takes items
@@ -572,8 +604,10 @@ template <int KS, int NT, int PC>
 __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
   __shared__ GsSmem<PC, kGsThreads> sm;
   __shared__ floatx4 red[kGsWaves][4 * NT][kWave];
+  PairKeep k0;
+  k0.a = sm.atab;
   const int na = build_worklist<kGsThreads, PC, 1>(a.gr, a.row_offset, a.row_end, sm.off,
-                                               sm.valid, sm.apairs, sm.wcount, sm.atab);
+                                                   sm.valid, sm.apairs, sm.wcount, k0);
   const uint32_t per = a.nch * a.ncg;
   const uint32_t npi = (uint32_t)na * per;
   const uint32_t total = npi + a.nz;
@@ -616,13 +650,14 @@ constexpr int kXlStride = 32 + 8;                       // LDS row stride of the
 // Fused fold of one batch (see gs_wide_item): rows[0, nb) of the sorted rows,
 // their xa (BF16, max_rank <= 32 columns) in xl, deltas staged in dl, n_out <=
 // kFuseCols.  Every thread of the 1024 calls it.
-__device__ __forceinline__ void wide_fold_batch(const GsArgs& a, const int* rows, int nb,
+__device__ __forceinline__ void wide_fold_batch(const GsArgs& a, uint64_t out_addr, uint32_t os,
+                                                uint32_t n_out, const int* rows, int nb,
                                                 uint64_t b_addr, float scale, const uint16_t* xl,
                                                 uint16_t* dl) {
   constexpr int kPieces = 32 * (kFuseCols / 8) / kGwThreads;  // 16-byte base pieces per thread
   const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(b_addr);
-  RLD_GLOBAL uint16_t* out = a.out();
-  const uint32_t R = a.R, n_out = a.n_out;
+  RLD_GLOBAL uint16_t* out = gp<uint16_t>(out_addr);
+  const uint32_t R = a.R;
   // The thread index passes through an empty asm: the fold's per-thread
   // offsets are then computed here, not hoisted to the kernel's start where
   // they would hold registers through the shrink.
@@ -651,7 +686,7 @@ __device__ __forceinline__ void wide_fold_batch(const GsArgs& a, const int* rows
       const int ei = tid + kGwThreads * j;
       const int rl = ei / (kFuseCols / 8);
       const uint32_t col = cc + (uint32_t)(ei % (kFuseCols / 8)) * 8u;
-      bv[j] = load16(out + (size_t)rows[rl < nb ? rl : 0] * a.os + (col < n_out ? col : cc));
+      bv[j] = load16(out + (size_t)rows[rl < nb ? rl : 0] * os + (col < n_out ? col : cc));
     }
     uint4 xf[2];
 #pragma unroll
@@ -686,18 +721,30 @@ __device__ __forceinline__ void wide_fold_batch(const GsArgs& a, const int* rows
       const uint32_t col = cc + (uint32_t)c8;
       if (rl < nb && col < n_out) {
         const uint4 dv = *reinterpret_cast<const uint4*>(&dl[rl * kFuseStride + c8]);
-        store16(out + (size_t)rows[rl] * a.os + col, fold8(bv[j], dv, scale));
+        store16(out + (size_t)rows[rl] * os + col, fold8(bv[j], dv, scale));
       }
     }
     __syncthreads();
   }
 }
 
-template <int NT, int PC, bool FUSE>
+// A projection of a wide launch: its xa and output, and the table entries the
+// worklist kept in LDS.
+struct WideProj {
+  uint64_t xa_, out_;
+  uint32_t os, n_out;
+  const uint64_t* atab;
+  const uint64_t* btab;
+  const float* bscale;
+};
+
+// Item (pair, half h) of a wide launch over NP projections that share the
+// routing (NP = 2: the pair kernel).  A projection that does not adapt the pair
+// writes zero xa rows for the item's rows.
+template <int NT, int PC, bool FUSE, int NP>
 __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
                              floatx4 (*red)[2 * NT][kWave], int pair, int h,
-                             const uint64_t* btab = nullptr, const float* bscale = nullptr,
-                             uint16_t* xl = nullptr) {
+                             const WideProj* pj, uint16_t* xl) {
   constexpr int KS = 4;   // MFMA steps per wave: 128 k
   constexpr int QB = 2;   // 16-row subtiles per batch
   constexpr int kRows = 16 * QB;
@@ -722,10 +769,10 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
   // loads it with each batch's x rows instead, so that it is not held through
   // the fold (which needs those registers).
   uint4 bop[NT][KS];
-  auto load_a = [&]() {
+  auto load_a = [&](const uint64_t* atab) {
     // the address is read from LDS at each call: computed once and kept, the
     // eight row addresses would hold registers through the fold
-    const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(sm.atab[pair]);
+    const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(atab[pair]);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const uint32_t col = 16u * j + cl;
@@ -746,7 +793,7 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
       }
   };
   if (!FUSE) {
-    load_a();
+    load_a(pj[0].atab);
     issue_point();
   }
   bool masked = full || FUSE;
@@ -759,7 +806,19 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
     }
     for (int b0 = kRows * h; b0 < cnt; b0 += 2 * kRows) {
       const int nb = min(cnt - b0, kRows);
-      if (FUSE) load_a();
+#pragma unroll
+      for (int pi = 0; pi < NP; ++pi) {
+      const WideProj& P = pj[pi];
+      if (NP > 1 && !((sm.valid[pair] >> pi) & 1)) {
+        // this projection does not adapt the pair: zero xa rows
+        for (int t = threadIdx.x; t < nb * (int)(R / 8); t += kGwThreads)
+          store16(gp<uint16_t>(P.xa_) +
+                      (size_t)((uint32_t)sm.list[b0 + t / (int)(R / 8)] - a.row_offset) * R +
+                      8 * (t % (int)(R / 8)),
+                  zero16());
+        continue;
+      }
+      if (FUSE) load_a(P.atab);
       uint4 aop[QB][KS];
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
@@ -808,34 +867,34 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
             if (FUSE) xl[li * kXlStride + col] = v;
             if (li < nb) {
               const uint32_t lr = (uint32_t)sm.list[b0 + li] - a.row_offset;
-              a.xa()[(size_t)lr * R + col] = v;
+              gp<uint16_t>(P.xa_)[(size_t)lr * R + col] = v;
             }
           }
         }
       }
       __syncthreads();
-      if (FUSE) wide_fold_batch(a, sm.list + b0, nb, btab[pair], bscale[pair], xl,
-                                reinterpret_cast<uint16_t*>(&red[0][0][0]));
+      if (FUSE)
+        wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0, nb, P.btab[pair],
+                        P.bscale[pair], xl, reinterpret_cast<uint16_t*>(&red[0][0][0]));
+      }
     }
   }
 }
 
 // Items of the wide kernels: pair halves in groups of 8 pairs, then row blocks.
-template <int NT, int PC, bool FUSE>
+template <int NT, int PC, bool FUSE, int NP>
 __device__ __forceinline__ void wide_items(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
                                            floatx4 (*red)[2 * NT][kWave], int na,
-                                           const uint64_t* btab, const float* bscale,
-                                           uint16_t* xl) {
+                                           const WideProj* pj, uint16_t* xl) {
   const uint32_t npi = 16u * (((uint32_t)na + 7u) / 8u);
   const uint32_t total = npi + a.nz;
   for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
     if (it < npi) {
       const uint32_t p = (it / 16u) * 8u + it % 8u;
       if (p < (uint32_t)na)
-        gs_wide_item<NT, PC, FUSE>(a, sm, red, sm.apairs[p], (int)((it / 8u) % 2u), btab, bscale,
-                                   xl);
+        gs_wide_item<NT, PC, FUSE, NP>(a, sm, red, sm.apairs[p], (int)((it / 8u) % 2u), pj, xl);
     } else {
-      gs_zero_item(a, sm, it - npi);
+      gs_zero_item(a, sm, it - npi, NP > 1 ? pj[1].xa_ : 0);
     }
   }
 }
@@ -844,28 +903,62 @@ template <int NT, int PC>
 __global__ __launch_bounds__(kGwThreads) void grouped_shrink_wide_kernel(GsArgs a) {
   __shared__ GsSmem<PC, kGwThreads> sm;
   __shared__ floatx4 red[kGwWaves][2 * NT][kWave];
+  PairKeep k0;
+  k0.a = sm.atab;
   const int na = build_worklist<kGwThreads, PC, 1>(a.gr, a.row_offset, a.row_end, sm.off,
-                                                   sm.valid, sm.apairs, sm.wcount, sm.atab);
-  wide_items<NT, PC, false>(a, sm, red, na, nullptr, nullptr, nullptr);
+                                                   sm.valid, sm.apairs, sm.wcount, k0);
+  WideProj pj[1];
+  pj[0] = WideProj{a.xa_, 0, 0, 0, sm.atab, nullptr, nullptr};
+  wide_items<NT, PC, false, 1>(a, sm, red, na, pj, nullptr);
 }
 
-// Shrink and fold of a window in one launch (rld_moe_grouped in the wide case).
-// The wave-sum buffer doubles as the delta tile of the fold.
-template <int NT, int PC>
-__global__ __launch_bounds__(kGwThreads) void grouped_fold_wide_kernel(GsArgs a) {
+// Shrink and fold of a window in one launch (rld_moe_grouped in the wide case);
+// NP = 2 folds two projections that share the routing (rld_moe_grouped_pair),
+// the second one's x rows read again from cache.  The wave-sum buffer doubles
+// as the delta tile of the fold.
+template <int NT, int PC, int NP>
+__device__ __forceinline__ void fold_wide_body(const GsArgs& a) {
   constexpr size_t kRedBytes = sizeof(floatx4) * kGwWaves * 2 * NT * kWave;
   constexpr size_t kDlBytes = sizeof(uint16_t) * 32 * kFuseStride;
   __shared__ GsSmem<PC, kGwThreads> sm;
-  __shared__ uint64_t btab[PC];
-  __shared__ float bscale[PC];
+  __shared__ uint64_t btab[NP][PC];
+  __shared__ float bscale[NP][PC];
+  __shared__ uint64_t atab2[NP > 1 ? PC : 1];
   __shared__ __attribute__((aligned(16))) uint16_t xl[32 * kXlStride];
   __shared__ __attribute__((aligned(16))) unsigned char buf[kRedBytes > kDlBytes ? kRedBytes
                                                                                 : kDlBytes];
   auto red = reinterpret_cast<floatx4 (*)[2 * NT][kWave]>(buf);
-  const int na = build_worklist<kGwThreads, PC, 3>(a.gr, a.row_offset, a.row_end, sm.off,
-                                                   sm.valid, sm.apairs, sm.wcount, sm.atab, btab,
-                                                   bscale, a.scale_table());
-  wide_items<NT, PC, true>(a, sm, red, na, btab, bscale, xl);
+  PairKeep k0, k1;
+  k0.a = sm.atab;
+  k0.b = btab[0];
+  k0.scale = bscale[0];
+  k0.scale_table = a.scale_table();
+  if (NP > 1) {
+    k1.a = atab2;
+    k1.b = btab[NP - 1];
+    k1.scale = bscale[NP - 1];
+    k1.scale_table = gp<const float>(a.scale2_);
+    k1.at = gp<const uint64_t>(a.atab2_);
+    k1.bt = gp<const uint64_t>(a.btab2_);
+  }
+  const int na = build_worklist<kGwThreads, PC, 3, NP>(a.gr, a.row_offset, a.row_end, sm.off,
+                                                       sm.valid, sm.apairs, sm.wcount, k0, k1);
+  WideProj pj[NP];
+  pj[0] = WideProj{a.xa_, a.out_, a.os, a.n_out, sm.atab, btab[0], bscale[0]};
+  if (NP > 1)
+    pj[NP - 1] = WideProj{a.xa2_, a.out2_, a.os2, a.n_out2, atab2, btab[NP - 1],
+                          bscale[NP - 1]};
+  wide_items<NT, PC, true, NP>(a, sm, red, na, pj, xl);
+}
+
+template <int NT, int PC>
+__global__ __launch_bounds__(kGwThreads) void grouped_fold_wide_kernel(GsArgs a) {
+  fold_wide_body<NT, PC, 1>(a);
+}
+
+template <int NT, int PC>
+__global__ __launch_bounds__(kGwThreads) void grouped_fold_pair_kernel(GsArgs a) {
+  fold_wide_body<NT, PC, 2>(a);
 }
 
 // Item: (pair, 512 output columns).  The pair's B rows for the columns go to
@@ -891,8 +984,12 @@ __global__ __launch_bounds__(kPeThreads) void grouped_expand_kernel(
   __shared__ int wcount[kPeThreads / kWave];
   __shared__ __attribute__((aligned(16))) uint16_t dl[kBatch * kDlStride];
 
+  PairKeep k0;
+  k0.b = btab;
+  k0.scale = bscale;
+  k0.scale_table = scale_table;
   const int na = build_worklist<kPeThreads, PC, 2>(gr, row_offset, row_end, off_s, valid, apairs,
-                                                   wcount, nullptr, btab, bscale, scale_table);
+                                                   wcount, k0);
   const int* off = off_s;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1208,4 +1305,80 @@ extern "C" int rld_moe_grouped(const rld_moe_route* route, const void* x, uint32
   return rld_moe_grouped_expand_fold(route, xa, num_tokens, expert_offsets, num_experts_off,
                                      sorted_token_ids, row_adapter, row_offset, row_end,
                                      base_out, out_row_stride, stream);
+}
+
+extern "C" int rld_moe_grouped_pair(const rld_moe_route* route_a, const rld_moe_route* route_b,
+                                    const void* x, uint32_t x_row_stride, int x_gather,
+                                    uint32_t num_tokens, const int32_t* expert_offsets,
+                                    uint32_t num_experts_off, const int32_t* sorted_token_ids,
+                                    const int32_t* row_adapter, uint32_t row_offset,
+                                    uint32_t row_end, void* base_a, uint32_t os_a, void* base_b,
+                                    uint32_t os_b, void* xa_a, void* xa_b, uint32_t xa_rows_cap,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_grouped(route_a, x_gather, expert_offsets, num_experts_off, sorted_token_ids,
+                         row_adapter, row_offset, row_end);
+  if (st) return st;
+  if ((st = check_grouped(route_b, x_gather, expert_offsets, num_experts_off, sorted_token_ids,
+                          row_adapter, row_offset, row_end)))
+    return st;
+  if ((st = check_rows(x, x_row_stride, route_a->k_in))) return st;
+  if ((st = check_rows(x, x_row_stride, route_b->k_in))) return st;
+  if ((st = check_rows(base_a, os_a, route_a->n_out))) return st;
+  if ((st = check_rows(base_b, os_b, route_b->n_out))) return st;
+  if (!xa_a || !xa_b) return RLD_EINVAL;
+  if (!aligned16(xa_a) || !aligned16(xa_b)) return RLD_EALIGN;
+  if (row_end - row_offset > xa_rows_cap) return RLD_ENOSPACE;
+  if (row_end == row_offset) return RLD_OK;
+  const bool together = route_a->k_in == route_b->k_in &&
+                        route_a->max_rank == route_b->max_rank &&
+                        route_a->max_loras == route_b->max_loras &&
+                        route_a->num_experts == route_b->num_experts &&
+                        grouped_wide(route_a->k_in, route_a->max_rank) &&
+                        route_a->n_out <= (uint32_t)kFuseCols &&
+                        route_b->n_out <= (uint32_t)kFuseCols &&
+                        small_caps(route_a, num_experts_off);  // LDS holds both routes' tables
+  if (!together) {
+    st = rld_moe_grouped(route_a, x, x_row_stride, x_gather, num_tokens, expert_offsets,
+                         num_experts_off, sorted_token_ids, row_adapter, row_offset, row_end,
+                         base_a, os_a, xa_a, xa_rows_cap, workspace, workspace_bytes, stream);
+    if (st) return st;
+    return rld_moe_grouped(route_b, x, x_row_stride, x_gather, num_tokens, expert_offsets,
+                           num_experts_off, sorted_token_ids, row_adapter, row_offset, row_end,
+                           base_b, os_b, xa_b, xa_rows_cap, workspace, workspace_bytes, stream);
+  }
+  const uint32_t W = row_end - row_offset;
+  GsArgs a = GsArgs{};
+  a.x_ = reinterpret_cast<uint64_t>(x);
+  a.xa_ = reinterpret_cast<uint64_t>(xa_a);
+  a.gr = make_rows(route_a, x_gather, num_tokens, expert_offsets, num_experts_off,
+                   sorted_token_ids, row_adapter);
+  a.xs = x_row_stride;
+  a.x_gather = x_gather ? 1u : 0u;
+  a.k_in = route_a->k_in;
+  a.R = route_a->max_rank;
+  a.row_offset = row_offset;
+  a.row_end = row_end;
+  a.kc = grouped_chunk(a.k_in, a.R);
+  a.nch = 1;
+  a.ncg = 1;
+  a.nz = div_ceil(W, (uint32_t)kGwThreads);
+  a.out_ = reinterpret_cast<uint64_t>(base_a);
+  a.os = os_a;
+  a.n_out = route_a->n_out;
+  a.scale_ = reinterpret_cast<uint64_t>(route_a->scale_table);
+  a.xa2_ = reinterpret_cast<uint64_t>(xa_b);
+  a.out2_ = reinterpret_cast<uint64_t>(base_b);
+  a.os2 = os_b;
+  a.n_out2 = route_b->n_out;
+  a.scale2_ = reinterpret_cast<uint64_t>(route_b->scale_table);
+  a.atab2_ = reinterpret_cast<uint64_t>(route_b->a_table);
+  a.btab2_ = reinterpret_cast<uint64_t>(route_b->b_table);
+  const uint64_t np = (uint64_t)route_a->max_loras * route_a->num_experts;
+  const uint64_t items = 16u * ((np + 7u) / 8u) + a.nz;
+  const uint32_t grid = (uint32_t)(items < kGwGrid ? items : kGwGrid);
+  auto kern = grouped_nt(a.R) == 1 ? grouped_fold_pair_kernel<1, kPairCapSmall>
+                                    : grouped_fold_pair_kernel<2, kPairCapSmall>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGwThreads), 0, reinterpret_cast<hipStream_t>(stream),
+                     a);
+  return launch_status();
 }

@@ -314,6 +314,27 @@ def test_grouped_workspace_contract():
     assert R.rld_moe_grouped_workspace_bytes(8192, 768, 32, 0, 128) == 0
 
 
+def test_grouped_pair_rejects_bad_arguments():
+    # both routes and both outputs are checked before any launch; an empty
+    # window is a no-op
+    mr = _moe_route()
+    pr = lambda **k: R.rld_moe_grouped_pair(  # noqa: E731
+        k.get("ra", mr), k.get("rb", mr), FAKE, 256, 1, 64, FAKE, 8, FAKE, FAKE,
+        k.get("lo", 0), k.get("hi", 64), k.get("ba", FAKE), k.get("osa", 256), k.get("bb", FAKE),
+        k.get("osb", 256), k.get("xa", FAKE), k.get("xb", FAKE), k.get("cap", 64), 0, 0, 0)
+    assert pr(lo=100, hi=100) == R.RLD_OK
+    assert pr(xb=0) == R.RLD_EINVAL
+    assert pr(xa=0) == R.RLD_EINVAL
+    assert pr(xb=FAKE + 8) == R.RLD_EALIGN
+    assert pr(bb=0) == R.RLD_EINVAL
+    assert pr(osb=8) == R.RLD_EINVAL                 # stride below n_out
+    assert pr(cap=63) == R.RLD_ENOSPACE
+    bad = R.rld_moe_route(FAKE, FAKE, FAKE, 2, 0, 256, 256, 16)
+    assert pr(rb=bad) == R.RLD_EINVAL
+    big = R.rld_moe_route(FAKE, FAKE, FAKE, 64, 128, 256, 256, 16)   # 8192 pairs
+    assert pr(ra=big) == R.RLD_EUNSUPPORTED
+
+
 def test_lora_rejects_bad_arguments():
     # the unrouted entry points: every argument error is found before a launch
     P = lambda **k: R.rld_pair(k.get("a", FAKE), k.get("b", FAKE), 0.5,  # noqa: E731

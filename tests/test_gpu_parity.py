@@ -374,6 +374,63 @@ def test_moe_grouped_full_config_sampled():
                                  f"full {p.name} out [{a},+64)")
 
 
+def _pair_run(wl, pa, pb, dev, cap, ra="wl"):
+    """Every window of the gate/up pair through rld_moe_grouped_pair: xa of
+    each window and the folded outputs of both projections."""
+    from routed_lora_delta_amd.pool import MoeRoute
+    rad = wl.row_adapter if ra == "wl" else ra
+    route_a = MoeRoute(pa.adapters, wl.max_loras, wl.num_experts, wl.max_rank, pa.k_in, pa.n_out,
+                       dev)
+    route_b = MoeRoute(pb.adapters, wl.max_loras, wl.num_experts, wl.max_rank, pb.k_in, pb.n_out,
+                       dev)
+    x = to_device_u16(pa.x.ravel(), dev)
+    base_a, base_b = Guarded(pa.base.ravel(), dev), Guarded(pb.base.ravel(), dev)
+    off, stid = dev_i32(wl.expert_offsets, dev), dev_i32(wl.sorted_token_ids, dev)
+    rd = dev_i32(rad, dev) if rad is not None else None
+    xa_a = torch.zeros(cap * wl.max_rank + 8, dtype=torch.int16, device=dev)
+    xa_b = torch.zeros(cap * wl.max_rank + 8, dtype=torch.int16, device=dev)
+    wsb = max(R.rld_moe_grouped_workspace_bytes(cap, p.k_in, wl.max_rank, wl.max_loras,
+                                                wl.num_experts) for p in (pa, pb))
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+    xas = []
+    for lo, hi in O.grouped_down_windows(wl.te, cap):
+        R.check(R.rld_moe_grouped_pair(route_a.route, route_b.route, x, pa.k_in, pa.x_gather,
+                                       wl.num_tokens, off, wl.num_experts, stid, rd, lo, hi,
+                                       base_a.ptr(), pa.n_out, base_b.ptr(), pb.n_out, xa_a,
+                                       xa_b, cap, ws, wsb), "rld_moe_grouped_pair")
+        torch.cuda.synchronize()
+        n = (hi - lo) * wl.max_rank
+        xas.append((from_device_u16(xa_a)[:n].copy(), from_device_u16(xa_b)[:n].copy()))
+    return xas, base_a.body(), base_b.body()
+
+
+@pytest.mark.parametrize("case", ["full", "small", "small_null", "fallback"])
+def test_moe_grouped_pair_equals_two_calls(case):
+    """rld_moe_grouped_pair on a gate/up pair equals rld_moe_grouped on each
+    projection, bit for bit (every window's xa and both folded outputs).  The
+    two projections adapt independent expert subsets, so some pairs fold in one
+    of them only.  full: the MoE prefill at full size (one launch per window);
+    small: k_in 2048 at n_out 264 (one launch); small_null: without
+    row_adapter; fallback: k_in 520 (two rld_moe_grouped calls)."""
+    dev = require_gpu()
+    if case == "full":
+        wl = W.moe_grouped(projections=("gate", "up"))
+    else:
+        hidden = 520 if case == "fallback" else 2048
+        wl = _small_grouped(seed=8, hidden=hidden, projections=("gate", "up"), cap=700,
+                            max_loras=1 if case == "small_null" else 3)
+    ra = None if case == "small_null" else "wl"
+    pa, pb = wl.projections
+    say(f"case: grouped pair {case} k_in={pa.k_in} n_out={pa.n_out} te={wl.te}")
+    xas, out_a, out_b = _pair_run(wl, pa, pb, dev, wl.cap, ra)
+    for p, out, which in ((pa, out_a, 0), (pb, out_b, 1)):
+        run = GroupedRun(wl, p, dev, cap=wl.cap, row_adapter=ra)
+        ref = run.run()
+        for (lo, hi), xa_ref, xa_pair in zip(O.grouped_down_windows(wl.te, wl.cap), ref, xas):
+            assert np.array_equal(xa_pair[which].reshape(xa_ref.shape), xa_ref), (p.name, lo)
+        assert np.array_equal(out, run.base.body()), p.name
+
+
 @pytest.mark.parametrize("max_loras,num_experts", [(5, 128), (1, 600)])
 def test_moe_grouped_large_route(max_loras, num_experts):
     """Routes past the small worklist capacity (more than 512 (slot, expert)
