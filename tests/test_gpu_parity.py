@@ -454,24 +454,28 @@ def test_moe_grouped_large_route(max_loras, num_experts):
         assert_out_close(run.base.body(), base, "large route out")
 
 
-@pytest.mark.parametrize("k_in,max_rank,proj", [(2048, 32, "gate"), (1032, 16, "gate"),
-                                                (1544, 32, "down"), (2048, 24, "down"),
-                                                (1160, 32, "gate")])
+@pytest.mark.parametrize("k_in,max_rank,proj,n_out", [
+    (2048, 32, "gate", 264), (1032, 16, "gate", 264), (1544, 32, "down", 264),
+    (2048, 24, "down", 264), (1160, 32, "gate", 264), (768, 32, "down", 2048),
+    (264, 16, "down", 1032), (520, 64, "gate", 264), (1032, 48, "gate", 264)])
 @pytest.mark.parametrize("separate", [False, True])
-def test_moe_grouped_wide(k_in, max_rank, proj, separate):
+def test_moe_grouped_wide(k_in, max_rank, proj, n_out, separate):
     """1024 < k_in <= 2048 at max_rank <= 32: one sixteen-wave block per pair
     half covers all of k_in; k_in not a multiple of 128 leaves one wave's range
     partly past k_in and later ones wholly past it.  Through rld_moe_grouped
-    (the shrink and fold in one kernel, n_out <= 768 here) or the two stages
-    separately.  Pairs of up to ~100 rows (both halves, several batches each),
-    windows of 333 rows against the oracle, and the full window bit-identical
-    to their union."""
+    (the shrink and fold in one kernel when n_out <= 768) or the two stages
+    separately.  The other rows of the table take the four-wave kernels (k_in
+    <= 1024: one chunk; max_rank 48 at k_in 1032: chunks of 512) and, for n_out
+    above 768, the separate expand.  Pairs of up to ~100 rows (both halves,
+    several batches each), windows of 333 rows against the oracle, and the full
+    window bit-identical to their union."""
     dev = require_gpu()
-    sizes = dict(hidden=k_in, inter=264) if proj == "gate" else dict(hidden=264, inter=k_in)
+    sizes = dict(hidden=k_in, inter=n_out) if proj == "gate" else dict(hidden=n_out, inter=k_in)
     wl = _small_grouped(seed=7, num_experts=4, n_adapted=3, max_rank=max_rank,
                         ranks=(8, max_rank), cap=333, projections=(proj,), **sizes)
     p = wl.projections[0]
-    say(f"case: grouped wide {proj} k_in={k_in} max_rank={max_rank} separate={separate}")
+    say(f"case: grouped wide {proj} k_in={k_in} n_out={n_out} max_rank={max_rank} "
+        f"separate={separate}")
     run = GroupedRun(wl, p, dev, cap=wl.cap)
     xas = run.run(separate=separate)
     base = p.base.ravel().copy()
