@@ -365,16 +365,12 @@ class Step:
                 keep += [rt, x, base, idx, rad, xa]
                 sb, eb, fl, _ = gather_bytes(wl)
 
-                def gshrink(rt=rt, x=x, idx=idx, rad=rad, xa=xa, wl=wl):
-                    return R.rld_moe_gather_shrink(rt.route, x, wl.k_in, idx, rad, wl.top_k,
-                                                   wl.n_rows, xa)
-
-                def gexpand(rt=rt, base=base, idx=idx, rad=rad, xa=xa, wl=wl):
-                    return R.rld_moe_gather_expand_fold(rt.route, xa, idx, rad, wl.top_k,
-                                                        wl.n_rows, base, wl.n_out)
-                add(("gather.down.shrink", "gather_shrink_kernel", gshrink, sb, fl / 2,
-                     wl.n_rows), "")
-                add(("gather.down.expand", "gather_expand_kernel", gexpand, eb, fl / 2, 0), "")
+                # one call: shrink and fold of every flat row in one kernel
+                def gfold(rt=rt, x=x, base=base, idx=idx, rad=rad, xa=xa, wl=wl):
+                    return R.rld_moe_gather(rt.route, x, wl.k_in, idx, rad, wl.top_k, wl.n_rows,
+                                            base, wl.n_out, xa)
+                add(("gather.down.fold", "gather_fold_kernel", gfold, sb + eb, fl, wl.n_rows),
+                    "")
                 self.rows += wl.n_rows
             elif tag == "grouped":
                 off = i32(wl.expert_offsets)

@@ -8,6 +8,10 @@
 //           in 16-byte pieces and the partial sums meet in a fixed xor-butterfly.
 //   expand  one block per (row, 512 columns); a thread owns two adjacent output
 //           columns, sums over max_rank in order, and folds 4 bytes of base_out.
+//   fold    rld_moe_gather: one block per row does both, the same arithmetic in
+//           the same order (so the same bits), with the xa row passed through
+//           LDS; the expand's launch, its routing loads and the xa read-back
+//           are saved.
 //
 #include "rld_device.hpp"
 #include "rld_internal.hpp"
@@ -53,15 +57,12 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float acc)
   return acc;
 }
 
-__global__ __launch_bounds__(256) void gather_shrink_kernel(GatherArgs a) {
-  const uint32_t rho = blockIdx.x;
+// xa row of flat row rho (valid pair): each wave owns every fourth column, its
+// lanes split k_in in 16-byte pieces, and the lane sums meet in a fixed
+// xor-butterfly.  The BF16 values go to xo and, when given, to xl (LDS).
+__device__ __forceinline__ void gather_shrink_row(const GatherArgs& a, uint32_t rho, int pair,
+                                                  RLD_GLOBAL uint16_t* xo, uint16_t* xl) {
   const uint32_t R = a.R, k_in = a.k_in;
-  RLD_GLOBAL uint16_t* xo = a.xa() + (size_t)rho * R;
-  const int pair = gather_pair(a, rho);
-  if (pair < 0) {
-    for (uint32_t k = threadIdx.x; k < R; k += 256) xo[k] = 0;
-    return;
-  }
   const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(a.a_table()[pair]);
   const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)rho * a.xs;
   const int lane = threadIdx.x & 63;
@@ -72,29 +73,74 @@ __global__ __launch_bounds__(256) void gather_shrink_kernel(GatherArgs a) {
     for (uint32_t c = lane * 8; c < k_in; c += 512) acc = dot8(load16(xr + c), load16(Ak + c), acc);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) xo[k] = (uint16_t)f32_to_bf16(acc);
+    if (lane == 0) {
+      const uint16_t v = (uint16_t)f32_to_bf16(acc);
+      xo[k] = v;
+      if (xl) xl[k] = v;
+    }
   }
 }
 
-__global__ __launch_bounds__(256) void gather_expand_kernel(GatherArgs a) {
-  const uint32_t rho = blockIdx.x;
+// 8 xa values from global memory or from LDS.
+__device__ __forceinline__ uint4 xa8(const RLD_GLOBAL uint16_t* p) { return load16(p); }
+__device__ __forceinline__ uint4 xa8(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Output columns j, j + 1 of flat row rho: the sum over max_rank in order
+// (xa from xr: global memory or LDS), folded into 4 bytes of base_out.
+template <typename XP>
+__device__ __forceinline__ void gather_fold_cols(const GatherArgs& a, uint32_t rho, int pair,
+                                                 uint32_t j, XP xr) {
   const uint32_t R = a.R;
-  const int pair = gather_pair(a, rho);
-  if (pair < 0) return;
-  const uint32_t j = blockIdx.y * kGatherCols + threadIdx.x * 2;
-  if (j >= a.n_out) return;
   const RLD_GLOBAL uint16_t* B0 = gp<const uint16_t>(a.b_table()[pair]) + (size_t)j * R;
   const RLD_GLOBAL uint16_t* B1 = B0 + R;
-  const RLD_GLOBAL uint16_t* xr = a.xa() + (size_t)rho * R;
   float d0 = 0.f, d1 = 0.f;
   for (uint32_t k = 0; k < R; k += 8) {
-    const uint4 xv = load16(xr + k);
+    const uint4 xv = xa8(xr + k);
     d0 = dot8(load16(B0 + k), xv, d0);
     d1 = dot8(load16(B1 + k), xv, d1);
   }
   RLD_GLOBAL uint32_t* p = reinterpret_cast<RLD_GLOBAL uint32_t*>(a.out() + (size_t)rho * a.os + j);
   const uint32_t dd = pack_bf16x2(d0, d1);
   *p = fold2(*p, dd, a.scale_table()[pair]);
+}
+
+__global__ __launch_bounds__(256) void gather_shrink_kernel(GatherArgs a) {
+  const uint32_t rho = blockIdx.x;
+  RLD_GLOBAL uint16_t* xo = a.xa() + (size_t)rho * a.R;
+  const int pair = gather_pair(a, rho);
+  if (pair < 0) {
+    for (uint32_t k = threadIdx.x; k < a.R; k += 256) xo[k] = 0;
+    return;
+  }
+  gather_shrink_row(a, rho, pair, xo, nullptr);
+}
+
+__global__ __launch_bounds__(256) void gather_expand_kernel(GatherArgs a) {
+  const uint32_t rho = blockIdx.x;
+  const int pair = gather_pair(a, rho);
+  if (pair < 0) return;
+  const uint32_t j = blockIdx.y * kGatherCols + threadIdx.x * 2;
+  if (j >= a.n_out) return;
+  gather_fold_cols(a, rho, pair, j, a.xa() + (size_t)rho * a.R);
+}
+
+// Shrink and fold of one flat row per block (rld_moe_gather): the two kernels
+// above in one, the xa row handed over in LDS.
+__global__ __launch_bounds__(256) void gather_fold_kernel(GatherArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xl[RLD_MAX_RANK];
+  const uint32_t rho = blockIdx.x;
+  RLD_GLOBAL uint16_t* xo = a.xa() + (size_t)rho * a.R;
+  const int pair = gather_pair(a, rho);
+  if (pair < 0) {
+    for (uint32_t k = threadIdx.x; k < a.R; k += 256) xo[k] = 0;
+    return;
+  }
+  gather_shrink_row(a, rho, pair, xo, xl);
+  __syncthreads();
+  for (uint32_t j = threadIdx.x * 2; j < a.n_out; j += 2 * 256)
+    gather_fold_cols(a, rho, pair, j, static_cast<const uint16_t*>(xl));
 }
 
 static GatherArgs gather_args(const rld_moe_route* route, const void* x, uint32_t x_row_stride,
@@ -174,9 +220,12 @@ extern "C" int rld_moe_gather(const rld_moe_route* route, const void* x, uint32_
   int st = check_gather(route, indices, top_k, n_rows);
   if (st || n_rows == 0) return st;
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
-  st = rld_moe_gather_shrink(route, x, x_row_stride, indices, row_adapter, top_k, n_rows, xa,
-                             stream);
-  if (st) return st;
-  return rld_moe_gather_expand_fold(route, xa, indices, row_adapter, top_k, n_rows, base_out,
-                                    out_row_stride, stream);
+  if ((st = check_rows(x, x_row_stride, route->k_in))) return st;
+  if (!xa) return RLD_EINVAL;
+  if (!aligned16(xa)) return RLD_EALIGN;
+  hipLaunchKernelGGL(gather_fold_kernel, dim3(n_rows), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream),
+                     gather_args(route, x, x_row_stride, indices, row_adapter, top_k, xa,
+                                 base_out, out_row_stride));
+  return launch_status();
 }

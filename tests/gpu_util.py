@@ -304,7 +304,9 @@ def compare_bgmv(run: BgmvRun, label: str):
 
 # -------------------------------------------------------------------- MoE ----
 
-def run_gather(wl, device, row_adapter="wl"):
+def run_gather(wl, device, row_adapter="wl", separate=False):
+    """The gather fold through rld_moe_gather (one launch), or with
+    separate=True through rld_moe_gather_shrink then _expand_fold."""
     ra = wl.row_adapter if row_adapter == "wl" else row_adapter
     route = MoeRoute(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank, wl.k_in, wl.n_out,
                      device)
@@ -313,8 +315,14 @@ def run_gather(wl, device, row_adapter="wl"):
     idx = dev_i32(wl.indices, device)
     rad = dev_i32(ra, device) if ra is not None else None
     xa = torch.zeros(wl.n_rows * wl.max_rank + 8, dtype=torch.int16, device=device)
-    R.check(R.rld_moe_gather(route.route, x, wl.k_in, idx, rad, wl.top_k, wl.n_rows,
-                             base.ptr(), wl.n_out, xa), "rld_moe_gather")
+    if separate:
+        R.check(R.rld_moe_gather_shrink(route.route, x, wl.k_in, idx, rad, wl.top_k, wl.n_rows,
+                                        xa), "rld_moe_gather_shrink")
+        R.check(R.rld_moe_gather_expand_fold(route.route, xa, idx, rad, wl.top_k, wl.n_rows,
+                                             base.ptr(), wl.n_out), "rld_moe_gather_expand_fold")
+    else:
+        R.check(R.rld_moe_gather(route.route, x, wl.k_in, idx, rad, wl.top_k, wl.n_rows,
+                                 base.ptr(), wl.n_out, xa), "rld_moe_gather")
     torch.cuda.synchronize()
     return (from_device_u16(xa)[: wl.n_rows * wl.max_rank].reshape(wl.n_rows, wl.max_rank),
             base.body())

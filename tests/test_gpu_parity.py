@@ -265,6 +265,10 @@ def test_moe_gather(variant):
     base2 = wl.base.reshape(wl.n_rows, wl.n_out)
     assert np.array_equal(out_g.reshape(wl.n_rows, wl.n_out)[inactive], base2[inactive])
     assert np.all(xa_g[inactive] == 0)
+    # the one-launch combined call and the two entry points agree bit for bit
+    xa_s, out_s = run_gather(wl, dev, ra, separate=True)
+    assert np.array_equal(xa_s, xa_g)
+    assert np.array_equal(out_s, out_g)
 
 
 # ----------------------------------------------------------------- grouped ---
