@@ -67,16 +67,36 @@ __device__ __forceinline__ void gather_shrink_row(const GatherArgs& a, uint32_t 
   const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)rho * a.xs;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  for (uint32_t k = wave; k < R; k += 4) {
-    const RLD_GLOBAL uint16_t* Ak = A + (size_t)k * k_in;
-    float acc = 0.f;
-    for (uint32_t c = lane * 8; c < k_in; c += 512) acc = dot8(load16(xr + c), load16(Ak + c), acc);
+  // columns k = wave + 4i, up to kCols at a time: the x piece and the A pieces
+  // of all of them go out together; each column still sums its pieces in
+  // ascending order
+  constexpr int kCols = 8;
+  for (uint32_t k0 = wave; k0 < R; k0 += 4 * kCols) {
+    float acc[kCols];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) {
-      const uint16_t v = (uint16_t)f32_to_bf16(acc);
-      xo[k] = v;
-      if (xl) xl[k] = v;
+    for (int i = 0; i < kCols; ++i) acc[i] = 0.f;
+    for (uint32_t c = lane * 8; c < k_in; c += 512) {
+      const uint4 xv = load16(xr + c);
+      uint4 av[kCols];
+#pragma unroll
+      for (int i = 0; i < kCols; ++i) {
+        const uint32_t k = k0 + 4u * i;
+        av[i] = load16(A + (size_t)(k < R ? k : k0) * k_in + c);
+      }
+#pragma unroll
+      for (int i = 0; i < kCols; ++i) acc[i] = dot8(xv, av[i], acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+      const uint32_t k = k0 + 4u * i;
+      float v = acc[i];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0 && k < R) {
+        const uint16_t b = (uint16_t)f32_to_bf16(v);
+        xo[k] = b;
+        if (xl) xl[k] = b;
+      }
     }
   }
 }
@@ -104,6 +124,36 @@ __device__ __forceinline__ void gather_fold_cols(const GatherArgs& a, uint32_t r
   RLD_GLOBAL uint32_t* p = reinterpret_cast<RLD_GLOBAL uint32_t*>(a.out() + (size_t)rho * a.os + j);
   const uint32_t dd = pack_bf16x2(d0, d1);
   *p = fold2(*p, dd, a.scale_table()[pair]);
+}
+
+// Output columns [j, j + 8) of flat row rho, max_rank <= 16: the same sums
+// and folds as gather_fold_cols, with the B rows of the eight columns, the base
+// values and xa (LDS) in one round.
+__device__ __forceinline__ void gather_fold_cols8(const GatherArgs& a, uint32_t rho, int pair,
+                                                  uint32_t j, const uint16_t* xl) {
+  const uint32_t R = a.R;
+  const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(a.b_table()[pair]) + (size_t)j * R;
+  RLD_GLOBAL uint16_t* op = a.out() + (size_t)rho * a.os + j;
+  uint4 bv[8][2];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) bv[c][q] = load16(B + (size_t)c * R + (8u * q < R ? 8u * q : 0));
+  const uint4 base = load16(op);
+  float d[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    d[c] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (8u * q < R) d[c] = dot8(bv[c][q], xa8(xl + 8 * q), d[c]);
+  }
+  const float scale = a.scale_table()[pair];
+  const uint4 o = make_uint4(fold2(base.x, pack_bf16x2(d[0], d[1]), scale),
+                             fold2(base.y, pack_bf16x2(d[2], d[3]), scale),
+                             fold2(base.z, pack_bf16x2(d[4], d[5]), scale),
+                             fold2(base.w, pack_bf16x2(d[6], d[7]), scale));
+  store16(op, o);
 }
 
 __global__ __launch_bounds__(256) void gather_shrink_kernel(GatherArgs a) {
@@ -139,8 +189,14 @@ __global__ __launch_bounds__(256) void gather_fold_kernel(GatherArgs a) {
   }
   gather_shrink_row(a, rho, pair, xo, xl);
   __syncthreads();
-  for (uint32_t j = threadIdx.x * 2; j < a.n_out; j += 2 * 256)
-    gather_fold_cols(a, rho, pair, j, static_cast<const uint16_t*>(xl));
+  if (a.R <= 16) {
+    // n_out is a multiple of 8
+    for (uint32_t j = threadIdx.x * 8; j < a.n_out; j += 8 * 256)
+      gather_fold_cols8(a, rho, pair, j, xl);
+  } else {
+    for (uint32_t j = threadIdx.x * 2; j < a.n_out; j += 2 * 256)
+      gather_fold_cols(a, rho, pair, j, static_cast<const uint16_t*>(xl));
+  }
 }
 
 static GatherArgs gather_args(const rld_moe_route* route, const void* x, uint32_t x_row_stride,
