@@ -292,7 +292,6 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
     }
   };
   using Q4 = std::integral_constant<int, kShrinkMT>;
-  using Q8 = std::integral_constant<int, 2 * kShrinkMT>;
 
   if (a.dense) {
     const int cnt = dense_tile_rows((uint32_t)s * kDenseShrinkRows, n, kDenseShrinkRows, sm.rows);
@@ -301,15 +300,13 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
   }
   // The usual case, straight-line: at most 256 rows (their seq_slot entries
   // are key0, so the scan issues no load that would wait behind the A tile)
-  // and at most 128 of them on this slot.
+  // and at most 64 of them on this slot.  (A 128-row batch would serve the
+  // next case in one pass, but its registers would cost every block of the
+  // kernel a third of its occupancy.)
   if (n <= 256) {
     const int cnt = append_hits(key0 == s, threadIdx.x, sm.rows, 0, sm.wcount);
     if (cnt <= kShrinkMT * 16) {
       if (cnt > 0) batch(Q4{}, 0, cnt);
-      return;
-    }
-    if (cnt <= 2 * kShrinkMT * 16) {
-      batch(Q8{}, 0, cnt);
       return;
     }
   }
@@ -582,11 +579,10 @@ extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x
   const uint32_t total = route->max_loras * a.nch * a.ncg;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(xcd_group_grid(total, a.ncg));
-  switch (bgmv_nt(a.R)) {
-    case 1: hipLaunchKernelGGL(bgmv_shrink_kernel<1>, grid, dim3(256), 0, hs, a, total); break;
-    case 2: hipLaunchKernelGGL(bgmv_shrink_kernel<2>, grid, dim3(256), 0, hs, a, total); break;
-    default: hipLaunchKernelGGL(bgmv_shrink_kernel<4>, grid, dim3(256), 0, hs, a, total); break;
-  }
+  if (bgmv_nt(a.R) == 1)
+    hipLaunchKernelGGL(bgmv_shrink_kernel<1>, grid, dim3(256), 0, hs, a, total);
+  else
+    hipLaunchKernelGGL(bgmv_shrink_kernel<2>, grid, dim3(256), 0, hs, a, total);
   if ((st = launch_status())) return st;
   if (a.nch > 1) {
     hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(n * (a.R / 4), kReduceThreads)),
@@ -661,7 +657,7 @@ static void dense_args(const rld_pair* pair, uint32_t m, BgmvArgs* a) {
   a->R = pair->max_rank;
   a->kc = bgmv_chunk(pair->k_in, pair->max_rank);
   a->nch = div_ceil(pair->k_in, a->kc);
-  a->ncg = div_ceil(pair->max_rank, 16u * bgmv_nt(pair->max_rank));
+  a->ncg = div_ceil(pair->max_rank, 16u * bgmv_nt(pair->max_rank, true));
 }
 
 extern "C" size_t rld_lora_workspace_bytes(uint32_t m, uint32_t k_in, uint32_t max_rank) {
@@ -692,7 +688,7 @@ extern "C" int rld_lora_shrink(const rld_pair* pair, const void* x, uint32_t x_r
   const uint32_t total = div_ceil(m, (uint32_t)kDenseShrinkRows) * a.nch * a.ncg;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(xcd_group_grid(total, a.ncg));
-  switch (bgmv_nt(a.R)) {
+  switch (bgmv_nt(a.R, true)) {
     case 1: hipLaunchKernelGGL(bgmv_shrink_kernel<1>, grid, dim3(256), 0, hs, a, total); break;
     case 2: hipLaunchKernelGGL(bgmv_shrink_kernel<2>, grid, dim3(256), 0, hs, a, total); break;
     default: hipLaunchKernelGGL(bgmv_shrink_kernel<4>, grid, dim3(256), 0, hs, a, total); break;

@@ -58,10 +58,14 @@ inline uint32_t bgmv_chunk(uint32_t k_in, uint32_t max_rank) {
   return k_in <= kc ? k_in : kc;
 }
 
-// 16-column MFMA tiles of xa per BGMV shrink item (1, 2 or 4).
-inline uint32_t bgmv_nt(uint32_t max_rank) {
+// 16-column MFMA tiles of xa per BGMV shrink item.  Routed calls take 1 or 2
+// (wider ranks take several column groups: four tiles' operands leave the
+// kernel two waves per SIMD, two tiles three).  The unrouted mode takes up to
+// 4: each of its items reads a whole 64-row x tile, which every further
+// column group would read again.
+inline uint32_t bgmv_nt(uint32_t max_rank, bool unrouted = false) {
   const uint32_t t = div_ceil(max_rank, 16u);
-  return t <= 1u ? 1u : (t <= 2u ? 2u : 4u);
+  return t <= 1u ? 1u : (t <= 2u || !unrouted ? 2u : 4u);
 }
 
 // Grid of xcd_group_item: 8 XCDs x whole groups, covering `total` items.
