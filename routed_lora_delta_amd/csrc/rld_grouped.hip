@@ -75,9 +75,11 @@ __device__ __forceinline__ void span_in_window(const int* off, const GroupedRows
                                                uint32_t& lo, uint32_t& hi) {
   lo = hi = row_end;
   if ((uint32_t)e >= g.E_off) return;
-  const int64_t a = off[e], b = off[e + 1];
-  lo = (uint32_t)max<int64_t>(a, row_offset);
-  hi = (uint32_t)min<int64_t>(b, row_end);
+  const int a = off[e], b = off[e + 1];
+  // integer clamps to the window (a negative bound counts as 0, so a span
+  // ending below zero is empty)
+  lo = (a < 0 || (uint32_t)a < row_offset) ? row_offset : (uint32_t)a;
+  hi = b < 0 ? 0u : ((uint32_t)b < row_end ? (uint32_t)b : row_end);
   if (hi < lo) hi = lo;
 }
 
@@ -132,7 +134,12 @@ __device__ __forceinline__ int append_pair_rows(const GroupedRows& g, const int*
 
 __device__ __forceinline__ void zero_xa_row(RLD_GLOBAL uint16_t* xa, uint32_t local_row,
                                             uint32_t R) {
-  for (uint32_t i = 0; i < R / 8; ++i) store16(xa + (size_t)local_row * R + 8 * i, zero16());
+  // R is a nonzero multiple of 8 (the host checks it): no guard before the first store
+  uint32_t i = 0;
+#pragma unroll 1
+  do {
+    store16(xa + (size_t)local_row * R + 8 * i, zero16());
+  } while (++i < R / 8);
 }
 
 // Every thread (NTH of them): stage expert_offsets in LDS, read the A/B table entries of every pair
@@ -314,14 +321,19 @@ template <class SM>
 __device__ __forceinline__ int gs_round(const GroupedRows& g, SM& sm, int e, int s, uint32_t c0,
                                         uint32_t hi, uint32_t x_gather, int cnt) {
   constexpr int RPT = SM::kRPT, NW = SM::kNW, NTH = NW * kWave;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The thread index passes through an empty asm, so that the lane masks and
+  // LDS addresses below are computed at each round rather than hoisted out of
+  // the callers' item loops, where they would hold registers throughout.
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   uint32_t r[RPT];
   bool hit[RPT];
   int t[RPT], sr[RPT];
 #pragma unroll
   for (int h = 0; h < RPT; ++h) {
-    r[h] = c0 + (uint32_t)(h * NTH) + threadIdx.x;
+    r[h] = c0 + (uint32_t)(h * NTH) + (uint32_t)tid;
     hit[h] = r[h] < hi && expert_of_row(sm.off, (int)g.E_off, (int)r[h]) == e;
     t[h] = (int)r[h];
     sr[h] = 0;
@@ -628,12 +640,14 @@ __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
 //                                same XCD, whose L2 then serves the second read
 //                                of A_{s,e})
 //   row block z of the window (1024 rows)
-// Item (p, h) takes the pair's rows 32h + 64i, i = 0, 1, ... in batches of 32:
-// wave w sums k range [128w, 128w + 128) in one MFMA chain of four steps for
-// all NT*16 xa columns, the 16 wave sums meet in LDS in wave order, and the sum
-// is rounded to xa.  A batch's x rows, and A_{s,e} over the wave's range, are
-// one round of loads: 16 x 128 KB of A and 32 x 4 KB of x rows in flight per
-// block.
+// Of the c rows the scan finds for the pair, item (p, 0) takes the first
+// ceil(c / 2) and item (p, 1) the rest, in batches of up to 16 kWideQB rows (a
+// pair of up to 96 rows is one batch per half): wave w sums k range
+// [128w, 128w + 128) in one MFMA chain of four steps for all NT*16 xa columns,
+// the 16 wave sums meet in LDS in wave order, and the sum is rounded to xa.
+// A batch's first 32 x rows and A_{s,e} over the wave's range are one round of
+// loads (A_{s,e} whole, 128 KB at max_rank 32, and 32 x 4 KB of x rows in
+// flight per block); rows 32..47 are a second round.
 //
 // FUSE (grouped_fold_wide_kernel, n_out <= kFuseCols): the block then folds the
 // batch's rows right away, the expand of the same pair on the xa it has just
@@ -642,19 +656,21 @@ __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
 // (from LDS) in one round, deltas -> LDS (over the wave-sum buffer) -> 16-byte
 // fold of the base rows.  The expand's own launch, row scan and xa round trip
 // through memory are saved.
+constexpr int kWideQB = 3;  // 16-row subtiles per batch of the wide kernels
 constexpr int kFuseTiles = 3;
 constexpr int kFuseCols = kGwWaves * kFuseTiles * 16;  // 768
 constexpr int kFuseStride = kFuseCols + 8;             // LDS row stride of the delta tile
 constexpr int kXlStride = 32 + 8;                       // LDS row stride of the xa tile
 
-// Fused fold of one batch (see gs_wide_item): rows[0, nb) of the sorted rows,
-// their xa (BF16, max_rank <= 32 columns) in xl, deltas staged in dl, n_out <=
-// kFuseCols.  Every thread of the 1024 calls it.
+// Fused fold of up to 32 rows of a batch (see gs_wide_item): rows[0, nb) of
+// the sorted rows, their xa (BF16, max_rank <= 32 columns) in xl, deltas
+// staged in dl, n_out <= kFuseCols.  Every thread of the 1024 calls it.
 __device__ __forceinline__ void wide_fold_batch(const GsArgs& a, uint64_t out_addr, uint32_t os,
                                                 uint32_t n_out, const int* rows, int nb,
                                                 uint64_t b_addr, float scale, const uint16_t* xl,
                                                 uint16_t* dl) {
-  constexpr int kPieces = 32 * (kFuseCols / 8) / kGwThreads;  // 16-byte base pieces per thread
+  constexpr int QB = 2;
+  constexpr int kPieces = 16 * QB * (kFuseCols / 8) / kGwThreads;  // 16-byte base pieces per thread
   const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(b_addr);
   RLD_GLOBAL uint16_t* out = gp<uint16_t>(out_addr);
   const uint32_t R = a.R;
@@ -688,9 +704,9 @@ __device__ __forceinline__ void wide_fold_batch(const GsArgs& a, uint64_t out_ad
       const uint32_t col = cc + (uint32_t)(ei % (kFuseCols / 8)) * 8u;
       bv[j] = load16(out + (size_t)rows[rl < nb ? rl : 0] * os + (col < n_out ? col : cc));
     }
-    uint4 xf[2];
+    uint4 xf[QB];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < QB; ++q)
       xf[q] = kin ? *reinterpret_cast<const uint4*>(&xl[(q * 16 + cl) * kXlStride + 8 * lg])
                   : zero16();
     issue_point();
@@ -701,7 +717,7 @@ __device__ __forceinline__ void wide_fold_batch(const GsArgs& a, uint64_t out_ad
       if (!kin || col >= n_out) bt[t] = zero16();
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < QB; ++q) {
       if (q * 16 >= nb) continue;
 #pragma unroll
       for (int t = 0; t < kFuseTiles; ++t) {
@@ -741,12 +757,11 @@ struct WideProj {
 // Item (pair, half h) of a wide launch over NP projections that share the
 // routing (NP = 2: the pair kernel).  A projection that does not adapt the pair
 // writes zero xa rows for the item's rows.
-template <int NT, int PC, bool FUSE, int NP>
+template <int NT, int PC, bool FUSE, int NP, int QB>
 __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
-                             floatx4 (*red)[2 * NT][kWave], int pair, int h,
+                             floatx4 (*red)[QB * NT][kWave], int pair, int h,
                              const WideProj* pj, uint16_t* xl) {
   constexpr int KS = 4;   // MFMA steps per wave: 128 k
-  constexpr int QB = 2;   // 16-row subtiles per batch
   constexpr int kRows = 16 * QB;
   const GroupedRows& g = a.gr;
   const uint32_t R = a.R, k_in = a.k_in;
@@ -804,8 +819,11 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
       mask_a();
       masked = true;
     }
-    for (int b0 = kRows * h; b0 < cnt; b0 += 2 * kRows) {
-      const int nb = min(cnt - b0, kRows);
+    // half h takes its share of the scanned rows, ceil(cnt / 2) for h = 0
+    const int split = (cnt + 1) / 2;
+    const int bend = h ? cnt : split;
+    for (int b0 = h ? split : 0; b0 < bend; b0 += kRows) {
+      const int nb = min(bend - b0, kRows);
 #pragma unroll
       for (int pi = 0; pi < NP; ++pi) {
       const WideProj& P = pj[pi];
@@ -819,39 +837,56 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
         continue;
       }
       if (FUSE) load_a(P.atab);
-      uint4 aop[QB][KS];
-#pragma unroll
-      for (int q = 0; q < QB; ++q) {
+      // x fragments of 16-row subtile q (clamped rows past nb, k past k_in zeroed)
+      auto load_x = [&](uint4 (&v)[KS], int q) {
         const int li = q * 16 + cl;
         const RLD_GLOBAL uint16_t* xr = x + (size_t)sm.xrow[b0 + (li < nb ? li : 0)] * a.xs;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const uint32_t kk = kw0 + 32u * ks + 8u * lg;
-          aop[q][ks] = load16(full ? xr + kk : xr + (kk < k_in ? kk : 0));
+          v[ks] = load16(full ? xr + kk : xr + (kk < k_in ? kk : 0));
         }
-      }
-      issue_point();
-      if (!full) {
-        if (FUSE) mask_a();
+      };
+      auto mask_x = [&](uint4 (&v)[KS]) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          if (kw0 + 32u * ks + 8u * lg >= k_in) {
-#pragma unroll
-            for (int q = 0; q < QB; ++q) aop[q][ks] = zero16();
-          }
-      }
-#pragma unroll
-      for (int q = 0; q < QB; ++q)
+          if (kw0 + 32u * ks + 8u * lg >= k_in) v[ks] = zero16();
+      };
+      auto mfma_x = [&](const uint4 (&v)[KS], int q) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(aop[q][ks], bop[j][ks], acc);
+          for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(v[ks], bop[j][ks], acc);
           red[wave][q * NT + j][lane] = acc;
         }
+      };
+      // Subtiles 0 and 1 go out with A; a third (rows 32..47 of the batch) is
+      // a second round, with A still held, so that the common batch needs no
+      // more registers than two subtiles.
+      {
+        uint4 aop[2][KS];
+        load_x(aop[0], 0);
+        load_x(aop[1], 1);
+        issue_point();
+        if (!full) {
+          if (FUSE) mask_a();
+          mask_x(aop[0]);
+          mask_x(aop[1]);
+        }
+        mfma_x(aop[0], 0);
+        mfma_x(aop[1], 1);
+      }
+      if (QB > 2 && nb > 32) {
+        uint4 x2[KS];
+        load_x(x2, 2);
+        issue_point();
+        if (!full) mask_x(x2);
+        mfma_x(x2, 2);
+      }
       __syncthreads();
       // one thread per (subtile, column tile, lane): the 16 wave sums in wave order
-      if (threadIdx.x < QB * NT * kWave) {
+      if (threadIdx.x < QB * NT * kWave && (int)(threadIdx.x / (NT * kWave)) * 16 < nb) {
         const int q = threadIdx.x / (NT * kWave);
         const int j = (threadIdx.x / kWave) % NT;
         const int ln = threadIdx.x & 63;
@@ -873,18 +908,24 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
         }
       }
       __syncthreads();
-      if (FUSE)
-        wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0, nb, P.btab[pair],
-                        P.bscale[pair], xl, reinterpret_cast<uint16_t*>(&red[0][0][0]));
+      if (FUSE) {
+        // 32 rows a pass: the rows past 32 of a batch are a second pass
+        uint16_t* dl = reinterpret_cast<uint16_t*>(&red[0][0][0]);
+        wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0, min(nb, 32), P.btab[pair],
+                        P.bscale[pair], xl, dl);
+        if (QB > 2 && nb > 32)
+          wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0 + 32, nb - 32, P.btab[pair],
+                          P.bscale[pair], xl + 32 * kXlStride, dl);
+      }
       }
     }
   }
 }
 
 // Items of the wide kernels: pair halves in groups of 8 pairs, then row blocks.
-template <int NT, int PC, bool FUSE, int NP>
+template <int NT, int PC, bool FUSE, int NP, int QB>
 __device__ __forceinline__ void wide_items(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
-                                           floatx4 (*red)[2 * NT][kWave], int na,
+                                           floatx4 (*red)[QB * NT][kWave], int na,
                                            const WideProj* pj, uint16_t* xl) {
   const uint32_t npi = 16u * (((uint32_t)na + 7u) / 8u);
   const uint32_t total = npi + a.nz;
@@ -892,7 +933,8 @@ __device__ __forceinline__ void wide_items(const GsArgs& a, GsSmem<PC, kGwThread
     if (it < npi) {
       const uint32_t p = (it / 16u) * 8u + it % 8u;
       if (p < (uint32_t)na)
-        gs_wide_item<NT, PC, FUSE, NP>(a, sm, red, sm.apairs[p], (int)((it / 8u) % 2u), pj, xl);
+        gs_wide_item<NT, PC, FUSE, NP, QB>(a, sm, red, sm.apairs[p], (int)((it / 8u) % 2u), pj,
+                                           xl);
     } else {
       gs_zero_item(a, sm, it - npi, NP > 1 ? pj[1].xa_ : 0);
     }
@@ -902,14 +944,14 @@ __device__ __forceinline__ void wide_items(const GsArgs& a, GsSmem<PC, kGwThread
 template <int NT, int PC>
 __global__ __launch_bounds__(kGwThreads) void grouped_shrink_wide_kernel(GsArgs a) {
   __shared__ GsSmem<PC, kGwThreads> sm;
-  __shared__ floatx4 red[kGwWaves][2 * NT][kWave];
+  __shared__ floatx4 red[kGwWaves][kWideQB * NT][kWave];
   PairKeep k0;
   k0.a = sm.atab;
   const int na = build_worklist<kGwThreads, PC, 1>(a.gr, a.row_offset, a.row_end, sm.off,
                                                    sm.valid, sm.apairs, sm.wcount, k0);
   WideProj pj[1];
   pj[0] = WideProj{a.xa_, 0, 0, 0, sm.atab, nullptr, nullptr};
-  wide_items<NT, PC, false, 1>(a, sm, red, na, pj, nullptr);
+  wide_items<NT, PC, false, 1, kWideQB>(a, sm, red, na, pj, nullptr);
 }
 
 // Shrink and fold of a window in one launch (rld_moe_grouped in the wide case);
@@ -918,16 +960,18 @@ __global__ __launch_bounds__(kGwThreads) void grouped_shrink_wide_kernel(GsArgs 
 // as the delta tile of the fold.
 template <int NT, int PC, int NP>
 __device__ __forceinline__ void fold_wide_body(const GsArgs& a) {
-  constexpr size_t kRedBytes = sizeof(floatx4) * kGwWaves * 2 * NT * kWave;
+  constexpr int QB = kWideQB;
+  constexpr size_t kRedBytes = sizeof(floatx4) * kGwWaves * QB * NT * kWave;
   constexpr size_t kDlBytes = sizeof(uint16_t) * 32 * kFuseStride;
   __shared__ GsSmem<PC, kGwThreads> sm;
   __shared__ uint64_t btab[NP][PC];
   __shared__ float bscale[NP][PC];
   __shared__ uint64_t atab2[NP > 1 ? PC : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t xl[32 * kXlStride];
+  // xa of a batch; whole 32-row passes of the fold read it
+  __shared__ __attribute__((aligned(16))) uint16_t xl[32 * ((QB + 1) / 2) * kXlStride];
   __shared__ __attribute__((aligned(16))) unsigned char buf[kRedBytes > kDlBytes ? kRedBytes
                                                                                 : kDlBytes];
-  auto red = reinterpret_cast<floatx4 (*)[2 * NT][kWave]>(buf);
+  auto red = reinterpret_cast<floatx4 (*)[QB * NT][kWave]>(buf);
   PairKeep k0, k1;
   k0.a = sm.atab;
   k0.b = btab[0];
@@ -948,7 +992,7 @@ __device__ __forceinline__ void fold_wide_body(const GsArgs& a) {
   if (NP > 1)
     pj[NP - 1] = WideProj{a.xa2_, a.out2_, a.os2, a.n_out2, atab2, btab[NP - 1],
                           bscale[NP - 1]};
-  wide_items<NT, PC, true, NP>(a, sm, red, na, pj, xl);
+  wide_items<NT, PC, true, NP, QB>(a, sm, red, na, pj, xl);
 }
 
 template <int NT, int PC>

@@ -352,6 +352,30 @@ def test_moe_grouped_edge_windows():
     assert np.array_equal(run2.base.body()[tail], p.base.ravel()[tail])
 
 
+@pytest.mark.parametrize("proj,hidden", [("down", 520), ("gate", 1032)])
+def test_moe_grouped_offsets_below_zero(proj, hidden):
+    """Non-decreasing offsets whose first entries are negative: experts 0 and 1
+    end at or below row 0 and own no row (their spans clamp to empty, never to
+    a range past the window), expert 2 owns rows [0, off[3]).  The chunked
+    kernels (down) and the one-launch wide fold (gate, k_in 1032)."""
+    dev = require_gpu()
+    wl = _small_grouped(projections=(proj,), hidden=hidden)
+    p = wl.projections[0]
+    say(f"case: grouped offsets below zero {proj} k_in={p.k_in}")
+    off = wl.expert_offsets.copy()
+    off[:3] = [-8, -4, 0]
+    run = GroupedRun(wl, p, dev, cap=wl.te)
+    run.off = dev_i32(off, dev)
+    xas = run.run([(0, wl.te)])
+    wl2 = W.MoeGroupedWorkload(**{**wl.__dict__, "expert_offsets": off,
+                                  "sorted_expert": O.expert_owner(off, 0, wl.te)})
+    assert wl2.sorted_expert.min() == 2
+    xa_o, out_o = oracle_grouped_window(wl2, p, 0, wl.te, p.base.ravel().copy())
+    assert_xa_close(xas[0], xa_o, "offsets below zero xa", abs_sums_grouped(wl2, p, 0, wl.te),
+                    shrink_depth("grouped", p.k_in, wl.max_rank))
+    assert_out_close(run.base.body(), out_o, "offsets below zero out")
+
+
 def test_moe_grouped_full_config_sampled():
     """The MoE grouped prefill at full size (4096 tokens, top-8 of 128 experts,
     te = 32768 sorted rows in windows of 8192, down 768 -> 2048 and gate/up
