@@ -258,6 +258,8 @@ def summarize(dirs, bench_json=None, workload="step"):
 LANES = {"q": (0, 0), "k": (0, 1), "v": (0, 2), "o": (1, 0),
          "gate": (0, 0), "up": (0, 1), "down": (1, 0)}
 MAX_LANES = 3
+# workloads whose first group of folds is one rld_bgmv_multi call
+MULTI_TAGS = {"attn"}
 
 
 def grouped_shrink_kernel(k_in, max_rank):
@@ -324,7 +326,39 @@ class Step:
                           torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev))
                          for _ in range(MAX_LANES)]
                 keep += [seq, bufs, lanes]
+                # the attention's q, k and v folds read the same rows: one
+                # rld_bgmv_multi call for them.  (Gate and up stay two calls on
+                # parallel branches, which overlap each other's launch gaps and
+                # tails: as one call the FFN's cost in the step was 106 us
+                # against 94.)
+                first = [c for c in wl.calls
+                         if tag in MULTI_TAGS and LANES.get(c.module, (0, 0))[0] == 0]
+                if len({(c.x_buf, c.x_row_stride, c.k_in, c.max_rank) for c in first}) != 1 \
+                        or len(first) < 2:
+                    first = []
+                if first:
+                    c0 = first[0]
+                    rts = [DenseRoute(c.adapters, c.max_loras, c.max_rank, c.k_in, c.n_out, dev)
+                           for c in first]
+                    mwsb = R.rld_bgmv_multi_workspace_bytes(wl.n, c0.k_in, c0.max_rank, len(first))
+                    mws = torch.zeros(max(mwsb, 16), dtype=torch.uint8, device=dev)
+                    xas = [lanes[i][0] for i in range(len(first))]
+                    outs = [bufs[c.out_buf].data_ptr() + 2 * c.out_offset for c in first]
+                    keep += [rts, mws]
+                    sb = sum(bgmv_bytes(wl, c)[0] + bgmv_bytes(wl, c)[1] for c in first)
+                    fl = sum(bgmv_bytes(wl, c)[2] for c in first)
+
+                    def multi(rts=rts, c0=c0, x=bufs[c0.x_buf].data_ptr(), seq=seq, outs=outs,
+                              oss=[c.out_row_stride for c in first], xas=xas, mws=mws,
+                              mwsb=mwsb, n=wl.n):
+                        return R.rld_bgmv_multi([r.route for r in rts], x, c0.x_row_stride, seq,
+                                                n, outs, oss, xas, mws, mwsb)
+                    add((f"{tag}.{'+'.join(c.module for c in first)}.multi", "bgmv_multi", multi,
+                         sb, fl, wl.n * len(first)), c0.module, 0)
+                    self.rows += wl.n * len(first)
                 for c in wl.calls:
+                    if any(c is f for f in first):
+                        continue
                     xa, ws = lanes[LANES.get(c.module, (0, 0))[1]]
                     sb, eb, fl, _ = bgmv_bytes(wl, c)
                     x = bufs[c.x_buf].data_ptr()

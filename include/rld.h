@@ -227,6 +227,31 @@ int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_stride,
              const int32_t* seq_slot, uint32_t n, void* base_out, uint32_t out_row_stride,
              void* xa, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Several routed BGMV folds over the same rows (apply_lora_bgmv once per
+ * route, as a layer's q, k and v, or gate and up, read one input): one shrink,
+ * one chunk reduce (k_in split only) and one expand launch serve every route,
+ * instead of that many per route.
+ *   routes          host array [nroutes] of routes, 1 <= nroutes <= 4
+ *                   (RLD_EUNSUPPORTED above); all with the same k_in and
+ *                   max_rank (RLD_EINVAL otherwise); max_loras and n_out may
+ *                   differ
+ *   x, seq_slot, n  as rld_bgmv, shared by every route
+ *   base_out, out_row_stride, xa
+ *                   host arrays [nroutes]: route r folds into base_out[r]
+ *                   (row stride out_row_stride[r]) through its own xa[r]
+ *                   (device BF16 [n, max_rank]); as rld_bgmv otherwise
+ *   workspace       rld_bgmv_multi_workspace_bytes(n, k_in, max_rank, nroutes)
+ *                   bytes (route r's partials at r times the single-route
+ *                   size), under the single-route contract
+ * Route r's results are bit-identical to rld_bgmv on that route alone.  The
+ * outputs of different routes must not overlap; n == 0 is a no-op. */
+size_t rld_bgmv_multi_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank,
+                                      uint32_t nroutes);
+int rld_bgmv_multi(const rld_route* const* routes, uint32_t nroutes, const void* x,
+                   uint32_t x_row_stride, const int32_t* seq_slot, uint32_t n,
+                   void* const* base_out, const uint32_t* out_row_stride, void* const* xa,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace the unrouted entry points need for m rows: the same k_in
  * split as the BGMV path (rld_bgmv_workspace_bytes(m, k_in, max_rank, 1)),
  * under the same contract.  0 when k_in fits one chunk. */

@@ -93,6 +93,9 @@ _SIGS = {
     "rld_bgmv_shrink": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
     "rld_bgmv_expand_fold": (c_int, [_R, _P, _P, c_uint32, _P, c_uint32, _P]),
     "rld_bgmv": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
+    "rld_bgmv_multi_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32, c_uint32]),
+    "rld_bgmv_multi": (c_int, [_P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, _P, _P,
+                               c_size_t, _P]),
     "rld_f16_to_bf16_host": (c_int, [_P, _P, c_size_t]),
     "rld_lora_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32]),
     "rld_lora_shrink": (c_int, [_L, _P, c_uint32, c_uint32, _P, _P, c_size_t, _P]),
@@ -239,6 +242,27 @@ def rld_bgmv(route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, xa, 
     return _lib.rld_bgmv(ctypes.byref(route), ptr(x), x_row_stride, ptr(seq_slot), n,
                          ptr(base_out), out_row_stride, ptr(xa), ptr(workspace), workspace_bytes,
                          stream_handle(stream))
+
+
+def rld_bgmv_multi_workspace_bytes(n, k_in, max_rank, nroutes):
+    return _lib.rld_bgmv_multi_workspace_bytes(n, k_in, max_rank, nroutes)
+
+
+def rld_bgmv_multi(routes, x, x_row_stride, seq_slot, n, base_out, out_row_stride, xa,
+                   workspace, workspace_bytes, stream=None, nroutes=None):
+    """routes, base_out, out_row_stride, xa: sequences with one entry per route
+    (marshalled into the host arrays the call takes); nroutes defaults to
+    len(routes)."""
+    k = len(routes)
+    nr = k if nroutes is None else nroutes
+    rt = (c_void_p * max(k, 1))(*[ctypes.addressof(r) for r in routes])
+    bo = (c_void_p * max(k, 1))(*[ptr(b) for b in base_out])
+    os_ = (c_uint32 * max(k, 1))(*out_row_stride)
+    xs = (c_void_p * max(k, 1))(*[ptr(v) for v in xa])
+    return _lib.rld_bgmv_multi(ctypes.cast(rt, c_void_p), nr, ptr(x), x_row_stride,
+                               ptr(seq_slot), n, ctypes.cast(bo, c_void_p),
+                               ctypes.cast(os_, c_void_p), ctypes.cast(xs, c_void_p),
+                               ptr(workspace), workspace_bytes, stream_handle(stream))
 
 
 def rld_f16_to_bf16_host(src, dst, n):

@@ -464,10 +464,9 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(BgmvArgs a, uint32_t t
 // columns); up to kReduceBatch chunk loads go out before their adds.
 constexpr int kReduceBatch = 24;
 
-__global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a) {
+// Thread t of a call's reduce: row t / (R/4), columns 4 (t % (R/4)) ..
+__device__ __forceinline__ void reduce_unit(const BgmvArgs& a, uint32_t t) {
   const uint32_t q4 = a.R / 4;
-  const uint32_t t = blockIdx.x * kReduceThreads + threadIdx.x;
-  if (t >= a.n * q4) return;
   const uint32_t row = t / q4;
   const uint32_t col = (t % q4) * 4;
   const RLD_GLOBAL floatx4* p =
@@ -490,10 +489,63 @@ __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a)
   *reinterpret_cast<RLD_GLOBAL u32x2*>(a.xa() + (size_t)row * a.R + col) = o;
 }
 
+__global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a) {
+  const uint32_t t = blockIdx.x * kReduceThreads + threadIdx.x;
+  if (t >= a.n * (a.R / 4)) return;
+  reduce_unit(a, t);
+}
+
 template <int NKS, int MT>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(BgmvArgs a) {
   __shared__ ExpandSmem<MT> sm;
   expand_item<NKS, MT>(a, (int)blockIdx.y, blockIdx.x * ExpandSmem<MT>::kCols, sm);
+}
+
+// Several routes over the same rows (rld_bgmv_multi): one launch of each
+// kernel serves every route, the routes' items concatenated (route r: shrink
+// items [first[r], first[r+1]), expand column tiles [tfirst[r], tfirst[r+1])).
+// Each route's items are the single-route call's items, so its results are
+// bit-identical to that call's.
+constexpr uint32_t kMaxRoutes = 4;
+
+struct BgmvMulti {
+  BgmvArgs a[kMaxRoutes];
+  uint32_t first[kMaxRoutes + 1];
+  uint32_t tfirst[kMaxRoutes + 1];
+  uint32_t nr;
+};
+
+__device__ __forceinline__ uint32_t route_of(const uint32_t* first, uint32_t nr, uint32_t w) {
+  uint32_t r = 0;
+  while (r + 1 < nr && w >= first[r + 1]) ++r;
+  return r;
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void bgmv_shrink_multi_kernel(BgmvMulti m, uint32_t total) {
+  __shared__ ShrinkSmem<NT> sm;
+  // every route has the same column groups: a group never spans two routes
+  const uint32_t w = xcd_group_item(m.a[0].ncg);
+  if (w >= total) return;
+  const uint32_t r = route_of(m.first, m.nr, w);
+  shrink_item<NT>(m.a[r], w - m.first[r], sm);
+}
+
+__global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_multi_kernel(BgmvMulti m) {
+  const uint32_t per = m.a[0].n * (m.a[0].R / 4);  // n and R are shared
+  const uint32_t t = blockIdx.x * kReduceThreads + threadIdx.x;
+  const uint32_t r = t / per;
+  if (r >= m.nr) return;
+  reduce_unit(m.a[r], t - r * per);
+}
+
+template <int NKS, int MT>
+__global__ __launch_bounds__(256) void bgmv_expand_multi_kernel(BgmvMulti m) {
+  __shared__ ExpandSmem<MT> sm;
+  const uint32_t r = route_of(m.tfirst, m.nr, blockIdx.x);
+  if (blockIdx.y >= m.a[r].max_loras) return;
+  expand_item<NKS, MT>(m.a[r], (int)blockIdx.y, (blockIdx.x - m.tfirst[r]) * ExpandSmem<MT>::kCols,
+                       sm);
 }
 
 // Workspace: fp32 partials [nch][n][R] (k split only).
@@ -549,6 +601,17 @@ static BgmvKernel pick_expand(uint32_t R) {
     case 2: return bgmv_expand_kernel<2, kExpMT>;
     case 3: return bgmv_expand_kernel<3, kExpMT>;
     default: return bgmv_expand_kernel<4, kExpMT>;
+  }
+}
+
+typedef void (*BgmvMultiKernel)(BgmvMulti);
+
+static BgmvMultiKernel pick_expand_multi(uint32_t R) {
+  switch (div_ceil(R, 32)) {
+    case 1: return bgmv_expand_multi_kernel<1, kExpMT>;
+    case 2: return bgmv_expand_multi_kernel<2, kExpMT>;
+    case 3: return bgmv_expand_multi_kernel<3, kExpMT>;
+    default: return bgmv_expand_multi_kernel<4, kExpMT>;
   }
 }
 
@@ -632,6 +695,75 @@ extern "C" int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_st
                        stream);
   if (st) return st;
   return rld_bgmv_expand_fold(route, xa, seq_slot, n, base_out, out_row_stride, stream);
+}
+
+extern "C" size_t rld_bgmv_multi_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t max_rank,
+                                                 uint32_t nroutes) {
+  if (k_in == 0 || max_rank == 0 || nroutes == 0) return 0;
+  return (size_t)nroutes * partial_bytes(n, k_in, max_rank);
+}
+
+extern "C" int rld_bgmv_multi(const rld_route* const* routes, uint32_t nroutes, const void* x,
+                              uint32_t x_row_stride, const int32_t* seq_slot, uint32_t n,
+                              void* const* base_out, const uint32_t* out_row_stride,
+                              void* const* xa, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!routes || nroutes == 0 || !base_out || !out_row_stride || !xa) return RLD_EINVAL;
+  if (nroutes > kMaxRoutes) return RLD_EUNSUPPORTED;
+  int st;
+  for (uint32_t r = 0; r < nroutes; ++r) {
+    if ((st = check_route(routes[r]))) return st;
+    if (routes[r]->max_loras > 65535u) return RLD_EUNSUPPORTED;
+    if (routes[r]->k_in != routes[0]->k_in || routes[r]->max_rank != routes[0]->max_rank)
+      return RLD_EINVAL;
+  }
+  if (n == 0) return RLD_OK;
+  const uint32_t k_in = routes[0]->k_in, R = routes[0]->max_rank;
+  if (!seq_slot) return RLD_EINVAL;
+  if ((st = check_rows(x, x_row_stride, k_in))) return st;
+  for (uint32_t r = 0; r < nroutes; ++r) {
+    if (!xa[r]) return RLD_EINVAL;
+    if (!aligned16(xa[r])) return RLD_EALIGN;
+    if ((st = check_rows(base_out[r], out_row_stride[r], routes[r]->n_out))) return st;
+  }
+  const size_t pb = partial_bytes(n, k_in, R);
+  if (pb) {
+    if (!workspace || workspace_bytes < nroutes * pb) return RLD_ENOSPACE;
+    if (!aligned16(workspace)) return RLD_EALIGN;
+  }
+  BgmvMulti m = {};
+  m.nr = nroutes;
+  uint32_t items = 0, tiles = 0, slots = 0;
+  for (uint32_t r = 0; r < nroutes; ++r) {
+    // each route's partials in its own part of the workspace
+    void* ws = pb ? static_cast<char*>(workspace) + r * pb : nullptr;
+    if ((st = make_args(routes[r], x, x_row_stride, seq_slot, n, xa[r], ws, pb, base_out[r],
+                        out_row_stride[r], &m.a[r])))
+      return st;
+    m.first[r] = items;
+    items += routes[r]->max_loras * m.a[r].nch * m.a[r].ncg;
+    m.tfirst[r] = tiles;
+    tiles += div_ceil(routes[r]->n_out, 64u * kExpMT);
+    slots = max(slots, routes[r]->max_loras);
+  }
+  m.first[nroutes] = items;
+  m.tfirst[nroutes] = tiles;
+  if (tiles > 0x7fffffffu) return RLD_EUNSUPPORTED;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid(xcd_group_grid(items, m.a[0].ncg));
+  if (bgmv_nt(R) == 1)
+    hipLaunchKernelGGL(bgmv_shrink_multi_kernel<1>, grid, dim3(256), 0, hs, m, items);
+  else
+    hipLaunchKernelGGL(bgmv_shrink_multi_kernel<2>, grid, dim3(256), 0, hs, m, items);
+  if ((st = launch_status())) return st;
+  if (m.a[0].nch > 1) {
+    hipLaunchKernelGGL(bgmv_reduce_multi_kernel,
+                       dim3(div_ceil(nroutes * n * (R / 4), kReduceThreads)),
+                       dim3(kReduceThreads), 0, hs, m);
+    if ((st = launch_status())) return st;
+  }
+  hipLaunchKernelGGL(pick_expand_multi(R), dim3(tiles, slots), dim3(256), 0, hs, m);
+  return launch_status();
 }
 
 // ------------------------------------------------------------ unrouted ----

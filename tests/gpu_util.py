@@ -193,6 +193,25 @@ class BgmvRun:
                                        self.bufs[c.out_buf].ptr(c.out_offset), c.out_row_stride,
                                        stream), f"rld_bgmv_expand_fold {c.module}")
 
+    def run_multi(self, idx, stream=None):
+        """Calls idx (same input buffer and stride) in one rld_bgmv_multi; returns
+        each route's xa [n, max_rank]."""
+        cs = [self.wl.calls[i] for i in idx]
+        assert len({(c.x_buf, c.x_row_stride, c.k_in, c.max_rank) for c in cs}) == 1
+        c0 = cs[0]
+        xas = [torch.zeros(max(1, self.wl.n) * c0.max_rank + 8, dtype=torch.int16,
+                           device=self.device) for _ in cs]
+        wsb = R.rld_bgmv_multi_workspace_bytes(self.wl.n, c0.k_in, c0.max_rank, len(cs))
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=self.device)
+        st = R.rld_bgmv_multi([self.routes[i].route for i in idx], self.bufs[c0.x_buf].ptr(),
+                              c0.x_row_stride, self.seq, self.wl.n,
+                              [self.bufs[c.out_buf].ptr(c.out_offset) for c in cs],
+                              [c.out_row_stride for c in cs], xas, ws, wsb, stream)
+        R.check(st, "rld_bgmv_multi")
+        torch.cuda.synchronize()
+        return [from_device_u16(x)[: self.wl.n * c0.max_rank].reshape(self.wl.n, c0.max_rank)
+                for x in xas]
+
     def run_all(self, keep_xa=True, two_stage=False):
         self.xa_by_call = []
         for i, c in enumerate(self.wl.calls):

@@ -223,6 +223,43 @@ def test_bgmv_rejects_bad_buffers():
     assert ex(xa=0) == R.RLD_EINVAL
 
 
+def test_bgmv_multi_rejects_bad_arguments():
+    """rld_bgmv_multi checks every route and buffer before any launch."""
+    q, k, v = _route(k_in=4096, n_out=4096), _route(k_in=4096, n_out=1024), \
+        _route(k_in=4096, n_out=1024)
+    n = 64
+    wsb = R.rld_bgmv_multi_workspace_bytes(n, 4096, 16, 3)
+    assert wsb == 3 * R.rld_bgmv_workspace_bytes(n, 4096, 16, 4)
+
+    def call(routes=(q, k, v), n=n, base=None, os_=None, xa=None, ws=FAKE, wsb=wsb, nr=None,
+             x=FAKE, seq=FAKE):
+        k_ = len(routes)
+        base = [FAKE] * k_ if base is None else base
+        os_ = [6144] * k_ if os_ is None else os_
+        xa = [FAKE] * k_ if xa is None else xa
+        return R.rld_bgmv_multi(list(routes), x, 4096, seq, n, base, os_, xa, ws, wsb,
+                                stream=0, nroutes=nr)
+
+    assert call(nr=0) == R.RLD_EINVAL
+    assert call(routes=(q, k, v, q, k), nr=5) == R.RLD_EUNSUPPORTED
+    assert call(routes=(q, _route(k_in=2048, n_out=1024))) == R.RLD_EINVAL   # k_in differs
+    assert call(routes=(q, _route(k_in=4096, max_rank=32))) == R.RLD_EINVAL  # rank differs
+    assert call(routes=(q, _route(k_in=4096, tables=False))) == R.RLD_EINVAL
+    assert call(n=0) == R.RLD_OK                                   # no-op, nothing launched
+    assert call(seq=0) == R.RLD_EINVAL
+    assert call(x=FAKE + 2) == R.RLD_EALIGN
+    assert call(xa=[FAKE, 0, FAKE]) == R.RLD_EINVAL
+    assert call(xa=[FAKE, FAKE + 8, FAKE]) == R.RLD_EALIGN
+    assert call(os_=[6144, 1000, 6144]) == R.RLD_EINVAL           # stride < n_out
+    assert call(base=[FAKE, FAKE, 0]) == R.RLD_EINVAL
+    assert call(wsb=wsb - 16) == R.RLD_ENOSPACE
+    assert call(ws=0) == R.RLD_ENOSPACE
+    assert call(ws=FAKE + 8) == R.RLD_EALIGN
+    # one chunk: no workspace
+    assert R.rld_bgmv_multi_workspace_bytes(n, 256, 16, 3) == 0
+    assert R.rld_bgmv_multi_workspace_bytes(n, 4096, 16, 0) == 0
+
+
 def test_bgmv_workspace_contract():
     # the workspace holds the k-split partials and per-slot bookkeeping; a short
     # one is refused before any launch, by every entry point that takes one

@@ -6,6 +6,8 @@ folded outputs within 2 BF16 ulp or 1e-3 absolute, and bit-exact everything
 that is routing: base rows, xa rows of base rows, regions outside [0, n_out)
 of each row, guard bands around every output buffer.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -114,6 +116,43 @@ def test_bgmv_out_of_range_slots_and_missing_tables():
         if s not in (0, 1):
             assert np.array_equal(out_g[row], wl.buffers["out"][row])
             assert np.all(run.xa_by_call[0][r] == 0)
+
+
+@pytest.mark.parametrize("case", ["attn_qkv", "ffn_gate_up", "small_one_chunk"])
+def test_bgmv_multi_equals_separate_calls(case):
+    """rld_bgmv_multi over routes that read the same rows is bit-identical, xa
+    and every output buffer, to rld_bgmv on each route alone: q, k and v of
+    the attention decode (the K and V folds inside [Q|K|V] rows), gate and up
+    of the FFN decode (k split, rank 64), and a one-chunk shape."""
+    dev = require_gpu()
+    if case == "attn_qkv":
+        wl, mods = W.bgmv_attn_decode(), ("q", "k", "v")
+    elif case == "ffn_gate_up":
+        wl, mods = W.bgmv_ffn_decode(), ("gate", "up")
+    else:
+        # two routes with different n_out and max_loras over one x and seq_slot
+        a = W.bgmv_custom(5, 40, 256, 264, 16, 4, (8, 16), base_frac=0.2, zipf=1.1)
+        b = W.bgmv_custom(6, 40, 256, 136, 16, 6, (8, 16))
+        c2 = dataclasses.replace(b.calls[0], module="proj2", out_buf="out2")
+        wl = W.BgmvWorkload("two routes", a.n, a.seq_slot,
+                            {**a.buffers, "out2": b.buffers["out"]}, [a.calls[0], c2])
+        mods = None
+    idx = [i for i, c in enumerate(wl.calls) if mods is None or c.module in mods]
+    say(f"case: bgmv multi {case} routes={len(idx)}")
+    sep = BgmvRun(wl, dev)
+    xa_sep = []
+    for i in idx:
+        sep.run_call(i)
+        torch.cuda.synchronize()
+        c = wl.calls[i]
+        xa_sep.append(from_device_u16(sep.xa)[: wl.n * c.max_rank].reshape(wl.n, c.max_rank))
+    multi = BgmvRun(wl, dev)
+    xa_multi = multi.run_multi(idx)
+    for i, a, b in zip(idx, xa_sep, xa_multi):
+        assert np.array_equal(a, b), f"xa of {wl.calls[i].module}"
+    o_sep, o_multi = sep.outputs(), multi.outputs()
+    for k in o_sep:
+        assert np.array_equal(o_sep[k], o_multi[k]), f"buffer {k}"
 
 
 def test_bgmv_batched_equals_single_rows():
