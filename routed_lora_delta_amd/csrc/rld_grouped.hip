@@ -454,10 +454,12 @@ __device__ __forceinline__ void gs_reduce_rows(const GsArgs& a, const GsSmem<PC,
   }
 }
 
-// Pair item (pair, chunk c, column group cg); see GsArgs.
+// Pair item (pair, chunk c, column group cg); see GsArgs.  h = 0 or 1 (one
+// chunk and one column group only): the item takes the first ceil(cnt / 2) or
+// the remaining rows of each scan round; h < 0: all of them.
 template <int KS, int NT, int PC>
 __device__ void gs_pair_item(const GsArgs& a, GsSmem<PC, kGsThreads>& sm, floatx4 (*red)[4 * NT][kWave], int pair,
-                             uint32_t c, uint32_t cg) {
+                             uint32_t c, uint32_t cg, int h = -1) {
   const GroupedRows& g = a.gr;
   const uint32_t R = a.R, k_in = a.k_in;
   const int s = pair / (int)g.E;
@@ -482,10 +484,11 @@ __device__ void gs_pair_item(const GsArgs& a, GsSmem<PC, kGsThreads>& sm, floatx
   const RLD_GLOBAL uint16_t* x = a.x();
   const bool one_chunk = a.nch == 1;
   const size_t W = a.row_end - a.row_offset;
-  // up to 64 rows of the segment, starting at b0
+  // up to 64 rows of the segment, starting at b0, below bend
   const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ta);
+  int bend = cnt;
   auto batch = [&](int b0) {
-    const int nb = min(cnt - b0, 64);
+    const int nb = min(bend - b0, 64);
     // Rows col0.. of A_{s,e} over this wave's k range (MFMA B operands) and the
     // x rows of the batch's four 16-row subtiles, all in one round of loads
     // (clamped in-bounds addresses).
@@ -559,14 +562,18 @@ __device__ void gs_pair_item(const GsArgs& a, GsSmem<PC, kGsThreads>& sm, floatx
     }
     __syncthreads();
   };
-  if (!multi && cnt <= 64) {
-    batch(0);  // the usual case
-  } else {
-    for (;;) {
-      for (int b0 = 0; b0 < cnt; b0 += 64) batch(b0);
-      if (c0 >= hi) break;
-      cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
+  // Each scan round's rows [b1, bend): all of them, or this item's half.
+  for (;;) {
+    const int split = (cnt + 1) / 2;
+    const int b1 = h > 0 ? split : 0;
+    bend = h == 0 ? split : cnt;
+    if (bend - b1 <= 64) {
+      if (b1 < bend) batch(b1);  // the usual case
+    } else {
+      for (int b0 = b1; b0 < bend; b0 += 64) batch(b0);
     }
+    if (c0 >= hi) break;
+    cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
   }
   if (one_chunk) return;
 
@@ -620,13 +627,26 @@ __global__ __launch_bounds__(kGsThreads) void grouped_shrink_kernel(GsArgs a) {
   k0.a = sm.atab;
   const int na = build_worklist<kGsThreads, PC, 1>(a.gr, a.row_offset, a.row_end, sm.off,
                                                    sm.valid, sm.apairs, sm.wcount, k0);
+  // One chunk and one column group: items (pair, row half), both halves of a
+  // pair on one XCD (item it runs on a block with blockIdx.x = it mod
+  // gridDim.x, a multiple of 8), whose L2 serves the second read of A_{s,e}.
+  // Otherwise (pair, chunk, column group).  Then the row blocks.
+  const bool halves = a.nch == 1 && a.ncg == 1;
   const uint32_t per = a.nch * a.ncg;
-  const uint32_t npi = (uint32_t)na * per;
+  const uint32_t npi = halves ? 16u * (((uint32_t)na + 7u) / 8u) : (uint32_t)na * per;
   const uint32_t total = npi + a.nz;
   for (uint32_t it = blockIdx.x; it < total; it += gridDim.x) {
     if (it < npi) {
-      const uint32_t rem = it % per;
-      gs_pair_item<KS, NT, PC>(a, sm, red, sm.apairs[it / per], rem / a.ncg, rem % a.ncg);
+      uint32_t p = it / per, c = 0, cg = 0;
+      int h = -1;
+      if (halves) {
+        p = (it / 16u) * 8u + it % 8u;
+        h = (int)((it / 8u) % 2u);
+      } else {
+        c = (it % per) / a.ncg;
+        cg = (it % per) % a.ncg;
+      }
+      if (p < (uint32_t)na) gs_pair_item<KS, NT, PC>(a, sm, red, sm.apairs[p], c, cg, h);
     } else {
       gs_zero_item(a, sm, it - npi);
     }
@@ -1274,8 +1294,12 @@ static int grouped_shrink(const rld_moe_route* route, const void* x, uint32_t x_
     return launch_status();
   }
   a.nz = div_ceil(W, (uint32_t)kGsThreads);
-  const uint64_t items = np * a.nch * a.ncg + a.nz;
-  const uint32_t grid = (uint32_t)(items < kGsGrid ? items : kGsGrid);
+  // one chunk and one column group: (pair, row half) items (the kernel pairs
+  // items it and it + 8 on one XCD, so the grid is a multiple of 8)
+  const uint64_t items = (a.nch == 1 && a.ncg == 1 ? 16u * ((np + 7u) / 8u)
+                                                   : np * a.nch * a.ncg) + a.nz;
+  const uint64_t items8 = (items + 7u) & ~(uint64_t)7u;
+  const uint32_t grid = (uint32_t)(items8 < kGsGrid ? items8 : kGsGrid);
   if (small_caps(route, num_experts_off))
     launch_gs_ks<kPairCapSmall>(a.kc / 128u, nt, a, grid, hs);
   else
