@@ -178,9 +178,103 @@ __global__ __launch_bounds__(256) void gather_expand_kernel(GatherArgs a) {
 
 // Shrink and fold of one flat row per block (rld_moe_gather): the two kernels
 // above in one, the xa row handed over in LDS.
+// Fold of flat row rho when max_rank <= 16, k_in <= 1024 and n_out <= 2048
+// (one 8-column piece per thread): the row's loads go out in three rounds --
+// its routing entries with its x and base values, the pair's table entries,
+// then A_{s,e} and B_{s,e} together -- instead of one round per step.  The
+// arithmetic is gather_shrink_row's and gather_fold_cols8's, in the same
+// order (a lane's k pieces lane*8 + 512m in ascending m, the same
+// xor-butterfly, the same rank order of the fold), so the bits are the same.
+__device__ __forceinline__ void gather_fold_row_small(const GatherArgs& a, uint32_t rho,
+                                                      uint16_t* xl) {
+  const uint32_t R = a.R, k_in = a.k_in;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t j = threadIdx.x * 8u;
+  const bool fold_j = j < a.n_out;
+  RLD_GLOBAL uint16_t* op = a.out() + (size_t)rho * a.os + (fold_j ? j : 0u);
+  const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)rho * a.xs;
+  // round 1: routing, x pieces, base values (clamped in-bounds addresses)
+  const int s = a.radapt_ ? a.row_adapter()[rho / a.top_k] : 0;
+  const int e = a.indices()[rho];
+  uint4 xv[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t c = (uint32_t)lane * 8u + 512u * m;
+    xv[m] = load16(xr + (c < k_in ? c : 0u));
+  }
+  const uint4 base = load16(op);
+  issue_point();
+  // round 2: the pair's table entries (index 0 when the routing is out of range)
+  const bool in_range = s >= 0 && (uint32_t)s < a.max_loras && e >= 0 && (uint32_t)e < a.E;
+  const int pair = in_range ? s * (int)a.E + e : 0;
+  const uint64_t ta = a.a_table()[pair], tb = a.b_table()[pair];
+  const float scale = a.scale_table()[pair];
+  RLD_GLOBAL uint16_t* xo = a.xa() + (size_t)rho * R;
+  if (!in_range || ta == 0ull || tb == 0ull) {
+    for (uint32_t k = threadIdx.x; k < R; k += 256) xo[k] = 0;
+    return;
+  }
+  // round 3: this wave's A_{s,e} rows k = wave + 4i and the B_{s,e} rows of
+  // this thread's eight output columns
+  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ta);
+  const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(tb) + (fold_j ? (size_t)j * R : 0);
+  uint4 av[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t k = (uint32_t)wave + 4u * i;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint32_t c = (uint32_t)lane * 8u + 512u * m;
+      av[i][m] = load16(A + (size_t)(k < R ? k : 0u) * k_in + (c < k_in ? c : 0u));
+    }
+  }
+  uint4 bv[8][2];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      bv[c][q] = load16(B + (fold_j ? (size_t)c * R + (8u * q < R ? 8u * q : 0u) : 0u));
+  issue_point();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t k = (uint32_t)wave + 4u * i;
+    float v = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      if ((uint32_t)lane * 8u + 512u * m < k_in) v = dot8(xv[m], av[i][m], v);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0 && k < R) {
+      const uint16_t b = (uint16_t)f32_to_bf16(v);
+      xo[k] = b;
+      xl[k] = b;
+    }
+  }
+  __syncthreads();
+  if (!fold_j) return;
+  float d[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    d[c] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (8u * q < R) d[c] = dot8(bv[c][q], xa8(xl + 8 * q), d[c]);
+  }
+  const uint4 o = make_uint4(fold2(base.x, pack_bf16x2(d[0], d[1]), scale),
+                             fold2(base.y, pack_bf16x2(d[2], d[3]), scale),
+                             fold2(base.z, pack_bf16x2(d[4], d[5]), scale),
+                             fold2(base.w, pack_bf16x2(d[6], d[7]), scale));
+  store16(op, o);
+}
+
 __global__ __launch_bounds__(256) void gather_fold_kernel(GatherArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xl[RLD_MAX_RANK];
   const uint32_t rho = blockIdx.x;
+  if (a.R <= 16u && a.k_in <= 1024u && a.n_out <= 2048u) {
+    gather_fold_row_small(a, rho, xl);
+    return;
+  }
   RLD_GLOBAL uint16_t* xo = a.xa() + (size_t)rho * a.R;
   const int pair = gather_pair(a, rho);
   if (pair < 0) {
