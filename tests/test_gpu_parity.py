@@ -771,7 +771,6 @@ def test_bgmv_graph_new_routing_each_replay():
     replay new seq_slot contents (including out-of-range slots) are written into
     the same device buffer.  Each replay meets the oracle for its own routing."""
     dev = require_gpu()
-    import dataclasses
     wl = W.bgmv_custom(31, 96, 4096, 1032, 16, 8, (8, 16), base_frac=0.1)
     say("case: bgmv graph, new seq_slot per replay")
     run = BgmvRun(wl, dev)
@@ -793,6 +792,51 @@ def test_bgmv_graph_new_routing_each_replay():
         run.xa_by_call = [from_device_u16(run.xa)[: wl.n * 16].reshape(wl.n, 16).copy()]
         compare_bgmv(run, f"replay {rep}")
         _base_rows_xa_zero(run.wl, run)
+
+
+def test_bgmv_multi_graph_new_routing_each_replay():
+    """rld_bgmv_multi (q, k and v of the attention decode) captured once;
+    before every replay new seq_slot contents (out-of-range slots included) go
+    into the captured buffer, and each replay is bit-identical, xa and outputs,
+    to one eager rld_bgmv per route on that routing."""
+    dev = require_gpu()
+    wl = W.bgmv_attn_decode()
+    idx = [i for i, c in enumerate(wl.calls) if c.module in ("q", "k", "v")]
+    cs = [wl.calls[i] for i in idx]
+    say("case: bgmv multi graph, new seq_slot per replay")
+    run = BgmvRun(wl, dev)
+    pristine = {k: b.t.clone() for k, b in run.bufs.items()}
+    xas = [torch.zeros(wl.n * 16 + 8, dtype=torch.int16, device=dev) for _ in cs]
+    wsb = R.rld_bgmv_multi_workspace_bytes(wl.n, cs[0].k_in, 16, len(cs))
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    args = ([run.routes[i].route for i in idx], run.bufs[cs[0].x_buf].ptr(), cs[0].x_row_stride,
+            run.seq, wl.n, [run.bufs[c.out_buf].ptr(c.out_offset) for c in cs],
+            [c.out_row_stride for c in cs], xas, ws, wsb)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        R.check(R.rld_bgmv_multi(*args, stream=s), "rld_bgmv_multi (capture)")
+    rng = np.random.default_rng(78)
+    for rep in range(3):
+        seq = rng.integers(-2, 18, size=wl.n).astype(np.int32)  # 16, 17: beyond max_loras
+        run.seq.copy_(torch.from_numpy(seq))
+        for k, b in run.bufs.items():
+            b.t.copy_(pristine[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = BgmvRun(dataclasses.replace(wl, seq_slot=seq), dev)
+        for i, xa in zip(idx, xas):
+            ref.run_call(i)
+            torch.cuda.synchronize()
+            want = from_device_u16(ref.xa)[: wl.n * 16]
+            assert np.array_equal(from_device_u16(xa)[: wl.n * 16], want), \
+                f"replay {rep}: xa of {wl.calls[i].module}"
+        got, exp = run.outputs(), ref.outputs()
+        for k in got:
+            assert np.array_equal(got[k], exp[k]), f"replay {rep}: buffer {k}"
 
 
 def test_grouped_graph_new_routing_each_replay():
