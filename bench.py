@@ -306,10 +306,11 @@ class Step:
         def i32(a):
             return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
 
-        def add(call, module, lane=None):
+        def add(call, module, lane=None, group=None):
             g, ln = LANES.get(module, (0, 0))
             self.calls.append(call)
-            self.sched.append((group0 + g, ln if lane is None else lane))
+            self.sched.append((group0 + (g if group is None else group),
+                               ln if lane is None else lane))
 
         for tag, wl in workloads:
             if tag in ("attn", "ffn", "lora"):
@@ -435,6 +436,11 @@ class Step:
                 byname = {p.name: p for p in projs}
                 paired = ("gate" in byname and "up" in byname
                           and grouped_pair_fused(byname["gate"], byname["up"], wl))
+                # Window k's down rows are the rows its gate and up folds wrote
+                # (the activation of sorted row r comes from gate and up of row
+                # r), so with the pair call each window is one chain on branch k:
+                # gate+up, then down, with no barrier across windows.
+                wgroup = 0 if paired else None
                 for p in projs:
                     rt, x, base = dev_p[p.name]
                     if paired and p.name == "up":
@@ -458,7 +464,8 @@ class Step:
                                     base_b, q.n_out, xa, xa_b, wl.cap, ws, wsb)
 
                             add((f"grouped.gate+up.[{lo},{hi}).fold", "grouped_fold_pair_kernel",
-                                 pair, sb + eb + sb2 + eb2, fl + fl2, 2 * (hi - lo)), p.name, lane)
+                                 pair, sb + eb + sb2 + eb2, fl + fl2, 2 * (hi - lo)), p.name, lane,
+                                wgroup)
                             continue
 
                         def shrink(rt=rt, x=x, p=p, lo=lo, hi=hi, off=off, stid=stid, rad=rad,
@@ -485,13 +492,13 @@ class Step:
 
                             add((f"grouped.{p.name}.[{lo},{hi}).fold",
                                  "grouped_fold_wide_kernel", fold, sb + eb, fl, hi - lo),
-                                p.name, lane)
+                                p.name, lane, wgroup)
                             continue
                         add((f"grouped.{p.name}.[{lo},{hi}).shrink",
                              grouped_shrink_kernel(p.k_in, wl.max_rank), shrink, sb, fl / 2,
-                             hi - lo), p.name, lane)
+                             hi - lo), p.name, lane, wgroup)
                         add((f"grouped.{p.name}.[{lo},{hi}).expand", "grouped_expand_kernel",
-                             expand, eb, fl / 2, 0), p.name, lane)
+                             expand, eb, fl / 2, 0), p.name, lane, wgroup)
                 self.rows += wl.te * len(projs)
             group0 = max((g for g, _ in self.sched), default=-1) + 1
         self._keep = keep
