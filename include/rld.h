@@ -52,7 +52,7 @@ extern "C" {
 #define RLD_OK 0
 #define RLD_EINVAL (-1)       /* null required pointer, zero or inconsistent size   */
 #define RLD_EALIGN (-2)       /* size, stride, offset or pointer not aligned (above) */
-#define RLD_EUNSUPPORTED (-3) /* e.g. max_rank > 128                                  */
+#define RLD_EUNSUPPORTED (-3) /* e.g. max_rank > 128, or more than 2^30 work items   */
 #define RLD_ELAUNCH (-4)      /* a kernel launch failed; see rld_last_hip_error()    */
 #define RLD_ENOSPACE (-5)     /* xa or workspace smaller than the call needs          */
 

@@ -591,6 +591,12 @@ static int make_args(const rld_route* route, const void* x, uint32_t x_row_strid
 
 typedef void (*BgmvKernel)(BgmvArgs);
 
+// A call's shrink items and chunk-reduce threads fit the 32-bit item indices
+// and grids of its launches (with room for the grid's rounding up).
+static bool launch_fits(uint64_t items, uint64_t reduce_threads) {
+  return items <= (1ull << 30) && reduce_threads <= (1ull << 30);
+}
+
 // Expand items of 256 output columns (16*4 per wave).  (512-column items,
 // half the blocks, measured slower on the decode FFN shapes.)
 constexpr int kExpMT = 4;
@@ -639,6 +645,8 @@ extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x
   if ((st = make_args(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
                       nullptr, 0, &a)))
     return st;
+  if (!launch_fits((uint64_t)route->max_loras * a.nch * a.ncg, (uint64_t)n * (a.R / 4)))
+    return RLD_EUNSUPPORTED;
   const uint32_t total = route->max_loras * a.nch * a.ncg;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(xcd_group_grid(total, a.ncg));
@@ -731,6 +739,13 @@ extern "C" int rld_bgmv_multi(const rld_route* const* routes, uint32_t nroutes, 
     if (!workspace || workspace_bytes < nroutes * pb) return RLD_ENOSPACE;
     if (!aligned16(workspace)) return RLD_EALIGN;
   }
+  {
+    uint64_t all = 0;
+    for (uint32_t r = 0; r < nroutes; ++r)
+      all += (uint64_t)routes[r]->max_loras * div_ceil(k_in, bgmv_chunk(k_in, R)) *
+             div_ceil(R, 16u * bgmv_nt(R));
+    if (!launch_fits(all, (uint64_t)nroutes * n * (R / 4))) return RLD_EUNSUPPORTED;
+  }
   BgmvMulti m = {};
   m.nr = nroutes;
   uint32_t items = 0, tiles = 0, slots = 0;
@@ -817,6 +832,9 @@ extern "C" int rld_lora_shrink(const rld_pair* pair, const void* x, uint32_t x_r
   a.xs = x_row_stride;
   a.xa_ = reinterpret_cast<uint64_t>(xa);
   a.partial_ = reinterpret_cast<uint64_t>(workspace);
+  if (!launch_fits((uint64_t)div_ceil(m, (uint32_t)kDenseShrinkRows) * a.nch * a.ncg,
+                   (uint64_t)m * (a.R / 4)))
+    return RLD_EUNSUPPORTED;
   const uint32_t total = div_ceil(m, (uint32_t)kDenseShrinkRows) * a.nch * a.ncg;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(xcd_group_grid(total, a.ncg));

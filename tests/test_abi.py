@@ -260,6 +260,19 @@ def test_bgmv_multi_rejects_bad_arguments():
     assert R.rld_bgmv_multi_workspace_bytes(n, 4096, 16, 0) == 0
 
 
+def test_bgmv_refuses_launches_past_32_bit_indices():
+    """A call whose items or chunk-reduce threads would not fit 32-bit indices
+    is refused before any launch (the workspace size passed is large enough)."""
+    rt = _route(k_in=4096, n_out=4096, max_rank=128, max_loras=4)
+    n = 1 << 26  # 2^26 rows x 32 reduce threads per row
+    big = 1 << 62
+    assert R.rld_bgmv_shrink(rt, FAKE, 4096, FAKE, n, FAKE, FAKE, big, 0) == R.RLD_EUNSUPPORTED
+    assert R.rld_bgmv_multi([rt, rt], FAKE, 4096, FAKE, n, [FAKE] * 2, [4096] * 2, [FAKE] * 2,
+                            FAKE, big, stream=0) == R.RLD_EUNSUPPORTED
+    pair = R.rld_pair(FAKE, FAKE, 1.0, 4096, 4096, 128)
+    assert R.rld_lora_shrink(pair, FAKE, 4096, n, FAKE, FAKE, big, 0) == R.RLD_EUNSUPPORTED
+
+
 def test_bgmv_workspace_contract():
     # the workspace holds the k-split partials and per-slot bookkeeping; a short
     # one is refused before any launch, by every entry point that takes one
