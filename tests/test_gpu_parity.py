@@ -278,8 +278,11 @@ def test_bgmv_shared_workspace_second_pass():
 
 # ------------------------------------------------------------------ gather ---
 
-@pytest.mark.parametrize("variant", ["config", "null_adapter", "ragged"])
+@pytest.mark.parametrize("variant", ["config", "null_adapter", "ragged", "ragged_rank16"])
 def test_moe_gather(variant):
+    """The gather fold against the oracle: the MoE decode config, no row_adapter,
+    and ragged shapes with out-of-range expert ids and slots (rank 24: the
+    general kernel path; rank 16 with k_in 1000: the three-round path)."""
     dev = require_gpu()
     if variant == "config":
         wl = W.moe_gather()
@@ -288,11 +291,19 @@ def test_moe_gather(variant):
         wl = W.moe_gather(num_tokens=20, top_k=4, num_experts=16, k_in=264, n_out=1032,
                           max_loras=1, n_adapted=10, max_rank=16)
         ra = None
-    else:
+    elif variant == "ragged":
         wl = W.moe_gather(num_tokens=13, top_k=6, num_experts=40, k_in=1000, n_out=520,
                           max_loras=5, n_adapted=25, ranks=(8, 24), max_rank=24)
         wl.indices[3] = -1
         wl.indices[10] = 999
+        ra = "wl"
+    else:
+        wl = W.moe_gather(num_tokens=13, top_k=6, num_experts=40, k_in=1000, n_out=520,
+                          max_loras=5, n_adapted=25, ranks=(8, 16), max_rank=16)
+        wl.indices[3] = -1
+        wl.indices[10] = 999
+        wl.row_adapter[2] = 7    # slot past max_loras: the token's rows stay base rows
+        wl.row_adapter[5] = -1
         ra = "wl"
     say(f"case: gather {variant} {wl.name}")
     xa_g, out_g = run_gather(wl, dev, ra)
