@@ -49,7 +49,8 @@ Readings where the pages are silent (each also listed with the design notes):
     (or, when absent, slot 0) picks the row of the table;
   * grouped path: the adapter lookup uses t = sorted_token_ids[r] in both the
     gather and the non-gather mode; rows outside every expert span, experts
-    beyond the table, tokens beyond num_tokens and unadapted pairs are skipped.
+    beyond the table, unadapted pairs and, whenever sorted_token_ids is given,
+    tokens outside [0, num_tokens) are skipped.
 
 Pins (``tests/test_oracle.py``): BF16 rounding against hand-derived bit
 patterns, exhaustive round trips and torch's float32->bfloat16 conversion;
@@ -351,10 +352,14 @@ def moe_grouped(pairs, num_experts: int, k_in: int, n_out: int, max_rank: int,
                 base_out: np.ndarray, out_row_stride: int):
     """Grouped fold of one chunk window [row_offset, row_end) of expert-sorted rows.
 
-    Row r: expert e from the expert_offsets spans; t = sorted_token_ids[r];
-    slot s = row_adapter[t] (slot 0 when row_adapter is None); the x row is
-    x[t] when x_gather else x[r]; base_out row r is folded in place; xa is
-    written at the window-local row r - row_offset.
+    Row r: expert e from the expert_offsets spans (an offsets array may list
+    more experts than the table holds: a row of an expert past the table is
+    skipped); t = sorted_token_ids[r], read whenever the map is given, and a
+    token outside [0, num_tokens) skips the row (the map may be None only
+    when neither the x gather nor row_adapter needs it); slot
+    s = row_adapter[t] (slot 0 when row_adapter is None); the x row is x[t]
+    when x_gather else x[r]; base_out row r is folded in place; xa is written
+    at the window-local row r - row_offset.
     Returns (xa [row_end-row_offset, max_rank], folded copy of base_out)."""
     max_loras = len(pairs)
     nloc = row_end - row_offset
@@ -363,7 +368,9 @@ def moe_grouped(pairs, num_experts: int, k_in: int, n_out: int, max_rank: int,
     if nloc <= 0:
         return xa, out
     owner = expert_owner(expert_offsets, row_offset, row_end)
-    need_token = x_gather or row_adapter is not None
+    if (x_gather or row_adapter is not None) and sorted_token_ids is None:
+        raise ValueError("sorted_token_ids is needed for the x gather and row_adapter")
+    need_token = sorted_token_ids is not None
     for r in range(row_offset, row_end):
         e = int(owner[r - row_offset])
         if e < 0 or e >= num_experts:

@@ -372,6 +372,60 @@ def pin_routing_probe_grouped(o):
                     assert np.array_equal(xa[r - lo], wxa)
 
 
+def pin_grouped_invalid_values(o):
+    """Grouped-path values the host cannot check ("Module moe_lora_grouped",
+    moe_lora_grouped_down: per-tile early return on empty, out-of-range or
+    unadapted expert spans), on the closed-form routing probe:
+      * sorted_token_ids entries >= num_tokens or < 0: whenever the map is
+        given, such a row is a base row, in all four combinations of x gather
+        and row_adapter; without the map (no gather, no row_adapter) no token
+        is read and every row of an adapted span folds on slot 0;
+      * an offsets array that lists more experts than the table holds: rows of
+        the experts past the table are base rows.
+    The base is -0.0 everywhere, so an untouched row (-0.0 bits) differs from a
+    row folded with a zero delta (-0.0 + 0 = +0.0)."""
+    P = _probe_grouped_workload()
+    te, n_out, R_ = P["te"], P["n_out"], P["max_rank"]
+    E_tab = P["num_experts"] - 4  # table of experts 0..11; offsets list 16
+    ads = [a for a in P["adapters"] if a.expert < E_tab]
+    pairs = o.pack_expert_pairs(ads, P["max_loras"], E_tab, R_)
+    stid = P["stid"].copy()
+    bad_rows = {3: P["num_tokens"], 58: 10 ** 6, 131: -1, 402: -7, te - 20: P["num_tokens"] + 3}
+    for r, t in bad_rows.items():
+        stid[r] = t
+    base = np.full(te * n_out, 0x8000, np.uint16)
+    neg0 = np.uint16(0x8000)
+    lo, hi = 2, te - 5
+    for gather in (False, True):
+        for ra in (P["row_adapter"], None):
+            for map_given in ((True, False) if (not gather and ra is None) else (True,)):
+                x = P["x_tok"] if gather else P["x_sorted"]
+                xa, out = o.moe_grouped(pairs, E_tab, P["k_in"], n_out, R_, x.ravel(), P["k_in"],
+                                        gather, P["num_tokens"], P["offsets"],
+                                        stid if map_given else None, ra, lo, hi, base, n_out)
+                out = out.reshape(te, n_out)
+                for r in range(te):
+                    e, t = int(P["sexp"][r]), int(stid[r])
+                    tok_ok = (0 <= t < P["num_tokens"]) or not map_given
+                    s = int(ra[t]) if (ra is not None and tok_ok) else 0
+                    folds = (lo <= r < hi and e < E_tab and tok_ok and s >= 0
+                             and bool(P["adapted"][s, e]))
+                    tx = t if gather else int(P["stid"][r])  # token whose x row is read
+                    if folds:
+                        want = np.zeros(n_out)
+                        want[:5] = (e, s, tx // 64, tx % 64, 1)
+                        assert np.array_equal(out[r], o.round_bf16(want)), (gather, r)
+                    else:
+                        assert np.all(out[r] == neg0), (gather, ra is None, map_given, r)
+                    if lo <= r < hi:
+                        wxa = np.zeros(R_)
+                        if folds:
+                            wxa[:3] = (1, tx // 64, tx % 64)
+                        assert np.array_equal(xa[r - lo], o.round_bf16(wxa)), (gather, r)
+                if map_given:
+                    assert all(np.all(out[r] == neg0) for r in bad_rows)
+
+
 def pin_routing_probe_gather(o):
     P = _probe_grouped_workload(num_tokens=40, top_k=8, num_experts=32, max_loras=4, seed=22)
     pairs = o.pack_expert_pairs(P["adapters"], P["max_loras"], P["num_experts"], P["max_rank"])
@@ -590,7 +644,7 @@ def pin_f16_to_bf16(o):
 PINS = [pin_bf16_known, pin_bf16_roundtrip, pin_bf16_midpoints, pin_bf16_vs_torch,
         pin_scale_closed_forms, pin_brute_force_bgmv, pin_textbook_lora, pin_pad_invariant,
         pin_inactive_and_strides, pin_batched_equals_rows, pin_fold_order,
-        pin_routing_probe_grouped, pin_routing_probe_gather, pin_window_union, pin_cross_path,
+        pin_routing_probe_grouped, pin_grouped_invalid_values, pin_routing_probe_gather, pin_window_union, pin_cross_path,
         pin_helpers, pin_lora_delta_brute_force, pin_lora_delta_textbook,
         pin_lora_delta_matches_routed, pin_f16_to_bf16]
 

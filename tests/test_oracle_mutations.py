@@ -185,12 +185,71 @@ def _mut_lora_ignores_x_stride(m):
     _lora_variant(m, x_stride_ok=False)
 
 
+def _grouped_variant(m, *, token_rule="given", expert_rule="skip"):
+    """A re-implementation of the grouped window fold with one mistake in the
+    rules for values the host cannot check."""
+    def moe_grouped(pairs, E, k_in, n_out, R, x, xs, xg, nt, off, stid, ra, lo, hi, base, os_):
+        xa = np.zeros((max(hi - lo, 0), R), np.uint16)
+        out = np.array(base, dtype=np.uint16, copy=True)
+        if hi <= lo:
+            return xa, out
+        owner = m.expert_owner(off, lo, hi)
+        if token_rule == "given":
+            need = stid is not None
+        elif token_rule == "gather_or_adapter":  # tokens of down rows never checked
+            need = xg or ra is not None
+        else:  # "never": no range check at all
+            need = False
+        for r in range(lo, hi):
+            e = int(owner[r - lo])
+            if e < 0:
+                continue
+            if e >= E:
+                if expert_rule == "skip":
+                    continue
+                if expert_rule == "clamp":
+                    e = E - 1
+            t = int(stid[r]) if stid is not None else -1
+            if need and not (0 <= t < nt):
+                continue
+            s = int(ra[t]) if ra is not None else 0
+            if not (0 <= s < len(pairs)):
+                continue
+            w = pairs[s][e]
+            if w is None or not w.active:
+                continue
+            xr = t if xg else r
+            o0 = r * os_
+            xa[r - lo], out[o0:o0 + n_out] = m.fold_row(x[xr * xs: xr * xs + k_in], w,
+                                                        out[o0:o0 + n_out])
+        return xa, out
+    m.moe_grouped = moe_grouped
+
+
+def _mut_grouped_tokens_unchecked(m):
+    _grouped_variant(m, token_rule="never")
+
+
+def _mut_grouped_tokens_checked_only_when_used(m):
+    _grouped_variant(m, token_rule="gather_or_adapter")
+
+
+def _mut_grouped_expert_past_table_clamped(m):
+    _grouped_variant(m, expert_rule="clamp")
+
+
+def _mut_grouped_expert_past_table_unchecked(m):
+    _grouped_variant(m, expert_rule="none")
+
+
 MUTANTS = [_mut_truncating_round, _mut_fused_fold, _mut_transposed_A, _mut_dropped_term,
            _mut_scale_before_round, _mut_unrounded_xa, _mut_sign, _mut_rslora_always,
            _mut_gather_token_mod, _mut_owner_off_by_one, _mut_grouped_adapter_by_row,
            _mut_ignore_out_offset, _mut_xa_not_zeroed, _mut_wc_floor, _mut_pack_first_wins,
            _mut_lora_transposed_B, _mut_lora_fused_fold, _mut_lora_unrounded_xa,
-           _mut_lora_ignores_x_stride]
+           _mut_lora_ignores_x_stride, _mut_grouped_tokens_unchecked,
+           _mut_grouped_tokens_checked_only_when_used, _mut_grouped_expert_past_table_clamped,
+           _mut_grouped_expert_past_table_unchecked]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
