@@ -294,10 +294,12 @@ class Step:
         import torch
 
         import routed_lora_delta_amd as R
-        from routed_lora_delta_amd.pool import DenseRoute, MoeRoute, SinglePair, to_device_u16
+        from routed_lora_delta_amd.pool import (DenseRoute, MoeRoute, SinglePair, grouped_windows,
+                                                to_device_u16)
 
         self.R, self.torch = R, torch
         self.calls = []  # (label, kernel name, fn, algorithmic bytes, flops, rows)
+        self.outputs = {}  # "<workload>.<buffer or projection>" -> device output tensor
         self.sched = []  # (group, lane) of each call
         self.rows = 0
         keep = []
@@ -327,6 +329,8 @@ class Step:
                           torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev))
                          for _ in range(MAX_LANES)]
                 keep += [seq, bufs, lanes]
+                for k, b in bufs.items():
+                    self.outputs[f"{tag}.{k}"] = b
                 # the attention's q, k and v folds read the same rows: one
                 # rld_bgmv_multi call for them.  (Gate and up stay two calls on
                 # parallel branches, which overlap each other's launch gaps and
@@ -398,6 +402,7 @@ class Step:
                 rad = i32(wl.row_adapter)
                 xa = torch.zeros(wl.n_rows * wl.max_rank + 8, dtype=torch.int16, device=dev)
                 keep += [rt, x, base, idx, rad, xa]
+                self.outputs["gather.out"] = base
                 sb, eb, fl, _ = gather_bytes(wl)
 
                 # one call: shrink and fold of every flat row in one kernel
@@ -411,8 +416,7 @@ class Step:
                 off = i32(wl.expert_offsets)
                 stid = i32(wl.sorted_token_ids)
                 rad = i32(wl.row_adapter)
-                wins = [(k * wl.cap, min((k + 1) * wl.cap, wl.te))
-                        for k in range(-(-wl.te // wl.cap))]
+                wins = grouped_windows(wl.te, wl.cap)
                 # per lane (module lane x window): xa, and a workspace sized for
                 # the largest projection
                 wsb = max(R.rld_moe_grouped_workspace_bytes(wl.cap, p.k_in, wl.max_rank,
@@ -433,6 +437,7 @@ class Step:
                     base = to_device_u16(p.base.ravel(), dev)
                     keep += [rt, x, base]
                     dev_p[p.name] = (rt, x, base)
+                    self.outputs[f"grouped.{p.name}"] = base
                 byname = {p.name: p for p in projs}
                 paired = ("gate" in byname and "up" in byname
                           and grouped_pair_fused(byname["gate"], byname["up"], wl))

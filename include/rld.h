@@ -324,8 +324,14 @@ size_t rld_moe_grouped_workspace_bytes(uint32_t window_rows, uint32_t k_in, uint
  *   expert_offsets   device int32 [num_experts_off + 1], non-decreasing prefix
  *                    sum; row r belongs to the expert e with
  *                    off[e] <= r < off[e+1]
- *   sorted_token_ids device int32, sorted row -> token (< num_tokens); may be
- *                    NULL when x_gather == 0 and row_adapter == NULL
+ *   sorted_token_ids device int32, sorted row -> token; may be NULL when
+ *                    x_gather == 0 and row_adapter == NULL.  When given, every
+ *                    row's token is read and a row whose token is outside
+ *                    [0, num_tokens) is a base row (in the shrink, the expand
+ *                    and the combined calls alike, whether or not x is gathered)
+ *   num_experts_off  entries of expert_offsets minus one; may exceed the
+ *                    route's num_experts, and rows of experts past the table
+ *                    are base rows
  *   row_adapter      device int32 [num_tokens] adapter slot per token, or NULL
  *                    (every row on slot 0)
  *   x                x_gather == 0: sorted rows, row r at x + r*x_row_stride;

@@ -1173,7 +1173,10 @@ static bool small_caps(const rld_moe_route* route, uint32_t num_experts_off) {
          num_experts_off < (uint32_t)off_cap<kPairCapSmall>();
 }
 
-static GroupedRows make_rows(const rld_moe_route* route, int x_gather, uint32_t num_tokens,
+// A row's token is read, and checked against num_tokens, whenever
+// sorted_token_ids is given: the shrink (which may gather x by token), the
+// expand (which never does) and the fused kernels then skip the same rows.
+static GroupedRows make_rows(const rld_moe_route* route, uint32_t num_tokens,
                              const int32_t* expert_offsets, uint32_t num_experts_off,
                              const int32_t* sorted_token_ids, const int32_t* row_adapter) {
   GroupedRows g;
@@ -1186,7 +1189,7 @@ static GroupedRows make_rows(const rld_moe_route* route, int x_gather, uint32_t 
   g.num_tokens = num_tokens;
   g.max_loras = route->max_loras;
   g.E = route->num_experts;
-  g.need_tok = (x_gather || row_adapter) ? 1 : 0;
+  g.need_tok = sorted_token_ids ? 1 : 0;
   return g;
 }
 
@@ -1256,7 +1259,7 @@ static int grouped_shrink(const rld_moe_route* route, const void* x, uint32_t x_
   a.xa_ = reinterpret_cast<uint64_t>(xa);
   a.part_ = reinterpret_cast<uint64_t>(workspace);
   a.ctr_ = reinterpret_cast<uint64_t>(workspace) + (workspace_bytes & ~(size_t)15);
-  a.gr = make_rows(route, x_gather, num_tokens, expert_offsets, num_experts_off,
+  a.gr = make_rows(route, num_tokens, expert_offsets, num_experts_off,
                    sorted_token_ids, row_adapter);
   a.xs = x_row_stride;
   a.x_gather = x_gather ? 1u : 0u;
@@ -1335,7 +1338,7 @@ extern "C" int rld_moe_grouped_expand_fold(const rld_moe_route* route, const voi
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
   if (row_end == row_offset) return RLD_OK;
   const uint32_t nct = div_ceil(route->n_out, kPeCols);
-  GroupedRows gr = make_rows(route, 0, num_tokens, expert_offsets, num_experts_off,
+  GroupedRows gr = make_rows(route, num_tokens, expert_offsets, num_experts_off,
                              sorted_token_ids, row_adapter);
   const bool sm = small_caps(route, num_experts_off);
   auto kern = grouped_expand_kernel<1, kPairCapLarge>;
@@ -1418,7 +1421,7 @@ extern "C" int rld_moe_grouped_pair(const rld_moe_route* route_a, const rld_moe_
   GsArgs a = GsArgs{};
   a.x_ = reinterpret_cast<uint64_t>(x);
   a.xa_ = reinterpret_cast<uint64_t>(xa_a);
-  a.gr = make_rows(route_a, x_gather, num_tokens, expert_offsets, num_experts_off,
+  a.gr = make_rows(route_a, num_tokens, expert_offsets, num_experts_off,
                    sorted_token_ids, row_adapter);
   a.xs = x_row_stride;
   a.x_gather = x_gather ? 1u : 0u;

@@ -15,9 +15,9 @@ from typing import Sequence
 import numpy as np
 import torch
 
-from . import (check, rld_adapter_entry, rld_f16_to_bf16_host, rld_moe_route,
-               rld_moe_tables_pack, rld_pad_adapter_host, rld_pair, rld_route, rld_route_pack,
-               rld_scale)
+from . import (check, rld_adapter_entry, rld_f16_to_bf16_host, rld_grouped_windows,
+               rld_moe_route, rld_moe_tables_pack, rld_pad_adapter_host, rld_pair, rld_route,
+               rld_route_pack, rld_scale)
 
 _ALIGN_ELEMS = 128  # 256 bytes of BF16
 
@@ -144,3 +144,15 @@ class MoeRoute:
         self.route = rld_moe_route(self.a_table.data_ptr(), self.b_table.data_ptr(),
                                    self.scale_table.data_ptr(), max_loras, num_experts, k_in,
                                    n_out, max_rank)
+
+
+def grouped_windows(total_rows: int, cap: int):
+    """The [start, end) launch windows of at most cap rows that cover
+    0..total_rows, from the library's rld_grouped_windows."""
+    n = max(1, -(-total_rows // cap)) if cap > 0 else 1
+    starts = np.zeros(n, np.uint32)
+    ends = np.zeros(n, np.uint32)
+    cnt = ctypes.c_uint32(0)
+    check(rld_grouped_windows(total_rows, cap, starts, ends, n, ctypes.byref(cnt)),
+          "rld_grouped_windows")
+    return [(int(a), int(b)) for a, b in zip(starts[:cnt.value], ends[:cnt.value])]

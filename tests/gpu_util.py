@@ -2,6 +2,7 @@
 against the oracle at the stated tolerances."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -10,7 +11,8 @@ import torch
 
 import oracle as O
 import routed_lora_delta_amd as R
-from routed_lora_delta_amd.pool import DenseRoute, MoeRoute, from_device_u16, to_device_u16
+from routed_lora_delta_amd.pool import (DenseRoute, MoeRoute, from_device_u16, grouped_windows,
+                                        to_device_u16)
 
 CANARY = 0x7E5A  # a finite BF16 pattern the fold never writes into guard bands
 GUARD = 512      # guard elements before and after every output buffer
@@ -19,6 +21,19 @@ GUARD = 512      # guard elements before and after every output buffer
 def say(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+# Every comparison against the oracle appends one record here; tests/conftest.py
+# writes them out at the end of the session (RLD_PARITY_OUT), so the number of
+# elements that needed the widened rules below is published rather than dropped.
+PARITY_RECORDS = []
+
+
+def _record(kind, label, size, exact, within, widened):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    PARITY_RECORDS.append(dict(test=test, label=label, kind=kind, elements=int(size),
+                               bit_exact=int(exact), within_stated=int(within),
+                               widened=int(widened)))
 
 
 def require_gpu():
@@ -93,7 +108,8 @@ def assert_xa_close(gpu, ora, label="", s_abs=None, depth=None, max_frac=1e-3):
     accepted only if its error is inside the rigorous fp32 summation bound
     gamma_D * sum|terms| (gamma_D = D u / (1 - D u), u = 2^-24, D the kernel's
     summation depth) plus one ulp, and such elements stay below max_frac of
-    the total.  Returns (elements off by one ulp, elements under the bound)."""
+    the total.  s_abs may be a callable that returns the sums.  Returns
+    (elements off by one ulp, elements under the bound)."""
     gpu = np.asarray(gpu, np.uint16)
     ora = np.asarray(ora, np.uint16)
     d = ulp_diff(gpu, ora)
@@ -103,6 +119,8 @@ def assert_xa_close(gpu, ora, label="", s_abs=None, depth=None, max_frac=1e-3):
         assert s_abs is not None and depth is not None, (
             f"{label}: {nb} elements differ by more than 1 ulp, first "
             f"{np.argwhere(bad)[:5].tolist()}")
+        if callable(s_abs):  # computed only when an element needs it
+            s_abs = s_abs()
         u = 2.0 ** -24
         gamma = depth * u / (1 - depth * u)
         g64, o64 = O.bf16_to_f64(gpu), O.bf16_to_f64(ora)
@@ -112,7 +130,9 @@ def assert_xa_close(gpu, ora, label="", s_abs=None, depth=None, max_frac=1e-3):
         assert not np.any(over), (f"{label}: {int(np.count_nonzero(over))} elements outside the "
                                   f"fp32 summation bound, first {np.argwhere(over)[:5].tolist()}")
         assert nb <= max(1, max_frac * gpu.size), f"{label}: {nb} elements beyond 1 ulp"
-    return int(np.count_nonzero(d == 1)), nb
+    n1 = int(np.count_nonzero(d == 1))
+    _record("xa", label, gpu.size, np.count_nonzero(d == 0), n1, nb)
+    return n1, nb
 
 
 def _spacing(bits):
@@ -153,7 +173,9 @@ def assert_out_close(gpu, ora, label="", delta=None, scale=None, sabs_d=None, de
         assert not np.any(over), (f"{label}: {int(np.count_nonzero(over))} outputs outside the "
                                   f"derived fold bound, first {np.argwhere(over)[:5].tolist()}")
         assert nb <= max(1, max_frac * gpu.size), f"{label}: {nb} outputs beyond 2 ulp / 1e-3"
-    return int(np.count_nonzero(d)), nb
+    nd = int(np.count_nonzero(d))
+    _record("out", label, gpu.size, gpu.size - nd, nd - nb, nb)
+    return nd, nb
 
 
 # ------------------------------------------------------------------- BGMV ----
@@ -359,12 +381,15 @@ def abs_sums_gather(wl, row_adapter="wl"):
     return out
 
 
-def abs_sums_grouped(wl, p, lo, hi, row_adapter="wl"):
+def abs_sums_grouped(wl, p, lo, hi, row_adapter="wl", stid=None):
     ra = wl.row_adapter if row_adapter == "wl" else row_adapter
+    stid = wl.sorted_token_ids if stid is None else stid
     pairs = {(a.slot, a.expert): a for a in p.adapters}
     out = np.zeros((hi - lo, wl.max_rank))
     for r in range(lo, hi):
-        t = int(wl.sorted_token_ids[r])
+        t = int(stid[r])
+        if not 0 <= t < wl.num_tokens:
+            continue
         s = int(ra[t]) if ra is not None else 0
         a = pairs.get((s, int(wl.sorted_expert[r])))
         if a is not None:
@@ -381,16 +406,24 @@ def oracle_gather(wl, row_adapter="wl"):
 
 
 class GroupedRun:
-    def __init__(self, wl, proj, device, cap=None, row_adapter="wl"):
+    """Device state of one grouped projection.  stid: "wl" (the workload's
+    sorted_token_ids), an int32 array that replaces it, or None (a NULL
+    pointer).  table_experts: build the route's tables for experts
+    [0, table_experts) only, while the offsets still list wl.num_experts."""
+
+    def __init__(self, wl, proj, device, cap=None, row_adapter="wl", stid="wl",
+                 table_experts=None):
         self.wl, self.p, self.device = wl, proj, device
         self.cap = cap or wl.cap
         self.ra = wl.row_adapter if row_adapter == "wl" else row_adapter
-        self.route = MoeRoute(proj.adapters, wl.max_loras, wl.num_experts, wl.max_rank, proj.k_in,
-                              proj.n_out, device)
+        te_ = table_experts or wl.num_experts
+        ads = [a for a in proj.adapters if a.expert < te_]
+        self.route = MoeRoute(ads, wl.max_loras, te_, wl.max_rank, proj.k_in, proj.n_out, device)
         self.x = to_device_u16(proj.x.ravel(), device)
         self.base = Guarded(proj.base.ravel(), device)
         self.off = dev_i32(wl.expert_offsets, device)
-        self.stid = dev_i32(wl.sorted_token_ids, device)
+        st = wl.sorted_token_ids if isinstance(stid, str) else stid
+        self.stid = dev_i32(st, device) if st is not None else None
         self.rad = dev_i32(self.ra, device) if self.ra is not None else None
         self.xa = torch.zeros(self.cap * wl.max_rank + 8, dtype=torch.int16, device=device)
         self.ws_bytes = R.rld_moe_grouped_workspace_bytes(self.cap, proj.k_in, wl.max_rank,
@@ -402,7 +435,7 @@ class GroupedRun:
         stages), or with separate=True through rld_moe_grouped_shrink then
         rld_moe_grouped_expand_fold."""
         wl, p = self.wl, self.p
-        windows = windows if windows is not None else O.grouped_down_windows(wl.te, self.cap)
+        windows = windows if windows is not None else grouped_windows(wl.te, self.cap)
         xas = []
         for lo, hi in windows:
             if separate:
@@ -430,9 +463,12 @@ class GroupedRun:
         return xas
 
 
-def oracle_grouped_window(wl, p, lo, hi, base, row_adapter="wl"):
+def oracle_grouped_window(wl, p, lo, hi, base, row_adapter="wl", stid="wl", table_experts=None):
     ra = wl.row_adapter if row_adapter == "wl" else row_adapter
-    pairs = O.pack_expert_pairs(p.adapters, wl.max_loras, wl.num_experts, wl.max_rank)
-    return O.moe_grouped(pairs, wl.num_experts, p.k_in, p.n_out, wl.max_rank, p.x.ravel(),
-                         p.k_in, p.x_gather, wl.num_tokens, wl.expert_offsets,
-                         wl.sorted_token_ids, ra, lo, hi, base, p.n_out)
+    st = wl.sorted_token_ids if isinstance(stid, str) else stid
+    te_ = table_experts or wl.num_experts
+    ads = [a for a in p.adapters if a.expert < te_]
+    pairs = O.pack_expert_pairs(ads, wl.max_loras, te_, wl.max_rank)
+    return O.moe_grouped(pairs, te_, p.k_in, p.n_out, wl.max_rank, p.x.ravel(), p.k_in,
+                         p.x_gather, wl.num_tokens, wl.expert_offsets, st, ra, lo, hi, base,
+                         p.n_out)

@@ -20,7 +20,8 @@ from gpu_util import (BgmvRun, GroupedRun, Guarded, abs_sums_bgmv, abs_sums_gath
                       compare_bgmv, dev_i32,
                       expand_depth, oracle_gather, oracle_grouped_window, require_gpu,
                       run_gather, say, shrink_depth)
-from routed_lora_delta_amd.pool import DenseRoute, SinglePair, from_device_u16, to_device_u16
+from routed_lora_delta_amd.pool import (DenseRoute, SinglePair, from_device_u16, grouped_windows,
+                                        to_device_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -342,7 +343,7 @@ def test_moe_grouped_small(proj, adapter_mode):
     xas = run.run()
     out_g = run.base.body()
     base = p.base.ravel().copy()
-    for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
+    for (lo, hi), xa_g in zip(grouped_windows(wl.te, wl.cap), xas):
         xa_o, base = oracle_grouped_window(wl, p, lo, hi, base, ra)
         assert_xa_close(xa_g, xa_o, f"grouped xa [{lo},{hi})",
                         abs_sums_grouped(wl, p, lo, hi, ra),
@@ -368,7 +369,7 @@ def test_moe_grouped_window_union_bit_exact():
         out_full = full.base.body()
         for cap in (64, 100, 333):
             part = GroupedRun(wl, p, dev, cap=cap)
-            xas = part.run(O.grouped_down_windows(wl.te, cap))
+            xas = part.run(grouped_windows(wl.te, cap))
             assert np.array_equal(np.concatenate(xas), xa_full), cap
             assert np.array_equal(part.base.body(), out_full), cap
 
@@ -426,30 +427,85 @@ def test_moe_grouped_offsets_below_zero(proj, hidden):
     assert_out_close(run.base.body(), out_o, "offsets below zero out")
 
 
-def test_moe_grouped_full_config_sampled():
+def _grouped_step_sequence(wl, dev):
+    """The MoE grouped prefill as the step issues it, window by window: the gate
+    and up folds of a window in one rld_moe_grouped_pair call, then the down
+    window through rld_moe_grouped_shrink and rld_moe_grouped_expand_fold.  The
+    windows come from the library's own rld_grouped_windows.  Returns the
+    windows, each projection's xa per window and folded output."""
+    from routed_lora_delta_amd.pool import MoeRoute
+    P = {p.name: p for p in wl.projections}
+    g, u, d = P["gate"], P["up"], P["down"]
+    rt = {p.name: MoeRoute(p.adapters, wl.max_loras, wl.num_experts, wl.max_rank, p.k_in,
+                           p.n_out, dev) for p in wl.projections}
+    x_tok = to_device_u16(g.x.ravel(), dev)
+    x_dn = to_device_u16(d.x.ravel(), dev)
+    base = {p.name: Guarded(p.base.ravel(), dev) for p in wl.projections}
+    off, stid = dev_i32(wl.expert_offsets, dev), dev_i32(wl.sorted_token_ids, dev)
+    rad = dev_i32(wl.row_adapter, dev)
+    wins = grouped_windows(wl.te, wl.cap)
+    assert wins == O.grouped_down_windows(wl.te, wl.cap)
+    xa = {n: [torch.zeros(wl.cap * wl.max_rank + 8, dtype=torch.int16, device=dev)
+              for _ in wins] for n in P}
+    wsb = max(R.rld_moe_grouped_workspace_bytes(wl.cap, p.k_in, wl.max_rank, wl.max_loras,
+                                                wl.num_experts) for p in wl.projections)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+    for k, (lo, hi) in enumerate(wins):
+        R.check(R.rld_moe_grouped_pair(rt["gate"].route, rt["up"].route, x_tok, g.k_in, 1,
+                                       wl.num_tokens, off, wl.num_experts, stid, rad, lo, hi,
+                                       base["gate"].ptr(), g.n_out, base["up"].ptr(), u.n_out,
+                                       xa["gate"][k], xa["up"][k], wl.cap, ws, wsb),
+                "rld_moe_grouped_pair")
+        R.check(R.rld_moe_grouped_shrink(rt["down"].route, x_dn, d.k_in, 0, wl.num_tokens, off,
+                                         wl.num_experts, stid, rad, lo, hi, xa["down"][k],
+                                         wl.cap, ws, wsb), "rld_moe_grouped_shrink")
+        R.check(R.rld_moe_grouped_expand_fold(rt["down"].route, xa["down"][k], wl.num_tokens,
+                                              off, wl.num_experts, stid, rad, lo, hi,
+                                              base["down"].ptr(), d.n_out),
+                "rld_moe_grouped_expand_fold")
+    torch.cuda.synchronize()
+    xas = {n: [from_device_u16(xa[n][k])[: (hi - lo) * wl.max_rank].reshape(hi - lo, wl.max_rank)
+               for k, (lo, hi) in enumerate(wins)] for n in P}
+    outs = {n: base[n].body() for n in P}
+    return wins, xas, outs
+
+
+def test_moe_grouped_full_config():
     """The MoE grouped prefill at full size (4096 tokens, top-8 of 128 experts,
     te = 32768 sorted rows in windows of 8192, down 768 -> 2048 and gate/up
-    2048 -> 768 gathered, rank 32, 4 slots), each projection window by window
-    as the step issues it; in every window three random 64-row blocks and the
-    last one against the oracle, rows computed one by one."""
+    2048 -> 768 gathered, rank 32, 4 slots), through the step's own call
+    sequence (the pair kernel for gate and up, shrink then expand for down):
+    every xa row of every window and every output element of all three
+    projections against the oracle; rows the oracle leaves untouched (slot -1,
+    unadapted pair) bit-identical to the base.  The bench's step, issued
+    eagerly on the same inputs, gives the same bits."""
     dev = require_gpu()
     wl = W.moe_grouped()
-    rng = np.random.default_rng(11)
+    say("case: grouped full config, step call sequence, every row")
+    wins, xas, outs = _grouped_step_sequence(wl, dev)
     for p in wl.projections:
-        say(f"case: grouped full config {p.name} k_in={p.k_in} n_out={p.n_out}")
-        run = GroupedRun(wl, p, dev)
-        xas = run.run()
-        out_g = run.base.body().reshape(wl.te, p.n_out)
-        for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
-            starts = sorted(rng.choice(np.arange(lo, hi - 64, 64), 3, replace=False)) + [hi - 64]
-            for a in starts:
-                xa_o, out_o = oracle_grouped_window(wl, p, a, a + 64, p.base.ravel().copy())
-                assert_xa_close(xa_g[a - lo: a - lo + 64], xa_o, f"full {p.name} xa [{a},+64)",
-                                abs_sums_grouped(wl, p, a, a + 64),
-                                shrink_depth("grouped", p.k_in, wl.max_rank))
-                assert_out_close(out_g[a: a + 64].ravel(),
-                                 out_o.reshape(wl.te, p.n_out)[a: a + 64].ravel(),
-                                 f"full {p.name} out [{a},+64)")
+        say(f"case: grouped full config oracle {p.name} k_in={p.k_in} n_out={p.n_out}")
+        base = p.base.ravel().copy()
+        for k, (lo, hi) in enumerate(wins):
+            xa_o, base = oracle_grouped_window(wl, p, lo, hi, base)
+            assert_xa_close(xas[p.name][k], xa_o, f"full {p.name} xa [{lo},{hi})",
+                            lambda lo=lo, hi=hi, p=p: abs_sums_grouped(wl, p, lo, hi),
+                            shrink_depth("grouped", p.k_in, wl.max_rank))
+            assert np.all(xas[p.name][k][np.all(xa_o == 0, axis=1)] == 0)
+        assert_out_close(outs[p.name], base, f"full {p.name} out")
+        rows_o = (base == p.base.ravel()).reshape(wl.te, p.n_out).all(axis=1)
+        assert np.array_equal(outs[p.name].reshape(wl.te, p.n_out)[rows_o],
+                              p.base.reshape(wl.te, p.n_out)[rows_o]), p.name
+        say(f"  {p.name}: {int((~rows_o).sum())} rows folded, {int(rows_o.sum())} untouched")
+    # the bench's step on the same workload, its calls issued eagerly in order
+    import bench
+    step = bench.Step(dev, [("grouped", wl)])
+    for c in step.calls:
+        R.check(c[2](), c[0])
+    torch.cuda.synchronize()
+    for p in wl.projections:
+        got = from_device_u16(step.outputs[f"grouped.{p.name}"])[: wl.te * p.n_out]
+        assert np.array_equal(got, outs[p.name]), f"bench step differs on {p.name}"
 
 
 def _pair_run(wl, pa, pb, dev, cap, ra="wl"):
@@ -471,7 +527,7 @@ def _pair_run(wl, pa, pb, dev, cap, ra="wl"):
                                                 wl.num_experts) for p in (pa, pb))
     ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
     xas = []
-    for lo, hi in O.grouped_down_windows(wl.te, cap):
+    for lo, hi in grouped_windows(wl.te, cap):
         R.check(R.rld_moe_grouped_pair(route_a.route, route_b.route, x, pa.k_in, pa.x_gather,
                                        wl.num_tokens, off, wl.num_experts, stid, rd, lo, hi,
                                        base_a.ptr(), pa.n_out, base_b.ptr(), pb.n_out, xa_a,
@@ -504,7 +560,7 @@ def test_moe_grouped_pair_equals_two_calls(case):
     for p, out, which in ((pa, out_a, 0), (pb, out_b, 1)):
         run = GroupedRun(wl, p, dev, cap=wl.cap, row_adapter=ra)
         ref = run.run()
-        for (lo, hi), xa_ref, xa_pair in zip(O.grouped_down_windows(wl.te, wl.cap), ref, xas):
+        for (lo, hi), xa_ref, xa_pair in zip(grouped_windows(wl.te, wl.cap), ref, xas):
             assert np.array_equal(xa_pair[which].reshape(xa_ref.shape), xa_ref), (p.name, lo)
         assert np.array_equal(out, run.base.body()), p.name
 
@@ -524,7 +580,7 @@ def test_moe_grouped_large_route(max_loras, num_experts):
         run = GroupedRun(wl, p, dev, cap=wl.cap, row_adapter=ra)
         xas = run.run()
         base = p.base.ravel().copy()
-        for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
+        for (lo, hi), xa_g in zip(grouped_windows(wl.te, wl.cap), xas):
             xa_o, base = oracle_grouped_window(wl, p, lo, hi, base, ra)
             assert_xa_close(xa_g, xa_o, f"large route xa [{lo},{hi})",
                             abs_sums_grouped(wl, p, lo, hi, ra),
@@ -557,7 +613,7 @@ def test_moe_grouped_wide(k_in, max_rank, proj, n_out, separate):
     run = GroupedRun(wl, p, dev, cap=wl.cap)
     xas = run.run(separate=separate)
     base = p.base.ravel().copy()
-    for (lo, hi), xa_g in zip(O.grouped_down_windows(wl.te, wl.cap), xas):
+    for (lo, hi), xa_g in zip(grouped_windows(wl.te, wl.cap), xas):
         xa_o, base = oracle_grouped_window(wl, p, lo, hi, base)
         assert_xa_close(xa_g, xa_o, f"wide xa [{lo},{hi})", abs_sums_grouped(wl, p, lo, hi),
                         shrink_depth("grouped", p.k_in, wl.max_rank))
@@ -592,7 +648,7 @@ def test_moe_grouped_long_pairs(max_loras, hidden, num_tokens):
                         shrink_depth("grouped", p.k_in, wl.max_rank))
         assert_out_close(full.base.body(), out_o, f"long pairs out {p.name}")
         part = GroupedRun(wl, p, dev, cap=700, row_adapter=ra)
-        xas = part.run(O.grouped_down_windows(wl.te, 700))
+        xas = part.run(grouped_windows(wl.te, 700))
         assert np.array_equal(np.concatenate(xas), xa_full)
         assert np.array_equal(part.base.body(), full.base.body())
 
@@ -611,7 +667,7 @@ def test_moe_grouped_graph_replays():
     want = eager.base.body()
     run = GroupedRun(wl, p, dev)
     pristine = run.base.t.clone()
-    wins = O.grouped_down_windows(wl.te, wl.cap)
+    wins = grouped_windows(wl.te, wl.cap)
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     s.wait_stream(torch.cuda.current_stream())
@@ -861,7 +917,7 @@ def test_grouped_graph_new_routing_each_replay():
     say("case: grouped graph, new routing per replay")
     run = GroupedRun(wl, p, dev)
     pristine = run.base.t.clone()
-    wins = O.grouped_down_windows(wl.te, wl.cap)
+    wins = grouped_windows(wl.te, wl.cap)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
