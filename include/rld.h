@@ -227,6 +227,27 @@ int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_stride,
              const int32_t* seq_slot, uint32_t n, void* base_out, uint32_t out_row_stride,
              void* xa, void* workspace, size_t workspace_bytes, void* stream);
 
+/* rld_bgmv for callers that cannot allocate: code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc.  The same fold, bit for
+ * bit, with the xa arena and the k-split partials in a fixed device array of
+ * RLD_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * (until the process ends) instead of caller buffers.  The call allocates
+ * nothing; its first call with a device current looks up that device's copy.
+ *   route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, stream:
+ *                   as rld_bgmv
+ * RLD_ENOSPACE (before anything runs) when the call needs more scratch than
+ * RLD_NOALLOC_SCRATCH_BYTES: the xa arena, n * max_rank * 2 bytes rounded up to
+ * a multiple of 256, plus rld_bgmv_workspace_bytes(n, k_in, max_rank, 1) (at
+ * k_in 12288 and max_rank 64, up to 1337 rows).  Nothing in the scratch must
+ * start at zero: every call
+ * writes all it reads.  All calls on one GPU share its scratch, which keeps the
+ * last call's contents: calls that may overlap on one GPU (different streams
+ * without ordering) race, so issue them on one stream or order them. */
+#define RLD_NOALLOC_SCRATCH_BYTES (8u << 20)
+int rld_bgmv_noalloc(const rld_route* route, const void* x, uint32_t x_row_stride,
+                     const int32_t* seq_slot, uint32_t n, void* base_out,
+                     uint32_t out_row_stride, void* stream);
+
 /* Several routed BGMV folds over the same rows (apply_lora_bgmv once per
  * route, as a layer's q, k and v, or gate and up, read one input): one shrink,
  * one chunk reduce (k_in split only) and one expand launch serve every route,

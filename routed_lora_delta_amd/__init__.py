@@ -23,6 +23,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rld.h")
 
 RLD_OK, RLD_EINVAL, RLD_EALIGN, RLD_EUNSUPPORTED, RLD_ELAUNCH, RLD_ENOSPACE = 0, -1, -2, -3, -4, -5
 RLD_MAX_RANK = 128
+RLD_NOALLOC_SCRATCH_BYTES = 8 << 20
 RLD_M_TILE = 64
 
 if not os.path.exists(LIB_PATH):
@@ -93,6 +94,7 @@ _SIGS = {
     "rld_bgmv_shrink": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
     "rld_bgmv_expand_fold": (c_int, [_R, _P, _P, c_uint32, _P, c_uint32, _P]),
     "rld_bgmv": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
+    "rld_bgmv_noalloc": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, c_uint32, _P]),
     "rld_bgmv_multi_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32, c_uint32]),
     "rld_bgmv_multi": (c_int, [_P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, _P, _P,
                                c_size_t, _P]),
@@ -242,6 +244,11 @@ def rld_bgmv(route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, xa, 
     return _lib.rld_bgmv(ctypes.byref(route), ptr(x), x_row_stride, ptr(seq_slot), n,
                          ptr(base_out), out_row_stride, ptr(xa), ptr(workspace), workspace_bytes,
                          stream_handle(stream))
+
+
+def rld_bgmv_noalloc(route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, stream=None):
+    return _lib.rld_bgmv_noalloc(ctypes.byref(route), ptr(x), x_row_stride, ptr(seq_slot), n,
+                                 ptr(base_out), out_row_stride, stream_handle(stream))
 
 
 def rld_bgmv_multi_workspace_bytes(n, k_in, max_rank, nroutes):

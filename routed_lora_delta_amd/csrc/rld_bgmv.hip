@@ -28,6 +28,7 @@
 //
 // rld_bgmv launches the shrink (and its reduce), then the expand, on the
 // caller's stream.
+#include <mutex>
 #include <type_traits>
 
 #include "rld_device.hpp"
@@ -883,4 +884,71 @@ extern "C" int rld_lora_delta(const rld_pair* pair, const void* x, uint32_t x_ro
   st = rld_lora_shrink(pair, x, x_row_stride, m, xa, workspace, workspace_bytes, stream);
   if (st) return st;
   return rld_lora_expand_fold(pair, xa, m, base_out, out_row_stride, stream);
+}
+
+// ------------------------------------------------------- no allocation ----
+//
+// rld_bgmv for callers that cannot allocate (code under HIP graph capture,
+// serving loops that forbid hipMalloc): the xa arena and the k-split partials
+// live in this file-scope device array instead of caller buffers.  Each GPU the
+// library runs on holds its own copy until the process ends.  Its device
+// address is taken once per device (hipGetSymbolAddress, with that device
+// current) and kept; kernels get that address as an argument, never the
+// array's name, which in host code is only a stand-in for the symbol.
+
+static __device__ __align__(256) unsigned char scratch[RLD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of `scratch` on the current device (looked up on the first
+// call made with that device current), or an error status.
+static int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    record_hip_error(e);
+    return RLD_ELAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return RLD_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      record_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return RLD_ELAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RLD_OK;
+}
+
+static size_t noalloc_xa_bytes(uint32_t n, uint32_t R) {
+  return ((size_t)n * R * 2 + 255) & ~(size_t)255;
+}
+
+extern "C" int rld_bgmv_noalloc(const rld_route* route, const void* x, uint32_t x_row_stride,
+                                const int32_t* seq_slot, uint32_t n, void* base_out,
+                                uint32_t out_row_stride, void* stream) {
+  int st = check_route(route);
+  if (st) return st;
+  if (n == 0) return RLD_OK;
+  if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
+  if ((st = check_rows(x, x_row_stride, route->k_in))) return st;
+  if (!seq_slot) return RLD_EINVAL;
+  // every size check before the device is touched
+  const size_t xab = noalloc_xa_bytes(n, route->max_rank);
+  const size_t pb = partial_bytes(n, route->k_in, route->max_rank);
+  if (xab + pb > (size_t)RLD_NOALLOC_SCRATCH_BYTES) return RLD_ENOSPACE;
+  void* sp = nullptr;
+  if ((st = scratch_on_current_device(&sp))) return st;
+  char* xa = static_cast<char*>(sp);
+  char* ws = pb ? xa + xab : nullptr;
+  return rld_bgmv(route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, xa, ws, pb,
+                  stream);
 }

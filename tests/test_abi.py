@@ -223,6 +223,30 @@ def test_bgmv_rejects_bad_buffers():
     assert ex(xa=0) == R.RLD_EINVAL
 
 
+def test_bgmv_noalloc_rejects_before_touching_the_device():
+    """rld_bgmv_noalloc checks its arguments and its scratch limit before any
+    HIP call: a call that needs more than RLD_NOALLOC_SCRATCH_BYTES returns
+    RLD_ENOSPACE (here, without a GPU, nothing else could run)."""
+    assert R.RLD_NOALLOC_SCRATCH_BYTES == 8 << 20
+    rt = _route(k_in=12288, n_out=4096, max_rank=64, max_loras=32)
+
+    def call(n, x=FAKE, seq=FAKE, out=FAKE, os_=4096, route=rt):
+        return R.rld_bgmv_noalloc(route, x, 12288, seq, n, out, os_, 0)
+
+    def need(n):  # xa arena (256-byte rounded) + the k-split partials
+        return -(-n * 64 * 2 // 256) * 256 + R.rld_bgmv_workspace_bytes(n, 12288, 64, 1)
+
+    assert need(1337) <= R.RLD_NOALLOC_SCRATCH_BYTES < need(1338)
+    assert call(1338) == R.RLD_ENOSPACE
+    assert call(1 << 20) == R.RLD_ENOSPACE
+    assert call(0) == R.RLD_OK                      # no-op
+    assert call(4, x=0) == R.RLD_EINVAL
+    assert call(4, seq=0) == R.RLD_EINVAL
+    assert call(4, out=FAKE + 2) == R.RLD_EALIGN
+    assert call(4, os_=1000) == R.RLD_EINVAL
+    assert call(4, route=_route(tables=False)) == R.RLD_EINVAL
+
+
 def test_bgmv_multi_rejects_bad_arguments():
     """rld_bgmv_multi checks every route and buffer before any launch."""
     q, k, v = _route(k_in=4096, n_out=4096), _route(k_in=4096, n_out=1024), \
