@@ -260,6 +260,11 @@ LANES = {"q": (0, 0), "k": (0, 1), "v": (0, 2), "o": (1, 0),
 MAX_LANES = 3
 # workloads whose first group of folds is one rld_bgmv_multi call
 MULTI_TAGS = {"attn"}
+# A whole decoder layer ("layer<i>" workloads of the multi-layer decode step):
+# q/k/v (one rld_bgmv_multi call), then o, then gate and up on two branches,
+# then down.  Layers follow each other.
+LAYER_LANES = {"q": (0, 0), "k": (0, 1), "v": (0, 2), "o": (1, 0),
+               "gate": (2, 0), "up": (2, 1), "down": (3, 0)}
 
 
 def grouped_shrink_kernel(k_in, max_rank):
@@ -308,15 +313,22 @@ class Step:
         def i32(a):
             return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
 
-        def add(call, module, lane=None, group=None):
-            g, ln = LANES.get(module, (0, 0))
+        def add(call, module, lane=None, group=None, lanes_map=LANES):
+            g, ln = lanes_map.get(module, (0, 0))
             self.calls.append(call)
             self.sched.append((group0 + (g if group is None else group),
                                ln if lane is None else lane))
 
+        seqs = {}     # one device seq_slot per host routing array (layers share theirs)
+        shared = {}   # the layers' xa arena and workspaces, allocated once
+        self.seqs = seqs
         for tag, wl in workloads:
-            if tag in ("attn", "ffn", "lora"):
-                seq = i32(wl.seq_slot)
+            layer = tag.startswith("layer")
+            lmap = LAYER_LANES if layer else LANES
+            if tag in ("attn", "ffn", "lora") or layer:
+                if id(wl.seq_slot) not in seqs:
+                    seqs[id(wl.seq_slot)] = i32(wl.seq_slot)
+                seq = seqs[id(wl.seq_slot)]
                 bufs = {k: to_device_u16(v, dev) for k, v in wl.buffers.items()}
                 rmax = max(c.max_rank for c in wl.calls)
                 if tag == "lora":
@@ -325,9 +337,15 @@ class Step:
                 else:
                     wsb = max(R.rld_bgmv_workspace_bytes(wl.n, c.k_in, c.max_rank, c.max_loras)
                               for c in wl.calls)
-                lanes = [(torch.zeros(wl.n * rmax + 8, dtype=torch.int16, device=dev),
-                          torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev))
-                         for _ in range(MAX_LANES)]
+                key = (wl.n, rmax, wsb)
+                if layer and key in shared:
+                    lanes = shared[key]
+                else:
+                    lanes = [(torch.zeros(wl.n * rmax + 8, dtype=torch.int16, device=dev),
+                              torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev))
+                             for _ in range(MAX_LANES)]
+                    if layer:
+                        shared[key] = lanes
                 keep += [seq, bufs, lanes]
                 for k, b in bufs.items():
                     self.outputs[f"{tag}.{k}"] = b
@@ -337,7 +355,7 @@ class Step:
                 # tails: as one call the FFN's cost in the step was 106 us
                 # against 94.)
                 first = [c for c in wl.calls
-                         if tag in MULTI_TAGS and LANES.get(c.module, (0, 0))[0] == 0]
+                         if (tag in MULTI_TAGS or layer) and lmap.get(c.module, (0, 0))[0] == 0]
                 if len({(c.x_buf, c.x_row_stride, c.k_in, c.max_rank) for c in first}) != 1 \
                         or len(first) < 2:
                     first = []
@@ -346,7 +364,13 @@ class Step:
                     rts = [DenseRoute(c.adapters, c.max_loras, c.max_rank, c.k_in, c.n_out, dev)
                            for c in first]
                     mwsb = R.rld_bgmv_multi_workspace_bytes(wl.n, c0.k_in, c0.max_rank, len(first))
-                    mws = torch.zeros(max(mwsb, 16), dtype=torch.uint8, device=dev)
+                    mkey = ("multi", wl.n, c0.k_in, c0.max_rank, len(first))
+                    if layer and mkey in shared:
+                        mws = shared[mkey]
+                    else:
+                        mws = torch.zeros(max(mwsb, 16), dtype=torch.uint8, device=dev)
+                        if layer:
+                            shared[mkey] = mws
                     xas = [lanes[i][0] for i in range(len(first))]
                     outs = [bufs[c.out_buf].data_ptr() + 2 * c.out_offset for c in first]
                     keep += [rts, mws]
@@ -359,12 +383,12 @@ class Step:
                         return R.rld_bgmv_multi([r.route for r in rts], x, c0.x_row_stride, seq,
                                                 n, outs, oss, xas, mws, mwsb)
                     add((f"{tag}.{'+'.join(c.module for c in first)}.multi", "bgmv_multi", multi,
-                         sb, fl, wl.n * len(first)), c0.module, 0)
+                         sb, fl, wl.n * len(first)), c0.module, 0, lanes_map=lmap)
                     self.rows += wl.n * len(first)
                 for c in wl.calls:
                     if any(c is f for f in first):
                         continue
-                    xa, ws = lanes[LANES.get(c.module, (0, 0))[1]]
+                    xa, ws = lanes[lmap.get(c.module, (0, 0))[1]]
                     sb, eb, fl, _ = bgmv_bytes(wl, c)
                     x = bufs[c.x_buf].data_ptr()
                     out = bufs[c.out_buf].data_ptr() + 2 * c.out_offset
@@ -389,9 +413,9 @@ class Step:
                             return R.rld_bgmv_expand_fold(rt.route, xa, seq, n, out,
                                                           c.out_row_stride)
                     add((f"{tag}.{c.module}.shrink", BGMV_SHRINK, shrink, sb, fl / 2, wl.n),
-                        c.module)
+                        c.module, lanes_map=lmap)
                     add((f"{tag}.{c.module}.expand", "bgmv_expand_kernel", expand, eb, fl / 2, 0),
-                        c.module)
+                        c.module, lanes_map=lmap)
                     self.rows += wl.n
             elif tag == "gather":
                 rt = MoeRoute(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank, wl.k_in,
@@ -557,6 +581,17 @@ class Step:
             events[-1].record()
 
 
+MODEL_LAYERS = 36
+
+
+def model_workloads(layers=MODEL_LAYERS):
+    """The multi-layer decode step: `layers` decoder layers of Qwen3-8B shapes,
+    each with its own pools for all seven projections, one batch routing."""
+    import workloads as W
+    seq = W.decode_routing()
+    return [(f"layer{i}", W.decode_layer(i, seq)) for i in range(layers)]
+
+
 def select_workloads(name):
     import workloads as W
     out = []
@@ -570,6 +605,8 @@ def select_workloads(name):
         out.append(("grouped", W.moe_grouped()))
     if name == "lora":
         out.append(("lora", W.lora_prefill()))
+    if name == "model":
+        out += model_workloads()
     return out
 
 
@@ -583,6 +620,8 @@ WORKLOAD_NAMES = {
     "grouped": "MoE grouped down/gate/up 4096 tokens top8 E128 te=32768 cap=8192 r32 L4",
     "lora": "unrouted single adapter, prefill m=4096, FFN gate/up 4096->12288, down "
             "12288->4096, r64",
+    "model": f"decode step of {MODEL_LAYERS} Qwen3-8B layers: q/k/v/o and gate/up/down folds "
+             "per layer (own pools), n=64, 16 slots r16, one batch routing",
 }
 
 # The BGMV shrink entry point is two launches when k_in is split (the shrink,
@@ -686,12 +725,18 @@ def run_gpu(args, traffic=True):
         full_seq.replay()
     torch.cuda.synchronize()
 
-    # timed region A: K replays of the whole step, back to back
+    # timed region A: K replays of the whole step, back to back (an event after
+    # each replay gives the per-replay spread; the wall clock gives the value)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         full.replay()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    rep_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
 
     # timed regions B and C: every call timed by HIP events on the launch stream
     per_call_ms = np.zeros(ncalls)
@@ -745,6 +790,9 @@ def run_gpu(args, traffic=True):
                 for k, v in kernels.items()}
     return {
         "ms_per_step": ms_per_step,
+        "replay_ms": {"median": round(float(np.median(rep_ms)), 5),
+                      "p10": round(float(np.percentile(rep_ms, 10)), 5),
+                      "p90": round(float(np.percentile(rep_ms, 90)), 5)},
         "ms_per_step_calls": float(seg_ms.sum()),
         "rows": step.rows,
         "bytes": step.bytes,
@@ -758,6 +806,48 @@ def run_gpu(args, traffic=True):
         "kernels": kern_out,
         "per_workload": per_workload,
     }
+
+
+def run_model(args):
+    """The multi-layer decode step: every layer's folds captured in one graph
+    (q/k/v, o, gate and up on two branches, down; layers in order), the xa
+    arena and workspaces shared by all layers, replayed K times.  Its adapter
+    pools (about 1.3 GB) are five times the 256 MB MALL, so replays stream
+    from HBM."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wls = model_workloads()
+    step = Step(dev, wls)
+    for _ in range(args.warmup):
+        step.enqueue()
+    torch.cuda.synchronize()
+    g = step.capture(range(len(step.calls)), torch.cuda.Stream(), parallel=True)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(args.steps):
+        g.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rep_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    ms = wall * 1e3 / args.steps
+    gbs = step.bytes / (ms * 1e-3) / 1e9
+    pool_bytes = sum(a.A.nbytes + a.B.nbytes for _, wl in wls for c in wl.calls
+                     for a in c.adapters)
+    return {"workload": WORKLOAD_NAMES["model"], "layers": len(wls),
+            "ms_per_step": round(ms, 5), "us_per_layer": round(ms * 1e3 / len(wls), 3),
+            "replay_ms": {"median": round(float(np.median(rep_ms)), 5),
+                          "p10": round(float(np.percentile(rep_ms, 10)), 5),
+                          "p90": round(float(np.percentile(rep_ms, 90)), 5)},
+            "rows_per_step": step.rows, "rows_per_s": round(step.rows / (ms * 1e-3), 1),
+            "algo_bytes_per_step": int(step.bytes), "hbm_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "adapter_bytes": int(pool_bytes)}
 
 
 # ------------------------------------------------------------- CPU oracle ---
@@ -822,6 +912,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-unrouted", action="store_true",
                     help="with the default step: skip the separate unrouted-path measurement")
+    ap.add_argument("--no-model", action="store_true",
+                    help="with the default step: skip the multi-layer decode step")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="print a markdown summary of rocprofv3 output directories and exit")
     ap.add_argument("--bench-json", help="with --summarize: a bench.py output line to include")
@@ -857,12 +949,16 @@ def main():
                    "algo_bytes_per_step": int(g["bytes"]), "flops_per_step": int(g["flops"])},
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "replay_ms": g["replay_ms"],
         "ms_per_step_calls": round(g["ms_per_step_calls"], 5),
         "roofline": g["roofline"],
         "cpu_baseline": None if args.no_cpu else cpu_baseline(args),
         "kernels": g["kernels"],
         "per_workload": g["per_workload"],
     }
+    if args.workload == "step" and not args.no_model:
+        # The multi-layer decode step, measured on its own; not part of `value`.
+        line["decode_model"] = run_model(args)
     if args.workload == "step" and not args.no_unrouted:
         # The unrouted single-adapter path (apply_lora_delta), measured the same
         # way on its own prefill workload; not part of the step or of `value`.

@@ -313,32 +313,42 @@ def compare_bgmv(run: BgmvRun, label: str):
         stats[c.module + ".xa"] = assert_xa_close(
             run.xa_by_call[i], xas[i], f"{label}/{c.module} xa",
             s_abs=abs_sums_bgmv(run.wl, c), depth=shrink_depth("bgmv", c.k_in, c.max_rank))
-    out_bufs = {c.out_buf for c in run.wl.calls}
+    stats.update(compare_bgmv_outputs(run.wl, outs, label, (xas, bufs)))
+    return stats
+
+
+def compare_bgmv_outputs(wl, outs, label, oracle=None):
+    """Every buffer of a BgmvWorkload after all its calls (outs: name -> BF16
+    bits) against the oracle: folded regions within the output tolerance,
+    everything else (base rows, strided gaps, inputs) bit-exact."""
+    xas, bufs = oracle if oracle is not None else oracle_bgmv(wl)
+    stats = {}
+    out_bufs = {c.out_buf for c in wl.calls}
     for k in bufs:
         if k in out_bufs:
             size = bufs[k].size
             dl, sc, sab = np.zeros(size, np.uint16), np.zeros(size), np.zeros(size)
-            for i, c in enumerate(run.wl.calls):
+            for i, c in enumerate(wl.calls):
                 if c.out_buf == k:
-                    d1, s1, a1 = oracle_delta_bgmv(run.wl, c, xas[i])
+                    d1, s1, a1 = oracle_delta_bgmv(wl, c, xas[i])
                     m = s1 != 0
                     dl[m], sc[m], sab[m] = d1[m], s1[m], a1[m]
-            depth = max(expand_depth("bgmv", c.max_rank) for c in run.wl.calls)
+            depth = max(expand_depth("bgmv", c.max_rank) for c in wl.calls)
             stats[k + ".out"] = assert_out_close(outs[k], bufs[k], f"{label}/{k}", dl, sc, sab,
                                                  depth)
         else:
             assert np.array_equal(outs[k], bufs[k]), f"{label}: input buffer {k} changed"
         # base rows and everything outside the folded regions: bit-exact
         touched = np.zeros(bufs[k].size, bool)
-        for c in run.wl.calls:
+        for c in wl.calls:
             if c.out_buf != k:
                 continue
-            for r in range(run.wl.n):
-                s = int(run.wl.seq_slot[r])
+            for r in range(wl.n):
+                s = int(wl.seq_slot[r])
                 if 0 <= s < c.max_loras and any(a.slot == s for a in c.adapters):
                     o0 = c.out_offset + r * c.out_row_stride
                     touched[o0:o0 + c.n_out] = True
-        assert np.array_equal(outs[k][~touched], run.wl.buffers[k][~touched]), (
+        assert np.array_equal(outs[k][~touched], wl.buffers[k][~touched]), (
             f"{label}: {k} changed outside the folded rows/regions")
     return stats
 

@@ -276,6 +276,58 @@ def bgmv_ffn_decode(seed_index: int = 2, n: int = 256, hidden: int = 4096,
                         buffers, calls)
 
 
+def decode_routing(seed_index: int = 6, n: int = 64, max_loras: int = 16,
+                   base_frac: float = 0.1) -> np.ndarray:
+    """seq_slot of one decode batch shared by every layer of a step: slots
+    uniform over 0..max_loras-1, base_frac of the rows on the base model."""
+    rng = rng_for(seed_index)
+    seq_slot = rng.integers(0, max_loras, size=n).astype(np.int32)
+    return _set_base_rows(rng, seq_slot, int(round(base_frac * n)))
+
+
+def decode_layer(layer: int, seq_slot: np.ndarray, seed_index: int = 6, hidden: int = 4096,
+                 kv_out: int = 1024, inter: int = 12288, max_loras: int = 16,
+                 ranks=(8, 16), alpha: float = 16.0) -> BgmvWorkload:
+    """One decoder layer of Qwen3-8B shapes with every projection adapted: q
+    hidden->hidden, k and v hidden->kv_out folded into [Q|K|V] rows (stride
+    hidden+2*kv_out, K at hidden, V at hidden+kv_out), o hidden->hidden, gate and
+    up hidden->inter, down inter->hidden.  The layer's own pools (max_loras
+    slots, true ranks from `ranks`, padded to the largest) and activations are
+    drawn from a generator seeded by the layer index; the batch's routing
+    seq_slot is shared by every layer."""
+    rng = rng_for(seed_index, salt=layer + 1)
+    n = len(seq_slot)
+    max_rank = max(ranks)
+    qkv_stride = hidden + 2 * kv_out
+    calls = []
+    for module, k_in, n_out, xbuf, obuf, off, ostride in (
+        ("q", hidden, hidden, "h", "q_out", 0, hidden),
+        ("k", hidden, kv_out, "h", "qkv", hidden, qkv_stride),
+        ("v", hidden, kv_out, "h", "qkv", hidden + kv_out, qkv_stride),
+        ("o", hidden, hidden, "attn", "o_out", 0, hidden),
+        ("gate", hidden, inter, "h2", "gate_out", 0, inter),
+        ("up", hidden, inter, "h2", "up_out", 0, inter),
+        ("down", inter, hidden, "act", "down_out", 0, hidden),
+    ):
+        ad = _dense_adapters(rng, max_loras, ranks, k_in, n_out, alpha)
+        calls.append(BgmvCall(module, k_in, n_out, max_rank, max_loras, ad, xbuf, k_in, obuf,
+                              off, ostride))
+    buffers = {
+        "h": _normal(rng, (n, hidden)).ravel(),
+        "attn": _normal(rng, (n, hidden)).ravel(),
+        "h2": _normal(rng, (n, hidden)).ravel(),
+        "act": _normal(rng, (n, inter)).ravel(),
+        "q_out": _normal(rng, (n, hidden)).ravel(),
+        "qkv": _normal(rng, (n, qkv_stride)).ravel(),
+        "o_out": _normal(rng, (n, hidden)).ravel(),
+        "gate_out": _normal(rng, (n, inter)).ravel(),
+        "up_out": _normal(rng, (n, inter)).ravel(),
+        "down_out": _normal(rng, (n, hidden)).ravel(),
+    }
+    return BgmvWorkload(f"decode layer {layer} n={n} q/k/v/o/gate/up/down", n, seq_slot,
+                        buffers, calls)
+
+
 def lora_prefill(seed_index: int = 5, m: int = 4096, hidden: int = 4096, inter: int = 12288,
                  rank: int = 64, alpha: float = 32.0) -> BgmvWorkload:
     """Unrouted single adapter over a prefill batch (the apply_lora_delta path):
