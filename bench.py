@@ -1040,7 +1040,7 @@ def main():
         # The unrouted single-adapter path (apply_lora_delta), measured the same
         # way on its own prefill workload; not part of the step or of `value`.
         ua = argparse.Namespace(**{**vars(args), "workload": "lora", "copy_calibration": False})
-        u = run_gpu(ua, traffic=False)
+        u = run_gpu(ua)
         ugbs = u["bytes"] / (u["ms_per_step"] * 1e-3) / 1e9
         line["unrouted"] = {
             "workload": WORKLOAD_NAMES["lora"], "ms_per_pass": round(u["ms_per_step"], 5),

@@ -8,11 +8,11 @@
 // per row.  The row list of a slot is rebuilt by every item from seq_slot (no
 // host read), in ascending row order.
 //
-//   shrink item  (slot, k_in chunk, up to 64 columns of xa).  Each of the four
-//                waves owns every fourth 32-wide K step of the chunk and issues
-//                all of its A fragments at once, then the x fragments of up to
-//                64 rows at once.  The waves' partial sums are added in wave
-//                order.  With one chunk the sum is rounded to xa right away;
+//   shrink item  (slot, k_in chunk, up to 64 columns of xa).  Each of the NW
+//                waves (4 or 8, by (k_in, max_rank)) owns every NW-th 32-wide K
+//                step of the chunk and issues all of its A fragments at once,
+//                then the x fragments of up to 64 (8 waves: 128) rows at once.
+//                The waves' partial sums are added in wave order.  With one chunk the sum is rounded to xa right away;
 //                otherwise it is stored as an fp32 partial [chunk][row][col]
 //                in the workspace (zeros for base rows), and a second, small
 //                kernel adds each row's chunks in chunk order and writes xa.
@@ -24,7 +24,9 @@
 //                operand (16 rows per MFMA).  The B tile, the base values and
 //                the xa rows of a 64-row pass go out in one round of loads,
 //                deltas are rounded to BF16 into LDS, and the fold writes
-//                16-byte coalesced vectors.
+//                16-byte coalesced vectors.  Grids too large for one round of the
+//                classic item's registers take a lean item that holds the B
+//                tile and moves rows in passes of 16 (same bits).
 //
 // rld_bgmv launches the shrink (and its reduce), then the expand, on the
 // caller's stream.
@@ -36,13 +38,23 @@
 
 namespace rld {
 
-constexpr int kShrinkMT = 4;     // 16-row M-subtiles per shrink pass
 constexpr int kReduceThreads = 256;
-constexpr int kShrinkSteps = 4;  // K steps per wave per chunk (chunk <= 512 = 4 waves x 4 x 32)
+constexpr int kChunkSteps = 16;  // 32-wide K steps of the longest chunk (512)
 constexpr int kListCap = 512;    // rows collected per pass over seq_slot
 constexpr int kExpRows = 64;     // rows per fold pass of the expand
 
-static_assert(kShrinkSteps * 4 * 32 >= 512, "a chunk is at most 512 elements");
+// Shape of a shrink block of NW waves: KS K steps per wave, batches of QT
+// 16-row subtiles (the x fragments of a batch are QT * KS = 16 per lane either
+// way), and MR subtiles per round of the wave reduce in LDS.
+template <int NT, int NW>
+struct ShrinkShape {
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static constexpr int kThreads = NW * kWave;
+  static constexpr int KS = kChunkSteps / NW;
+  static constexpr int QT = 16 / KS;
+  static constexpr int MR = NW * NT * 4 <= 64 ? 4 : 2;
+  static_assert(KS * NW * 32 >= 512, "a chunk is at most 512 elements");
+};
 
 // Kernel arguments; device addresses are kept as integers and read through
 // the global-pointer accessors.
@@ -68,11 +80,11 @@ struct BgmvArgs {
   __device__ RLD_GLOBAL uint16_t* out() const { return gp<uint16_t>(out_); }
 };
 
-template <int NT>
+template <int NT, int NW>
 struct ShrinkSmem {
   int rows[kListCap];
-  int wcount[4];
-  floatx4 red[4][kShrinkMT * NT][kWave];
+  int wcount[NW];
+  floatx4 red[NW][ShrinkShape<NT, NW>::MR * NT][kWave];
 };
 
 // Expand item of 64*MT output columns (16*MT per wave).
@@ -85,6 +97,19 @@ struct ExpandSmem {
   __attribute__((aligned(16))) uint16_t dl[kExpRows * kStride];
 };
 
+// Lean expand item (256 output columns, rows in passes of 16): a fraction of
+// the registers and LDS of ExpandSmem<4>'s item, so that six blocks share a CU
+// and a decode call's (column tile, slot) grid goes out in one round.
+constexpr int kLeanRows = 16;   // rows per pass of the lean expand item (16 or 32)
+struct ExpandLeanSmem {
+  static constexpr int kCols = 256;
+  static constexpr int kStride = kCols + 8;
+  static constexpr int kRows = kLeanRows;
+  int rows[kListCap];
+  int wcount[4];
+  __attribute__((aligned(16))) uint16_t dl[kRows * kStride];
+};
+
 __device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
   if (s < 0 || (uint32_t)s >= a.max_loras) return false;
   const uint64_t ta = a.a_table()[s], tb = a.b_table()[s];  // both in flight together
@@ -92,24 +117,26 @@ __device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
 }
 
 // Appends to `rows` (LDS) the rows of slot s from seq_slot[*pos ...], until
-// n is reached or the list cannot take another 256; advances *pos.  Returns
+// n is reached or the list cannot take another NW*64; advances *pos.  Returns
 // the count (the same in every thread).  key0 is this thread's seq_slot entry
-// of the first 256 rows (row threadIdx.x), loaded by the caller ahead of its
+// of the first NW*64 rows (row threadIdx.x), loaded by the caller ahead of its
 // tile loads so the first scan does not wait behind them.
+template <int NW = 4>
 __device__ __forceinline__ int collect_slot_rows(const RLD_GLOBAL int32_t* seq_slot, uint32_t n,
                                                  uint32_t* pos, int s, int* rows, int* wcount,
                                                  int key0) {
+  constexpr int NTH = NW * kWave;
   int cnt = 0;
-  while (*pos < n && cnt <= kListCap - 256) {
+  while (*pos < n && cnt <= kListCap - NTH) {
     const uint32_t row = *pos + threadIdx.x;
     const int key = *pos == 0 ? key0 : (row < n ? seq_slot[row] : -1);
-    cnt += append_hits(row < n && key == s, row, rows, cnt, wcount);
-    *pos += 256;
+    cnt += append_hits<NW>(row < n && key == s, row, rows, cnt, wcount);
+    *pos += NTH;
   }
   return cnt;
 }
 
-// This thread's seq_slot entry among the first 256 rows (-1 past n).  The
+// This thread's seq_slot entry among the first blockDim rows (-1 past n).  The
 // load is unconditional (a row < n is always readable) so that it stays in the
 // prologue, ahead of the tile loads.
 __device__ __forceinline__ int first_key(const RLD_GLOBAL int32_t* seq_slot, uint32_t n) {
@@ -133,22 +160,25 @@ __device__ __forceinline__ SlotEntry slot_entry(const BgmvArgs& a, int s) {
   return e;
 }
 
-// Rows of the shrink / expand tiles of the unrouted mode.
-constexpr int kDenseShrinkRows = 64;
+// Rows of the shrink / expand tiles of the unrouted mode: a shrink tile is
+// one batch of its block (64 rows with four waves, 128 with eight).
+__host__ __device__ constexpr int dense_shrink_rows(int nw) { return nw == 8 ? 128 : 64; }
 constexpr int kDenseExpandRows = 128;
 
 // Unrouted mode: rows [r0, r0 + cnt) of a tile into the LDS row list.
 __device__ __forceinline__ int dense_tile_rows(uint32_t r0, uint32_t n, int tile, int* rows) {
   const int cnt = (int)min((uint32_t)tile, n - r0);
-  for (int i = threadIdx.x; i < cnt; i += 256) rows[i] = (int)(r0 + i);
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) rows[i] = (int)(r0 + i);
   __syncthreads();
   return cnt;
 }
 
 // Shrink item w (slot-major over (slot, chunk, column group)); the group
 // covers xa columns [16*NT*cg, 16*NT*(cg+1)).
-template <int NT>
-__device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
+template <int NT, int NW>
+__device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT, NW>& sm) {
+  using SS = ShrinkShape<NT, NW>;
+  constexpr int NTH = SS::kThreads, KS = SS::KS, QT = SS::QT, MR = SS::MR;
   const uint32_t n = a.n, R = a.R, nchunks = a.nch, ncg = a.ncg;
   const uint32_t cg = w % ncg;
   const uint32_t c = (w / ncg) % nchunks;
@@ -173,10 +203,10 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
   // blocks have nothing else to do): the item of chunk c and column group cg
   // writes the base rows' xa columns of the group (no k split) or their
   // partials of chunk c (so the chunk reduce needs no routing).  One row per
-  // thread; the first 256 rows' slots are key0.
+  // thread; the first NTH rows' slots are key0.
   if (!a.dense && (uint32_t)s == a.max_loras - 1) {
     const uint32_t c1 = min(col0 + 16u * NT, R);
-    for (uint32_t r0 = 0; r0 < n; r0 += 256) {
+    for (uint32_t r0 = 0; r0 < n; r0 += NTH) {
       const uint32_t row = r0 + threadIdx.x;
       const int key = r0 == 0 ? key0 : (row < n ? a.seq_slot()[row] : 0);
       if (row >= n || slot_active(a, key)) continue;
@@ -198,12 +228,12 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
   const uint32_t ke = min(kb + a.kc, a.k_in);
   const uint32_t nsteps = (ke - kb + 31) / 32;
 
-  // K steps of this wave: wave, wave + 4, ... of the chunk
-  uint32_t kof[kShrinkSteps];
-  bool kok[kShrinkSteps];
+  // K steps of this wave: wave, wave + NW, ... of the chunk
+  uint32_t kof[KS];
+  bool kok[KS];
 #pragma unroll
-  for (int i = 0; i < kShrinkSteps; ++i) {
-    const uint32_t st = wave + 4 * i;
+  for (int i = 0; i < KS; ++i) {
+    const uint32_t st = wave + NW * i;
     kof[i] = kb + st * 32 + lg * 8;
     kok[i] = st < nsteps && kof[i] < ke;
   }
@@ -213,29 +243,28 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
   // subtiles, in one round of loads (unconditional A loads: out-of-range
   // lanes read the chunk's first element of row 0).  The slot's table entry
   // arrived with its seq_slot entries, so nothing is gained by issuing A
-  // before the row scan.  Subtiles go through the wave reduce kShrinkMT at a
-  // time.
-  auto batch = [&](auto qt_tag, int b0, int cnt) {
-    constexpr int QT = decltype(qt_tag)::value;
+  // before the row scan.  Subtiles go through the wave reduce MR at a time;
+  // (subtile, column tile) p of a round is added by wave p % NW.
+  auto batch = [&](int b0, int cnt) {
     const int nb = min(cnt - b0, QT * 16);
     const int nmt = (nb + 15) >> 4;
-    uint4 bop[NT][kShrinkSteps];
+    uint4 bop[NT][KS];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const uint32_t col = col0 + 16u * j + cl;
       const RLD_GLOBAL uint16_t* Arow = A + (size_t)(col < R ? col : 0) * a.k_in;
 #pragma unroll
-      for (int i = 0; i < kShrinkSteps; ++i)
+      for (int i = 0; i < KS; ++i)
         bop[j][i] = load16((col < R && kok[i]) ? Arow + kof[i] : A + kb);
     }
-    uint4 xf[QT][kShrinkSteps];
+    uint4 xf[QT][KS];
 #pragma unroll
     for (int q = 0; q < QT; ++q) {
       const int li = q * 16 + cl;
       const bool ok = li < nb;
       const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)(ok ? sm.rows[b0 + li] : 0) * a.xs;
 #pragma unroll
-      for (int i = 0; i < kShrinkSteps; ++i)
+      for (int i = 0; i < KS; ++i)
         xf[q][i] = (q < nmt && ok && kok[i]) ? load16(xr + kof[i]) : zero16();
     }
     issue_point();
@@ -244,36 +273,34 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int i = 0; i < kShrinkSteps; ++i)
+      for (int i = 0; i < KS; ++i)
         if (!kok[i]) bop[j][i] = zero16();
 #pragma unroll
-    for (int h = 0; h < QT / kShrinkMT; ++h) {
-      if (h * kShrinkMT >= nmt) break;
+    for (int h = 0; h < QT / MR; ++h) {
+      if (h * MR >= nmt) break;
 #pragma unroll
-      for (int qq = 0; qq < kShrinkMT; ++qq) {
-        const int q = h * kShrinkMT + qq;
+      for (int qq = 0; qq < MR; ++qq) {
+        const int q = h * MR + qq;
         if (q < nmt) {
 #pragma unroll
           for (int j = 0; j < NT; ++j) {
             floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < kShrinkSteps; ++i)
-              acc = mfma_bf16_16x16x32(xf[q][i], bop[j][i], acc);
+            for (int i = 0; i < KS; ++i) acc = mfma_bf16_16x16x32(xf[q][i], bop[j][i], acc);
             sm.red[wave][qq * NT + j][lane] = acc;
           }
         }
       }
       __syncthreads();
-      const int qq = wave;  // this wave adds subtile h*kShrinkMT + wave
-      const int q = h * kShrinkMT + qq;
-      if (q < nmt) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
+      for (int p = wave; p < MR * NT; p += NW) {
+        const int qq = p / NT, j = p % NT;
+        const int q = h * MR + qq;
+        if (q < nmt) {
           const uint32_t col = col0 + 16u * j + cl;
-          floatx4 sum = sm.red[0][qq * NT + j][lane];
-          sum += sm.red[1][qq * NT + j][lane];
-          sum += sm.red[2][qq * NT + j][lane];
-          sum += sm.red[3][qq * NT + j][lane];
+          floatx4 sum = sm.red[0][p][lane];
+#pragma unroll
+          for (int v = 1; v < NW; ++v) sum += sm.red[v][p][lane];
           if (col < R) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -292,31 +319,30 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT>& sm) {
       __syncthreads();
     }
   };
-  using Q4 = std::integral_constant<int, kShrinkMT>;
 
   if (a.dense) {
-    const int cnt = dense_tile_rows((uint32_t)s * kDenseShrinkRows, n, kDenseShrinkRows, sm.rows);
-    batch(Q4{}, 0, cnt);
+    constexpr int kTile = dense_shrink_rows(NW);
+    static_assert(kTile == QT * 16, "an unrouted tile is one batch");
+    const int cnt = dense_tile_rows((uint32_t)s * kTile, n, kTile, sm.rows);
+    batch(0, cnt);
     return;
   }
-  // The usual case, straight-line: at most 256 rows (their seq_slot entries
+  // The usual case, straight-line: at most NTH rows (their seq_slot entries
   // are key0, so the scan issues no load that would wait behind the A tile)
-  // and at most 64 of them on this slot.  (A 128-row batch would serve the
-  // next case in one pass, but its registers would cost every block of the
-  // kernel a third of its occupancy.)
-  if (n <= 256) {
-    const int cnt = append_hits(key0 == s, threadIdx.x, sm.rows, 0, sm.wcount);
-    if (cnt <= kShrinkMT * 16) {
-      if (cnt > 0) batch(Q4{}, 0, cnt);
+  // and at most one batch of them on this slot.
+  if (n <= (uint32_t)NTH) {
+    const int cnt = append_hits<NW>(key0 == s, threadIdx.x, sm.rows, 0, sm.wcount);
+    if (cnt <= QT * 16) {
+      if (cnt > 0) batch(0, cnt);
       return;
     }
   }
   uint32_t pos = 0;
-  int cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
+  int cnt = collect_slot_rows<NW>(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
   for (;;) {
-    for (int b0 = 0; b0 < cnt; b0 += kShrinkMT * 16) batch(Q4{}, b0, cnt);
+    for (int b0 = 0; b0 < cnt; b0 += QT * 16) batch(b0, cnt);
     if (pos >= n) break;
-    cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
+    cnt = collect_slot_rows<NW>(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
   }
 }
 
@@ -449,14 +475,135 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem<MT
   }
 }
 
-template <int NT>
-__global__ __launch_bounds__(256) void bgmv_shrink_kernel(BgmvArgs a, uint32_t total) {
-  __shared__ ShrinkSmem<NT> sm;
+// Lean expand item (slot s, 256 output columns from j0; routed mode only).
+// The same per-row arithmetic as expand_item (one MFMA chain over max_rank
+// per 16 x 16 tile, BF16 rounding, the fold), so results are bit-identical;
+// rows go through in passes of 16, the next pass's xa and base values in
+// flight while the current pass folds.
+template <int NKS>
+__device__ void expand_lean_item(const BgmvArgs& a, int s, uint32_t j0, ExpandLeanSmem& sm) {
+  constexpr int kStride = ExpandLeanSmem::kStride;
+  constexpr int kRows = ExpandLeanSmem::kRows;
+  const uint32_t n = a.n, R = a.R, n_out = a.n_out, os = a.os;
+  const int key0 = first_key(a.seq_slot(), n);
+  const SlotEntry ent = slot_entry(a, s);
+  if (!ent.active()) return;
+  const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(ent.b);
+  const float scale = ent.scale;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lg = lane >> 4;
+  const int cl = lane & 15;
+  // fold mapping: 32 vectors of 8 columns per row; vector i of a thread is
+  // row frow + 8*i of the pass
+  const int frow = threadIdx.x >> 5;
+  const int c8 = (threadIdx.x & 31) * 8;
+  const bool fcol_ok = j0 + c8 < n_out;
+
+  int cnt;
+  uint32_t pos = 0;
+  if (n <= 256) {
+    cnt = append_hits(key0 == s, threadIdx.x, sm.rows, 0, sm.wcount);
+    pos = n;
+  } else {
+    cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
+  }
+  if (cnt == 0 && pos >= n) return;
+
+  // The B rows of this wave's 64 columns as MFMA A operands, once per item
+  // (unconditional: out-of-range lanes read B's first element).
+  uint4 aop[4][NKS];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t col = j0 + wave * 64 + m * 16 + cl;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint32_t k = ks * 32 + lg * 8;
+      aop[m][ks] = load16((col < n_out && k < R) ? B + (size_t)col * R + k : B);
+    }
+  }
+  // xa fragments and base values of rows b0 .. b0+15 of the list
+  constexpr int PT = kRows / 16;  // 16-row subtiles of a pass
+  constexpr int FV = kRows / 8;   // fold vectors of a thread per pass
+  auto load_xa = [&](int b0, int cnt_, uint4 (&bop)[PT][NKS]) {
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const bool ok = p * 16 + cl < cnt_ - b0;
+      const RLD_GLOBAL uint16_t* xr = a.xa() + (size_t)(ok ? sm.rows[b0 + p * 16 + cl] : 0) * R;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint32_t k = ks * 32 + lg * 8;
+        bop[p][ks] = (ok && k < R) ? load16(xr + k) : zero16();
+      }
+    }
+  };
+  auto load_base = [&](int b0, int cnt_, uint4 (&bv)[FV]) {
+    const int nb = min(cnt_ - b0, kRows);
+#pragma unroll
+    for (int i = 0; i < FV; ++i) {
+      const int rl = frow + 8 * i;
+      bv[i] = (rl < nb && fcol_ok) ? load16(a.out() + (size_t)sm.rows[b0 + rl] * os + j0 + c8)
+                                   : zero16();
+    }
+  };
+  for (;;) {
+    uint4 bop[PT][NKS], bv[FV];
+    if (cnt > 0) {
+      load_xa(0, cnt, bop);
+      load_base(0, cnt, bv);
+    }
+    issue_point();
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        if (ks * 32 + lg * 8 >= (int)R) aop[m][ks] = zero16();
+    // pass: MFMA (deltas to LDS), the next pass's xa goes out, the fold, the
+    // next pass's base values go out
+    for (int b0 = 0; b0 < cnt; b0 += kRows) {
+      const int nb = min(cnt - b0, kRows);
+      const bool more = b0 + kRows < cnt;
+#pragma unroll
+      for (int p = 0; p < PT; ++p) {
+        if (p * 16 >= nb) break;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) acc = mfma_bf16_16x16x32(aop[m][ks], bop[p][ks], acc);
+          // lane holds delta[row p*16+cl][cols m*16 + 4*lg .. +3] of this wave's slice
+          *reinterpret_cast<uint2*>(&sm.dl[(p * 16 + cl) * kStride + wave * 64 + m * 16 + 4 * lg]) =
+              make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        }
+      }
+      if (more) load_xa(b0 + kRows, cnt, bop);
+      issue_point();
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < FV; ++i) {
+        const int rl = frow + 8 * i;
+        if (rl < nb && fcol_ok) {
+          const uint4 dv = *reinterpret_cast<const uint4*>(&sm.dl[rl * kStride + c8]);
+          store16(a.out() + (size_t)sm.rows[b0 + rl] * os + j0 + c8, fold8(bv[i], dv, scale));
+        }
+      }
+      if (more) load_base(b0 + kRows, cnt, bv);
+      issue_point();
+      __syncthreads();
+    }
+    if (pos >= n) break;
+    cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
+  }
+}
+
+template <int NT, int NW>
+__global__ __launch_bounds__(NW * kWave) void bgmv_shrink_kernel(BgmvArgs a, uint32_t total) {
+  __shared__ ShrinkSmem<NT, NW> sm;
   // the column groups of one (slot, chunk) share an XCD, and so the x rows in
   // its L2
   const uint32_t w = xcd_group_item(a.ncg);
   if (w >= total) return;
-  shrink_item<NT>(a, w, sm);
+  shrink_item<NT, NW>(a, w, sm);
 }
 
 // k split: xa[row, 4 columns] = bf16(sum over chunks, in chunk order, of the
@@ -496,6 +643,12 @@ __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a)
   reduce_unit(a, t);
 }
 
+template <int NKS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NKS <= 2 ? (kLeanRows == 16 ? 6 : 5) : 4))) void bgmv_expand_lean_kernel(BgmvArgs a) {
+  __shared__ ExpandLeanSmem sm;
+  expand_lean_item<NKS>(a, (int)blockIdx.y, blockIdx.x * ExpandLeanSmem::kCols, sm);
+}
+
 template <int NKS, int MT>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(BgmvArgs a) {
   __shared__ ExpandSmem<MT> sm;
@@ -522,14 +675,15 @@ __device__ __forceinline__ uint32_t route_of(const uint32_t* first, uint32_t nr,
   return r;
 }
 
-template <int NT>
-__global__ __launch_bounds__(256) void bgmv_shrink_multi_kernel(BgmvMulti m, uint32_t total) {
-  __shared__ ShrinkSmem<NT> sm;
+template <int NT, int NW>
+__global__ __launch_bounds__(NW * kWave) void bgmv_shrink_multi_kernel(BgmvMulti m,
+                                                                        uint32_t total) {
+  __shared__ ShrinkSmem<NT, NW> sm;
   // every route has the same column groups: a group never spans two routes
   const uint32_t w = xcd_group_item(m.a[0].ncg);
   if (w >= total) return;
   const uint32_t r = route_of(m.first, m.nr, w);
-  shrink_item<NT>(m.a[r], w - m.first[r], sm);
+  shrink_item<NT, NW>(m.a[r], w - m.first[r], sm);
 }
 
 __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_multi_kernel(BgmvMulti m) {
@@ -613,6 +767,23 @@ static BgmvKernel pick_expand(uint32_t R) {
 
 typedef void (*BgmvMultiKernel)(BgmvMulti);
 
+// The classic expand holds 168 registers a lane at max_rank 64, three blocks
+// a CU: 768 resident on MI355X's 256 CUs.  A routed grid larger than that
+// (the FFN decode shapes: 48 column tiles x 32 slots) takes the lean item,
+// six blocks a CU, which runs the grid in one round; the results are the same
+// bits either way.
+constexpr uint32_t kClassicExpandResident = 768;
+
+static BgmvKernel pick_expand_routed(uint32_t R, uint32_t tiles, uint32_t slots) {
+  if ((uint64_t)tiles * slots <= kClassicExpandResident) return pick_expand(R);
+  switch (div_ceil(R, 32)) {
+    case 1: return bgmv_expand_lean_kernel<1>;
+    case 2: return bgmv_expand_lean_kernel<2>;
+    case 3: return bgmv_expand_lean_kernel<3>;
+    default: return bgmv_expand_lean_kernel<4>;
+  }
+}
+
 static BgmvMultiKernel pick_expand_multi(uint32_t R) {
   switch (div_ceil(R, 32)) {
     case 1: return bgmv_expand_multi_kernel<1, kExpMT>;
@@ -620,6 +791,21 @@ static BgmvMultiKernel pick_expand_multi(uint32_t R) {
     case 3: return bgmv_expand_multi_kernel<3, kExpMT>;
     default: return bgmv_expand_multi_kernel<4, kExpMT>;
   }
+}
+
+typedef void (*ShrinkKernel)(BgmvArgs, uint32_t);
+typedef void (*ShrinkMultiKernel)(BgmvMulti, uint32_t);
+
+// Shrink kernel of (column tiles per item, waves per block).
+static ShrinkKernel pick_shrink(uint32_t nt, uint32_t nw) {
+  if (nw == 8) return nt == 4 ? bgmv_shrink_kernel<4, 8> : bgmv_shrink_kernel<2, 8>;
+  return nt == 1 ? bgmv_shrink_kernel<1, 4>
+                 : (nt == 2 ? bgmv_shrink_kernel<2, 4> : bgmv_shrink_kernel<4, 4>);
+}
+
+static ShrinkMultiKernel pick_shrink_multi(uint32_t nt, uint32_t nw) {
+  if (nw == 8) return bgmv_shrink_multi_kernel<2, 8>;
+  return nt == 1 ? bgmv_shrink_multi_kernel<1, 4> : bgmv_shrink_multi_kernel<2, 4>;
 }
 
 }  // namespace rld
@@ -651,10 +837,8 @@ extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x
   const uint32_t total = route->max_loras * a.nch * a.ncg;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(xcd_group_grid(total, a.ncg));
-  if (bgmv_nt(a.R) == 1)
-    hipLaunchKernelGGL(bgmv_shrink_kernel<1>, grid, dim3(256), 0, hs, a, total);
-  else
-    hipLaunchKernelGGL(bgmv_shrink_kernel<2>, grid, dim3(256), 0, hs, a, total);
+  const uint32_t nw = bgmv_shrink_waves(a.k_in, a.R);
+  hipLaunchKernelGGL(pick_shrink(bgmv_nt(a.R), nw), grid, dim3(nw * kWave), 0, hs, a, total);
   if ((st = launch_status())) return st;
   if (a.nch > 1) {
     hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(n * (a.R / 4), kReduceThreads)),
@@ -687,8 +871,11 @@ extern "C" int rld_bgmv_expand_fold(const rld_route* route, const void* xa,
   a.n_out = route->n_out;
   a.R = route->max_rank;
   a.os = out_row_stride;
-  hipLaunchKernelGGL(pick_expand(a.R), dim3(div_ceil(route->n_out, 64 * kExpMT), route->max_loras),
-                     dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
+  const uint32_t tiles = div_ceil(route->n_out, 64u * kExpMT);
+  static_assert(ExpandLeanSmem::kCols == 64 * kExpMT, "both expands take 256-column tiles");
+  hipLaunchKernelGGL(pick_expand_routed(a.R, tiles, route->max_loras),
+                     dim3(tiles, route->max_loras), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), a);
   return launch_status();
 }
 
@@ -767,10 +954,8 @@ extern "C" int rld_bgmv_multi(const rld_route* const* routes, uint32_t nroutes, 
   if (tiles > 0x7fffffffu) return RLD_EUNSUPPORTED;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(xcd_group_grid(items, m.a[0].ncg));
-  if (bgmv_nt(R) == 1)
-    hipLaunchKernelGGL(bgmv_shrink_multi_kernel<1>, grid, dim3(256), 0, hs, m, items);
-  else
-    hipLaunchKernelGGL(bgmv_shrink_multi_kernel<2>, grid, dim3(256), 0, hs, m, items);
+  const uint32_t nw = bgmv_shrink_waves(k_in, R);
+  hipLaunchKernelGGL(pick_shrink_multi(bgmv_nt(R), nw), grid, dim3(nw * kWave), 0, hs, m, items);
   if ((st = launch_status())) return st;
   if (m.a[0].nch > 1) {
     hipLaunchKernelGGL(bgmv_reduce_multi_kernel,
@@ -833,17 +1018,16 @@ extern "C" int rld_lora_shrink(const rld_pair* pair, const void* x, uint32_t x_r
   a.xs = x_row_stride;
   a.xa_ = reinterpret_cast<uint64_t>(xa);
   a.partial_ = reinterpret_cast<uint64_t>(workspace);
-  if (!launch_fits((uint64_t)div_ceil(m, (uint32_t)kDenseShrinkRows) * a.nch * a.ncg,
-                   (uint64_t)m * (a.R / 4)))
+  // the routed calls' wave rule, so a row's sums are added in the same order
+  const uint32_t nw = bgmv_shrink_waves(a.k_in, a.R);
+  const uint32_t tile = (uint32_t)dense_shrink_rows((int)nw);
+  if (!launch_fits((uint64_t)div_ceil(m, tile) * a.nch * a.ncg, (uint64_t)m * (a.R / 4)))
     return RLD_EUNSUPPORTED;
-  const uint32_t total = div_ceil(m, (uint32_t)kDenseShrinkRows) * a.nch * a.ncg;
+  const uint32_t total = div_ceil(m, tile) * a.nch * a.ncg;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(xcd_group_grid(total, a.ncg));
-  switch (bgmv_nt(a.R, true)) {
-    case 1: hipLaunchKernelGGL(bgmv_shrink_kernel<1>, grid, dim3(256), 0, hs, a, total); break;
-    case 2: hipLaunchKernelGGL(bgmv_shrink_kernel<2>, grid, dim3(256), 0, hs, a, total); break;
-    default: hipLaunchKernelGGL(bgmv_shrink_kernel<4>, grid, dim3(256), 0, hs, a, total); break;
-  }
+  hipLaunchKernelGGL(pick_shrink(bgmv_nt(a.R, true), nw), grid, dim3(nw * kWave), 0, hs, a,
+                     total);
   if ((st = launch_status())) return st;
   if (a.nch > 1) {
     hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(m * (a.R / 4), kReduceThreads)),

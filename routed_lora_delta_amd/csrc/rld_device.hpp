@@ -100,9 +100,10 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// A block of 256 threads appends to `list` (LDS), in thread order, the `row`
-// of every thread whose `hit` is set.  Returns the number appended (in every
-// thread).  `wcount` is LDS scratch of 4 ints.
+// A block of NW waves appends to `list` (LDS), in thread order, the `row` of
+// every thread whose `hit` is set.  Returns the number appended (in every
+// thread).  `wcount` is LDS scratch of NW ints.
+template <int NW = 4>
 __device__ __forceinline__ int append_hits(bool hit, uint32_t row, int* list, int base,
                                            int* wcount) {
   const int lane = threadIdx.x & 63;
@@ -113,7 +114,7 @@ __device__ __forceinline__ int append_hits(bool hit, uint32_t row, int* list, in
   int off = base;
   int tot = 0;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < NW; ++v) {
     off += (v < wave) ? wcount[v] : 0;
     tot += wcount[v];
   }

@@ -58,6 +58,17 @@ inline uint32_t bgmv_chunk(uint32_t k_in, uint32_t max_rank) {
   return k_in <= kc ? k_in : kc;
 }
 
+// Waves of a BGMV shrink block: the chunk's 32-wide K steps are dealt to them
+// round robin, and their sums are added in wave order, so this is part of the
+// summation order and a function of (k_in, max_rank) only.  Eight waves of two
+// steps hold the x fragments of 128 rows in the registers four waves of four
+// steps need for 64, so a slot with up to 128 rows of the batch is one round of
+// loads.
+inline uint32_t bgmv_shrink_waves(uint32_t k_in, uint32_t max_rank) {
+  (void)k_in;
+  return max_rank > 16 ? 8u : 4u;
+}
+
 // 16-column MFMA tiles of xa per BGMV shrink item.  Routed calls take 1 or 2
 // (wider ranks take several column groups: four tiles' operands leave the
 // kernel two waves per SIMD, two tiles three).  The unrouted mode takes up to

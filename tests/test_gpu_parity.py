@@ -58,6 +58,13 @@ BGMV_SHAPES = [
     (600, 1536, 264, 32, 40, (16, 32), (0, 39)),
     (1200, 256, 264, 16, 2, (8, 16), ()),
     (1400, 1024, 264, 16, 2, (8, 16), ()),  # k split with > 512 rows per slot
+    # (column tiles x slots) grids above 768 take the lean expand item: rank
+    # steps 1, 2 (one half masked at rank 48) and 4, more than 256 rows, a
+    # ragged last column tile
+    (700, 1024, 8192, 64, 32, (8, 16, 32, 64), (5,)),
+    (90, 512, 6144, 48, 40, (16, 48), ()),
+    (64, 256, 4096, 128, 64, (64, 128), ()),
+    (257, 768, 3336, 8, 80, (4, 8), (2,)),
 ]
 
 
