@@ -382,7 +382,9 @@ class Step:
                               mwsb=mwsb, n=wl.n):
                         return R.rld_bgmv_multi([r.route for r in rts], x, c0.x_row_stride, seq,
                                                 n, outs, oss, xas, mws, mwsb)
-                    add((f"{tag}.{'+'.join(c.module for c in first)}.multi", "bgmv_multi", multi,
+                    label = (ONEPASS if R.rld_bgmv_launches([r.route for r in rts], wl.n) == 1
+                             else "bgmv_multi")
+                    add((f"{tag}.{'+'.join(c.module for c in first)}.multi", label, multi,
                          sb, fl, wl.n * len(first)), c0.module, 0, lanes_map=lmap)
                     self.rows += wl.n * len(first)
                 for c in wl.calls:
@@ -404,6 +406,16 @@ class Step:
                     else:
                         rt = DenseRoute(c.adapters, c.max_loras, c.max_rank, c.k_in, c.n_out, dev)
                         keep.append(rt)
+                        if R.rld_bgmv_launches(rt.route, wl.n) == 1:
+                            # one launch: rld_bgmv's one-pass form
+                            def fold(rt=rt, c=c, x=x, seq=seq, out=out, xa=xa, ws=ws, wsb=wsb,
+                                     n=wl.n):
+                                return R.rld_bgmv(rt.route, x, c.x_row_stride, seq, n, out,
+                                                  c.out_row_stride, xa, ws, wsb)
+                            add((f"{tag}.{c.module}.fold", ONEPASS, fold, sb + eb, fl, wl.n),
+                                c.module, lanes_map=lmap)
+                            self.rows += wl.n
+                            continue
 
                         def shrink(rt=rt, c=c, x=x, seq=seq, xa=xa, ws=ws, wsb=wsb, n=wl.n):
                             return R.rld_bgmv_shrink(rt.route, x, c.x_row_stride, seq, n, xa, ws,
@@ -628,7 +640,8 @@ WORKLOAD_NAMES = {
 # then the chunk reduce); the bench times the pair as one entry.
 BGMV_SHRINK = "bgmv_shrink_kernel+bgmv_reduce_kernel"
 # launches behind one bench entry (the step's BGMV calls all split k_in)
-KERNEL_LAUNCHES = {BGMV_SHRINK: 2, "bgmv_multi": 3}
+ONEPASS = "bgmv_onepass_kernel"
+KERNEL_LAUNCHES = {BGMV_SHRINK: 2, "bgmv_multi": 3, ONEPASS: 1}
 
 
 def _timed_eager(step, idx, lead_graph, steps, torch):

@@ -221,11 +221,27 @@ int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x_row_stride
 int rld_bgmv_expand_fold(const rld_route* route, const void* xa, const int32_t* seq_slot,
                          uint32_t n, void* base_out, uint32_t out_row_stride, void* stream);
 
-/* apply_lora_bgmv: rld_bgmv_shrink then rld_bgmv_expand_fold on the same
- * stream. */
+/* apply_lora_bgmv: the results of rld_bgmv_shrink then rld_bgmv_expand_fold
+ * on the same stream (xa written, outputs folded), bit for bit.  At
+ * max_rank <= 16, k_in <= 4096 and n <= 256 with few enough (slot, column
+ * group) items (decode batches of the attention shapes) this is one launch
+ * instead of three: each block recomputes its slot's xa in the shrink's
+ * summation order and expands its columns from LDS; the workspace is then
+ * unused, but the workspace arguments are checked as for the two stages.
+ * rld_bgmv_launches gives the count for a call. */
 int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_stride,
              const int32_t* seq_slot, uint32_t n, void* base_out, uint32_t out_row_stride,
              void* xa, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernel launches of rld_bgmv (one route: routes = &route, nroutes = 1) or of
+ * rld_bgmv_multi over these routes, for a batch of n rows: 1 in the one-pass
+ * form, 3 with a k_in split (shrink, chunk reduce, expand), 2 without one.
+ * 0 for n == 0 or routes the calls reject (a missing table, a zero dimension,
+ * one that is not a multiple of 8, max_rank above RLD_MAX_RANK, routes of
+ * different k_in or max_rank, nroutes outside 1..4).  The one-pass form is
+ * taken at max_rank <= 16, k_in <= 4096 and n <= 256 when the routes'
+ * (slot, 512 output columns) items number at most 256. */
+int rld_bgmv_launches(const rld_route* const* routes, uint32_t nroutes, uint32_t n);
 
 /* rld_bgmv for callers that cannot allocate: code under HIP graph capture,
  * serving loops and harnesses that forbid hipMalloc.  The same fold, bit for
@@ -251,7 +267,7 @@ int rld_bgmv_noalloc(const rld_route* route, const void* x, uint32_t x_row_strid
 /* Several routed BGMV folds over the same rows (apply_lora_bgmv once per
  * route, as a layer's q, k and v, or gate and up, read one input): one shrink,
  * one chunk reduce (k_in split only) and one expand launch serve every route,
- * instead of that many per route.
+ * instead of that many per route (in rld_bgmv's one-pass form, one launch).
  *   routes          host array [nroutes] of routes, 1 <= nroutes <= 4
  *                   (RLD_EUNSUPPORTED above); all with the same k_in and
  *                   max_rank (RLD_EINVAL otherwise); max_loras and n_out may

@@ -95,6 +95,7 @@ _SIGS = {
     "rld_bgmv_expand_fold": (c_int, [_R, _P, _P, c_uint32, _P, c_uint32, _P]),
     "rld_bgmv": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, c_size_t, _P]),
     "rld_bgmv_noalloc": (c_int, [_R, _P, c_uint32, _P, c_uint32, _P, c_uint32, _P]),
+    "rld_bgmv_launches": (c_int, [_P, c_uint32, c_uint32]),
     "rld_bgmv_multi_workspace_bytes": (c_size_t, [c_uint32, c_uint32, c_uint32, c_uint32]),
     "rld_bgmv_multi": (c_int, [_P, c_uint32, _P, c_uint32, _P, c_uint32, _P, _P, _P, _P,
                                c_size_t, _P]),
@@ -244,6 +245,14 @@ def rld_bgmv(route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, xa, 
     return _lib.rld_bgmv(ctypes.byref(route), ptr(x), x_row_stride, ptr(seq_slot), n,
                          ptr(base_out), out_row_stride, ptr(xa), ptr(workspace), workspace_bytes,
                          stream_handle(stream))
+
+
+def rld_bgmv_launches(routes, n):
+    """Launches of rld_bgmv (one route) or rld_bgmv_multi (a list of routes)."""
+    if not isinstance(routes, (list, tuple)):
+        routes = [routes]
+    arr = (ctypes.c_void_p * len(routes))(*[ctypes.addressof(r) for r in routes])
+    return _lib.rld_bgmv_launches(ctypes.cast(arr, c_void_p), len(routes), n)
 
 
 def rld_bgmv_noalloc(route, x, x_row_stride, seq_slot, n, base_out, out_row_stride, stream=None):

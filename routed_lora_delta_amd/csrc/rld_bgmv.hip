@@ -110,6 +110,31 @@ struct ExpandLeanSmem {
   __attribute__((aligned(16))) uint16_t dl[kRows * kStride];
 };
 
+// One-pass fold (rld_bgmv / rld_bgmv_multi at max_rank <= 16, k_in <= 4096,
+// decode-sized batches): one launch, no workspace.  A block takes (slot s,
+// 512 output columns) and first recomputes the xa of s's rows itself, in the
+// summation order of the k-split shrink and its chunk reduce: its sixteen
+// waves take one 256-wide chunk each and run, inside the wave, the four
+// chains of the shrink's four waves (steps w, w+4, w+8, w+12 of the chunk)
+// and their wave-order sum; the chunk sums meet in LDS and are added in chunk
+// order, then rounded.  Every block of a slot therefore holds the xa bits the
+// three launches would have written, and expands its columns from LDS with
+// the expand's arithmetic.  The slot's A tile is read by each of its column
+// groups (from cache after the first; the groups of a slot share an XCD).
+constexpr int kOpThreads = 1024;
+constexpr int kOpWaves = kOpThreads / kWave;
+constexpr int kOpCols = 512;       // output columns per item (32 per wave)
+constexpr int kOpChunk = 256;      // the k-split chunk at max_rank <= 16
+constexpr int kOpMaxRows = 256;    // n of the calls that take this path
+struct OnePassSmem {
+  static constexpr int kStride = kOpCols + 8;
+  int rows[kOpMaxRows];
+  int wcount[kOpWaves];
+  floatx4 red[kOpWaves][kWave];                    // chunk sums of a 16-row batch
+  __attribute__((aligned(16))) uint16_t xs[16 * 16];  // the batch's xa, row-major
+  __attribute__((aligned(16))) uint16_t dl[16 * kStride];
+};
+
 __device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
   if (s < 0 || (uint32_t)s >= a.max_loras) return false;
   const uint64_t ta = a.a_table()[s], tb = a.b_table()[s];  // both in flight together
@@ -596,6 +621,126 @@ __device__ void expand_lean_item(const BgmvArgs& a, int s, uint32_t j0, ExpandLe
   }
 }
 
+// One-pass item: slot s, output columns [j0, j0 + 512) of route a.  With
+// xa_writer it also stores the xa rows of s (column group 0 of each slot),
+// with zero_writer the zero xa rows of rows that fold nothing.
+__device__ void onepass_item(const BgmvArgs& a, int s, uint32_t j0, bool xa_writer,
+                             bool zero_writer, OnePassSmem& sm) {
+  constexpr int kStride = OnePassSmem::kStride;
+  const uint32_t n = a.n, R = a.R, k_in = a.k_in, n_out = a.n_out, os = a.os;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lg = lane >> 4;
+  const int cl = lane & 15;
+  // every row's slot (n <= 1024) and the slot's table entries: one round
+  const int key = threadIdx.x < n ? a.seq_slot()[threadIdx.x] : -1;
+  const SlotEntry ent = slot_entry(a, s);
+  if (zero_writer && threadIdx.x < n && !slot_active(a, key)) {
+    for (uint32_t cc = 0; cc < R; cc += 8)
+      store16(a.xa() + (size_t)threadIdx.x * R + cc, zero16());
+  }
+  if (!ent.active()) return;
+  const int cnt = append_hits<kOpWaves>(key == s, threadIdx.x, sm.rows, 0, sm.wcount);
+  if (cnt == 0) return;
+  const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(ent.a);
+  const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(ent.b);
+  const float scale = ent.scale;
+
+  // this wave's chunk c = wave: the shrink's wave w of that chunk owns steps
+  // w + 4i (i < 4); a step is valid below the chunk's end
+  const uint32_t c = (uint32_t)wave;
+  const bool has_chunk = c < a.nch;
+  const uint32_t kb = c * a.kc;
+  const uint32_t ke = has_chunk ? min(kb + a.kc, k_in) : kb;
+  const uint32_t nsteps = has_chunk ? (ke - kb + 31) / 32 : 0;
+  // A fragments of the chunk's 8 steps (column cl of xa, clamped like the shrink)
+  const RLD_GLOBAL uint16_t* Arow = A + (size_t)(cl < (int)R ? cl : 0) * k_in;
+  uint4 af[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const uint32_t kof = kb + st * 32 + lg * 8;
+    const bool ok = (uint32_t)st < nsteps && kof < ke;
+    af[st] = load16((cl < (int)R && ok) ? Arow + kof : A + (has_chunk ? kb : 0));
+    if (!ok) af[st] = zero16();
+  }
+  // B rows of this wave's 32 output columns as MFMA A operands (one K step:
+  // max_rank <= 16 < 32), clamped like the expand
+  uint4 aop[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t col = j0 + wave * 32 + m * 16 + cl;
+    const uint32_t k = lg * 8;
+    aop[m] = load16((col < n_out && k < R) ? B + (size_t)col * R + k : B);
+    if (k >= R) aop[m] = zero16();
+  }
+  // fold mapping: thread t folds row t / 64 of the batch, columns 8 (t % 64) ..
+  const int frow = threadIdx.x >> 6;
+  const int c8 = (threadIdx.x & 63) * 8;
+  const bool fcol_ok = j0 + c8 < n_out;
+
+  for (int b0 = 0; b0 < cnt; b0 += 16) {
+    const int nb = min(cnt - b0, 16);
+    // x fragments of the batch's rows (row cl) for the chunk's steps; base values
+    uint4 xf[8];
+    {
+      const bool ok = cl < nb;
+      const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)(ok ? sm.rows[b0 + cl] : 0) * a.xs;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const uint32_t kof = kb + st * 32 + lg * 8;
+        xf[st] = (ok && (uint32_t)st < nsteps && kof < ke) ? load16(xr + kof) : zero16();
+      }
+    }
+    const uint4 bv = (frow < nb && fcol_ok)
+                         ? load16(a.out() + (size_t)sm.rows[b0 + frow] * os + j0 + c8)
+                         : zero16();
+    issue_point();
+    // the shrink's four wave chains of chunk c and their wave-order sum
+    floatx4 part = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int st = w + 4 * i;
+        acc = mfma_bf16_16x16x32(st < 8 ? xf[st] : zero16(), st < 8 ? af[st] : zero16(), acc);
+      }
+      part = w == 0 ? acc : part + acc;
+    }
+    sm.red[wave][lane] = part;
+    __syncthreads();
+    // chunk sums in chunk order, rounded: xa[row 4g+i][col] of lane (g, col)
+    if (threadIdx.x < 256) {
+      const int l = threadIdx.x >> 2, i = threadIdx.x & 3;
+      float sum = sm.red[0][l][i];
+      for (uint32_t cc = 1; cc < a.nch; ++cc) sum = sum + sm.red[cc][l][i];
+      const int row = 4 * (l >> 4) + i, col = l & 15;
+      const uint16_t v = (uint16_t)f32_to_bf16(sum);
+      sm.xs[row * 16 + col] = v;
+      if (xa_writer && row < nb && (uint32_t)col < R)
+        a.xa()[(size_t)sm.rows[b0 + row] * R + col] = v;
+    }
+    __syncthreads();
+    // expand: xa of row cl, k = 8 lg .. (zero past max_rank)
+    const uint4 bop = (uint32_t)(lg * 8) < R
+                          ? *reinterpret_cast<const uint4*>(&sm.xs[cl * 16 + lg * 8])
+                          : zero16();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const floatx4 acc = mfma_bf16_16x16x32(aop[m], bop, floatx4{0.f, 0.f, 0.f, 0.f});
+      // lane holds delta[row cl][cols m*16 + 4*lg .. +3] of this wave's slice
+      *reinterpret_cast<uint2*>(&sm.dl[cl * kStride + wave * 32 + m * 16 + 4 * lg]) =
+          make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    }
+    __syncthreads();
+    if (frow < nb && fcol_ok) {
+      const uint4 dv = *reinterpret_cast<const uint4*>(&sm.dl[frow * kStride + c8]);
+      store16(a.out() + (size_t)sm.rows[b0 + frow] * os + j0 + c8, fold8(bv, dv, scale));
+    }
+    __syncthreads();
+  }
+}
+
 template <int NT, int NW>
 __global__ __launch_bounds__(NW * kWave) void bgmv_shrink_kernel(BgmvArgs a, uint32_t total) {
   __shared__ ShrinkSmem<NT, NW> sm;
@@ -703,6 +848,21 @@ __global__ __launch_bounds__(256) void bgmv_expand_multi_kernel(BgmvMulti m) {
                        sm);
 }
 
+// Items of a one-pass launch: (route r, slot s, column group g), g fastest,
+// so that a slot's groups are consecutive and land on one XCD.
+__global__ __launch_bounds__(kOpThreads) void bgmv_onepass_kernel(BgmvMulti m, uint32_t total) {
+  __shared__ OnePassSmem sm;
+  const uint32_t w = xcd_work_item(total);
+  if (w >= total) return;
+  const uint32_t r = route_of(m.first, m.nr, w);
+  const BgmvArgs& a = m.a[r];
+  const uint32_t ng = (a.n_out + kOpCols - 1) / kOpCols;
+  const uint32_t t = w - m.first[r];
+  const int s = (int)(t / ng);
+  const uint32_t g = t % ng;
+  onepass_item(a, s, g * kOpCols, g == 0, g == 0 && (uint32_t)s == a.max_loras - 1, sm);
+}
+
 // Workspace: fp32 partials [nch][n][R] (k split only).
 static size_t round16(size_t v) { return (v + 15) & ~(size_t)15; }
 
@@ -808,6 +968,28 @@ static ShrinkMultiKernel pick_shrink_multi(uint32_t nt, uint32_t nw) {
   return nt == 1 ? bgmv_shrink_multi_kernel<1, 4> : bgmv_shrink_multi_kernel<2, 4>;
 }
 
+static uint32_t onepass_items(const rld_route* route) {
+  return div_ceil(route->n_out, (uint32_t)kOpCols) * route->max_loras;
+}
+
+// The one-pass fold serves calls whose k-split shrink has 256-wide chunks
+// (at most sixteen) and four waves, over batches of at most kOpMaxRows rows,
+// when its (slot, column group) items fit one round of one block per CU (each
+// item reads its slot's whole A tile, so more items would mostly add reads);
+// its results are those of the three launches, bit for bit, so the choice is
+// free.
+constexpr uint64_t kOpMaxItems = 256;
+
+static bool use_onepass(const rld_route* const* routes, uint32_t nroutes, uint32_t n) {
+  const uint32_t k_in = routes[0]->k_in, R = routes[0]->max_rank;
+  if (!(R <= 16 && n <= (uint32_t)kOpMaxRows && k_in <= (uint32_t)(kOpWaves * kOpChunk) &&
+        bgmv_chunk(k_in, R) <= (uint32_t)kOpChunk && bgmv_shrink_waves(k_in, R) == 4))
+    return false;
+  uint64_t items = 0;
+  for (uint32_t r = 0; r < nroutes; ++r) items += onepass_items(routes[r]);
+  return items <= kOpMaxItems;
+}
+
 }  // namespace rld
 
 using namespace rld;
@@ -816,6 +998,16 @@ extern "C" size_t rld_bgmv_workspace_bytes(uint32_t n, uint32_t k_in, uint32_t m
                                            uint32_t max_loras) {
   if (k_in == 0 || max_rank == 0 || max_loras == 0) return 0;
   return partial_bytes(n, k_in, max_rank);
+}
+
+extern "C" int rld_bgmv_launches(const rld_route* const* routes, uint32_t nroutes, uint32_t n) {
+  if (!routes || nroutes == 0 || nroutes > kMaxRoutes || n == 0) return 0;
+  for (uint32_t r = 0; r < nroutes; ++r)
+    if (check_route(routes[r]) != RLD_OK || routes[r]->k_in != routes[0]->k_in ||
+        routes[r]->max_rank != routes[0]->max_rank)
+      return 0;
+  if (use_onepass(routes, nroutes, n)) return 1;
+  return bgmv_chunk(routes[0]->k_in, routes[0]->max_rank) < routes[0]->k_in ? 3 : 2;
 }
 
 extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x_row_stride,
@@ -887,6 +1079,23 @@ extern "C" int rld_bgmv(const rld_route* route, const void* x, uint32_t x_row_st
   if (st) return st;
   if (n == 0) return RLD_OK;
   if ((st = check_rows(base_out, out_row_stride, route->n_out))) return st;
+  if (use_onepass(&route, 1, n)) {
+    // the checks of the two stages, then one launch
+    if (route->max_loras > 65535u) return RLD_EUNSUPPORTED;
+    if (!seq_slot || !xa) return RLD_EINVAL;
+    if ((st = check_rows(x, x_row_stride, route->k_in))) return st;
+    if (!aligned16(xa)) return RLD_EALIGN;
+    BgmvMulti m = {};
+    m.nr = 1;
+    if ((st = make_args(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
+                        base_out, out_row_stride, &m.a[0])))
+      return st;
+    const uint32_t items = onepass_items(route);
+    m.first[1] = items;
+    hipLaunchKernelGGL(bgmv_onepass_kernel, dim3(xcd_grid(items)), dim3(kOpThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), m, items);
+    return launch_status();
+  }
   st = rld_bgmv_shrink(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
                        stream);
   if (st) return st;
@@ -953,6 +1162,16 @@ extern "C" int rld_bgmv_multi(const rld_route* const* routes, uint32_t nroutes, 
   m.tfirst[nroutes] = tiles;
   if (tiles > 0x7fffffffu) return RLD_EUNSUPPORTED;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (use_onepass(routes, nroutes, n)) {
+    uint32_t op = 0;
+    for (uint32_t r = 0; r < nroutes; ++r) {
+      m.first[r] = op;
+      op += onepass_items(routes[r]);
+    }
+    m.first[nroutes] = op;
+    hipLaunchKernelGGL(bgmv_onepass_kernel, dim3(xcd_grid(op)), dim3(kOpThreads), 0, hs, m, op);
+    return launch_status();
+  }
   const dim3 grid(xcd_group_grid(items, m.a[0].ncg));
   const uint32_t nw = bgmv_shrink_waves(k_in, R);
   hipLaunchKernelGGL(pick_shrink_multi(bgmv_nt(R), nw), grid, dim3(nw * kWave), 0, hs, m, items);

@@ -473,3 +473,25 @@ def test_scale_table_values_are_exact_closed_forms():
         out = ctypes.c_float()
         R.rld_scale(alpha, r, 1, ctypes.byref(out))
         assert out.value == float(np.float32(alpha / math.sqrt(r)))
+
+
+def test_bgmv_launch_count():
+    """rld_bgmv's launch count: one in the one-pass form (max_rank <= 16,
+    k_in <= 4096, n <= 256, at most 256 (slot, 512-column) items over the
+    routes), three with a k_in split, two without one, zero for an empty
+    batch or routes the calls reject."""
+    L = R.rld_bgmv_launches
+    q = _route(4096, 4096, 16, 16)                     # 8 x 16 = 128 items
+    kv = _route(4096, 1024, 16, 16)                    # 2 x 16 = 32
+    assert L(q, 64) == 1 and L(q, 256) == 1 and L(q, 257) == 3
+    assert L([q, kv, kv], 64) == 1                     # 192 items
+    assert L([q, q, kv], 64) == 3                      # 288 items
+    assert L(_route(4096, 12288, 16, 16), 64) == 3     # 384 items
+    assert L(_route(8192, 4096, 16, 16), 64) == 3      # k_in above 16 chunks
+    assert L(_route(4096, 12288, 64, 32), 256) == 3    # rank 64
+    assert L(_route(200, 264, 8, 3), 5) == 1           # one chunk shorter than 256
+    assert L(_route(512, 768, 64, 4), 64) == 2         # rank 64, one 512 chunk
+    assert L(_route(256, 264, 16, 4), 300) == 2
+    assert L(q, 0) == 0
+    assert L(_route(4096, 4096, 16, 16, tables=False), 64) == 0
+    assert L([q, _route(4096, 4096, 24, 16)], 64) == 0  # different max_rank

@@ -163,6 +163,63 @@ def test_bgmv_multi_equals_separate_calls(case):
         assert np.array_equal(o_sep[k], o_multi[k]), f"buffer {k}"
 
 
+ONEPASS_CASES = [
+    # n, k_in, n_out, max_rank, max_loras, ranks, absent slots, zipf, seq out of range
+    (64, 4096, 4096, 16, 16, (8, 16), (), None, False),      # attention q / o shape
+    (37, 1000, 520, 16, 16, (8, 16), (3, 7), None, True),    # 4 chunks, a partial last step
+    (5, 200, 264, 8, 3, (4, 8), (), None, False),            # one chunk shorter than 256
+    (256, 4096, 1032, 16, 16, (8, 16), (), 1.1, False),      # busy slots: several 16-row batches
+    (1, 256, 256, 8, 2, (4, 8), (), None, False),
+]
+
+
+@pytest.mark.parametrize("case", ONEPASS_CASES, ids=lambda c: f"n{c[0]}k{c[1]}o{c[2]}r{c[3]}")
+def test_bgmv_onepass_equals_three_launches(case):
+    """At max_rank <= 16 and decode batch sizes rld_bgmv is one launch whose
+    blocks recompute their slot's xa in the summation order of the k-split
+    shrink and its chunk reduce; its xa and folded outputs are bit-identical
+    to rld_bgmv_shrink + rld_bgmv_expand_fold (three launches), base rows,
+    absent slots and slots past max_loras included."""
+    dev = require_gpu()
+    n, k_in, n_out, R_, L, ranks, absent, zipf, oob = case
+    wl = W.bgmv_custom(21, n, k_in, n_out, R_, L, ranks, base_frac=0.1, absent=absent, zipf=zipf)
+    if oob:
+        seq = wl.seq_slot.copy()
+        seq[::9] = L + 3  # past the table: base rows
+        wl = dataclasses.replace(wl, seq_slot=seq)
+    say(f"case: one-pass vs three launches {case}")
+    one, three = BgmvRun(wl, dev), BgmvRun(wl, dev)
+    assert R.rld_bgmv_launches(one.routes[0].route, n) == 1
+    one.run_all()
+    three.run_all(two_stage=True)
+    assert np.array_equal(one.xa_by_call[0], three.xa_by_call[0]), "xa"
+    assert np.array_equal(one.outputs()["out"], three.outputs()["out"]), "folded outputs"
+    compare_bgmv(one, str(case))
+    _base_rows_xa_zero(wl, one)
+
+
+def test_bgmv_onepass_multi_equals_three_launches():
+    """rld_bgmv_multi over the attention decode's q, k and v (one launch in the
+    one-pass form) against each route through the two stage entry points."""
+    dev = require_gpu()
+    wl = W.bgmv_attn_decode()
+    idx = [i for i, c in enumerate(wl.calls) if c.module in ("q", "k", "v")]
+    say("case: one-pass multi q/k/v vs three launches per route")
+    multi = BgmvRun(wl, dev)
+    assert R.rld_bgmv_launches([multi.routes[i].route for i in idx], wl.n) == 1
+    xa_multi = multi.run_multi(idx)
+    three = BgmvRun(wl, dev)
+    for i, xm in zip(idx, xa_multi):
+        three.run_call_two_stage(i)
+        torch.cuda.synchronize()
+        c = wl.calls[i]
+        xt = from_device_u16(three.xa)[: wl.n * c.max_rank].reshape(wl.n, c.max_rank)
+        assert np.array_equal(xm, xt), f"xa of {c.module}"
+    o_m, o_t = multi.outputs(), three.outputs()
+    for k in o_m:
+        assert np.array_equal(o_m[k], o_t[k]), f"buffer {k}"
+
+
 def test_bgmv_batched_equals_single_rows():
     """BGMV over n rows is bit-identical to n calls with n = 1 on offset
     pointers (xa and folded output)."""
