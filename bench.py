@@ -129,8 +129,13 @@ def _kernel_key(name):
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` in `workload` from the committed
     counter summary in profiles/ (calibrated FETCH_SIZE + WRITE_SIZE), or None
-    when there is none for this workload and the current kernel sources."""
+    when there is none for this workload and the current kernel sources.  A
+    label "a+b" (a call's two launches, as the shrink and its chunk reduce)
+    sums the two kernels' figures."""
     import glob
+    if "+" in kernel:
+        parts = [measured_traffic(k, workload) for k in kernel.split("+")]
+        return None if any(p is None for p in parts) else int(sum(parts))
     digest = source_digest()
     for f in sorted(glob.glob(os.path.join(PROFILES, "*counters*.md"))):
         with open(f) as fh:
@@ -816,6 +821,21 @@ def run_gpu(args, traffic=True):
                "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         if tag == "grouped":
             ent["mfma_util"] = round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)
+        # the workload's dominant kernel against the HBM roofline (its launches
+        # of this workload; per-launch time from the back-to-back timing)
+        wk = {}
+        for c in calls:
+            k = wk.setdefault(c[1], [0, 0])
+            k[0] += 1
+            k[1] += int(c[3])
+        kn, (nl, kb) = max(wk.items(), key=lambda kv: kernel_ms[kv[0]] * kv[1][0])
+        kach = kb / nl / (kernel_ms[kn] * 1e-3) / 1e9
+        ent["roofline"] = {"bound": "hbm", "kernel": kn, "achieved": round(kach, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(kach / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic(kn, args.workload) if traffic else None,
+                           "algo_bytes_per_launch": int(kb / nl),
+                           "avg_launch_us": round(kernel_ms[kn] * 1e3, 3), "launches": nl}
         per_workload[tag] = ent
 
     kern_out = {k: {"launches_per_step": v["launches"],
