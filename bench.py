@@ -266,10 +266,12 @@ MAX_LANES = 3
 # workloads whose first group of folds is one rld_bgmv_multi call
 MULTI_TAGS = {"attn"}
 # A whole decoder layer ("layer<i>" workloads of the multi-layer decode step):
-# q/k/v (one rld_bgmv_multi call), then o, then gate and up on two branches,
-# then down.  Layers follow each other.
+# q/k/v (one rld_bgmv_multi call), then o, then gate, then up, then down;
+# layers follow each other.  (Gate and up are independent, but at n = 64 and
+# rank 16 their kernels on two graph branches cost the 36-layer step 2.31 ms
+# against 2.16 ms on one: the branches' cross-queue waits outweigh the overlap.)
 LAYER_LANES = {"q": (0, 0), "k": (0, 1), "v": (0, 2), "o": (1, 0),
-               "gate": (2, 0), "up": (2, 1), "down": (3, 0)}
+               "gate": (2, 0), "up": (2, 0), "down": (3, 0)}
 
 
 def grouped_shrink_kernel(k_in, max_rank):
@@ -866,7 +868,7 @@ def run_gpu(args, traffic=True):
 
 def run_model(args):
     """The multi-layer decode step: every layer's folds captured in one graph
-    (q/k/v, o, gate and up on two branches, down; layers in order), the xa
+    (q/k/v, o, gate, up, down; layers in order), the xa
     arena and workspaces shared by all layers, replayed K times.  Its adapter
     pools (about 1.3 GB) are five times the 256 MB MALL, so replays stream
     from HBM."""
