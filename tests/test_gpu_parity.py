@@ -343,11 +343,13 @@ def test_bgmv_shared_workspace_second_pass():
 
 # ------------------------------------------------------------------ gather ---
 
-@pytest.mark.parametrize("variant", ["config", "null_adapter", "ragged", "ragged_rank16"])
+@pytest.mark.parametrize("variant", ["config", "null_adapter", "ragged", "ragged_rank16",
+                                     "many_pairs"])
 def test_moe_gather(variant):
     """The gather fold against the oracle: the MoE decode config, no row_adapter,
     and ragged shapes with out-of-range expert ids and slots (rank 24: the
-    general kernel path; rank 16 with k_in 1000: the three-round path)."""
+    general kernel path; rank 16 with k_in 1000: the three-round path), and a
+    route of 1152 (slot, expert) pairs at the decode shape."""
     dev = require_gpu()
     if variant == "config":
         wl = W.moe_gather()
@@ -361,6 +363,10 @@ def test_moe_gather(variant):
                           max_loras=5, n_adapted=25, ranks=(8, 24), max_rank=24)
         wl.indices[3] = -1
         wl.indices[10] = 999
+        ra = "wl"
+    elif variant == "many_pairs":
+        wl = W.moe_gather(num_tokens=24, top_k=8, num_experts=128, k_in=768, n_out=2048,
+                          max_loras=9, n_adapted=64, max_rank=16)
         ra = "wl"
     else:
         wl = W.moe_gather(num_tokens=13, top_k=6, num_experts=40, k_in=1000, n_out=520,
