@@ -599,7 +599,11 @@ template <int PC, int NTH>
 __device__ __forceinline__ void gs_zero_item(const GsArgs& a, const GsSmem<PC, NTH>& sm,
                                              uint32_t z, uint64_t xa2 = 0) {
   const GroupedRows& g = a.gr;
-  const uint32_t r = a.row_offset + z * NTH + threadIdx.x;
+  // the thread index passes through an empty asm, so that the row addresses
+  // below are computed here and not hoisted into the callers' item loops
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const uint32_t r = a.row_offset + z * NTH + (uint32_t)tid;
   if (r >= a.row_end) return;
   const int e = expert_of_row(sm.off, (int)g.E_off, (int)r);
   bool fold = e >= 0 && (uint32_t)e < g.E;
@@ -684,16 +688,22 @@ constexpr int kXlStride = 32 + 8;                       // LDS row stride of the
 
 // Fused fold of up to 32 rows of a batch (see gs_wide_item): rows[0, nb) of
 // the sorted rows, their xa (BF16, max_rank <= 32 columns) in xl, deltas
-// staged in dl, n_out <= kFuseCols.  Every thread of the 1024 calls it.
-__device__ __forceinline__ void wide_fold_batch(const GsArgs& a, uint64_t out_addr, uint32_t os,
-                                                uint32_t n_out, const int* rows, int nb,
-                                                uint64_t b_addr, float scale, const uint16_t* xl,
-                                                uint16_t* dl) {
-  constexpr int QB = 2;
-  constexpr int kPieces = 16 * QB * (kFuseCols / 8) / kGwThreads;  // 16-byte base pieces per thread
+// staged in dl, n_out <= kFuseCols.  Every thread of the 1024 calls it.  The
+// pass's global operands (each wave's B tiles, the base pieces) go out in
+// wide_fold_issue, which may run ahead of the wave sums that write xl;
+// wide_fold_finish reads xl and folds.
+constexpr int kFoldPieces = 16 * 2 * (kFuseCols / 8) / kGwThreads;  // 16-byte base pieces per thread
+struct FoldOps {
+  uint4 bt[kFuseTiles];
+  uint4 bv[kFoldPieces];
+};
+
+template <bool ISSUE_B = true, bool ISSUE_BASE = true>
+__device__ __forceinline__ void wide_fold_issue(uint64_t out_addr, uint32_t os, uint32_t n_out,
+                                                uint32_t R, const int* rows, int nb,
+                                                uint64_t b_addr, FoldOps& f) {
   const RLD_GLOBAL uint16_t* B = gp<const uint16_t>(b_addr);
-  RLD_GLOBAL uint16_t* out = gp<uint16_t>(out_addr);
-  const uint32_t R = a.R;
+  const RLD_GLOBAL uint16_t* out = gp<const uint16_t>(out_addr);
   // The thread index passes through an empty asm: the fold's per-thread
   // offsets are then computed here, not hoisted to the kernel's start where
   // they would hold registers through the shrink.
@@ -704,64 +714,83 @@ __device__ __forceinline__ void wide_fold_batch(const GsArgs& a, uint64_t out_ad
   const int lg = lane >> 4;
   const int cl = lane & 15;
   const bool kin = (uint32_t)(8 * lg) < R;  // this lane's 8 k of the 32-wide step hold rank
-  // One column chunk (n_out <= kFuseCols), in straight-line code: a loop over
-  // chunks, entered with the xa stores outstanding, waits for them before the
-  // chunk's loads.
-  {
-    constexpr uint32_t cc = 0;
-    // one round: B tiles, base pieces, xa fragments (clamped in-bounds addresses)
-    uint4 bt[kFuseTiles];
+  if (ISSUE_B) {
 #pragma unroll
     for (int t = 0; t < kFuseTiles; ++t) {
-      const uint32_t col = cc + (uint32_t)(wave * kFuseTiles + t) * 16u + cl;
-      bt[t] = load16(B + (size_t)(col < n_out ? col : 0) * R + (kin ? 8 * lg : 0));
+      const uint32_t col = (uint32_t)(wave * kFuseTiles + t) * 16u + cl;
+      f.bt[t] = load16(B + (size_t)(col < n_out ? col : 0) * R + (kin ? 8 * lg : 0));
     }
-    uint4 bv[kPieces];
-#pragma unroll
-    for (int j = 0; j < kPieces; ++j) {
-      const int ei = tid + kGwThreads * j;
-      const int rl = ei / (kFuseCols / 8);
-      const uint32_t col = cc + (uint32_t)(ei % (kFuseCols / 8)) * 8u;
-      bv[j] = load16(out + (size_t)rows[rl < nb ? rl : 0] * os + (col < n_out ? col : cc));
-    }
-    uint4 xf[QB];
-#pragma unroll
-    for (int q = 0; q < QB; ++q)
-      xf[q] = kin ? *reinterpret_cast<const uint4*>(&xl[(q * 16 + cl) * kXlStride + 8 * lg])
-                  : zero16();
-    issue_point();
-    // k past max_rank and columns past n_out contribute nothing
-#pragma unroll
-    for (int t = 0; t < kFuseTiles; ++t) {
-      const uint32_t col = cc + (uint32_t)(wave * kFuseTiles + t) * 16u + cl;
-      if (!kin || col >= n_out) bt[t] = zero16();
-    }
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      if (q * 16 >= nb) continue;
-#pragma unroll
-      for (int t = 0; t < kFuseTiles; ++t) {
-        const floatx4 acc = mfma_bf16_16x16x32(bt[t], xf[q], floatx4{0.f, 0.f, 0.f, 0.f});
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<u32x2*>(
-            &dl[(q * 16 + cl) * kFuseStride + (wave * kFuseTiles + t) * 16 + 4 * lg]) =
-            u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPieces; ++j) {
-      const int ei = tid + kGwThreads * j;
-      const int rl = ei / (kFuseCols / 8);
-      const int c8 = (ei % (kFuseCols / 8)) * 8;
-      const uint32_t col = cc + (uint32_t)c8;
-      if (rl < nb && col < n_out) {
-        const uint4 dv = *reinterpret_cast<const uint4*>(&dl[rl * kFuseStride + c8]);
-        store16(out + (size_t)rows[rl] * os + col, fold8(bv[j], dv, scale));
-      }
-    }
-    __syncthreads();
   }
+  if (ISSUE_BASE) {
+#pragma unroll
+    for (int j = 0; j < kFoldPieces; ++j) {
+      const int ei = tid + kGwThreads * j;
+      const int rl = ei / (kFuseCols / 8);
+      const uint32_t col = (uint32_t)(ei % (kFuseCols / 8)) * 8u;
+      f.bv[j] = load16(out + (size_t)rows[rl < nb ? rl : 0] * os + (col < n_out ? col : 0u));
+    }
+  }
+}
+
+__device__ __forceinline__ void wide_fold_finish(uint64_t out_addr, uint32_t os, uint32_t n_out,
+                                                 uint32_t R, const int* rows, int nb,
+                                                 float scale, FoldOps& f, const uint16_t* xl,
+                                                 uint16_t* dl) {
+  constexpr int QB = 2;
+  RLD_GLOBAL uint16_t* out = gp<uint16_t>(out_addr);
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lg = lane >> 4;
+  const int cl = lane & 15;
+  const bool kin = (uint32_t)(8 * lg) < R;
+  uint4 xf[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q)
+    xf[q] = kin ? *reinterpret_cast<const uint4*>(&xl[(q * 16 + cl) * kXlStride + 8 * lg])
+                : zero16();
+  // k past max_rank and columns past n_out contribute nothing
+#pragma unroll
+  for (int t = 0; t < kFuseTiles; ++t) {
+    const uint32_t col = (uint32_t)(wave * kFuseTiles + t) * 16u + cl;
+    if (!kin || col >= n_out) f.bt[t] = zero16();
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    if (q * 16 >= nb) continue;
+#pragma unroll
+    for (int t = 0; t < kFuseTiles; ++t) {
+      const floatx4 acc = mfma_bf16_16x16x32(f.bt[t], xf[q], floatx4{0.f, 0.f, 0.f, 0.f});
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2*>(
+          &dl[(q * 16 + cl) * kFuseStride + (wave * kFuseTiles + t) * 16 + 4 * lg]) =
+          u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kFoldPieces; ++j) {
+    const int ei = tid + kGwThreads * j;
+    const int rl = ei / (kFuseCols / 8);
+    const int c8 = (ei % (kFuseCols / 8)) * 8;
+    const uint32_t col = (uint32_t)c8;
+    if (rl < nb && col < n_out) {
+      const uint4 dv = *reinterpret_cast<const uint4*>(&dl[rl * kFuseStride + c8]);
+      store16(out + (size_t)rows[rl] * os + col, fold8(f.bv[j], dv, scale));
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void wide_fold_batch(const GsArgs& a, uint64_t out_addr, uint32_t os,
+                                                uint32_t n_out, const int* rows, int nb,
+                                                uint64_t b_addr, float scale, const uint16_t* xl,
+                                                uint16_t* dl) {
+  FoldOps f;
+  wide_fold_issue(out_addr, os, n_out, a.R, rows, nb, b_addr, f);
+  issue_point();
+  wide_fold_finish(out_addr, os, n_out, a.R, rows, nb, scale, f, xl, dl);
 }
 
 // A projection of a wide launch: its xa and output, and the table entries the
@@ -848,8 +877,11 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
       for (int pi = 0; pi < NP; ++pi) {
       const WideProj& P = pj[pi];
       if (NP > 1 && !((sm.valid[pair] >> pi) & 1)) {
-        // this projection does not adapt the pair: zero xa rows
-        for (int t = threadIdx.x; t < nb * (int)(R / 8); t += kGwThreads)
+        // this projection does not adapt the pair: zero xa rows (thread index
+        // through an empty asm: these addresses are not hoisted out of the loops)
+        int t0 = (int)threadIdx.x;
+        asm volatile("" : "+v"(t0));
+        for (int t = t0; t < nb * (int)(R / 8); t += kGwThreads)
           store16(gp<uint16_t>(P.xa_) +
                       (size_t)((uint32_t)sm.list[b0 + t / (int)(R / 8)] - a.row_offset) * R +
                       8 * (t % (int)(R / 8)),
@@ -904,12 +936,23 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
         if (!full) mask_x(x2);
         mfma_x(x2, 2);
       }
+      // the fold's first 32-row pass: its B tiles and base values go out now,
+      // so that their round trip overlaps the wave sums
+      FoldOps f0;
+      issue_point();  // after the MFMAs' wave sums are stored
+      if (FUSE)
+        wide_fold_issue<true, false>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32),
+                                     P.btab[pair], f0);
+      issue_point();
       __syncthreads();
       // one thread per (subtile, column tile, lane): the 16 wave sums in wave order
-      if (threadIdx.x < QB * NT * kWave && (int)(threadIdx.x / (NT * kWave)) * 16 < nb) {
-        const int q = threadIdx.x / (NT * kWave);
-        const int j = (threadIdx.x / kWave) % NT;
-        const int ln = threadIdx.x & 63;
+      // (thread index through an empty asm: the xa addresses are computed here)
+      int ts = (int)threadIdx.x;
+      asm volatile("" : "+v"(ts));
+      if (ts < QB * NT * kWave && (ts / (NT * kWave)) * 16 < nb) {
+        const int q = ts / (NT * kWave);
+        const int j = (ts / kWave) % NT;
+        const int ln = ts & 63;
         const uint32_t col = 16u * j + (ln & 15);
         floatx4 sum = red[0][q * NT + j][ln];
 #pragma unroll
@@ -931,8 +974,11 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
       if (FUSE) {
         // 32 rows a pass: the rows past 32 of a batch are a second pass
         uint16_t* dl = reinterpret_cast<uint16_t*>(&red[0][0][0]);
-        wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0, min(nb, 32), P.btab[pair],
-                        P.bscale[pair], xl, dl);
+        wide_fold_issue<false, true>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32),
+                                     P.btab[pair], f0);
+        issue_point();
+        wide_fold_finish(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32), P.bscale[pair],
+                         f0, xl, dl);
         if (QB > 2 && nb > 32)
           wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0 + 32, nb - 32, P.btab[pair],
                           P.bscale[pair], xl + 32 * kXlStride, dl);
