@@ -46,13 +46,15 @@ constexpr int kExpRows = 64;     // rows per fold pass of the expand
 // Shape of a shrink block of NW waves: KS K steps per wave, batches of QT
 // 16-row subtiles (the x fragments of a batch are QT * KS = 16 per lane either
 // way), and MR subtiles per round of the wave reduce in LDS.
-template <int NT, int NW>
+template <int NT, int NW, int QTO = 0>
 struct ShrinkShape {
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static constexpr int kThreads = NW * kWave;
   static constexpr int KS = kChunkSteps / NW;
-  static constexpr int QT = 16 / KS;
-  static constexpr int MR = NW * NT * 4 <= 64 ? 4 : 2;
+  static constexpr int QT = QTO ? QTO : 16 / KS;
+  // 64-row batches (QTO = 4) keep the LDS of two subtiles' wave sums, so that
+  // three blocks share a CU
+  static constexpr int MR = QTO ? 2 : (NW * NT * 4 <= 64 ? 4 : 2);
   static_assert(KS * NW * 32 >= 512, "a chunk is at most 512 elements");
 };
 
@@ -80,11 +82,11 @@ struct BgmvArgs {
   __device__ RLD_GLOBAL uint16_t* out() const { return gp<uint16_t>(out_); }
 };
 
-template <int NT, int NW>
+template <int NT, int NW, int QTO = 0>
 struct ShrinkSmem {
   int rows[kListCap];
   int wcount[NW];
-  floatx4 red[NW][ShrinkShape<NT, NW>::MR * NT][kWave];
+  floatx4 red[NW][ShrinkShape<NT, NW, QTO>::MR * NT][kWave];
 };
 
 // Expand item of 64*MT output columns (16*MT per wave).
@@ -200,9 +202,9 @@ __device__ __forceinline__ int dense_tile_rows(uint32_t r0, uint32_t n, int tile
 
 // Shrink item w (slot-major over (slot, chunk, column group)); the group
 // covers xa columns [16*NT*cg, 16*NT*(cg+1)).
-template <int NT, int NW>
-__device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT, NW>& sm) {
-  using SS = ShrinkShape<NT, NW>;
+template <int NT, int NW, int QTO = 0>
+__device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT, NW, QTO>& sm) {
+  using SS = ShrinkShape<NT, NW, QTO>;
   constexpr int NTH = SS::kThreads, KS = SS::KS, QT = SS::QT, MR = SS::MR;
   const uint32_t n = a.n, R = a.R, nchunks = a.nch, ncg = a.ncg;
   const uint32_t cg = w % ncg;
@@ -317,19 +319,23 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT, NW>& s
         }
       }
       __syncthreads();
+      // (the lane index through an empty asm: the store addresses below are
+      // computed here, not hoisted out of the batch and held)
+      int tl = lane;
+      asm volatile("" : "+v"(tl));
 #pragma unroll
       for (int p = wave; p < MR * NT; p += NW) {
         const int qq = p / NT, j = p % NT;
         const int q = h * MR + qq;
         if (q < nmt) {
-          const uint32_t col = col0 + 16u * j + cl;
+          const uint32_t col = col0 + 16u * j + (uint32_t)(tl & 15);
           floatx4 sum = sm.red[0][p][lane];
 #pragma unroll
           for (int v = 1; v < NW; ++v) sum += sm.red[v][p][lane];
           if (col < R) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int li = q * 16 + 4 * lg + i;
+              const int li = q * 16 + 4 * (tl >> 4) + i;
               if (li < nb) {
                 const uint32_t row = (uint32_t)sm.rows[b0 + li];
                 if (nchunks == 1)
@@ -345,12 +351,14 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT, NW>& s
     }
   };
 
-  if (a.dense) {
-    constexpr int kTile = dense_shrink_rows(NW);
-    static_assert(kTile == QT * 16, "an unrouted tile is one batch");
-    const int cnt = dense_tile_rows((uint32_t)s * kTile, n, kTile, sm.rows);
-    batch(0, cnt);
-    return;
+  if constexpr (QTO == 0) {
+    if (a.dense) {
+      constexpr int kTile = dense_shrink_rows(NW);
+      static_assert(kTile == QT * 16, "an unrouted tile is one batch");
+      const int cnt = dense_tile_rows((uint32_t)s * kTile, n, kTile, sm.rows);
+      batch(0, cnt);
+      return;
+    }
   }
   // The usual case, straight-line: at most NTH rows (their seq_slot entries
   // are key0, so the scan issues no load that would wait behind the A tile)
@@ -741,14 +749,15 @@ __device__ void onepass_item(const BgmvArgs& a, int s, uint32_t j0, bool xa_writ
   }
 }
 
-template <int NT, int NW>
-__global__ __launch_bounds__(NW * kWave) void bgmv_shrink_kernel(BgmvArgs a, uint32_t total) {
-  __shared__ ShrinkSmem<NT, NW> sm;
+template <int NT, int NW, int QTO = 0>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(QTO ? 6 : 1)))
+void bgmv_shrink_kernel(BgmvArgs a, uint32_t total) {
+  __shared__ ShrinkSmem<NT, NW, QTO> sm;
   // the column groups of one (slot, chunk) share an XCD, and so the x rows in
   // its L2
   const uint32_t w = xcd_group_item(a.ncg);
   if (w >= total) return;
-  shrink_item<NT, NW>(a, w, sm);
+  shrink_item<NT, NW, QTO>(a, w, sm);
 }
 
 // k split: xa[row, 4 columns] = bf16(sum over chunks, in chunk order, of the
@@ -956,8 +965,18 @@ static BgmvMultiKernel pick_expand_multi(uint32_t R) {
 typedef void (*ShrinkKernel)(BgmvArgs, uint32_t);
 typedef void (*ShrinkMultiKernel)(BgmvMulti, uint32_t);
 
+// Routed eight-wave calls with k_in above 4096 (the FFN down projection: 1536
+// items of 24 chunks) take 64-row batches and a two-subtile wave-sum round:
+// 80 registers and 35 KB of LDS, three blocks a CU instead of two, so the
+// items run in two rounds instead of three.  Batching does not enter a row's
+// sums, so the results are the same bits.
+static bool shrink_rows64(uint32_t k_in, uint32_t nt, uint32_t nw) {
+  return nw == 8 && nt == 2 && k_in > 4096u;
+}
+
 // Shrink kernel of (column tiles per item, waves per block).
-static ShrinkKernel pick_shrink(uint32_t nt, uint32_t nw) {
+static ShrinkKernel pick_shrink(uint32_t nt, uint32_t nw, bool rows64 = false) {
+  if (rows64) return bgmv_shrink_kernel<2, 8, 4>;
   if (nw == 8) return nt == 4 ? bgmv_shrink_kernel<4, 8> : bgmv_shrink_kernel<2, 8>;
   return nt == 1 ? bgmv_shrink_kernel<1, 4>
                  : (nt == 2 ? bgmv_shrink_kernel<2, 4> : bgmv_shrink_kernel<4, 4>);
@@ -1030,7 +1049,8 @@ extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(xcd_group_grid(total, a.ncg));
   const uint32_t nw = bgmv_shrink_waves(a.k_in, a.R);
-  hipLaunchKernelGGL(pick_shrink(bgmv_nt(a.R), nw), grid, dim3(nw * kWave), 0, hs, a, total);
+  hipLaunchKernelGGL(pick_shrink(bgmv_nt(a.R), nw, shrink_rows64(a.k_in, bgmv_nt(a.R), nw)),
+                     grid, dim3(nw * kWave), 0, hs, a, total);
   if ((st = launch_status())) return st;
   if (a.nch > 1) {
     hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(n * (a.R / 4), kReduceThreads)),
