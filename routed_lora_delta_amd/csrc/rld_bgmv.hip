@@ -130,11 +130,18 @@ constexpr int kOpChunk = 256;      // the k-split chunk at max_rank <= 16
 constexpr int kOpMaxRows = 256;    // n of the calls that take this path
 struct OnePassSmem {
   static constexpr int kStride = kOpCols + 8;
+  static constexpr int kStageRow = 33;  // uint4 per staged A row (32 + 1: no bank conflicts)
   int rows[kOpMaxRows];
   int wcount[kOpWaves];
-  floatx4 red[kOpWaves][kWave];                    // chunk sums of a 16-row batch
   __attribute__((aligned(16))) uint16_t xs[16 * 16];  // the batch's xa, row-major
-  __attribute__((aligned(16))) uint16_t dl[16 * kStride];
+  union {
+    // each wave's chunk of the A tile (16 rows x 512 bytes), staged once
+    uint4 stage[kOpWaves][16 * kStageRow];
+    struct {
+      floatx4 red[kOpWaves][kWave];  // chunk sums of a 16-row batch
+      __attribute__((aligned(16))) uint16_t dl[16 * kStride];
+    } w;
+  } u;
 };
 
 __device__ __forceinline__ bool slot_active(const BgmvArgs& a, int s) {
@@ -661,15 +668,21 @@ __device__ void onepass_item(const BgmvArgs& a, int s, uint32_t j0, bool xa_writ
   const uint32_t kb = c * a.kc;
   const uint32_t ke = has_chunk ? min(kb + a.kc, k_in) : kb;
   const uint32_t nsteps = has_chunk ? (ke - kb + 31) / 32 : 0;
-  // A fragments of the chunk's 8 steps (column cl of xa, clamped like the shrink)
-  const RLD_GLOBAL uint16_t* Arow = A + (size_t)(cl < (int)R ? cl : 0) * k_in;
-  uint4 af[8];
+  // The chunk's A tile (rows 0..15 of A_s, the xa columns, clamped past
+  // max_rank like the shrink) in the contiguous shape: load i takes rows 2i
+  // and 2i + 1, a lane 16 bytes of one row's 512.  From L2 (the tile's later
+  // readers are the slot's other column groups) this shape arrives about three
+  // times faster than the MFMA fragments' 16 rows x 64 bytes; the tile goes
+  // through this wave's LDS region into the fragments.
+  uint4 araw[8];
+  {
+    const uint32_t kof = kb + (uint32_t)(lane & 31) * 8u;
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const uint32_t kof = kb + st * 32 + lg * 8;
-    const bool ok = (uint32_t)st < nsteps && kof < ke;
-    af[st] = load16((cl < (int)R && ok) ? Arow + kof : A + (has_chunk ? kb : 0));
-    if (!ok) af[st] = zero16();
+    for (int i = 0; i < 8; ++i) {
+      const int r = 2 * i + (lane >> 5);
+      const RLD_GLOBAL uint16_t* ar = A + (size_t)(r < (int)R ? r : 0) * k_in;
+      araw[i] = load16(kof < ke ? ar + kof : A);
+    }
   }
   // B rows of this wave's 32 output columns as MFMA A operands (one K step:
   // max_rank <= 16 < 32), clamped like the expand
@@ -686,23 +699,46 @@ __device__ void onepass_item(const BgmvArgs& a, int s, uint32_t j0, bool xa_writ
   const int c8 = (threadIdx.x & 63) * 8;
   const bool fcol_ok = j0 + c8 < n_out;
 
+  // x fragments of a batch's rows (row cl) for the chunk's steps; base values
+  uint4 xf[8];
+  uint4 bv;
+  auto load_batch = [&](int b0) {
+    const int nb = min(cnt - b0, 16);
+    const bool ok = cl < nb;
+    const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)(ok ? sm.rows[b0 + cl] : 0) * a.xs;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const uint32_t kof = kb + st * 32 + lg * 8;
+      xf[st] = (ok && (uint32_t)st < nsteps && kof < ke) ? load16(xr + kof) : zero16();
+    }
+    bv = (frow < nb && fcol_ok) ? load16(a.out() + (size_t)sm.rows[b0 + frow] * os + j0 + c8)
+                                : zero16();
+  };
+  load_batch(0);
+  issue_point();
+  // A fragments of the chunk's 8 steps from the staged tile (zero past the
+  // chunk, as the shrink's masked steps); then every wave has its fragments and
+  // the staging region is free for the wave sums and the delta tile
+  uint4 af[8];
+  {
+    uint4* stg = sm.u.stage[wave];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) stg[(2 * i + (lane >> 5)) * OnePassSmem::kStageRow + (lane & 31)] = araw[i];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const uint32_t kof = kb + st * 32 + lg * 8;
+      const bool ok = (uint32_t)st < nsteps && kof < ke;
+      af[st] = ok ? stg[cl * OnePassSmem::kStageRow + st * 4 + lg] : zero16();
+    }
+  }
+  __syncthreads();
+
   for (int b0 = 0; b0 < cnt; b0 += 16) {
     const int nb = min(cnt - b0, 16);
-    // x fragments of the batch's rows (row cl) for the chunk's steps; base values
-    uint4 xf[8];
-    {
-      const bool ok = cl < nb;
-      const RLD_GLOBAL uint16_t* xr = a.x() + (size_t)(ok ? sm.rows[b0 + cl] : 0) * a.xs;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const uint32_t kof = kb + st * 32 + lg * 8;
-        xf[st] = (ok && (uint32_t)st < nsteps && kof < ke) ? load16(xr + kof) : zero16();
-      }
+    if (b0 > 0) {
+      load_batch(b0);
+      issue_point();
     }
-    const uint4 bv = (frow < nb && fcol_ok)
-                         ? load16(a.out() + (size_t)sm.rows[b0 + frow] * os + j0 + c8)
-                         : zero16();
-    issue_point();
     // the shrink's four wave chains of chunk c and their wave-order sum
     floatx4 part = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -715,13 +751,13 @@ __device__ void onepass_item(const BgmvArgs& a, int s, uint32_t j0, bool xa_writ
       }
       part = w == 0 ? acc : part + acc;
     }
-    sm.red[wave][lane] = part;
+    sm.u.w.red[wave][lane] = part;
     __syncthreads();
     // chunk sums in chunk order, rounded: xa[row 4g+i][col] of lane (g, col)
     if (threadIdx.x < 256) {
       const int l = threadIdx.x >> 2, i = threadIdx.x & 3;
-      float sum = sm.red[0][l][i];
-      for (uint32_t cc = 1; cc < a.nch; ++cc) sum = sum + sm.red[cc][l][i];
+      float sum = sm.u.w.red[0][l][i];
+      for (uint32_t cc = 1; cc < a.nch; ++cc) sum = sum + sm.u.w.red[cc][l][i];
       const int row = 4 * (l >> 4) + i, col = l & 15;
       const uint16_t v = (uint16_t)f32_to_bf16(sum);
       sm.xs[row * 16 + col] = v;
@@ -737,12 +773,12 @@ __device__ void onepass_item(const BgmvArgs& a, int s, uint32_t j0, bool xa_writ
     for (int m = 0; m < 2; ++m) {
       const floatx4 acc = mfma_bf16_16x16x32(aop[m], bop, floatx4{0.f, 0.f, 0.f, 0.f});
       // lane holds delta[row cl][cols m*16 + 4*lg .. +3] of this wave's slice
-      *reinterpret_cast<uint2*>(&sm.dl[cl * kStride + wave * 32 + m * 16 + 4 * lg]) =
+      *reinterpret_cast<uint2*>(&sm.u.w.dl[cl * kStride + wave * 32 + m * 16 + 4 * lg]) =
           make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
     }
     __syncthreads();
     if (frow < nb && fcol_ok) {
-      const uint4 dv = *reinterpret_cast<const uint4*>(&sm.dl[frow * kStride + c8]);
+      const uint4 dv = *reinterpret_cast<const uint4*>(&sm.u.w.dl[frow * kStride + c8]);
       store16(a.out() + (size_t)sm.rows[b0 + frow] * os + j0 + c8, fold8(bv, dv, scale));
     }
     __syncthreads();
