@@ -866,6 +866,19 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
     load_a_to(bop, pj[0].atab);
     issue_point();
   }
+  // MERGED: both projections of a pair kernel adapt the pair (a code path of
+  // its own, so that the second projection's A tiles, which go out before the
+  // row scan, hold registers only there)
+  auto run = [&](auto merged_tag) {
+  constexpr bool MERGED = decltype(merged_tag)::value;
+  uint4 a1[MERGED ? NT : 1][KS];
+  bool a_loaded = false;
+  if constexpr (MERGED) {
+    load_a_to(bop, pj[0].atab);
+    load_a_to(a1, pj[NP - 1].atab);
+    issue_point();
+    a_loaded = true;
+  }
   bool masked = full || FUSE;
   uint32_t c0 = lo;
   while (c0 < hi) {
@@ -949,16 +962,18 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
           wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0 + 32, nb - 32, P.btab[pair],
                           P.bscale[pair], xl + 32 * kXlStride, dl);
       };
-      if constexpr (NP > 1 && FUSE) {
-        if ((sm.valid[pair] & 3) == 3) {
+      if constexpr (MERGED) {
+        {
           // Both projections adapt the pair: one pass over the batch's x rows
           // runs the chains of both (each the chain the projection alone runs),
           // the first projection's go to the wave-sum buffer, the second's stay
           // in registers through the first one's sums and fold.
-          uint4 a1[NT][KS];
           floatx4 acc1[QB][NT];
-          load_a_to(bop, pj[0].atab);
-          load_a_to(a1, pj[1].atab);
+          if (!a_loaded) {
+            load_a_to(bop, pj[0].atab);
+            load_a_to(a1, pj[1].atab);
+          }
+          a_loaded = false;
           auto mfma_both = [&](const uint4 (&v)[KS], int q) {
 #pragma unroll
             for (int j = 0; j < NT; ++j) red[wave][q * NT + j][lane] = chain(v, bop[j]);
@@ -987,6 +1002,12 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
             if (!full) mask_x(x2);
             mfma_both(x2, 2);
           }
+          // the A tiles are dead until the next batch reloads them: constants
+          // here, so that they hold no registers through the sums and folds
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) bop[j][ks] = a1[j][ks] = zero16();
           FoldOps f0;
           issue_point();
           wide_fold_issue<true, false>(pj[0].out_, pj[0].os, pj[0].n_out, R, sm.list + b0,
@@ -1014,7 +1035,7 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
           fold(pj[1], f1);
           continue;
         }
-      }
+      } else {
 #pragma unroll
       for (int pi = 0; pi < NP; ++pi) {
         const WideProj& P = pj[pi];
@@ -1067,8 +1088,14 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
         __syncthreads();
         if (FUSE) fold(P, f0);
       }
+      }
     }
   }
+  };
+  if (NP > 1 && FUSE && (sm.valid[pair] & 3) == 3)
+    run(std::integral_constant<bool, (NP > 1 && FUSE)>{});
+  else
+    run(std::integral_constant<bool, false>{});
 }
 
 // Items of the wide kernels: pair halves in groups of 8 pairs, then row blocks.
