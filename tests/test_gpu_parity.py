@@ -608,17 +608,25 @@ def _pair_run(wl, pa, pb, dev, cap, ra="wl"):
     return xas, base_a.body(), base_b.body()
 
 
-@pytest.mark.parametrize("case", ["full", "small", "small_null", "fallback"])
+@pytest.mark.parametrize("case", ["full", "small", "small_null", "fallback", "long"])
 def test_moe_grouped_pair_equals_two_calls(case):
     """rld_moe_grouped_pair on a gate/up pair equals rld_moe_grouped on each
     projection, bit for bit (every window's xa and both folded outputs).  The
     two projections adapt independent expert subsets, so some pairs fold in one
     of them only.  full: the MoE prefill at full size (one launch per window);
     small: k_in 2048 at n_out 264 (one launch); small_null: without
-    row_adapter; fallback: k_in 520 (two rld_moe_grouped calls)."""
+    row_adapter; fallback: k_in 520 (two rld_moe_grouped calls); long: pairs
+    of hundreds of rows that both projections adapt (several row batches per
+    item, and expert spans past one 1024-row scan segment)."""
     dev = require_gpu()
     if case == "full":
         wl = W.moe_grouped(projections=("gate", "up"))
+    elif case == "long":
+        wl = W.moe_grouped(9, num_tokens=2400, top_k=2, num_experts=4, hidden=2048, inter=264,
+                           max_loras=2, n_adapted=4, ranks=(8, 16, 32), max_rank=32,
+                           cap=4800, projections=("gate", "up"))
+        spans = np.diff(np.asarray(wl.expert_offsets))
+        assert spans.max() > 1024, spans
     else:
         hidden = 520 if case == "fallback" else 2048
         wl = _small_grouped(seed=8, hidden=hidden, projections=("gate", "up"), cap=700,
