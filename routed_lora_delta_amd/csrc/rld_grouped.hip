@@ -828,16 +828,17 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
   // 128): one pointer per operand row, the steps at immediate offsets.
   // Otherwise clamped in-bounds addresses, and k past k_in zeroed once loaded.
   const bool full = kw0 + 32u * KS <= k_in;
-  // A_{s,e} over the wave's k range serves every batch of the item: it goes
-  // out before the row scan, whose first wait covers it.  The fused kernel
-  // loads it with each batch's x rows instead, so that it is not held through
-  // the fold (which needs those registers).
+  // A_{s,e} over the wave's k range serves every batch of the item: the shrink
+  // kernel issues it before the row scan, whose first wait covers it.  The
+  // fused kernels load it with each batch's x rows instead, so that it is not
+  // held through the fold (which needs those registers); only the merged path
+  // of the pair kernel issues its first batch's tiles before the scan.
   uint4 bop[NT][KS];
   auto load_a_to = [&](uint4 (&dst)[NT][KS], const uint64_t* atab) {
     // the address is read from LDS at each call: computed once and kept, the
     // eight row addresses would hold registers through the fold
-    // (and the lane's offsets from a laundered thread index, so that they are
-    // not hoisted to the kernel's start either)
+    // (the lane's offsets too, from a thread index laundered through an empty
+    // asm, so that they are not hoisted to the kernel's start)
     const RLD_GLOBAL uint16_t* A = gp<const uint16_t>(atab[pair]);
     int tl = (int)threadIdx.x;
     asm volatile("" : "+v"(tl));
@@ -870,227 +871,227 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
   // its own, so that the second projection's A tiles, which go out before the
   // row scan, hold registers only there)
   auto run = [&](auto merged_tag) {
-  constexpr bool MERGED = decltype(merged_tag)::value;
-  uint4 a1[MERGED ? NT : 1][KS];
-  bool a_loaded = false;
-  if constexpr (MERGED) {
-    load_a_to(bop, pj[0].atab);
-    load_a_to(a1, pj[NP - 1].atab);
-    issue_point();
-    a_loaded = true;
-  }
-  bool masked = full || FUSE;
-  uint32_t c0 = lo;
-  while (c0 < hi) {
-    const int cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
-    if (!masked) {
-      mask_a_to(bop);
-      masked = true;
+    constexpr bool MERGED = decltype(merged_tag)::value;
+    uint4 a1[MERGED ? NT : 1][KS];
+    bool a_loaded = false;
+    if constexpr (MERGED) {
+      load_a_to(bop, pj[0].atab);
+      load_a_to(a1, pj[NP - 1].atab);
+      issue_point();
+      a_loaded = true;
     }
-    // half h takes its share of the scanned rows, ceil(cnt / 2) for h = 0
-    const int split = (cnt + 1) / 2;
-    const int bend = h ? cnt : split;
-    for (int b0 = h ? split : 0; b0 < bend; b0 += kRows) {
-      const int nb = min(bend - b0, kRows);
-      // x fragments of 16-row subtile q (clamped rows past nb, k past k_in zeroed)
-      auto load_x = [&](uint4 (&v)[KS], int q) {
-        int tl = (int)threadIdx.x;  // laundered: the offsets are not hoisted
-        asm volatile("" : "+v"(tl));
-        const int li = q * 16 + (tl & 15);
-        const uint32_t xk0 = (uint32_t)(tl >> 6) * (32u * KS) + 8u * ((tl >> 4) & 3);
-        const RLD_GLOBAL uint16_t* xr = x + (size_t)sm.xrow[b0 + (li < nb ? li : 0)] * a.xs;
+    bool masked = full || FUSE;
+    uint32_t c0 = lo;
+    while (c0 < hi) {
+      const int cnt = gs_scan(g, sm, e, s, &c0, hi, a.x_gather);
+      if (!masked) {
+        mask_a_to(bop);
+        masked = true;
+      }
+      // half h takes its share of the scanned rows, ceil(cnt / 2) for h = 0
+      const int split = (cnt + 1) / 2;
+      const int bend = h ? cnt : split;
+      for (int b0 = h ? split : 0; b0 < bend; b0 += kRows) {
+        const int nb = min(bend - b0, kRows);
+        // x fragments of 16-row subtile q (clamped rows past nb, k past k_in zeroed)
+        auto load_x = [&](uint4 (&v)[KS], int q) {
+          int tl = (int)threadIdx.x;  // laundered: the offsets are not hoisted
+          asm volatile("" : "+v"(tl));
+          const int li = q * 16 + (tl & 15);
+          const uint32_t xk0 = (uint32_t)(tl >> 6) * (32u * KS) + 8u * ((tl >> 4) & 3);
+          const RLD_GLOBAL uint16_t* xr = x + (size_t)sm.xrow[b0 + (li < nb ? li : 0)] * a.xs;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint32_t kk = xk0 + 32u * ks;
-          v[ks] = load16(full ? xr + kk : xr + (kk < k_in ? kk : 0));
-        }
-      };
-      auto mask_x = [&](uint4 (&v)[KS]) {
+          for (int ks = 0; ks < KS; ++ks) {
+            const uint32_t kk = xk0 + 32u * ks;
+            v[ks] = load16(full ? xr + kk : xr + (kk < k_in ? kk : 0));
+          }
+        };
+        auto mask_x = [&](uint4 (&v)[KS]) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          if (kw0 + 32u * ks + 8u * lg >= k_in) v[ks] = zero16();
-      };
-      // the wave's chain of subtile q, column tile j: its K steps in order
-      auto chain = [&](const uint4 (&v)[KS], const uint4 (&w)[KS]) {
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int ks = 0; ks < KS; ++ks)
+            if (kw0 + 32u * ks + 8u * lg >= k_in) v[ks] = zero16();
+        };
+        // the wave's chain of subtile q, column tile j: its K steps in order
+        auto chain = [&](const uint4 (&v)[KS], const uint4 (&w)[KS]) {
+          floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(v[ks], w[ks], acc);
-        return acc;
-      };
-      auto mfma_x = [&](const uint4 (&v)[KS], int q) {
+          for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(v[ks], w[ks], acc);
+          return acc;
+        };
+        auto mfma_x = [&](const uint4 (&v)[KS], int q) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) red[wave][q * NT + j][lane] = chain(v, bop[j]);
-      };
-      // one thread per (subtile, column tile, lane): the 16 wave sums in wave
-      // order, rounded, to xl (fused) and the projection's xa rows (thread
-      // index through an empty asm: the xa addresses are computed here)
-      auto wave_sums = [&](const WideProj& P) {
-        int ts = (int)threadIdx.x;
-        asm volatile("" : "+v"(ts));
-        if (ts < QB * NT * kWave && (ts / (NT * kWave)) * 16 < nb) {
-          const int q = ts / (NT * kWave);
-          const int j = (ts / kWave) % NT;
-          const int ln = ts & 63;
-          const uint32_t col = 16u * j + (ln & 15);
-          floatx4 sum = red[0][q * NT + j][ln];
+          for (int j = 0; j < NT; ++j) red[wave][q * NT + j][lane] = chain(v, bop[j]);
+        };
+        // one thread per (subtile, column tile, lane): the 16 wave sums in wave
+        // order, rounded, to xl (fused) and the projection's xa rows (thread
+        // index through an empty asm: the xa addresses are computed here)
+        auto wave_sums = [&](const WideProj& P) {
+          int ts = (int)threadIdx.x;
+          asm volatile("" : "+v"(ts));
+          if (ts < QB * NT * kWave && (ts / (NT * kWave)) * 16 < nb) {
+            const int q = ts / (NT * kWave);
+            const int j = (ts / kWave) % NT;
+            const int ln = ts & 63;
+            const uint32_t col = 16u * j + (ln & 15);
+            floatx4 sum = red[0][q * NT + j][ln];
 #pragma unroll
-          for (int v = 1; v < kGwWaves; ++v) sum += red[v][q * NT + j][ln];
-          if (col < R) {
+            for (int v = 1; v < kGwWaves; ++v) sum += red[v][q * NT + j][ln];
+            if (col < R) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int li = q * 16 + 4 * (ln >> 4) + i;
-              const uint16_t v = (uint16_t)f32_to_bf16(sum[i]);
-              if (FUSE) xl[li * kXlStride + col] = v;
-              if (li < nb) {
-                const uint32_t lr = (uint32_t)sm.list[b0 + li] - a.row_offset;
-                gp<uint16_t>(P.xa_)[(size_t)lr * R + col] = v;
+              for (int i = 0; i < 4; ++i) {
+                const int li = q * 16 + 4 * (ln >> 4) + i;
+                const uint16_t v = (uint16_t)f32_to_bf16(sum[i]);
+                if (FUSE) xl[li * kXlStride + col] = v;
+                if (li < nb) {
+                  const uint32_t lr = (uint32_t)sm.list[b0 + li] - a.row_offset;
+                  gp<uint16_t>(P.xa_)[(size_t)lr * R + col] = v;
+                }
               }
             }
           }
-        }
-      };
-      // the fold of the batch's rows, 32 rows a pass (the B tiles of the first
-      // pass already issued into f)
-      auto fold = [&](const WideProj& P, FoldOps& f) {
-        uint16_t* dl = reinterpret_cast<uint16_t*>(&red[0][0][0]);
-        wide_fold_issue<false, true>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32),
-                                     P.btab[pair], f);
-        issue_point();
-        wide_fold_finish(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32), P.bscale[pair], f,
-                         xl, dl);
-        if (QB > 2 && nb > 32)
-          wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0 + 32, nb - 32, P.btab[pair],
-                          P.bscale[pair], xl + 32 * kXlStride, dl);
-      };
-      if constexpr (MERGED) {
-        {
-          // Both projections adapt the pair: one pass over the batch's x rows
-          // runs the chains of both (each the chain the projection alone runs),
-          // the first projection's go to the wave-sum buffer, the second's stay
-          // in registers through the first one's sums and fold.
-          floatx4 acc1[QB][NT];
-          if (!a_loaded) {
-            load_a_to(bop, pj[0].atab);
-            load_a_to(a1, pj[1].atab);
-          }
-          a_loaded = false;
-          auto mfma_both = [&](const uint4 (&v)[KS], int q) {
-#pragma unroll
-            for (int j = 0; j < NT; ++j) red[wave][q * NT + j][lane] = chain(v, bop[j]);
-#pragma unroll
-            for (int j = 0; j < NT; ++j) acc1[q][j] = chain(v, a1[j]);
-          };
+        };
+        // the fold of the batch's rows, 32 rows a pass (the B tiles of the first
+        // pass already issued into f)
+        auto fold = [&](const WideProj& P, FoldOps& f) {
+          uint16_t* dl = reinterpret_cast<uint16_t*>(&red[0][0][0]);
+          wide_fold_issue<false, true>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32),
+                                       P.btab[pair], f);
+          issue_point();
+          wide_fold_finish(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32), P.bscale[pair], f,
+                           xl, dl);
+          if (QB > 2 && nb > 32)
+            wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0 + 32, nb - 32, P.btab[pair],
+                            P.bscale[pair], xl + 32 * kXlStride, dl);
+        };
+        if constexpr (MERGED) {
           {
-            uint4 xq[2][KS];
-            load_x(xq[0], 0);
-            load_x(xq[1], 1);
+            // Both projections adapt the pair: one pass over the batch's x rows
+            // runs the chains of both (each the chain the projection alone runs),
+            // the first projection's go to the wave-sum buffer, the second's stay
+            // in registers through the first one's sums and fold.
+            floatx4 acc1[QB][NT];
+            if (!a_loaded) {
+              load_a_to(bop, pj[0].atab);
+              load_a_to(a1, pj[1].atab);
+            }
+            a_loaded = false;
+            auto mfma_both = [&](const uint4 (&v)[KS], int q) {
+#pragma unroll
+              for (int j = 0; j < NT; ++j) red[wave][q * NT + j][lane] = chain(v, bop[j]);
+#pragma unroll
+              for (int j = 0; j < NT; ++j) acc1[q][j] = chain(v, a1[j]);
+            };
+            {
+              uint4 xq[2][KS];
+              load_x(xq[0], 0);
+              load_x(xq[1], 1);
+              issue_point();
+              if (!full) {
+                mask_a_to(bop);
+                mask_a_to(a1);
+                mask_x(xq[0]);
+                mask_x(xq[1]);
+              }
+              mfma_both(xq[0], 0);
+              mfma_both(xq[1], 1);
+            }
+            if (QB > 2 && nb > 32) {
+              uint4 x2[KS];
+              issue_point();  // not hoisted above the first subtiles' MFMAs
+              load_x(x2, 2);
+              issue_point();
+              if (!full) mask_x(x2);
+              mfma_both(x2, 2);
+            }
+            // the A tiles are dead until the next batch reloads them: constants
+            // here, so that they hold no registers through the sums and folds
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+              for (int ks = 0; ks < KS; ++ks) bop[j][ks] = a1[j][ks] = zero16();
+            FoldOps f0;
+            issue_point();
+            wide_fold_issue<true, false>(pj[0].out_, pj[0].os, pj[0].n_out, R, sm.list + b0,
+                                         min(nb, 32), pj[0].btab[pair], f0);
+            issue_point();
+            __syncthreads();
+            wave_sums(pj[0]);
+            __syncthreads();
+            fold(pj[0], f0);
+            // the second projection: its chains to the (free again) buffer
+#pragma unroll
+            for (int q = 0; q < QB; ++q)
+              if (q < 2 || nb > 32) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) red[wave][q * NT + j][lane] = acc1[q][j];
+              }
+            FoldOps f1;
+            issue_point();
+            wide_fold_issue<true, false>(pj[1].out_, pj[1].os, pj[1].n_out, R, sm.list + b0,
+                                         min(nb, 32), pj[1].btab[pair], f1);
+            issue_point();
+            __syncthreads();
+            wave_sums(pj[1]);
+            __syncthreads();
+            fold(pj[1], f1);
+            continue;
+          }
+        } else {
+#pragma unroll
+        for (int pi = 0; pi < NP; ++pi) {
+          const WideProj& P = pj[pi];
+          if (NP > 1 && !((sm.valid[pair] >> pi) & 1)) {
+            // this projection does not adapt the pair: zero xa rows (thread index
+            // through an empty asm: these addresses are not hoisted out of the loops)
+            int t0 = (int)threadIdx.x;
+            asm volatile("" : "+v"(t0));
+            for (int t = t0; t < nb * (int)(R / 8); t += kGwThreads)
+              store16(gp<uint16_t>(P.xa_) +
+                          (size_t)((uint32_t)sm.list[b0 + t / (int)(R / 8)] - a.row_offset) * R +
+                          8 * (t % (int)(R / 8)),
+                      zero16());
+            continue;
+          }
+          if (FUSE) load_a_to(bop, P.atab);
+          // Subtiles 0 and 1 go out with A; a third (rows 32..47 of the batch) is
+          // a second round, with A still held, so that the common batch needs no
+          // more registers than two subtiles.
+          {
+            uint4 aop[2][KS];
+            load_x(aop[0], 0);
+            load_x(aop[1], 1);
             issue_point();
             if (!full) {
-              mask_a_to(bop);
-              mask_a_to(a1);
-              mask_x(xq[0]);
-              mask_x(xq[1]);
+              if (FUSE) mask_a_to(bop);
+              mask_x(aop[0]);
+              mask_x(aop[1]);
             }
-            mfma_both(xq[0], 0);
-            mfma_both(xq[1], 1);
+            mfma_x(aop[0], 0);
+            mfma_x(aop[1], 1);
           }
           if (QB > 2 && nb > 32) {
             uint4 x2[KS];
-            issue_point();  // not hoisted above the first subtiles' MFMAs
             load_x(x2, 2);
             issue_point();
             if (!full) mask_x(x2);
-            mfma_both(x2, 2);
+            mfma_x(x2, 2);
           }
-          // the A tiles are dead until the next batch reloads them: constants
-          // here, so that they hold no registers through the sums and folds
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) bop[j][ks] = a1[j][ks] = zero16();
+          // the fold's first 32-row pass: its B tiles go out now, so that their
+          // round trip overlaps the wave sums
           FoldOps f0;
-          issue_point();
-          wide_fold_issue<true, false>(pj[0].out_, pj[0].os, pj[0].n_out, R, sm.list + b0,
-                                       min(nb, 32), pj[0].btab[pair], f0);
-          issue_point();
-          __syncthreads();
-          wave_sums(pj[0]);
-          __syncthreads();
-          fold(pj[0], f0);
-          // the second projection: its chains to the (free again) buffer
-#pragma unroll
-          for (int q = 0; q < QB; ++q)
-            if (q < 2 || nb > 32) {
-#pragma unroll
-              for (int j = 0; j < NT; ++j) red[wave][q * NT + j][lane] = acc1[q][j];
-            }
-          FoldOps f1;
-          issue_point();
-          wide_fold_issue<true, false>(pj[1].out_, pj[1].os, pj[1].n_out, R, sm.list + b0,
-                                       min(nb, 32), pj[1].btab[pair], f1);
+          issue_point();  // after the MFMAs' wave sums are stored
+          if (FUSE)
+            wide_fold_issue<true, false>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32),
+                                         P.btab[pair], f0);
           issue_point();
           __syncthreads();
-          wave_sums(pj[1]);
+          wave_sums(P);
           __syncthreads();
-          fold(pj[1], f1);
-          continue;
+          if (FUSE) fold(P, f0);
         }
-      } else {
-#pragma unroll
-      for (int pi = 0; pi < NP; ++pi) {
-        const WideProj& P = pj[pi];
-        if (NP > 1 && !((sm.valid[pair] >> pi) & 1)) {
-          // this projection does not adapt the pair: zero xa rows (thread index
-          // through an empty asm: these addresses are not hoisted out of the loops)
-          int t0 = (int)threadIdx.x;
-          asm volatile("" : "+v"(t0));
-          for (int t = t0; t < nb * (int)(R / 8); t += kGwThreads)
-            store16(gp<uint16_t>(P.xa_) +
-                        (size_t)((uint32_t)sm.list[b0 + t / (int)(R / 8)] - a.row_offset) * R +
-                        8 * (t % (int)(R / 8)),
-                    zero16());
-          continue;
         }
-        if (FUSE) load_a_to(bop, P.atab);
-        // Subtiles 0 and 1 go out with A; a third (rows 32..47 of the batch) is
-        // a second round, with A still held, so that the common batch needs no
-        // more registers than two subtiles.
-        {
-          uint4 aop[2][KS];
-          load_x(aop[0], 0);
-          load_x(aop[1], 1);
-          issue_point();
-          if (!full) {
-            if (FUSE) mask_a_to(bop);
-            mask_x(aop[0]);
-            mask_x(aop[1]);
-          }
-          mfma_x(aop[0], 0);
-          mfma_x(aop[1], 1);
-        }
-        if (QB > 2 && nb > 32) {
-          uint4 x2[KS];
-          load_x(x2, 2);
-          issue_point();
-          if (!full) mask_x(x2);
-          mfma_x(x2, 2);
-        }
-        // the fold's first 32-row pass: its B tiles go out now, so that their
-        // round trip overlaps the wave sums
-        FoldOps f0;
-        issue_point();  // after the MFMAs' wave sums are stored
-        if (FUSE)
-          wide_fold_issue<true, false>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32),
-                                       P.btab[pair], f0);
-        issue_point();
-        __syncthreads();
-        wave_sums(P);
-        __syncthreads();
-        if (FUSE) fold(P, f0);
-      }
       }
     }
-  }
   };
   if (NP > 1 && FUSE && (sm.valid[pair] & 3) == 3)
     run(std::integral_constant<bool, (NP > 1 && FUSE)>{});
