@@ -898,6 +898,26 @@ def run_model(args):
     gbs = step.bytes / (ms * 1e-3) / 1e9
     pool_bytes = sum(a.A.nbytes + a.B.nbytes for _, wl in wls for c in wl.calls
                      for a in c.adapters)
+    # The same graph with every row routed to the base model (seq_slot -1, the
+    # graph-safe routing upload): every launch, routing scan and zero xa row
+    # stays, no adapter byte is read and nothing folds, so the difference is
+    # the cost of applying the adapters (the pages' no-apply lever, by routing).
+    seqs = list(step.seqs.values())
+    saved = [sq.clone() for sq in seqs]
+    for sq in seqs:
+        sq.fill_(-1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    nf_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    for sq, v in zip(seqs, saved):
+        sq.copy_(v)
+    torch.cuda.synchronize()
     return {"workload": WORKLOAD_NAMES["model"], "layers": len(wls),
             "ms_per_step": round(ms, 5), "us_per_layer": round(ms * 1e3 / len(wls), 3),
             "replay_ms": {"median": round(float(np.median(rep_ms)), 5),
@@ -905,7 +925,11 @@ def run_model(args):
                           "p90": round(float(np.percentile(rep_ms, 90)), 5)},
             "rows_per_step": step.rows, "rows_per_s": round(step.rows / (ms * 1e-3), 1),
             "algo_bytes_per_step": int(step.bytes), "hbm_gbs": round(gbs, 1),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "adapter_bytes": int(pool_bytes)}
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "adapter_bytes": int(pool_bytes),
+            "no_fold": {"ms_per_step": round(nf_ms, 5),
+                        "what": "the same graph with every row routed to the base model "
+                                "(seq_slot -1): launches, routing scans and zero xa rows, no "
+                                "adapter read, no fold"}}
 
 
 # ------------------------------------------------------------- CPU oracle ---
