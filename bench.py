@@ -266,10 +266,11 @@ MAX_LANES = 3
 # workloads whose first group of folds is one rld_bgmv_multi call
 MULTI_TAGS = {"attn"}
 # A whole decoder layer ("layer<i>" workloads of the multi-layer decode step):
-# q/k/v (one rld_bgmv_multi call), then o, then gate, then up, then down;
-# layers follow each other.  (Gate and up are independent, but at n = 64 and
-# rank 16 their kernels on two graph branches cost the 36-layer step 2.31 ms
-# against 2.16 ms on one: the branches' cross-queue waits outweigh the overlap.)
+# q/k/v (one rld_bgmv_multi call), then o, then gate and up (one rld_bgmv_multi
+# call: three launches instead of six, 1.82 against 2.09 ms for the 36-layer
+# step), then down; layers follow each other.  (As two calls on two graph
+# branches gate and up cost the step 2.31 ms against 2.16 ms on one stream: at
+# n = 64 and rank 16 the branches' cross-queue waits outweigh the overlap.)
 LAYER_LANES = {"q": (0, 0), "k": (0, 1), "v": (0, 2), "o": (1, 0),
                "gate": (2, 0), "up": (2, 0), "down": (3, 0)}
 
@@ -357,16 +358,19 @@ class Step:
                 for k, b in bufs.items():
                     self.outputs[f"{tag}.{k}"] = b
                 # the attention's q, k and v folds read the same rows: one
-                # rld_bgmv_multi call for them.  (Gate and up stay two calls on
-                # parallel branches, which overlap each other's launch gaps and
-                # tails: as one call the FFN's cost in the step was 106 us
-                # against 94.)
-                first = [c for c in wl.calls
-                         if (tag in MULTI_TAGS or layer) and lmap.get(c.module, (0, 0))[0] == 0]
-                if len({(c.x_buf, c.x_row_stride, c.k_in, c.max_rank) for c in first}) != 1 \
-                        or len(first) < 2:
-                    first = []
-                if first:
+                # rld_bgmv_multi call for them, and in a decoder layer of the
+                # multi-layer step one for gate and up as well.  (In the step's
+                # FFN workload gate and up stay two calls on parallel branches,
+                # which overlap each other's launch gaps and tails: as one call
+                # the FFN's cost in the step was 106 us against 94.)
+                multi_groups = [0] if tag in MULTI_TAGS else ([0, 2] if layer else [])
+                in_multi = []
+                for mg in multi_groups:
+                    first = [c for c in wl.calls if lmap.get(c.module, (0, 0))[0] == mg]
+                    if len({(c.x_buf, c.x_row_stride, c.k_in, c.max_rank) for c in first}) != 1 \
+                            or len(first) < 2:
+                        continue
+                    in_multi += first
                     c0 = first[0]
                     rts = [DenseRoute(c.adapters, c.max_loras, c.max_rank, c.k_in, c.n_out, dev)
                            for c in first]
@@ -395,7 +399,7 @@ class Step:
                          sb, fl, wl.n * len(first)), c0.module, 0, lanes_map=lmap)
                     self.rows += wl.n * len(first)
                 for c in wl.calls:
-                    if any(c is f for f in first):
+                    if any(c is f for f in in_multi):
                         continue
                     xa, ws = lanes[lmap.get(c.module, (0, 0))[1]]
                     sb, eb, fl, _ = bgmv_bytes(wl, c)
