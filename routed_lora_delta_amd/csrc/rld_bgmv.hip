@@ -38,7 +38,7 @@
 
 namespace rld {
 
-constexpr int kReduceThreads = 256;
+constexpr int kReduceThreads = 64;  // chunk reduce: one-wave blocks, one element a thread
 constexpr int kChunkSteps = 16;  // 32-wide K steps of the longest chunk (512)
 constexpr int kListCap = 512;    // rows collected per pass over seq_slot
 constexpr int kExpRows = 64;     // rows per fold pass of the expand
@@ -796,23 +796,23 @@ void bgmv_shrink_kernel(BgmvArgs a, uint32_t total) {
   shrink_item<NT, NW, QTO>(a, w, sm);
 }
 
-// k split: xa[row, 4 columns] = bf16(sum over chunks, in chunk order, of the
+// k split: xa[row, column] = bf16(sum over chunks, in chunk order, of the
 // partials).  Base rows have zero partials (written by the shrink), so every
-// row is handled alike and no routing is read.  One thread per (row, 4
-// columns); up to kReduceBatch chunk loads go out before their adds.
+// row is handled alike and no routing is read.  One thread per xa element in
+// one-wave blocks, so that the partials' reads spread over many CUs (a call's
+// n*R elements are a few thousand at decode sizes); up to kReduceBatch chunk
+// loads go out before their adds.
 constexpr int kReduceBatch = 24;
 
-// Thread t of a call's reduce: row t / (R/4), columns 4 (t % (R/4)) ..
+// Thread t of a call's reduce: row t / R, column t % R.
 __device__ __forceinline__ void reduce_unit(const BgmvArgs& a, uint32_t t) {
-  const uint32_t q4 = a.R / 4;
-  const uint32_t row = t / q4;
-  const uint32_t col = (t % q4) * 4;
-  const RLD_GLOBAL floatx4* p =
-      reinterpret_cast<const RLD_GLOBAL floatx4*>(a.partial() + (size_t)row * a.R + col);
-  const size_t cstride = (size_t)a.n * a.R / 4;  // floatx4 per chunk
-  floatx4 sum = floatx4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t row = t / a.R;
+  const uint32_t col = t % a.R;
+  const RLD_GLOBAL float* p = a.partial() + (size_t)row * a.R + col;
+  const size_t cstride = (size_t)a.n * a.R;  // floats per chunk
+  float sum = 0.f;
   for (uint32_t c0 = 0; c0 < a.nch; c0 += kReduceBatch) {
-    floatx4 v[kReduceBatch];
+    float v[kReduceBatch];
 #pragma unroll
     for (int j = 0; j < kReduceBatch; ++j) v[j] = p[(c0 + j < a.nch ? c0 + j : c0) * cstride];
     // every load of the batch goes out before the first add (no instruction
@@ -822,14 +822,12 @@ __device__ __forceinline__ void reduce_unit(const BgmvArgs& a, uint32_t t) {
     for (int j = 0; j < kReduceBatch; ++j)
       if (c0 + j < a.nch) sum = (c0 + j == 0) ? v[j] : sum + v[j];
   }
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 o = {pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
-  *reinterpret_cast<RLD_GLOBAL u32x2*>(a.xa() + (size_t)row * a.R + col) = o;
+  a.xa()[(size_t)row * a.R + col] = (uint16_t)f32_to_bf16(sum);
 }
 
 __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_kernel(BgmvArgs a) {
   const uint32_t t = blockIdx.x * kReduceThreads + threadIdx.x;
-  if (t >= a.n * (a.R / 4)) return;
+  if (t >= a.n * a.R) return;
   reduce_unit(a, t);
 }
 
@@ -877,7 +875,7 @@ __global__ __launch_bounds__(NW * kWave) void bgmv_shrink_multi_kernel(BgmvMulti
 }
 
 __global__ __launch_bounds__(kReduceThreads) void bgmv_reduce_multi_kernel(BgmvMulti m) {
-  const uint32_t per = m.a[0].n * (m.a[0].R / 4);  // n and R are shared
+  const uint32_t per = m.a[0].n * m.a[0].R;  // n and R are shared
   const uint32_t t = blockIdx.x * kReduceThreads + threadIdx.x;
   const uint32_t r = t / per;
   if (r >= m.nr) return;
@@ -1079,7 +1077,7 @@ extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x
   if ((st = make_args(route, x, x_row_stride, seq_slot, n, xa, workspace, workspace_bytes,
                       nullptr, 0, &a)))
     return st;
-  if (!launch_fits((uint64_t)route->max_loras * a.nch * a.ncg, (uint64_t)n * (a.R / 4)))
+  if (!launch_fits((uint64_t)route->max_loras * a.nch * a.ncg, (uint64_t)n * a.R))
     return RLD_EUNSUPPORTED;
   const uint32_t total = route->max_loras * a.nch * a.ncg;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -1089,7 +1087,7 @@ extern "C" int rld_bgmv_shrink(const rld_route* route, const void* x, uint32_t x
                      grid, dim3(nw * kWave), 0, hs, a, total);
   if ((st = launch_status())) return st;
   if (a.nch > 1) {
-    hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(n * (a.R / 4), kReduceThreads)),
+    hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(n * a.R, kReduceThreads)),
                        dim3(kReduceThreads), 0, hs, a);
     return launch_status();
   }
@@ -1197,7 +1195,7 @@ extern "C" int rld_bgmv_multi(const rld_route* const* routes, uint32_t nroutes, 
     for (uint32_t r = 0; r < nroutes; ++r)
       all += (uint64_t)routes[r]->max_loras * div_ceil(k_in, bgmv_chunk(k_in, R)) *
              div_ceil(R, 16u * bgmv_nt(R));
-    if (!launch_fits(all, (uint64_t)nroutes * n * (R / 4))) return RLD_EUNSUPPORTED;
+    if (!launch_fits(all, (uint64_t)nroutes * n * R)) return RLD_EUNSUPPORTED;
   }
   BgmvMulti m = {};
   m.nr = nroutes;
@@ -1234,7 +1232,7 @@ extern "C" int rld_bgmv_multi(const rld_route* const* routes, uint32_t nroutes, 
   if ((st = launch_status())) return st;
   if (m.a[0].nch > 1) {
     hipLaunchKernelGGL(bgmv_reduce_multi_kernel,
-                       dim3(div_ceil(nroutes * n * (R / 4), kReduceThreads)),
+                       dim3(div_ceil(nroutes * n * R, kReduceThreads)),
                        dim3(kReduceThreads), 0, hs, m);
     if ((st = launch_status())) return st;
   }
@@ -1296,7 +1294,7 @@ extern "C" int rld_lora_shrink(const rld_pair* pair, const void* x, uint32_t x_r
   // the routed calls' wave rule, so a row's sums are added in the same order
   const uint32_t nw = bgmv_shrink_waves(a.k_in, a.R);
   const uint32_t tile = (uint32_t)dense_shrink_rows((int)nw);
-  if (!launch_fits((uint64_t)div_ceil(m, tile) * a.nch * a.ncg, (uint64_t)m * (a.R / 4)))
+  if (!launch_fits((uint64_t)div_ceil(m, tile) * a.nch * a.ncg, (uint64_t)m * a.R))
     return RLD_EUNSUPPORTED;
   const uint32_t total = div_ceil(m, tile) * a.nch * a.ncg;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -1305,7 +1303,7 @@ extern "C" int rld_lora_shrink(const rld_pair* pair, const void* x, uint32_t x_r
                      total);
   if ((st = launch_status())) return st;
   if (a.nch > 1) {
-    hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(m * (a.R / 4), kReduceThreads)),
+    hipLaunchKernelGGL(bgmv_reduce_kernel, dim3(div_ceil(m * a.R, kReduceThreads)),
                        dim3(kReduceThreads), 0, hs, a);
     return launch_status();
   }
