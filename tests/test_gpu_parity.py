@@ -567,7 +567,10 @@ def test_moe_grouped_full_config():
         assert np.array_equal(outs[p.name].reshape(wl.te, p.n_out)[rows_o],
                               p.base.reshape(wl.te, p.n_out)[rows_o]), p.name
         say(f"  {p.name}: {int((~rows_o).sum())} rows folded, {int(rows_o.sum())} untouched")
-    # the bench's step on the same workload, its calls issued eagerly in order
+    # the bench's step on the same workload, its calls issued eagerly in order,
+    # and (fresh buffers) its captured graph replayed once: each window is a
+    # chain on a branch of its own (gate+up, then down, which reuses the
+    # window's xa arena), so a missing edge or a shared buffer would show here
     import bench
     step = bench.Step(dev, [("grouped", wl)])
     for c in step.calls:
@@ -576,6 +579,13 @@ def test_moe_grouped_full_config():
     for p in wl.projections:
         got = from_device_u16(step.outputs[f"grouped.{p.name}"])[: wl.te * p.n_out]
         assert np.array_equal(got, outs[p.name]), f"bench step differs on {p.name}"
+    step2 = bench.Step(dev, [("grouped", wl)])
+    graph = step2.capture(range(len(step2.calls)), torch.cuda.Stream(), parallel=True)
+    graph.replay()
+    torch.cuda.synchronize()
+    for p in wl.projections:
+        got = from_device_u16(step2.outputs[f"grouped.{p.name}"])[: wl.te * p.n_out]
+        assert np.array_equal(got, outs[p.name]), f"bench step graph differs on {p.name}"
 
 
 def _pair_run(wl, pa, pb, dev, cap, ra="wl"):
