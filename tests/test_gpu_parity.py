@@ -618,7 +618,7 @@ def _pair_run(wl, pa, pb, dev, cap, ra="wl"):
     return xas, base_a.body(), base_b.body()
 
 
-@pytest.mark.parametrize("case", ["full", "small", "small_null", "fallback", "long"])
+@pytest.mark.parametrize("case", ["full", "small", "small_null", "fallback", "long", "ragged_k"])
 def test_moe_grouped_pair_equals_two_calls(case):
     """rld_moe_grouped_pair on a gate/up pair equals rld_moe_grouped on each
     projection, bit for bit (every window's xa and both folded outputs).  The
@@ -627,10 +627,16 @@ def test_moe_grouped_pair_equals_two_calls(case):
     small: k_in 2048 at n_out 264 (one launch); small_null: without
     row_adapter; fallback: k_in 520 (two rld_moe_grouped calls); long: pairs
     of hundreds of rows that both projections adapt (several row batches per
-    item, and expert spans past one 1024-row scan segment)."""
+    item, and expert spans past one 1024-row scan segment); ragged_k: k_in
+    2000, not a multiple of the waves' 128-wide k ranges."""
     dev = require_gpu()
     if case == "full":
         wl = W.moe_grouped(projections=("gate", "up"))
+    elif case == "ragged_k":
+        # k_in 2000: the last waves' k ranges end inside k_in or past it (masked
+        # operands), every expert adapted by both projections (one pass for both)
+        wl = _small_grouped(seed=11, hidden=2000, projections=("gate", "up"), cap=700,
+                            n_adapted=16)
     elif case == "long":
         wl = W.moe_grouped(9, num_tokens=2400, top_k=2, num_experts=4, hidden=2048, inter=264,
                            max_loras=2, n_adapted=4, ranks=(8, 16, 32), max_rank=32,
