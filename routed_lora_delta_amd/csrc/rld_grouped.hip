@@ -686,19 +686,21 @@ constexpr int kFuseCols = kGwWaves * kFuseTiles * 16;  // 768
 constexpr int kFuseStride = kFuseCols + 8;             // LDS row stride of the delta tile
 constexpr int kXlStride = 32 + 8;                       // LDS row stride of the xa tile
 
-// Fused fold of up to 32 rows of a batch (see gs_wide_item): rows[0, nb) of
-// the sorted rows, their xa (BF16, max_rank <= 32 columns) in xl, deltas
+// Fused fold of a batch of up to 16*FQ rows (see gs_wide_item): rows[0, nb)
+// of the sorted rows, their xa (BF16, max_rank <= 32 columns) in xl, deltas
 // staged in dl, n_out <= kFuseCols.  Every thread of the 1024 calls it.  The
-// pass's global operands (each wave's B tiles, the base pieces) go out in
+// fold's global operands (each wave's B tiles, the base pieces) go out in
 // wide_fold_issue, which may run ahead of the wave sums that write xl;
 // wide_fold_finish reads xl and folds.
-constexpr int kFoldPieces = 16 * 2 * (kFuseCols / 8) / kGwThreads;  // 16-byte base pieces per thread
+// 16-byte base pieces per thread for a fold of FQ 16-row subtiles
+template <int FQ>
+constexpr int fold_pieces() { return (16 * FQ * (kFuseCols / 8) + kGwThreads - 1) / kGwThreads; }
 struct FoldOps {
   uint4 bt[kFuseTiles];
-  uint4 bv[kFoldPieces];
+  uint4 bv[fold_pieces<3>()];
 };
 
-template <bool ISSUE_B = true, bool ISSUE_BASE = true>
+template <bool ISSUE_B = true, bool ISSUE_BASE = true, int FQ = 2>
 __device__ __forceinline__ void wide_fold_issue(uint64_t out_addr, uint32_t os, uint32_t n_out,
                                                 uint32_t R, const int* rows, int nb,
                                                 uint64_t b_addr, FoldOps& f) {
@@ -723,7 +725,7 @@ __device__ __forceinline__ void wide_fold_issue(uint64_t out_addr, uint32_t os, 
   }
   if (ISSUE_BASE) {
 #pragma unroll
-    for (int j = 0; j < kFoldPieces; ++j) {
+    for (int j = 0; j < fold_pieces<FQ>(); ++j) {
       const int ei = tid + kGwThreads * j;
       const int rl = ei / (kFuseCols / 8);
       const uint32_t col = (uint32_t)(ei % (kFuseCols / 8)) * 8u;
@@ -732,11 +734,12 @@ __device__ __forceinline__ void wide_fold_issue(uint64_t out_addr, uint32_t os, 
   }
 }
 
+template <int FQ = 2>
 __device__ __forceinline__ void wide_fold_finish(uint64_t out_addr, uint32_t os, uint32_t n_out,
                                                  uint32_t R, const int* rows, int nb,
                                                  float scale, FoldOps& f, const uint16_t* xl,
                                                  uint16_t* dl) {
-  constexpr int QB = 2;
+  constexpr int QB = FQ;
   RLD_GLOBAL uint16_t* out = gp<uint16_t>(out_addr);
   int tid = (int)threadIdx.x;
   asm volatile("" : "+v"(tid));
@@ -770,7 +773,7 @@ __device__ __forceinline__ void wide_fold_finish(uint64_t out_addr, uint32_t os,
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kFoldPieces; ++j) {
+  for (int j = 0; j < fold_pieces<FQ>(); ++j) {
     const int ei = tid + kGwThreads * j;
     const int rl = ei / (kFuseCols / 8);
     const int c8 = (ei % (kFuseCols / 8)) * 8;
@@ -781,16 +784,6 @@ __device__ __forceinline__ void wide_fold_finish(uint64_t out_addr, uint32_t os,
     }
   }
   __syncthreads();
-}
-
-__device__ __forceinline__ void wide_fold_batch(const GsArgs& a, uint64_t out_addr, uint32_t os,
-                                                uint32_t n_out, const int* rows, int nb,
-                                                uint64_t b_addr, float scale, const uint16_t* xl,
-                                                uint16_t* dl) {
-  FoldOps f;
-  wide_fold_issue(out_addr, os, n_out, a.R, rows, nb, b_addr, f);
-  issue_point();
-  wide_fold_finish(out_addr, os, n_out, a.R, rows, nb, scale, f, xl, dl);
 }
 
 // A projection of a wide launch: its xa and output, and the table entries the
@@ -950,18 +943,24 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
             }
           }
         };
-        // the fold of the batch's rows, 32 rows a pass (the B tiles of the first
-        // pass already issued into f)
+        // the fold of the batch's rows in one pass (the B tiles already issued
+        // into f): up to 48 rows, whose delta tile (74.5 KB) fits the wave-sum
+        // buffer; batches of up to 32 rows take the two-subtile form
         auto fold = [&](const WideProj& P, FoldOps& f) {
           uint16_t* dl = reinterpret_cast<uint16_t*>(&red[0][0][0]);
-          wide_fold_issue<false, true>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32),
-                                       P.btab[pair], f);
-          issue_point();
-          wide_fold_finish(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32), P.bscale[pair], f,
-                           xl, dl);
-          if (QB > 2 && nb > 32)
-            wide_fold_batch(a, P.out_, P.os, P.n_out, sm.list + b0 + 32, nb - 32, P.btab[pair],
-                            P.bscale[pair], xl + 32 * kXlStride, dl);
+          if (QB > 2 && nb > 32) {
+            wide_fold_issue<false, true, 3>(P.out_, P.os, P.n_out, R, sm.list + b0, nb,
+                                            P.btab[pair], f);
+            issue_point();
+            wide_fold_finish<3>(P.out_, P.os, P.n_out, R, sm.list + b0, nb, P.bscale[pair], f, xl,
+                                dl);
+          } else {
+            wide_fold_issue<false, true, 2>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32),
+                                            P.btab[pair], f);
+            issue_point();
+            wide_fold_finish<2>(P.out_, P.os, P.n_out, R, sm.list + b0, min(nb, 32), P.bscale[pair],
+                                f, xl, dl);
+          }
         };
         if constexpr (MERGED) {
           {
@@ -1076,8 +1075,8 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
             if (!full) mask_x(x2);
             mfma_x(x2, 2);
           }
-          // the fold's first 32-row pass: its B tiles go out now, so that their
-          // round trip overlaps the wave sums
+          // the fold's B tiles go out now, so that their round trip overlaps
+          // the wave sums
           FoldOps f0;
           issue_point();  // after the MFMAs' wave sums are stored
           if (FUSE)
@@ -1139,12 +1138,12 @@ template <int NT, int PC, int NP>
 __device__ __forceinline__ void fold_wide_body(const GsArgs& a) {
   constexpr int QB = kWideQB;
   constexpr size_t kRedBytes = sizeof(floatx4) * kGwWaves * QB * NT * kWave;
-  constexpr size_t kDlBytes = sizeof(uint16_t) * 32 * kFuseStride;
+  constexpr size_t kDlBytes = sizeof(uint16_t) * 16 * QB * kFuseStride;  // a batch's delta tile
   __shared__ GsSmem<PC, kGwThreads> sm;
   __shared__ uint64_t btab[NP][PC];
   __shared__ float bscale[NP][PC];
   __shared__ uint64_t atab2[NP > 1 ? PC : 1];
-  // xa of a batch; whole 32-row passes of the fold read it
+  // xa of a batch (up to 64 rows of room), which the fold reads
   __shared__ __attribute__((aligned(16))) uint16_t xl[32 * ((QB + 1) / 2) * kXlStride];
   __shared__ __attribute__((aligned(16))) unsigned char buf[kRedBytes > kDlBytes ? kRedBytes
                                                                                 : kDlBytes];
