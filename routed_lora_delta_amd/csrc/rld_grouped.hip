@@ -980,10 +980,37 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
 #pragma unroll
               for (int j = 0; j < NT; ++j) acc1[q][j] = chain(v, a1[j]);
             };
+            // A third subtile (rows 32..47) goes out with the first two, but to
+            // LDS (direct loads, no registers): each lane's four 16-byte
+            // fragments land at lane * 16 in four 1 KB pieces of this wave's
+            // wave-sum entries of subtiles 1 and 2 (4 KB at NT = 2), which are
+            // written only after the pieces are read back.  At NT = 1 those
+            // entries hold 2 KB: the third subtile is a second round of loads.
+            const bool third = NT >= 2 && QB > 2 && nb > 32;
+            auto stage_x2 = [&]() {
+              static_assert(KS * kWave * 16 <= (QB * NT - NT) * kWave * (int)sizeof(floatx4) ||
+                                NT < 2,
+                            "the staged subtile fits the wave's entries of subtiles 1 and 2");
+              int tl = (int)threadIdx.x;  // laundered: the offsets are not hoisted
+              asm volatile("" : "+v"(tl));
+              const int li = 32 + (tl & 15);
+              const uint32_t xk0 = (uint32_t)(tl >> 6) * (32u * KS) + 8u * ((tl >> 4) & 3);
+              const RLD_GLOBAL uint16_t* xr =
+                  x + (size_t)sm.xrow[b0 + (li < nb ? li : 0)] * a.xs;
+              unsigned char* st = reinterpret_cast<unsigned char*>(&red[wave][NT][0]);
+#pragma unroll
+              for (int ks = 0; ks < KS; ++ks) {
+                const uint32_t kk = xk0 + 32u * ks;
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(full ? xr + kk : xr + (kk < k_in ? kk : 0)),
+                    (__attribute__((address_space(3))) void*)(st + ks * kWave * 16), 16, 0, 0);
+              }
+            };
             {
               uint4 xq[2][KS];
               load_x(xq[0], 0);
               load_x(xq[1], 1);
+              if (third) stage_x2();
               issue_point();
               if (!full) {
                 mask_a_to(bop);
@@ -992,9 +1019,27 @@ __device__ void gs_wide_item(const GsArgs& a, GsSmem<PC, kGwThreads>& sm,
                 mask_x(xq[1]);
               }
               mfma_both(xq[0], 0);
-              mfma_both(xq[1], 1);
+              if (third) {
+                // subtile 1's first-projection chains wait in registers while
+                // the third subtile is read back from where they go
+                floatx4 g1[NT];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) g1[j] = chain(xq[1], bop[j]);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc1[1][j] = chain(xq[1], a1[j]);
+                uint4 x2[KS];
+                const uint4* st = reinterpret_cast<const uint4*>(&red[wave][NT][0]);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) x2[ks] = st[ks * kWave + lane];
+                if (!full) mask_x(x2);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) red[wave][NT + j][lane] = g1[j];
+                mfma_both(x2, 2);
+              } else {
+                mfma_both(xq[1], 1);
+              }
             }
-            if (QB > 2 && nb > 32) {
+            if (NT < 2 && QB > 2 && nb > 32) {
               uint4 x2[KS];
               issue_point();  // not hoisted above the first subtiles' MFMAs
               load_x(x2, 2);
