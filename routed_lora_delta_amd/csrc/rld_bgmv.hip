@@ -387,8 +387,14 @@ __device__ void shrink_item(const BgmvArgs& a, uint32_t w, ShrinkSmem<NT, NW, QT
 }
 
 // Expand item (slot s, 64*MT output columns from j0).  NKS = ceil(max_rank/32).
+// With zcount = 2 or 4 (routed launches over more than 64 rows) the slot's rows
+// of a decode batch are split between that many items: part z folds rows
+// [z * P, (z + 1) * P) of the slot's list, P = 128 / zcount, so that a heavily
+// routed slot's rows run beside each other instead of one batch after another
+// (each row's arithmetic is the same either way).
 template <int NKS, int MT>
-__device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem<MT>& sm) {
+__device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem<MT>& sm,
+                            uint32_t zpart = 0, uint32_t zcount = 1) {
   constexpr int kCols = ExpandSmem<MT>::kCols;
   constexpr int kStride = ExpandSmem<MT>::kStride;
   constexpr int kRowVecs = kCols / 8;            // 16-byte vectors per row of the tile
@@ -418,7 +424,7 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem<MT
   const int c8 = (threadIdx.x % kRowVecs) * 8;
   const bool fcol_ok = j0 + c8 < n_out;
 
-  // rows b0 .. b0+63 of the slot's list
+  // rows b0 .. min(b0 + 64, cnt) - 1 of the slot's list
   auto batch = [&](int b0, int cnt) {
     const int nb = min(cnt - b0, kExpRows);
     // One round of loads: the B_s rows of this wave's 16*MT columns as MFMA A
@@ -503,11 +509,18 @@ __device__ void expand_item(const BgmvArgs& a, int s, uint32_t j0, ExpandSmem<MT
   if (n <= 256) {
     const int cnt = append_hits(key0 == s, threadIdx.x, sm.rows, 0, sm.wcount);
     if (cnt <= 2 * kExpRows) {
-      if (cnt > 0) batch(0, cnt);
-      if (cnt > kExpRows) batch(kExpRows, cnt);
+      if (zcount == 1) {
+        if (cnt > 0) batch(0, cnt);
+        if (cnt > kExpRows) batch(kExpRows, cnt);
+      } else {
+        const int part = 2 * kExpRows / (int)zcount;
+        const int r0 = (int)zpart * part;
+        if (r0 < cnt) batch(r0, min(r0 + part, cnt));
+      }
       return;
     }
   }
+  if (zpart != 0) return;  // part 0 folds every batch of the general case
   uint32_t pos = 0;
   while (pos < n) {
     const int cnt = collect_slot_rows(a.seq_slot(), n, &pos, s, sm.rows, sm.wcount, key0);
@@ -840,7 +853,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NKS <= 2 ? 
 template <int NKS, int MT>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(BgmvArgs a) {
   __shared__ ExpandSmem<MT> sm;
-  expand_item<NKS, MT>(a, (int)blockIdx.y, blockIdx.x * ExpandSmem<MT>::kCols, sm);
+  expand_item<NKS, MT>(a, (int)blockIdx.y, blockIdx.x * ExpandSmem<MT>::kCols, sm, blockIdx.z,
+                       gridDim.z);
 }
 
 // Several routes over the same rows (rld_bgmv_multi): one launch of each
@@ -1119,8 +1133,12 @@ extern "C" int rld_bgmv_expand_fold(const rld_route* route, const void* xa,
   a.os = out_row_stride;
   const uint32_t tiles = div_ceil(route->n_out, 64u * kExpMT);
   static_assert(ExpandLeanSmem::kCols == 64 * kExpMT, "both expands take 256-column tiles");
+  // the classic item splits a slot's rows of a batch over four items (grid z)
+  // once a slot can hold more than one 64-row batch
+  const bool classic = (uint64_t)tiles * route->max_loras <= kClassicExpandResident;
+  const uint32_t zc = classic && n > (uint32_t)kExpRows ? 4u : 1u;
   hipLaunchKernelGGL(pick_expand_routed(a.R, tiles, route->max_loras),
-                     dim3(tiles, route->max_loras), dim3(256), 0,
+                     dim3(tiles, route->max_loras, zc), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), a);
   return launch_status();
 }
