@@ -65,6 +65,11 @@ BGMV_SHAPES = [
     (90, 512, 6144, 48, 40, (16, 48), ()),
     (64, 256, 4096, 128, 64, (64, 128), ()),
     (257, 768, 3336, 8, 80, (4, 8), (2,)),
+    # the classic expand's four row parts (n > 64): a slot of more than 128 of
+    # 256 rows (the general path, part 0 alone) beside one of 65-128 rows
+    # (three or four parts), and one slot holding every active row of 128
+    (256, 1024, 1032, 64, 2, (64,), ()),
+    (128, 2048, 1032, 32, 1, (32,), ()),
 ]
 
 
