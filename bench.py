@@ -24,7 +24,9 @@ calls the same way after a replay of the captured grouped part (region C), so
 the host is always ahead of the GPU and an event pair brackets exactly one
 call.  The kernel with the largest total time is reported against its
 roofline: achieved = its algorithmic bytes per launch / its mean launch
-duration.
+duration.  Each workload is also captured alone, its independent calls on
+parallel branches as in the step, and timed as that graph after a replay of
+the rest of the step (per_workload[*].graph).
 Algorithmic bytes are counted from the actual inputs: x rows that fold, A and
 B of each distinct (slot[, expert]) pair a call touches, the base rows read
 and written, xa written and read, and the index arrays.
@@ -674,6 +676,21 @@ def _timed_eager(step, idx, lead_graph, steps, torch):
                      for evs in evsets]).mean(axis=0)
 
 
+def _timed_graph(graph, lead_graph, steps, torch):
+    """K times: replay lead_graph, then `graph` between two HIP events on the
+    launch stream.  Returns the median replay duration in ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        lead_graph.replay()
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+
 def _timed_by_kernel(step, lead_graph, steps, torch):
     """Per-kernel launch duration: K times, replay lead_graph (so the host runs
     ahead), then for each kernel issue all of its launches of the step back to
@@ -827,6 +844,14 @@ def run_gpu(args, traffic=True):
                "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         if tag == "grouped":
             ent["mfma_util"] = round(fl / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)
+        # the workload alone as the step issues it (its independent calls on
+        # parallel graph branches), after a replay of the rest of the step
+        if len(wls) > 1:
+            wsel = [a for a, _ in (segs[j] for j in sel)]
+            lead = g_other if tag == "grouped" else g_grouped
+            gms = _timed_graph(capture(wsel, parallel=True), lead, args.steps, torch)
+            ent["graph"] = {"ms": round(gms, 5), "gbs": round(by / (gms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(by / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         # the workload's dominant kernel against the HBM roofline (its launches
         # of this workload; per-launch time from the back-to-back timing)
         wk = {}
