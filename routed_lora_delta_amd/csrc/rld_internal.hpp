@@ -12,7 +12,8 @@ void record_hip_error(hipError_t e);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool mult8(uint64_t v) { return (v & 7u) == 0; }
-inline uint32_t div_ceil(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+// ceil(a / b) without the wrap of a + b - 1 near 2^32
+inline uint32_t div_ceil(uint32_t a, uint32_t b) { return a / b + (a % b != 0u ? 1u : 0u); }
 
 // Checks common to every route: dims non-zero, multiples of 8, rank bound.
 inline int check_dims(uint32_t k_in, uint32_t n_out, uint32_t max_rank) {

@@ -144,7 +144,10 @@ def test_pack_expert_tables_matches_oracle(ids):
 
 
 @pytest.mark.parametrize("total,cap", [(0, 8192), (1, 8192), (32768, 8192), (32769, 8192),
-                                       (300, 100), (300, 64), (8191, 8192), (5, 1)])
+                                       (300, 100), (300, 64), (8191, 8192), (5, 1),
+                                       # totals and caps near 2^32: no wrap in the ceil
+                                       (0xFFFFFFFF, 0x80000000), (0xFFFFFFFF, 0xFFFFFFFF),
+                                       (0xFFFFFFFE, 0x7FFFFFFF), (0xFFFFFFFF, 0x10000000)])
 def test_grouped_windows_and_wc_match_oracle(total, cap):
     mx = 1024
     st = np.zeros(mx, np.uint32)
