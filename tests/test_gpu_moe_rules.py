@@ -346,3 +346,153 @@ def test_gather_graph_new_routing_each_replay():
         assert np.array_equal(out_g.reshape(wl.n_rows, wl.n_out)[inactive], b2[inactive])
         assert np.all(xa_g[inactive] == 0)
         _ = torch.ones(1 << 20, device=dev).sum().item()  # eager work between replays
+
+
+# ------------------------------------------------------------ row strides --
+#
+# Every entry point takes element row strides for x and for the folded output
+# ("Function apply_lora_bgmv", STRIDES paragraph): a fold may land inside a
+# wider row.  The MoE folds read x rows at x + row * x_row_stride and fold
+# [0, n_out) of base_out + row * out_row_stride; the rest of each row is left
+# untouched.
+
+def _strided(rows_bits, width, stride, rng):
+    """rows_bits [rows, width] inside a buffer of rows x stride BF16 values whose
+    gaps hold other values (finite, so that a stray read would show)."""
+    rows = rows_bits.reshape(-1, width)
+    buf = (rng.integers(0x3C00, 0x4000, size=(rows.shape[0], stride))).astype(np.uint16)
+    buf[:, :width] = rows
+    return buf
+
+
+@pytest.mark.parametrize("separate", [False, True])
+@pytest.mark.parametrize("rank", [16, 24])
+def test_gather_strided_rows(rank, separate):
+    """The gather fold with x rows of stride k_in + 40 and outputs of stride
+    n_out + 24 (the three-round path at rank 16, the general one at rank 24):
+    xa and the folded [0, n_out) of every row meet the oracle's strided fold;
+    the rest of each output row is bit-exact."""
+    dev = require_gpu()
+    wl = W.moe_gather(num_tokens=13, top_k=6, num_experts=40, k_in=1000, n_out=520, max_loras=5,
+                      n_adapted=25, ranks=(8, rank), max_rank=rank)
+    rng = np.random.default_rng(41)
+    xs, os_ = wl.k_in + 40, wl.n_out + 24
+    xbuf = _strided(wl.x, wl.k_in, xs, rng)
+    bbuf = _strided(wl.base, wl.n_out, os_, rng)
+    say(f"case: gather strided rows rank {rank} separate={separate}")
+    route = MoeRoute(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank, wl.k_in, wl.n_out,
+                     dev)
+    x = to_device_u16(xbuf.ravel(), dev)
+    base = Guarded(bbuf.ravel(), dev)
+    idx = dev_i32(wl.indices, dev)
+    rad = dev_i32(wl.row_adapter, dev)
+    xa = torch.zeros(wl.n_rows * wl.max_rank + 8, dtype=torch.int16, device=dev)
+    if separate:
+        R.check(R.rld_moe_gather_shrink(route.route, x, xs, idx, rad, wl.top_k, wl.n_rows, xa),
+                "rld_moe_gather_shrink")
+        R.check(R.rld_moe_gather_expand_fold(route.route, xa, idx, rad, wl.top_k, wl.n_rows,
+                                             base.ptr(), os_), "rld_moe_gather_expand_fold")
+    else:
+        R.check(R.rld_moe_gather(route.route, x, xs, idx, rad, wl.top_k, wl.n_rows, base.ptr(),
+                                 os_, xa), "rld_moe_gather")
+    torch.cuda.synchronize()
+    xa_g = from_device_u16(xa)[: wl.n_rows * wl.max_rank].reshape(wl.n_rows, wl.max_rank)
+    out_g = base.body().reshape(wl.n_rows, os_)
+    pairs = O.pack_expert_pairs(wl.adapters, wl.max_loras, wl.num_experts, wl.max_rank)
+    xa_o, out_o = O.moe_gather(pairs, wl.num_experts, wl.k_in, wl.n_out, wl.max_rank,
+                               xbuf.ravel(), xs, wl.indices, wl.row_adapter, wl.top_k, wl.n_rows,
+                               bbuf.ravel(), os_)
+    out_o = out_o.reshape(wl.n_rows, os_)
+    assert_xa_close(xa_g, xa_o, "strided gather xa", abs_sums_gather(wl),
+                    shrink_depth("gather", wl.k_in, wl.max_rank))
+    assert_out_close(out_g[:, :wl.n_out].ravel(), out_o[:, :wl.n_out].ravel(),
+                     "strided gather out")
+    assert np.array_equal(out_g[:, wl.n_out:], bbuf[:, wl.n_out:]), "row gaps changed"
+
+
+@pytest.mark.parametrize("call", ["fold", "separate", "pair"])
+def test_grouped_strided_rows(call):
+    """The grouped fold with strided rows: gate (x gathered by token from rows of
+    stride hidden + 24) and down (sorted x rows of stride inter + 40), outputs
+    of stride n_out + 40 and n_out + 16; through rld_moe_grouped, the two stage
+    entry points, or rld_moe_grouped_pair for gate and up.  xa and the folded
+    [0, n_out) of every row meet the oracle's strided fold over every window;
+    the rest of each output row is bit-exact."""
+    dev = require_gpu()
+    wl = _small(seed=9, hidden=1040, inter=264)
+    rng = np.random.default_rng(43)
+    byname = {p.name: p for p in wl.projections}
+    names = ["gate", "up"] if call == "pair" else ["gate", "down"]
+    wins = grouped_windows(wl.te, wl.cap)
+    off = dev_i32(wl.expert_offsets, dev)
+    stid = dev_i32(wl.sorted_token_ids, dev)
+    rad = dev_i32(wl.row_adapter, dev)
+    st = {}
+    for name in names:
+        p = byname[name]
+        xs = p.k_in + (24 if p.x_gather else 40)
+        os_ = p.n_out + (40 if name != "up" else 16)
+        xbuf = _strided(p.x, p.k_in, xs, rng)
+        bbuf = _strided(p.base, p.n_out, os_, rng)
+        route = MoeRoute(p.adapters, wl.max_loras, wl.num_experts, wl.max_rank, p.k_in, p.n_out,
+                         dev)
+        wsb = R.rld_moe_grouped_workspace_bytes(wl.cap, p.k_in, wl.max_rank, wl.max_loras,
+                                                wl.num_experts)
+        st[name] = dict(p=p, xs=xs, os=os_, xbuf=xbuf, bbuf=bbuf, route=route,
+                        x=to_device_u16(xbuf.ravel(), dev), base=Guarded(bbuf.ravel(), dev),
+                        xa=torch.zeros(wl.cap * wl.max_rank + 8, dtype=torch.int16, device=dev),
+                        ws=torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev), wsb=wsb,
+                        xas=[])
+    say(f"case: grouped strided rows via {call}")
+
+    def keep_xa(s, lo, hi):
+        torch.cuda.synchronize()
+        s["xas"].append(from_device_u16(s["xa"])[: (hi - lo) * wl.max_rank]
+                        .reshape(hi - lo, wl.max_rank).copy())
+
+    for lo, hi in wins:
+        if call == "pair":
+            a, b = st["gate"], st["up"]
+            R.check(R.rld_moe_grouped_pair(a["route"].route, b["route"].route, a["x"], a["xs"],
+                                           a["p"].x_gather, wl.num_tokens, off, wl.num_experts,
+                                           stid, rad, lo, hi, a["base"].ptr(), a["os"],
+                                           b["base"].ptr(), b["os"], a["xa"], b["xa"], wl.cap,
+                                           a["ws"], a["wsb"]), "rld_moe_grouped_pair")
+            keep_xa(a, lo, hi)
+            keep_xa(b, lo, hi)
+            continue
+        for s in st.values():
+            p = s["p"]
+            if call == "separate":
+                R.check(R.rld_moe_grouped_shrink(s["route"].route, s["x"], s["xs"], p.x_gather,
+                                                 wl.num_tokens, off, wl.num_experts, stid, rad,
+                                                 lo, hi, s["xa"], wl.cap, s["ws"], s["wsb"]),
+                        "rld_moe_grouped_shrink")
+                R.check(R.rld_moe_grouped_expand_fold(s["route"].route, s["xa"], wl.num_tokens,
+                                                      off, wl.num_experts, stid, rad, lo, hi,
+                                                      s["base"].ptr(), s["os"]),
+                        "rld_moe_grouped_expand_fold")
+            else:
+                R.check(R.rld_moe_grouped(s["route"].route, s["x"], s["xs"], p.x_gather,
+                                          wl.num_tokens, off, wl.num_experts, stid, rad, lo, hi,
+                                          s["base"].ptr(), s["os"], s["xa"], wl.cap, s["ws"],
+                                          s["wsb"]), "rld_moe_grouped")
+            keep_xa(s, lo, hi)
+    torch.cuda.synchronize()
+    for name, s in st.items():
+        p = s["p"]
+        pairs = O.pack_expert_pairs(p.adapters, wl.max_loras, wl.num_experts, wl.max_rank)
+        out_o = s["bbuf"].ravel()
+        for (lo, hi), xa_g in zip(wins, s["xas"]):
+            xa_o, out_o = O.moe_grouped(pairs, wl.num_experts, p.k_in, p.n_out, wl.max_rank,
+                                        s["xbuf"].ravel(), s["xs"], p.x_gather, wl.num_tokens,
+                                        wl.expert_offsets, wl.sorted_token_ids, wl.row_adapter,
+                                        lo, hi, out_o, s["os"])
+            assert_xa_close(xa_g, xa_o, f"strided {name} xa [{lo},{hi})",
+                            abs_sums_grouped(wl, p, lo, hi),
+                            shrink_depth("grouped", p.k_in, wl.max_rank))
+        out_g = s["base"].body().reshape(wl.te, s["os"])
+        out_o = out_o.reshape(wl.te, s["os"])
+        assert_out_close(out_g[:, :p.n_out].ravel(), out_o[:, :p.n_out].ravel(),
+                         f"strided {name} out")
+        assert np.array_equal(out_g[:, p.n_out:], s["bbuf"][:, p.n_out:]), f"{name}: row gaps"
