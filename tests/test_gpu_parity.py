@@ -349,7 +349,7 @@ def test_bgmv_shared_workspace_second_pass():
 # ------------------------------------------------------------------ gather ---
 
 @pytest.mark.parametrize("variant", ["config", "null_adapter", "ragged", "ragged_rank16",
-                                     "many_pairs"])
+                                     "many_pairs", "rank128"])
 def test_moe_gather(variant):
     """The gather fold against the oracle: the MoE decode config, no row_adapter,
     and ragged shapes with out-of-range expert ids and slots (rank 24: the
@@ -372,6 +372,10 @@ def test_moe_gather(variant):
     elif variant == "many_pairs":
         wl = W.moe_gather(num_tokens=24, top_k=8, num_experts=128, k_in=768, n_out=2048,
                           max_loras=9, n_adapted=64, max_rank=16)
+        ra = "wl"
+    elif variant == "rank128":  # the largest max_rank the boundary takes
+        wl = W.moe_gather(num_tokens=13, top_k=6, num_experts=40, k_in=1000, n_out=520,
+                          max_loras=5, n_adapted=25, ranks=(64, 128), max_rank=128)
         ra = "wl"
     else:
         wl = W.moe_gather(num_tokens=13, top_k=6, num_experts=40, k_in=1000, n_out=520,
@@ -690,7 +694,8 @@ def test_moe_grouped_large_route(max_loras, num_experts):
 @pytest.mark.parametrize("k_in,max_rank,proj,n_out", [
     (2048, 32, "gate", 264), (1032, 16, "gate", 264), (1544, 32, "down", 264),
     (2048, 24, "down", 264), (1160, 32, "gate", 264), (768, 32, "down", 2048),
-    (264, 16, "down", 1032), (520, 64, "gate", 264), (1032, 48, "gate", 264)])
+    (264, 16, "down", 1032), (520, 64, "gate", 264), (1032, 48, "gate", 264),
+    (520, 128, "gate", 264), (264, 128, "down", 1032)])
 @pytest.mark.parametrize("separate", [False, True])
 def test_moe_grouped_wide(k_in, max_rank, proj, n_out, separate):
     """1024 < k_in <= 2048 at max_rank <= 32: one sixteen-wave block per pair
