@@ -70,6 +70,8 @@ BGMV_SHAPES = [
     # (three or four parts), and one slot holding every active row of 128
     (256, 1024, 1032, 64, 2, (64,), ()),
     (128, 2048, 1032, 32, 1, (32,), ()),
+    # a thousand slots, most of them without a row of the batch
+    (64, 1024, 264, 16, 1000, (8, 16), ()),
 ]
 
 
@@ -131,12 +133,14 @@ def test_bgmv_out_of_range_slots_and_missing_tables():
             assert np.all(run.xa_by_call[0][r] == 0)
 
 
-@pytest.mark.parametrize("case", ["attn_qkv", "ffn_gate_up", "small_one_chunk"])
+@pytest.mark.parametrize("case", ["attn_qkv", "ffn_gate_up", "small_one_chunk", "four_routes"])
 def test_bgmv_multi_equals_separate_calls(case):
     """rld_bgmv_multi over routes that read the same rows is bit-identical, xa
     and every output buffer, to rld_bgmv on each route alone: q, k and v of
     the attention decode (the K and V folds inside [Q|K|V] rows), gate and up
-    of the FFN decode (k split, rank 64), and a one-chunk shape."""
+    of the FFN decode (k split, rank 64), a one-chunk shape, and the most
+    routes a call takes (four, k split at rank 32, different n_out and
+    max_loras)."""
     dev = require_gpu()
     if case == "attn_qkv":
         wl, mods = W.bgmv_attn_decode(), ("q", "k", "v")
@@ -150,6 +154,14 @@ def test_bgmv_multi_equals_separate_calls(case):
         wl = W.BgmvWorkload("two routes", a.n, a.seq_slot,
                             {**a.buffers, "out2": b.buffers["out"]}, [a.calls[0], c2])
         mods = None
+    if case == "four_routes":
+        parts = [W.bgmv_custom(s, 90, 1024, n_out, 32, L, (8, 32), base_frac=0.1, zipf=1.1)
+                 for s, n_out, L in ((5, 264, 3), (6, 136, 5), (7, 520, 4), (8, 1032, 6))]
+        calls, bufs = [], {"x": parts[0].buffers["x"]}
+        for j, w in enumerate(parts):
+            calls.append(dataclasses.replace(w.calls[0], module=f"proj{j}", out_buf=f"out{j}"))
+            bufs[f"out{j}"] = w.buffers["out"]
+        wl = W.BgmvWorkload("four routes", 90, parts[0].seq_slot, bufs, calls)
     idx = [i for i, c in enumerate(wl.calls) if mods is None or c.module in mods]
     say(f"case: bgmv multi {case} routes={len(idx)}")
     sep = BgmvRun(wl, dev)
