@@ -29,7 +29,10 @@ parallel branches as in the step, and timed as that graph after a replay of
 the rest of the step (per_workload[*].graph).
 Algorithmic bytes are counted from the actual inputs: x rows that fold, A and
 B of each distinct (slot[, expert]) pair a call touches, the base rows read
-and written, xa written and read, and the index arrays.
+and written, xa written and read, and the index arrays.  A launch that folds
+two calls counts both calls' bytes; for the MoE gate+up pair launch, which
+reads the shared x once and never reads xa back, the roofline objects also
+give the rate on the bytes that launch itself must move (read_once_*).
 
 The CPU oracle (test infrastructure) is timed on a bounded sample of the same
 step for the cpu_baseline field only.
@@ -87,13 +90,20 @@ def gather_bytes(wl):
     return shrink, expand, 2 * act * R * (wl.k_in + wl.n_out), act
 
 
-def grouped_window_bytes(wl, p, lo, hi):
+def _grouped_active(wl, p, lo, hi):
+    """Sorted rows [lo, hi) that projection p folds: (active mask, token ids,
+    slots, experts)."""
     pairs = {(a.slot, a.expert) for a in p.adapters}
     toks = wl.sorted_token_ids[lo:hi]
     exps = wl.sorted_expert[lo:hi]
     slots = (wl.row_adapter[toks] if wl.row_adapter is not None
              else np.zeros(hi - lo, np.int32))
     act = np.array([(int(s), int(e)) in pairs for s, e in zip(slots, exps)], bool)
+    return act, toks, slots, exps
+
+
+def grouped_window_bytes(wl, p, lo, hi):
+    act, toks, slots, exps = _grouped_active(wl, p, lo, hi)
     S = len({(int(s), int(e)) for s, e, a in zip(slots, exps, act) if a})
     n_act, R, nw = int(act.sum()), wl.max_rank, hi - lo
     x_rows = len(set(toks[act].tolist())) if p.x_gather else n_act
@@ -101,6 +111,22 @@ def grouped_window_bytes(wl, p, lo, hi):
     shrink = 2 * (x_rows * p.k_in + S * R * p.k_in + nw * R) + idx
     expand = 2 * (S * p.n_out * R + n_act * R + 2 * n_act * p.n_out) + idx
     return shrink, expand, 2 * n_act * R * (p.k_in + p.n_out), n_act
+
+
+def grouped_pair_read_once_bytes(wl, p, q, lo, hi):
+    """What one launch folding projections p and q of window [lo, hi) over the
+    same gathered x must itself move: the two calls' bytes of
+    grouped_window_bytes with x read once, over the union of the tokens either
+    projection folds, and without the xa read-back (the launch writes xa and
+    keeps it on chip for the fold)."""
+    sb, eb, _, _ = grouped_window_bytes(wl, p, lo, hi)
+    sb2, eb2, _, _ = grouped_window_bytes(wl, q, lo, hi)
+    ap, toks, _, _ = _grouped_active(wl, p, lo, hi)
+    aq, _, _, _ = _grouped_active(wl, q, lo, hi)
+    xp, xq = len(set(toks[ap].tolist())), len(set(toks[aq].tolist()))
+    xu = len(set(toks[ap | aq].tolist()))
+    return (sb + eb + sb2 + eb2 - 2 * p.k_in * (xp + xq - xu)
+            - 2 * wl.max_rank * int(ap.sum() + aq.sum()))
 
 
 # ------------------------------------------------------ counters and profiles --
@@ -314,6 +340,9 @@ class Step:
 
         self.R, self.torch = R, torch
         self.calls = []  # (label, kernel name, fn, algorithmic bytes, flops, rows)
+        # label -> bytes a fused launch itself moves (inputs shared by its calls
+        # read once, no xa read-back), where that differs from the calls' sum
+        self.read_once = {}
         self.outputs = {}  # "<workload>.<buffer or projection>" -> device output tensor
         self.sched = []  # (group, lane) of each call
         self.rows = 0
@@ -517,9 +546,10 @@ class Step:
                                     off, wl.num_experts, stid, rad, lo, hi, base, p.n_out,
                                     base_b, q.n_out, xa, xa_b, wl.cap, ws, wsb)
 
-                            add((f"grouped.gate+up.[{lo},{hi}).fold", "grouped_fold_pair_kernel",
-                                 pair, sb + eb + sb2 + eb2, fl + fl2, 2 * (hi - lo)), p.name, lane,
-                                wgroup)
+                            label = f"grouped.gate+up.[{lo},{hi}).fold"
+                            add((label, "grouped_fold_pair_kernel", pair, sb + eb + sb2 + eb2,
+                                 fl + fl2, 2 * (hi - lo)), p.name, lane, wgroup)
+                            self.read_once[label] = grouped_pair_read_once_bytes(wl, p, q, lo, hi)
                             continue
 
                         def shrink(rt=rt, x=x, p=p, lo=lo, hi=hi, off=off, stid=stid, rad=rad,
@@ -719,6 +749,18 @@ def _timed_by_kernel(step, lead_graph, steps, torch):
     return out
 
 
+def _read_once_fields(read_once, avg_launch_s):
+    """For a fused kernel: its achieved rate and fraction of peak on the bytes
+    the launch itself must move (read_once_bytes_per_launch), beside the
+    per-call figure that `achieved` uses.  Empty for other kernels."""
+    if not read_once or any(v is None for v in read_once):
+        return {}
+    b = sum(read_once) / len(read_once)
+    a = b / avg_launch_s / 1e9
+    return {"read_once_bytes_per_launch": int(b), "read_once_achieved": round(a, 1),
+            "read_once_frac": round(a / HBM_PEAK_GBS, 4)}
+
+
 def launch_floor_us(torch, dev, lead_graph, launches=200):
     """The empty-launch floor: a one-element fill kernel issued `launches`
     times back to back on the launch stream after a lead replay (the host
@@ -827,6 +869,7 @@ def run_gpu(args, traffic=True):
     bytes_per_launch = dom["bytes"] / dom["launches"]
     achieved = bytes_per_launch / avg_launch_s / 1e9
     traffic = measured_traffic(dom_name, args.workload) if traffic else None
+    read_once = [step.read_once.get(c[0]) for c in step.calls if c[1] == dom_name]
 
     per_workload = {}
     for tag, _ in wls:
@@ -866,7 +909,9 @@ def run_gpu(args, traffic=True):
                            "frac": round(kach / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic(kn, args.workload) if traffic else None,
                            "algo_bytes_per_launch": int(kb / nl),
-                           "avg_launch_us": round(kernel_ms[kn] * 1e3, 3), "launches": nl}
+                           "avg_launch_us": round(kernel_ms[kn] * 1e3, 3), "launches": nl,
+                           **_read_once_fields([step.read_once.get(c[0]) for c in calls
+                                                if c[1] == kn], kernel_ms[kn] * 1e-3)}
         per_workload[tag] = ent
 
     kern_out = {k: {"launches_per_step": v["launches"],
@@ -888,7 +933,8 @@ def run_gpu(args, traffic=True):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algo_bytes_per_launch": int(bytes_per_launch),
                      "avg_launch_us": round(avg_launch_s * 1e6, 3),
-                     "launches_per_step": dom["launches"]},
+                     "launches_per_step": dom["launches"],
+                     **_read_once_fields(read_once, avg_launch_s)},
         "kernels": kern_out,
         "per_workload": per_workload,
         "launch_floor_us": round(floor_us, 3),
