@@ -30,9 +30,10 @@ the rest of the step (per_workload[*].graph).
 Algorithmic bytes are counted from the actual inputs: x rows that fold, A and
 B of each distinct (slot[, expert]) pair a call touches, the base rows read
 and written, xa written and read, and the index arrays.  A launch that folds
-two calls counts both calls' bytes; for the MoE gate+up pair launch, which
-reads the shared x once and never reads xa back, the roofline objects also
-give the rate on the bytes that launch itself must move (read_once_*).
+two calls counts both calls' bytes; for the launches that read a shared x
+once or keep xa on chip (the MoE gate+up pair launch, the BGMV one-pass form)
+the roofline objects also give the rate on the bytes that launch itself must
+move (read_once_*).
 
 The CPU oracle (test infrastructure) is timed on a bounded sample of the same
 step for the cpu_baseline field only.
@@ -72,6 +73,21 @@ def bgmv_bytes(wl, c):
     expand = 2 * (S * c.n_out * R + n_act * R + 2 * n_act * c.n_out) + idx
     flops = 2 * n_act * R * (c.k_in + c.n_out)
     return shrink, expand, flops, n_act
+
+
+def bgmv_read_once_bytes(wl, calls, onepass):
+    """What one launch serving BGMV calls over the same x rows must itself move:
+    the calls' bytes of bgmv_bytes with x read once, over the union of the rows
+    any call folds, and, in the one-pass form (which keeps xa on chip), without
+    the xa read-back."""
+    total, act_any, xa_back = 0, np.zeros(wl.n, bool), 0
+    for c in calls:
+        sb, eb, _, n_act = bgmv_bytes(wl, c)
+        act, _ = _bgmv_active(wl, c)
+        total += sb + eb - 2 * n_act * c.k_in
+        act_any |= act
+        xa_back += 2 * n_act * c.max_rank
+    return total + 2 * int(act_any.sum()) * calls[0].k_in - (xa_back if onepass else 0)
 
 
 def gather_bytes(wl):
@@ -426,8 +442,10 @@ class Step:
                                                 n, outs, oss, xas, mws, mwsb)
                     label = (ONEPASS if R.rld_bgmv_launches([r.route for r in rts], wl.n) == 1
                              else "bgmv_multi")
-                    add((f"{tag}.{'+'.join(c.module for c in first)}.multi", label, multi,
-                         sb, fl, wl.n * len(first)), c0.module, 0, lanes_map=lmap)
+                    mlabel = f"{tag}.{'+'.join(c.module for c in first)}.multi"
+                    add((mlabel, label, multi, sb, fl, wl.n * len(first)), c0.module, 0,
+                        lanes_map=lmap)
+                    self.read_once[mlabel] = bgmv_read_once_bytes(wl, first, label == ONEPASS)
                     self.rows += wl.n * len(first)
                 for c in wl.calls:
                     if any(c is f for f in in_multi):
@@ -456,6 +474,8 @@ class Step:
                                                   c.out_row_stride, xa, ws, wsb)
                             add((f"{tag}.{c.module}.fold", ONEPASS, fold, sb + eb, fl, wl.n),
                                 c.module, lanes_map=lmap)
+                            self.read_once[f"{tag}.{c.module}.fold"] = bgmv_read_once_bytes(
+                                wl, [c], True)
                             self.rows += wl.n
                             continue
 

@@ -5,8 +5,9 @@ measured launch time, so a miscount would misstate every fraction of peak).
 Per call the count is: the x rows that fold (for a gathered x, the distinct
 tokens), A and B of every distinct (slot[, expert]) pair the call touches, the
 base rows read and written, xa written and read, and the index arrays.  For the
-MoE gate+up pair launch the read-once figure takes x once over the union of the
-tokens either projection folds, and no xa read-back."""
+MoE gate+up pair launch and the BGMV one-pass form the read-once figure takes
+x once over the union of the rows (tokens) any of the launch's calls folds, and
+no xa read-back."""
 from __future__ import annotations
 
 import os
@@ -111,3 +112,21 @@ def test_read_once_fields():
     assert f["read_once_bytes_per_launch"] == 8000000
     assert abs(f["read_once_achieved"] - 800.0) < 1e-6
     assert abs(f["read_once_frac"] - 0.1) < 1e-9
+
+
+def test_bgmv_read_once_bytes_take_x_once():
+    wl = W.bgmv_attn_decode()
+    qkv = [c for c in wl.calls if c.module in ("q", "k", "v")]
+    total = sum(sum(B.bgmv_bytes(wl, c)[:2]) for c in qkv)
+    rows = [r for r in range(wl.n)
+            if any(int(wl.seq_slot[r]) in {a.slot for a in c.adapters} for c in qkv)]
+    n_acts = [B.bgmv_bytes(wl, c)[3] for c in qkv]
+    k_in, R = qkv[0].k_in, qkv[0].max_rank
+    x_dup = 2 * k_in * (sum(n_acts) - len(rows))
+    assert B.bgmv_read_once_bytes(wl, qkv, False) == total - x_dup
+    assert B.bgmv_read_once_bytes(wl, qkv, True) == total - x_dup - 2 * R * sum(n_acts)
+    # one call: only the xa read-back differs
+    c = qkv[0]
+    sb, eb, _, n_act = B.bgmv_bytes(wl, c)
+    assert B.bgmv_read_once_bytes(wl, [c], False) == sb + eb
+    assert B.bgmv_read_once_bytes(wl, [c], True) == sb + eb - 2 * R * n_act
