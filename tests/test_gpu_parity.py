@@ -319,10 +319,12 @@ def test_bgmv_delta_stage():
                         abs_sums_rows(xa_g[i][None], slots[s].B)[0], expand_depth("bgmv", R_))
 
 
-def test_bgmv_attn_decode_config():
+# each full-size configuration at its own seed and at a second one
+@pytest.mark.parametrize("seed_index", [1, 101], ids=lambda v: f"seed{v}")
+def test_bgmv_attn_decode_config(seed_index):
     """Qwen3-8B attention side: q contiguous, k/v folded inside [Q|K|V] rows."""
     dev = require_gpu()
-    wl = W.bgmv_attn_decode()
+    wl = W.bgmv_attn_decode(seed_index)
     say(f"case: {wl.name}")
     run = BgmvRun(wl, dev)
     run.run_all()
@@ -330,9 +332,10 @@ def test_bgmv_attn_decode_config():
     _base_rows_xa_zero(wl, run)
 
 
-def test_bgmv_ffn_decode_config():
+@pytest.mark.parametrize("seed_index", [2, 102], ids=lambda v: f"seed{v}")
+def test_bgmv_ffn_decode_config(seed_index):
     dev = require_gpu()
-    wl = W.bgmv_ffn_decode()
+    wl = W.bgmv_ffn_decode(seed_index)
     say(f"case: {wl.name}")
     run = BgmvRun(wl, dev)
     run.run_all()
@@ -360,8 +363,8 @@ def test_bgmv_shared_workspace_second_pass():
 
 # ------------------------------------------------------------------ gather ---
 
-@pytest.mark.parametrize("variant", ["config", "null_adapter", "ragged", "ragged_rank16",
-                                     "many_pairs", "rank128"])
+@pytest.mark.parametrize("variant", ["config", "config_seed103", "null_adapter", "ragged",
+                                     "ragged_rank16", "many_pairs", "rank128"])
 def test_moe_gather(variant):
     """The gather fold against the oracle: the MoE decode config, no row_adapter,
     and ragged shapes with out-of-range expert ids and slots (rank 24: the
@@ -370,6 +373,9 @@ def test_moe_gather(variant):
     dev = require_gpu()
     if variant == "config":
         wl = W.moe_gather()
+        ra = "wl"
+    elif variant == "config_seed103":
+        wl = W.moe_gather(seed_index=103)
         ra = "wl"
     elif variant == "null_adapter":
         wl = W.moe_gather(num_tokens=20, top_k=4, num_experts=16, k_in=264, n_out=1032,
@@ -561,7 +567,8 @@ def _grouped_step_sequence(wl, dev):
     return wins, xas, outs
 
 
-def test_moe_grouped_full_config():
+@pytest.mark.parametrize("seed_index", [4, 104], ids=lambda v: f"seed{v}")
+def test_moe_grouped_full_config(seed_index):
     """The MoE grouped prefill at full size (4096 tokens, top-8 of 128 experts,
     te = 32768 sorted rows in windows of 8192, down 768 -> 2048 and gate/up
     2048 -> 768 gathered, rank 32, 4 slots), through the step's own call
@@ -571,8 +578,8 @@ def test_moe_grouped_full_config():
     unadapted pair) bit-identical to the base.  The bench's step, issued
     eagerly on the same inputs, gives the same bits."""
     dev = require_gpu()
-    wl = W.moe_grouped()
-    say("case: grouped full config, step call sequence, every row")
+    wl = W.moe_grouped(seed_index)
+    say(f"case: grouped full config seed {seed_index}, step call sequence, every row")
     wins, xas, outs = _grouped_step_sequence(wl, dev)
     for p in wl.projections:
         say(f"case: grouped full config oracle {p.name} k_in={p.k_in} n_out={p.n_out}")
