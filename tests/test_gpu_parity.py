@@ -89,18 +89,34 @@ def test_bgmv_shapes(shape):
 
 
 def test_bgmv_gated_q_fold():
-    """A gated model's q projection writes [Q | gate] rows; the q delta folds into
-    the Q half (offset 0, row stride 2*n_out) before the two are de-interleaved,
-    and the gate half stays bit-identical (compare_bgmv checks every element of
-    the buffer outside the folded regions)."""
+    """A gated model's q projection writes rows of interleaved [Q | gate] values;
+    the q pair's delta folds over the whole q_proj width, at offset 0 of that
+    raw row, before the Q and gate values are de-interleaved (Qwen3 attention
+    LoRA weights page, the q pair's fold site).  The q adapter's B therefore has
+    2 * 4096 rows here, and the row stride is that width."""
+    dev = require_gpu()
+    n, k_in, q_width = 48, 4096, 2 * 4096
+    wl = W.bgmv_custom(12, n, k_in, q_width, 16, 16, (8, 16), base_frac=0.1,
+                       out_row_stride=q_width, out_offset=0)
+    say("case: gated q fold over the whole [Q|gate] row")
+    run = BgmvRun(wl, dev)
+    run.run_all()
+    compare_bgmv(run, "gated q")
+
+
+def test_bgmv_partial_row_fold():
+    """A fold that covers the first half of each output row (offset 0, row
+    stride 2 * n_out): the other half of every row stays bit-identical
+    (compare_bgmv checks every element of the buffer outside the folded
+    regions; the assertion below restates it for the second halves)."""
     dev = require_gpu()
     n, k_in, n_out = 48, 4096, 4096
     wl = W.bgmv_custom(12, n, k_in, n_out, 16, 16, (8, 16), base_frac=0.1,
                        out_row_stride=2 * n_out, out_offset=0)
-    say("case: gated q fold into [Q|gate] rows")
+    say("case: fold into the first half of each row")
     run = BgmvRun(wl, dev)
     run.run_all()
-    compare_bgmv(run, "gated q")
+    compare_bgmv(run, "partial row")
     out = run.outputs()["out"].reshape(n, 2 * n_out)
     assert np.array_equal(out[:, n_out:], wl.buffers["out"].reshape(n, 2 * n_out)[:, n_out:])
 
